@@ -1,0 +1,274 @@
+"""Pins of the fp64 drafter oracle (oracle/drafter.py): closed forms, invariants, special cases
+and brute force.  The composed forward pass has no worked example on the pages, so beyond these
+pins of its parts it is "parity unpinned".  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import drafter as od
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY = synth.workload("tiny-fp32").shape
+
+
+@pytest.fixture(scope="module")
+def tiny_w():
+    return {k: v.numpy() for k, v in synth.make_weights(TINY, seed=0).items()}
+
+
+def _hidden(n, seq=0, start=0):
+    return synth.make_hidden(TINY, n, seed=0, seq=seq, start=start).numpy()
+
+
+# ---- mixing + RMSNorm -------------------------------------------------------------------------
+
+def test_mix_weights_sum_to_one(tiny_w):
+    w = od.mix_weights(tiny_w["mix_logits"])
+    assert w.shape == (TINY.n_layers, TINY.n_target_layers)
+    assert np.all(np.abs(w.sum(1) - 1.0) < 1e-15) and np.all(w > 0)
+
+
+def test_one_hot_mix_selects_one_target_layer(tiny_w):
+    h = _hidden(10)
+    for i in range(TINY.n_target_layers):
+        W = dict(tiny_w)
+        lg = np.zeros_like(W["mix_logits"])
+        lg[:, i] = 1e4
+        W["mix_logits"] = lg
+        for l in range(TINY.n_layers):
+            c = od.context_features(TINY, W, l, h)
+            # w = (1, 0, 0) exactly in fp64, so the mix is h_i bit for bit
+            ref = od.rmsnorm(h[:, i, :].astype(np.float64), W["mix_norm_w"][l], TINY.rms_eps)
+            assert np.array_equal(c, ref)
+
+
+def test_equal_mix_logits_give_the_mean(tiny_w):
+    h = _hidden(5)
+    W = dict(tiny_w)
+    W["mix_logits"] = np.full_like(W["mix_logits"], 0.3)
+    c = od.context_features(TINY, W, 0, h)
+    mean = h.astype(np.float64).mean(axis=1)
+    ref = od.rmsnorm(mean, W["mix_norm_w"][0], TINY.rms_eps)
+    assert np.max(np.abs(c - ref)) < 1e-12
+
+
+def test_mixing_is_permutation_invariant(tiny_w):
+    h = _hidden(6)
+    perm = np.array([2, 0, 1])
+    W2 = dict(tiny_w)
+    W2["mix_logits"] = tiny_w["mix_logits"][:, perm]
+    a = od.context_features(TINY, tiny_w, 1, h)
+    b = od.context_features(TINY, W2, 1, h[:, perm, :])
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_rmsnorm_closed_form():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 33)) * rng.uniform(0.01, 10, size=(7, 1))
+    eps = 1e-6
+    y = od.rmsnorm(x, np.ones(33), eps)
+    ms = np.mean(x * x, axis=1)
+    assert np.allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-13, atol=0)
+    # direction is kept, the gain multiplies element-wise
+    g = rng.uniform(0.5, 1.5, 33)
+    assert np.allclose(od.rmsnorm(x, g, eps), y * g, rtol=1e-14)
+    assert np.all(np.sign(y) == np.sign(x))
+
+
+# ---- RoPE ---------------------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(1).standard_normal((1, 3, 64))
+    assert np.array_equal(od.rope(x, [0], 1e6), x)
+
+
+def test_rope_two_dims_is_complex_rotation():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 1, 2))
+    pos = np.array([0, 1, 7, 100, 4000])
+    y = od.rope(x, pos, 1e6)
+    z = (x[:, 0, 0] + 1j * x[:, 0, 1]) * np.exp(1j * pos)
+    assert np.allclose(y[:, 0, 0], z.real, atol=1e-12) and np.allclose(y[:, 0, 1], z.imag,
+                                                                         atol=1e-12)
+
+
+def test_rope_relative_position_property():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 128))
+    k = rng.standard_normal((1, 1, 128))
+    for p1, p2, s in [(5, 3, 100), (0, 17, 2000), (3000, 10, 77)]:
+        a = np.dot(od.rope(q, [p1], 1e6)[0, 0], od.rope(k, [p2], 1e6)[0, 0])
+        b = np.dot(od.rope(q, [p1 + s], 1e6)[0, 0], od.rope(k, [p2 + s], 1e6)[0, 0])
+        assert abs(a - b) < 1e-9
+        assert abs(np.linalg.norm(od.rope(q, [p1], 1e6)) - np.linalg.norm(q)) < 1e-12
+
+
+# ---- attention ----------------------------------------------------------------------------------
+
+def test_attention_single_key_returns_its_value():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, 64))
+    k = rng.standard_normal((1, 64))
+    v = rng.standard_normal((1, 64))
+    assert np.allclose(od.attention(q, k, v), np.repeat(v, 3, 0), atol=1e-15)
+
+
+def test_attention_identical_keys_average_values():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 32))
+    k = np.repeat(rng.standard_normal((1, 32)), 9, 0)
+    v = rng.standard_normal((9, 32))
+    assert np.allclose(od.attention(q, k, v), np.repeat(v.mean(0, keepdims=True), 4, 0),
+                       atol=1e-14)
+
+
+def test_attention_matches_explicit_loops():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((3, 8))
+    k = rng.standard_normal((5, 8)) * 3
+    v = rng.standard_normal((5, 8))
+    out = np.zeros((3, 8))
+    for i in range(3):
+        s = [sum(q[i, d] * k[j, d] for d in range(8)) / math.sqrt(8) for j in range(5)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        tot = sum(e)
+        for j in range(5):
+            out[i] += e[j] / tot * v[j]
+    assert np.allclose(od.attention(q, k, v), out, atol=1e-14)
+
+
+# ---- the composed forward: structure the pages fix ----------------------------------------------
+
+def _fwd(W, toks, h, **kw):
+    return od.drafter_forward(TINY, W, toks, 1, hidden=h, **kw)
+
+
+def test_block_attention_is_bidirectional(tiny_w):
+    """Changing a later block token changes the outputs of earlier mask positions."""
+    h = _hidden(64)
+    toks = [5] + [TINY.mask_token_id] * 7
+    a = _fwd(tiny_w, toks, h)["logits"]
+    toks2 = list(toks)
+    toks2[6] = 17
+    b = _fwd(tiny_w, toks2, h)["logits"]
+    assert np.max(np.abs(a[0] - b[0])) > 1e-6       # row 0 = block position 1 sees position 6
+
+
+def test_every_block_output_reaches_every_context_position(tiny_w):
+    h = _hidden(64)
+    toks = [5] + [TINY.mask_token_id] * 7
+    a = _fwd(tiny_w, toks, h)["logits"]
+    for p in (0, 31, 63):
+        h2 = h.copy()
+        h2[p] += 1.0
+        b = _fwd(tiny_w, toks, h2)["logits"]
+        assert np.all(np.max(np.abs(a - b), axis=1) > 1e-8)
+
+
+def test_mask_rows_differ(tiny_w):
+    """Positions make the identical [MASK] inputs produce different outputs."""
+    h = _hidden(64)
+    lg = _fwd(tiny_w, [5] + [TINY.mask_token_id] * 7, h)["logits"]
+    for i in range(1, lg.shape[0]):
+        assert np.max(np.abs(lg[i] - lg[0])) > 1e-6
+
+
+def test_incremental_ingest_equals_cold(tiny_w):
+    h = _hidden(64)
+    for l in range(TINY.n_layers):
+        k64, v64 = od.context_kv(TINY, tiny_w, l, h)
+        k56, v56 = od.context_kv(TINY, tiny_w, l, h[:56])
+        k8, v8 = od.context_kv(TINY, tiny_w, l, h[56:], pos0=56)
+        assert np.allclose(np.concatenate([k56, k8], 1), k64, atol=1e-13, rtol=0)
+        assert np.allclose(np.concatenate([v56, v8], 1), v64, atol=1e-13, rtol=0)
+    toks = [9] + [TINY.mask_token_id] * 7
+    cold = _fwd(tiny_w, toks, h)
+    warm = od.drafter_forward(TINY, tiny_w, toks, 1, ctx_kv=cold["ctx_kv"])
+    assert np.array_equal(cold["logits"], warm["logits"])
+
+
+def test_shared_kv_projection_equals_one_projection_over_both_sources(tiny_w):
+    """With W_kc = W_kd and W_vc = W_vd (the 'no KV split' ablation on the DFlare page), one
+    layer's attention equals a single K/V projection of [context features; block features],
+    written out here with explicit per-head loops."""
+    W = dict(tiny_w)
+    W["wk_ctx"], W["wv_ctx"] = W["wk_draft"], W["wv_draft"]
+    one = TINY.__class__(**{**TINY.__dict__, "n_layers": 1})
+    W1 = {k: (v[:1] if k not in ("embed", "lm_head", "final_norm_w") else v) for k, v in
+          W.items()}
+    h = _hidden(12)
+    toks = [3] + [one.mask_token_id] * 7
+    out = od.drafter_forward(one, W1, toks, 1, hidden=h, keep=True)["resid"][0]
+    # independent recomputation of layer 0's attention block output
+    c = od.context_features(one, W1, 0, h)
+    x = W1["embed"][toks].astype(np.float64)
+    xn = od.rmsnorm(x, W1["attn_norm_w"][0], one.rms_eps)
+    feats = np.concatenate([c, xn], 0)                                    # [12 + 8, H]
+    pos = np.arange(20)
+    K = od.rope((feats @ W1["wk_draft"][0].T.astype(np.float64)).reshape(20, 2, 64), pos, 1e6)
+    Vv = (feats @ W1["wv_draft"][0].T.astype(np.float64)).reshape(20, 2, 64)
+    Q = od.rope((xn @ W1["wq"][0].T.astype(np.float64)).reshape(8, 4, 64), pos[12:], 1e6)
+    o = np.zeros((8, 4, 64))
+    for hh in range(4):
+        g = hh // 2
+        for i in range(8):
+            s = np.array([np.dot(Q[i, hh], K[j, g]) for j in range(20)]) / 8.0
+            e = np.exp(s - s.max())
+            o[i, hh] = (e / e.sum()) @ Vv[:, g]
+    x = x + o.reshape(8, 256) @ W1["wo"][0].T.astype(np.float64)
+    xm = od.rmsnorm(x, W1["mlp_norm_w"][0], one.rms_eps)
+    gt = xm @ W1["w_gate"][0].T.astype(np.float64)
+    up = xm @ W1["w_up"][0].T.astype(np.float64)
+    x = x + (gt / (1 + np.exp(-gt)) * up) @ W1["w_down"][0].T.astype(np.float64)
+    assert np.max(np.abs(out - x)) < 1e-12
+
+
+def test_silu_closed_form():
+    z = np.array([0.0, 1.0, -1.0, 40.0, -40.0])
+    s = od.silu(z)
+    assert s[0] == 0.0
+    assert abs(s[1] - 1 / (1 + math.exp(-1))) < 1e-16
+    assert abs(s[2] + 1 / (1 + math.e)) < 1e-16
+    assert abs(s[3] - 40.0) < 1e-12 and abs(s[4]) < 1e-15
+
+
+def test_logits_cover_mask_rows_only(tiny_w):
+    lg = _fwd(tiny_w, [5] + [TINY.mask_token_id] * 7, _hidden(64))["logits"]
+    assert lg.shape == (7, TINY.vocab)
+
+
+# ---- the workload shapes follow the pages' stated structure -------------------------------------
+
+def test_workloads_follow_page_constants():
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    for name in ("qwen3-4b", "qwen3-8b"):
+        wl = synth.workload(name)
+        assert (wl.shape.n_layers, wl.block_len, wl.shape.n_target_layers) == (
+            g["dflare_qwen"]["draft_layers"], g["dflare_qwen"]["block_len"],
+            g["dflare_qwen"]["target_layers"])
+        assert wl.shape.n_layers * wl.shape.n_target_layers == \
+            g["dflare_mix_coefficients_7x9"]["value"]
+    wl = synth.workload("gpt-oss-20b")
+    assert (wl.shape.n_layers, wl.block_len, wl.shape.n_target_layers) == (
+        g["dflare_gpt_oss"]["draft_layers"], g["dflare_gpt_oss"]["block_len"],
+        g["dflare_gpt_oss"]["target_layers"])
+    wl = synth.workload("specdiff2-7b")
+    assert wl.block_len == g["specdiff2_window"]["diffucoder_gamma"] and wl.n_anchor == 0
+    assert wl.n_drafts <= g["specdiff2_selection_K_T"]["K_max"]
+    assert wl.temperature in g["specdiff2_selection_K_T"]["temperatures"]
+    # planted per-position rates reproduce the pages' acceptance lengths
+    for name, tau in g["dflare_accept_len_T0"].items():
+        if name == "cite":
+            continue
+        wl = synth.workload(name)
+        a = wl.planted_alpha
+        assert abs(1 + sum(a ** m for m in range(1, wl.n_draft + 1)) - tau) < 0.01
+    # reading: the reported streak, like the acceptance length, counts the verifier's own token
+    wl = synth.workload("specdiff2-7b")
+    a = wl.planted_alpha
+    assert abs(1 + sum(a ** m for m in range(1, 33)) - g["specdiff2_avg_streak"]["value"]) < 0.01
