@@ -1,0 +1,249 @@
+"""Benchmark of the block-diffusion drafting hot path on one MI355X.
+
+A step is one draft_block call (ingest of the newly committed positions, the block forward, the
+LM head and argmax drafting) followed by verify_greedy on the target's logits, for the
+Qwen3-8B-shaped drafter at batch 32 (block 16, 7 draft layers mixing 9 target layers, cached
+context lengths uniform in [256, 3072]).  Inputs are synthetic and resident in HBM before timing.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X datasheet
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s, MI355X datasheet
+WORKLOAD = "qwen3-8b"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps-only", action="store_true",
+                    help="skip the instrumented pass and the cold-ingest timing")
+    return ap.parse_args()
+
+
+def algorithmic_costs(wl, ctx, new):
+    """Per-stage algorithmic (bytes, flops) of one step: weights, cache and logits read once,
+    activations read and written once."""
+    sh = wl.shape
+    N, B = wl.batch, wl.block_len
+    M, D = N * B, wl.n_draft
+    Md = N * D
+    H, F, V, Ld, Lt = sh.hidden, sh.ffn, sh.vocab, sh.n_layers, sh.n_target_layers
+    qd, kd, hd, kvh = sh.q_dim, sh.kv_dim, sh.head_dim, sh.n_kv_heads
+    grp = sh.n_q_heads // kvh
+    es = 2 if sh.dtype == "bf16" else 4
+    T = int(np.sum(new))
+    keys = ctx + new + B                              # keys attended per sequence
+    c = {}
+    c["mix"] = (T * Lt * H * es + Ld * T * H * es, 0)
+    c["gemm_ctxkv"] = (Ld * (2 * kd * H * es + T * H * es + T * 2 * kd * es),
+                       2 * T * 2 * kd * H * Ld)
+    c["gemm_qkv"] = (Ld * ((qd + 2 * kd) * H * es + M * H * es + M * (qd + 2 * kd) * es),
+                     2 * M * (qd + 2 * kd) * H * Ld)
+    c["attn"] = (Ld * (int(np.sum(keys)) * kvh * hd * 2 * es + 2 * M * qd * es),
+                 Ld * int(np.sum(keys)) * kvh * 4 * B * grp * hd)
+    c["gemm_o"] = (Ld * (H * qd * es + M * qd * es + 2 * M * H * 4), 2 * M * H * qd * Ld)
+    c["gemm_gateup"] = (Ld * (2 * F * H * es + M * H * es + M * F * es), 2 * M * 2 * F * H * Ld)
+    c["gemm_down"] = (Ld * (H * F * es + M * F * es + 2 * M * H * 4), 2 * M * H * F * Ld)
+    c["gemm_lmhead"] = (V * H * es + Md * H * es, 2 * Md * V * H)
+    c["rownorm"] = ((2 * Ld + 1) * M * H * (4 + es) + M * H * (es + 4), 0)
+    c["verify"] = (N * wl.verify_rows * V * 4, 0)
+    return c
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path needs no inter-GPU exchange; see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import block_diffusion_drafter_draft_amd as dbd
+    import synth
+
+    dev = "cuda"
+    wl = synth.workload(args.workload)
+    sh = wl.shape
+    N, B, D, V = wl.batch, wl.block_len, wl.n_draft, sh.vocab
+    t_setup = time.time()
+    ctx, new = synth.make_lengths(wl, 0)
+    cap = synth.capacity_for(wl, ctx, new)
+    W = synth.make_weights(sh, 0, dev)
+    desc, ws_w = dbd.model_desc(sh), dbd.weights_struct(W)
+    tokens = synth.make_block_tokens(wl, 0, dev)
+    dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
+    kv_k = torch.zeros((sh.n_layers, N, sh.n_kv_heads, cap, sh.head_dim), dtype=dt, device=dev)
+    kv_v = torch.zeros((sh.n_layers, N, sh.n_kv_heads, sh.head_dim, cap), dtype=dt, device=dev)
+    hidden = [synth.make_hidden(sh, int(ctx[i] + new[i]), 0, i, dev) for i in range(N)]
+    cold_rows = torch.cat([hidden[i][: int(ctx[i])] for i in range(N)], 0).contiguous()
+    step_rows = torch.cat([hidden[i][int(ctx[i]):] for i in range(N)], 0).contiguous()
+    T_cold, T_step = cold_rows.shape[0], step_rows.shape[0]
+    ws = torch.empty(dbd.draft_workspace_bytes(desc, N, B, wl.n_anchor, T_cold, 1, 0.0, cap),
+                     dtype=torch.uint8, device=dev)
+    off_cold = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32), device=dev)
+    off_step = torch.tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32), device=dev)
+    zeros = torch.zeros(N, dtype=torch.int32, device=dev)
+    ctx_t = torch.tensor(ctx.astype(np.int32), device=dev)
+    drafts = torch.empty((N, 1, D), dtype=torch.int32, device=dev)
+    # target logits with a planted accepted-prefix length per sequence
+    v_drafts = synth.make_drafts(N, 1, D, V, seed=1, device=dev)[:, 0].contiguous()
+    tlogits, _ = synth.make_planted_verify_logits(v_drafts, wl.verify_rows, V,
+                                                  wl.planted_alpha, seed=1, device=dev)
+    vws = torch.empty(dbd.verify_workspace_bytes(N, wl.verify_rows, V), dtype=torch.uint8,
+                      device=dev)
+    n_acc = torch.empty(N, dtype=torch.int32, device=dev)
+    bonus = torch.empty(N, dtype=torch.int32, device=dev)
+    committed = torch.empty((N, D + 1), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    # fill the cache: cold ingest of every cached position (also the mix kernel's large regime)
+    def cold():
+        dbd.draft_block(desc, ws_w, tokens, cold_rows, off_cold, zeros, kv_k, kv_v, drafts, ws,
+                        T_cold)
+    cold()
+    torch.cuda.synchronize()
+
+    def step():
+        dbd.draft_block(desc, ws_w, tokens, step_rows, off_step, ctx_t, kv_k, kv_v, drafts, ws,
+                        T_step)
+        dbd.verify_greedy(tlogits, drafts[:, 0], n_acc, bonus, committed, vws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # instrumented pass: per-stage kernel time from HIP events the library records on its stream
+    costs = algorithmic_costs(wl, ctx, new)
+    stages = {}
+    cold_info = None
+    if not args.profile_steps_only:
+        dbd.timing_reset()
+        dbd.timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        tm = dbd.timing_read()
+        dbd.timing_reset()
+        cold()
+        torch.cuda.synchronize()
+        tc = dbd.timing_read()
+        dbd.timing_enable(False)
+        dbd.timing_reset()
+        for name, (tot, n) in tm.items():
+            if n == 0:
+                continue
+            b, f = costs.get(name, (0, 0))
+            t = tot / args.steps * 1e-3
+            stages[name] = {"ms_per_step": round(tot / args.steps, 4),
+                            "launches_per_step": n // args.steps,
+                            "GBps": round(b / t / 1e9, 1) if b else None,
+                            "TFLOPs": round(f / t / 1e12, 1) if f else None,
+                            "roof_us": round(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6, 2)}
+        mix_b = T_cold * (sh.n_target_layers + sh.n_layers) * sh.hidden * 2
+        cold_info = {"rows": T_cold,
+                     "mix_ms": round(tc["mix"][0], 3),
+                     "mix_GBps": round(mix_b / (tc["mix"][0] * 1e-3) / 1e9, 1),
+                     "ctxkv_gemm_ms": round(tc["gemm_ctxkv"][0], 3),
+                     "ctxkv_TFLOPs": round(2 * T_cold * 2 * sh.kv_dim * sh.hidden * sh.n_layers
+                                           / (tc["gemm_ctxkv"][0] * 1e-3) / 1e12, 1)}
+
+    # dominant kernel by time, and its roofline
+    roofline = None
+    if stages:
+        dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+        b, f = costs[dom]
+        n = stages[dom]["launches_per_step"]
+        avg_s = stages[dom]["ms_per_step"] / n * 1e-3
+        if f and f / b > MFMA_BF16_PEAK / HBM_PEAK:
+            ach = f / n / avg_s / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 1),
+                        "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                        "frac": round(ach * 1e12 / MFMA_BF16_PEAK, 4)}
+        else:
+            ach = b / n / avg_s / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
+                        "unit": "GB/s", "frac": round(ach * 1e9 / HBM_PEAK, 4)}
+        roofline.update({"kernel": dom, "launches_per_step": n,
+                         "avg_launch_us": round(avg_s * 1e6, 2), "traffic": None})
+    step_roof_s = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in costs.values())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, W, tokens, hidden, ctx, new, tlogits, v_drafts)
+
+    blocks_s = N / (ms * 1e-3)
+    out = {
+        "metric": "drafted 16-tok blocks/s (draft fwd+verify) Qwen3-8B-shape bs=32; % roofline",
+        "value": round(blocks_s, 1), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}-shaped drafter: hidden {sh.hidden}, "
+                               f"{sh.n_q_heads}q/{sh.n_kv_heads}kv x {sh.head_dim}, ffn {sh.ffn}, "
+                               f"{sh.n_layers} draft layers x {sh.n_target_layers} target layers,"
+                               f" vocab {V}, block {B}, batch {N}, cached ctx "
+                               f"U[{wl.ctx_lo},{wl.ctx_hi}], greedy verify",
+                   "batch": N, "block_len": B, "ctx_total": int(np.sum(ctx)),
+                   "new_rows": int(T_step)},
+        "drafted_tok_per_s": round(blocks_s * D, 1),
+        "step_roofline_us": round(step_roof_s * 1e6, 1),
+        "step_roofline_frac": round(step_roof_s / (ms * 1e-3), 4),
+        "roofline": roofline,
+        "stages": stages,
+        "cold_ingest": cold_info,
+        "cpu_baseline": cpu,
+        "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, W, tokens, hidden, ctx, new, tlogits, v_drafts):
+    """The oracle as it stands, on one sequence of the same workload: its drafter step from the
+    cached context (context K/V precomputed by the oracle, untimed) plus greedy verification of
+    that sequence's target rows."""
+    from threadpoolctl import threadpool_info
+    from oracle import accept, drafter as od
+    sh = wl.shape
+    i = 0
+    Wc = {k: v.detach().to("cpu") for k, v in W.items()}
+    h = hidden[i].to("cpu")
+    C = int(ctx[i] + new[i])
+    kv = [od.context_kv(sh, Wc, l, h[:C]) for l in range(sh.n_layers)]
+    toks = tokens[i].to("cpu").numpy()
+    tl = tlogits[i: i + 1].to("cpu").numpy()
+    vd = v_drafts[i: i + 1].to("cpu").numpy()
+    t0 = time.perf_counter()
+    out = od.drafter_forward(sh, Wc, toks, wl.n_anchor, ctx_kv=kv)
+    accept.verify_greedy(tl, vd)
+    t = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    assert out["logits"].shape[0] == wl.n_draft
+    return {"value": round(1.0 / t, 4), "unit": "blocks/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"1 of {wl.batch} sequences (ctx {C}): fp64 drafter step from the cached "
+                      f"context + greedy verify, {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+// Internal declarations shared by the translation units of libdbd.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte copies
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- element conversions
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------- wave64 reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// (value, index) maximum; ties and NaN-free equal values go to the lower index; NaN never wins.
+__device__ __forceinline__ void argmax_combine(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, 64);
+    int oi = __shfl_xor(i, o, 64);
+    argmax_combine(v, i, ov, oi);
+  }
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    v += ((uint64_t)hi << 32) | lo;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- argument structs
+// Per-row metadata produced at the start of draft_block (all device pointers into workspace).
+struct RowMeta {
+  int32_t* blk_pos;     // [N*B]   position of block row, -1 if its sequence is invalid
+  int32_t* ctx_seq;     // [T_new] sequence of ingest row, -1 if invalid
+  int32_t* ctx_pos;     // [T_new] position of ingest row, -1 if invalid
+  int32_t* seq_keys;    // [N]     keys the block attends to (P + B), 0 if invalid
+  float2* rope_blk;     // [N*B][hd/2] (cos, sin)
+  float2* rope_ctx;     // [T_new][hd/2]
+};
+
+// GEMM: C = A[M,K] . Bv[N,K]^T where the virtual B rows come from up to three weight tensors
+// (concatenated along N) or, in gate/up mode, from two tensors interleaved per column tile.
+struct BSeg {
+  const void* ptr;
+  int n0, n1;           // virtual columns [n0, n1) read rows 0 .. n1-n0-1 of ptr
+};
+struct GemmArgs {
+  const void* A;
+  int64_t lda, a_bs;    // row stride, batch (grid.z) stride, in elements
+  BSeg seg[3];
+  int nseg;
+  int64_t ldb, b_bs;
+  int gateup;           // 1: tile t holds gate rows [t*BN/2, +BN/2) then up rows; seg0 = gate,
+                        //    seg1 = up, both with n1 - n0 = F
+  int M, N, K;          // N = virtual columns
+};
+
+// Epilogue selectors and their parameters.
+enum EpiKind { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_CTXKV = 3, EPI_SWIGLU = 4,
+               EPI_ARGMAX = 5 };
+struct EpiArgs {
+  int kind;
+  // store / residual / argmax-logits
+  void* C;              // EPI_STORE_F32: float*; EPI_RESID: float* residual (x += acc)
+  int64_t ldc, c_bs;
+  // attention projections
+  void* q_out;          // [M, qd] element T
+  void* kv_k;           // cache (element T)
+  void* kv_v;
+  int64_t layer_off_k;  // element offset of this layer's block in the cache (QKV epilogue)
+  int64_t layer_stride; // elements per layer in the cache (CTXKV epilogue: layer = grid.z)
+  int qd, kd, hd, kvh, block_len, batch, cap;
+  const int32_t* row_seq;   // CTXKV: ctx_seq
+  const int32_t* row_pos;   // QKV: blk_pos; CTXKV: ctx_pos
+  const float2* rope;       // rope table for the rows
+  // SwiGLU
+  void* act;            // [M, F] element T
+  int F;
+  // LM-head argmax
+  float* part_val;      // [M, ntiles]
+  int32_t* part_idx;
+  int ntiles;
+  float* logits;        // optional [M, N] fp32
+};
+
+// Attention over the cache: every block row of sequence n, head h, attends to cache positions
+// 0 .. seq_keys[n]-1 of kv head h / grp.
+struct AttnArgs {
+  const void* q;        // [N*B, qd]
+  const void* kv_k;     // layer base: [N, kvh, cap, hd]
+  const void* kv_v;     // layer base: [N, kvh, hd, cap]
+  const int32_t* seq_keys;
+  void* out;            // [N*B, qd]
+  float* part_o;        // [N, kvh, S_max, R, hd]
+  float2* part_ml;      // [N, kvh, S_max, R] (running max in log2 units, sum)
+  int batch, kvh, grp, block_len, cap, qd, s_max, split;
+  float scale_log2;     // log2(e) / sqrt(hd)
+};
+
+// ---------------------------------------------------------------- launchers (one per TU)
+hipError_t launch_prep(const int32_t* ctx_len, const int32_t* new_offsets, int batch,
+                       int block_len, int n_new_total, int cap, int hd, const double* inv_freq,
+                       RowMeta meta, int32_t* seq_status, hipStream_t s);
+hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls, int n_tok,
+                              int H, int Lt, int Ld, const float* mix_logits, const void* g,
+                              void* out, float eps, hipStream_t s);
+hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H,
+                        int V, float* x, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, int rows, int H,
+                          float eps, int block_len, int n_anchor, hipStream_t s);
+hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
+                       hipStream_t s);
+hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
+hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,
+                                  int ntiles, const int32_t* blk_pos, int block_len,
+                                  int n_anchor, int n_draft, int32_t* out, hipStream_t s);
+hipError_t launch_argmax_partial(const float* x, int rows, int vocab, int chunk, float* pv,
+                                 int32_t* pi, int32_t* pflag, hipStream_t s);
+hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int rows, int nch,
+                               int32_t* out_idx, float* out_max, hipStream_t s);
+hipError_t launch_zsum_partial(const float* x, int rows, int vocab, int chunk, const float* pv,
+                               const int32_t* pi, float inv_t, uint64_t* zpart, float* row_max,
+                               int32_t* row_arg, hipStream_t s);
+hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
+                              const uint64_t* zpart, const float* row_max, float inv_t,
+                              int n_draft, int n_drafts, uint64_t seed,
+                              const int32_t* row_valid_pos, int block_len, int n_anchor,
+                              int32_t* out, hipStream_t s);
+hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int32_t* pflag,
+                                  int nch, const int32_t* drafts, int draft_stride, int batch,
+                                  int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,
+                                  int32_t* committed, int32_t* row_flags, hipStream_t s);
+hipError_t launch_select_finalize(const float* x, int vocab, int chunk, const uint64_t* zpart,
+                                  const float* row_max, const int32_t* row_arg,
+                                  const int32_t* pflag, const int32_t* drafts, int batch,
+                                  int n_drafts, int gamma, int n_rows, int32_t* selected,
+                                  double* scores, int32_t* n_acc, int32_t* bonus,
+                                  int32_t* committed, int32_t* row_flags, hipStream_t s);
+
+inline int vocab_chunk() { return 4096; }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace dbd

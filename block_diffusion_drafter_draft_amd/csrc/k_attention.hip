@@ -1,0 +1,269 @@
+// Block attention over the cache (DFlare page, section on parallel drafting: attention inside
+// the block is bidirectional and the block sees the whole context).  No mask: every row of the
+// block attends to all cache positions 0 .. P+B-1 of its sequence (context, then the block's own
+// keys, which draft_block wrote into the cache first).
+//
+// Work item: (key split s, kv head g, sequence n); one wave per 16 query rows of the GQA group
+// (rows r = b + B*h over block positions b and the group's heads h).  Per 64-key chunk the K rows
+// and the transposed V are staged in LDS; each wave computes S^T = K.Q^T with the gfx950 MFMA
+// 16x16x32 bf16, so that its lanes hold 8 consecutive keys of one query (keys are permuted inside
+// the MFMA tiles), runs the online softmax in fp32 (exp2 domain) and feeds P^T straight from
+// registers into O^T += V^T.P^T.  Splits of one (n, g) are merged by attn_combine_kernel.
+#include "dbd_internal.h"
+
+namespace dbd {
+
+constexpr int KCH = 64;        // keys per LDS chunk
+
+// ------------------------------------------------------------------ helpers
+template <int HD>
+__device__ __forceinline__ int kswz(int row, int c) {
+  // K tile row = HD*2 bytes.  The S^T operand reads rows {8(i/4) + i%4 (+4)}: spread them over
+  // distinct 16-byte slots.
+  if constexpr (HD == 128) return c ^ ((row & 3) | (((row >> 3) & 3) << 2));
+  else return c ^ (((row >> 1) & 1) | (((row >> 3) & 3) << 1));
+}
+__device__ __forceinline__ int vswz(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+template <int HD>
+__global__ __launch_bounds__(1024) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int KC = HD / 8;                    // 16-byte chunks per K row
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KCH * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[HD * KCH];
+  const int s = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+  const int L = a.seq_keys[n];
+  const int k_begin = s * a.split;
+  if (L <= 0 || k_begin >= L) return;
+  const int k_end = min(L, k_begin + a.split);
+  const int nsplit = (L + a.split - 1) / a.split;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthr = blockDim.x;
+  const int R = a.block_len * a.grp;
+
+  const bf16* Kg = (const bf16*)a.kv_k + ((int64_t)n * a.kvh + g) * a.cap * HD;
+  const bf16* Vg = (const bf16*)a.kv_v + ((int64_t)n * a.kvh + g) * HD * a.cap;
+
+  // this lane's query row (column of S^T / O^T)
+  const int r = wave * 16 + (lane & 15);
+  const bool rvalid = r < R;
+  const int b = rvalid ? r % a.block_len : 0, h = rvalid ? r / a.block_len : 0;
+  const int64_t qrow = (int64_t)n * a.block_len + b;
+  const int qcol = (g * a.grp + h) * HD;
+  bf16x8 qf[HD / 32];
+  {
+    const bf16* qp = (const bf16*)a.q + qrow * a.qd + qcol + (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < HD / 32; ++ks) {
+      if (rvalid) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+      else for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.f;
+    }
+  }
+  f32x4 acc[HD / 16];
+#pragma unroll
+  for (int i = 0; i < HD / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // key rows of the two S^T tiles in a 32-key group: lane group G = lane/16 ends up holding
+  // keys 8G .. 8G+7
+  const int i16 = lane & 15;
+  const int kr0 = 8 * (i16 >> 2) + (i16 & 3);
+  const int kr1 = kr0 + 4;
+
+  for (int c0 = k_begin; c0 < k_end; c0 += KCH) {
+    // stage K rows [c0, c0+64) and V^T columns [c0, c0+64); positions >= k_end read as 0 in V
+    for (int idx = tid; idx < KCH * KC; idx += nthr) {
+      const int row = idx / KC, c = idx % KC;
+      u32x4 v = *reinterpret_cast<const u32x4*>(Kg + (int64_t)(c0 + row) * HD + c * 8);
+      *reinterpret_cast<u32x4*>(Ks + row * HD + kswz<HD>(row, c) * 8) = v;
+    }
+    for (int idx = tid; idx < HD * (KCH / 8); idx += nthr) {
+      const int d = idx / (KCH / 8), c = idx % (KCH / 8);
+      const int k0 = c0 + c * 8;
+      u32x4 v = *reinterpret_cast<const u32x4*>(Vg + (int64_t)d * a.cap + k0);
+      if (k0 + 8 > k_end) {
+        bf16* e = reinterpret_cast<bf16*>(&v);
+        for (int j = 0; j < 8; ++j)
+          if (k0 + j >= k_end) e[j] = (bf16)0.f;
+      }
+      *reinterpret_cast<u32x4*>(Vs + d * KCH + vswz(d, c) * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < KCH / 32; ++sub) {
+      const int key0 = c0 + sub * 32;
+      if (key0 < k_end) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        const int row0 = sub * 32 + kr0, row1 = sub * 32 + kr1;
+#pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks) {
+          const int c = ks * 4 + (lane >> 4);
+          bf16x8 k0v = *reinterpret_cast<const bf16x8*>(Ks + row0 * HD + kswz<HD>(row0, c) * 8);
+          bf16x8 k1v = *reinterpret_cast<const bf16x8*>(Ks + row1 * HD + kswz<HD>(row1, c) * 8);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks], s1, 0, 0, 0);
+        }
+        // lane holds S^T[key0 + 8*(lane/16) + e][query], e = 0..7
+        float sv[8];
+        const int kb = key0 + 8 * (lane >> 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = kb + e < k_end ? s0[e] * a.scale_log2 : -INFINITY;
+          sv[4 + e] = kb + 4 + e < k_end ? s1[e] * a.scale_log2 : -INFINITY;
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        bf16x8 pb;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2f(sv[e] - m_new);
+          ps += p;
+          pb[e] = (bf16)p;
+        }
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) {
+          acc[dt] *= alpha;
+          const int d = dt * 16 + (lane & 15);
+          const int c = sub * 4 + (lane >> 4);
+          bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + d * KCH + vswz(d, c) * 8);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // per-lane partial sums of the 4 lane groups belong to the same query
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!rvalid) return;
+  // acc[dt][i] = O^T[d = dt*16 + 4*(lane/16) + i][query]
+  if (nsplit == 1) {
+    const float inv = 1.f / l_run;
+    bf16* o = (bf16*)a.out + qrow * a.qd + qcol;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[dt * 16 + (lane >> 4) * 4 + i] = (bf16)(acc[dt][i] * inv);
+  } else {
+    const int64_t pr = (((int64_t)n * a.kvh + g) * a.s_max + s) * R + r;
+    float* po = a.part_o + pr * HD;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[dt * 16 + (lane >> 4) * 4 + i] = acc[dt][i];
+    if (lane < 16) a.part_ml[pr] = make_float2(m_run, l_run);
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+// Plain fp32 attention for the fp32 drafter: one workgroup per (split, kv head, sequence), one
+// query row at a time; scores one key per thread, values one dimension per thread.
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int HD) {
+  __shared__ float p[256];
+  __shared__ float q[128];
+  __shared__ float red[8];
+  const int s = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+  const int L = a.seq_keys[n];
+  const int k_begin = s * a.split;
+  if (L <= 0 || k_begin >= L) return;
+  const int k_end = min(L, k_begin + a.split);
+  const int nk = k_end - k_begin;
+  const int nsplit = (L + a.split - 1) / a.split;
+  const int tid = threadIdx.x;
+  const int R = a.block_len * a.grp;
+  const float* Kg = (const float*)a.kv_k + ((int64_t)n * a.kvh + g) * a.cap * HD;
+  const float* Vg = (const float*)a.kv_v + ((int64_t)n * a.kvh + g) * HD * a.cap;
+  for (int r = 0; r < R; ++r) {
+    const int b = r % a.block_len, h = r / a.block_len;
+    const int64_t qrow = (int64_t)n * a.block_len + b;
+    const int qcol = (g * a.grp + h) * HD;
+    __syncthreads();
+    if (tid < HD) q[tid] = ((const float*)a.q)[qrow * a.qd + qcol + tid];
+    __syncthreads();
+    float sc = -INFINITY;
+    if (tid < nk) {
+      const float* kr = Kg + (int64_t)(k_begin + tid) * HD;
+      float acc = 0.f;
+      for (int d = 0; d < HD; ++d) acc += q[d] * kr[d];
+      sc = acc * a.scale_log2;
+    }
+    float m = wave_max(sc);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float e = tid < nk ? exp2f(sc - m) : 0.f;
+    p[tid] = e;
+    float l = wave_sum(e);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = l;
+    __syncthreads();
+    l = red[4] + red[5] + red[6] + red[7];
+    if (tid < HD) {
+      const float* vr = Vg + (int64_t)tid * a.cap + k_begin;
+      float o = 0.f;
+      for (int k = 0; k < nk; ++k) o += p[k] * vr[k];
+      if (nsplit == 1) {
+        ((float*)a.out)[qrow * a.qd + qcol + tid] = o / l;
+      } else {
+        const int64_t pr = (((int64_t)n * a.kvh + g) * a.s_max + s) * R + r;
+        a.part_o[pr * HD + tid] = o;
+        if (tid == 0) a.part_ml[pr] = make_float2(m, l);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine splits
+template <typename T>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int HD) {
+  const int g = blockIdx.x, n = blockIdx.y;
+  const int L = a.seq_keys[n];
+  const int nsplit = (L + a.split - 1) / a.split;
+  if (L <= 0 || nsplit <= 1) return;
+  const int R = a.block_len * a.grp;
+  const int64_t base = ((int64_t)n * a.kvh + g) * a.s_max;
+  for (int idx = threadIdx.x; idx < R * HD; idx += blockDim.x) {
+    const int r = idx / HD, d = idx % HD;
+    float m = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.part_ml[(base + s) * R + r].x);
+    float l = 0.f, o = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float2 ml = a.part_ml[(base + s) * R + r];
+      const float w = exp2f(ml.x - m);
+      l += w * ml.y;
+      o += w * a.part_o[((base + s) * R + r) * HD + d];
+    }
+    const int b = r % a.block_len, h = r / a.block_len;
+    const int64_t qrow = (int64_t)n * a.block_len + b;
+    ((T*)a.out)[qrow * a.qd + (g * a.grp + h) * HD + d] = from_f<T>(o / l);
+  }
+}
+
+hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.s_max, a.kvh, a.batch);
+  const int R = a.block_len * a.grp;
+  if (dtype == 1) {
+    const int nw = ceil_div(R, 16);
+    if (hd == 128)
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(64 * nw), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(64 * nw), 0, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(attn_combine_kernel<bf16>, dim3(a.kvh, a.batch), dim3(256), 0, s, a, hd);
+  } else {
+    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, a, hd);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.kvh, a.batch), dim3(256), 0, s, a, hd);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dbd

@@ -1,0 +1,281 @@
+// Row kernels of draft_block: per-row metadata and rotary tables, the ingest mix + RMSNorm
+// (DFlare page, section on per-draft-layer mixing), the embedding gather and RMSNorm.
+#include "dbd_internal.h"
+
+namespace dbd {
+
+// ------------------------------------------------------------------ prep
+// One thread per (row, frequency pair).  Rows 0 .. N*B-1 are block rows, then the ingest rows.
+// A sequence is valid when its offsets are ordered, lie in [0, n_new_total] and its block fits
+// the cache: ctx_len + n_new + B <= cap.  Invalid sequences get position -1 everywhere.
+struct Freqs {
+  double v[64];
+};
+
+__device__ __forceinline__ bool seq_ok(const int32_t* ctx_len, const int32_t* off, int n,
+                                       int block_len, int n_new_total, int cap, int* P) {
+  int c = ctx_len[n], a = off[n], b = off[n + 1];
+  bool ok = c >= 0 && a >= 0 && b >= a && b <= n_new_total &&
+            (int64_t)c + (b - a) + block_len <= cap;
+  *P = c + (b - a);
+  return ok;
+}
+
+__global__ void prep_kernel(const int32_t* __restrict__ ctx_len,
+                            const int32_t* __restrict__ off, int batch, int block_len,
+                            int n_new_total, int cap, int half, Freqs fq, RowMeta meta,
+                            int32_t* seq_status) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nblk = batch * block_len;
+  const int64_t total = (int64_t)(nblk + n_new_total) * half;
+  if (gid < batch) {
+    int P;
+    bool ok = seq_ok(ctx_len, off, (int)gid, block_len, n_new_total, cap, &P);
+    meta.seq_keys[gid] = ok ? P + block_len : 0;
+    if (seq_status) seq_status[gid] = ok ? 0 : 2;
+  }
+  if (gid >= total) return;
+  const int row = (int)(gid / half);
+  const int i = (int)(gid % half);
+  int pos;
+  if (row < nblk) {
+    const int n = row / block_len, b = row % block_len;
+    int P;
+    bool ok = seq_ok(ctx_len, off, n, block_len, n_new_total, cap, &P);
+    pos = ok ? P + b : -1;
+    if (i == 0) meta.blk_pos[row] = pos;
+  } else {
+    const int t = row - nblk;
+    // sequence of ingest row t: the last n with off[n] <= t (offsets are non-decreasing)
+    int lo = 0, hi = batch - 1, n = -1;
+    while (lo <= hi) {
+      int mid = (lo + hi) >> 1;
+      if (off[mid] <= t) { n = mid; lo = mid + 1; } else { hi = mid - 1; }
+    }
+    pos = -1;
+    if (n >= 0 && t < off[n + 1]) {
+      int P;
+      if (seq_ok(ctx_len, off, n, block_len, n_new_total, cap, &P)) pos = ctx_len[n] + (t - off[n]);
+    }
+    if (i == 0) {
+      meta.ctx_seq[t] = pos >= 0 ? n : -1;
+      meta.ctx_pos[t] = pos;
+    }
+  }
+  // rotation angle pos * theta^(-2i/hd) in fp64, stored as fp32 (cos, sin)
+  double ang = (double)(pos < 0 ? 0 : pos) * fq.v[i];
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  float2 r = make_float2((float)cs, (float)sn);
+  if (row < nblk) meta.rope_blk[(int64_t)row * half + i] = r;
+  else meta.rope_ctx[(int64_t)(row - nblk) * half + i] = r;
+}
+
+hipError_t launch_prep(const int32_t* ctx_len, const int32_t* new_offsets, int batch,
+                       int block_len, int n_new_total, int cap, int hd, const double* inv_freq,
+                       RowMeta meta, int32_t* seq_status, hipStream_t s) {
+  Freqs fq;
+  const int half = hd / 2;
+  for (int i = 0; i < 64; ++i) fq.v[i] = i < half ? inv_freq[i] : 0.0;
+  int64_t total = (int64_t)(batch * block_len + n_new_total) * half;
+  if (total < batch) total = batch;
+  const int threads = 256;
+  const int blocks = (int)ceil_div64(total, threads);
+  hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(threads), 0, s, ctx_len, new_offsets, batch,
+                     block_len, n_new_total, cap, half, fq, meta, seq_status);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ mix + RMSNorm
+// One workgroup per ingested token.  Each thread owns CPT chunks of VEC consecutive hidden
+// elements, reads the token's L_t target layers once (16-byte coalesced loads) and keeps the L_d
+// mixed values in registers; the L_d sums of squares are reduced together.
+constexpr int kMaxLd = 8;
+constexpr int kMaxLt = 16;
+
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { static constexpr int n = 8; };
+template <> struct Vec16<float> { static constexpr int n = 4; };
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
+    const T* __restrict__ hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt, int Ld,
+    const float* __restrict__ mix_logits, const T* __restrict__ g, T* __restrict__ out,
+    float eps) {
+  constexpr int VEC = Vec16<T>::n;
+  __shared__ float w[kMaxLd * kMaxLt];
+  __shared__ float red[kMaxLd][4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < Ld) {
+    const float* lg = mix_logits + tid * Lt;
+    float m = -INFINITY;
+    for (int i = 0; i < Lt; ++i) m = fmaxf(m, lg[i]);
+    float sum = 0.f;
+    for (int i = 0; i < Lt; ++i) sum += expf(lg[i] - m);
+    for (int i = 0; i < Lt; ++i) w[tid * Lt + i] = expf(lg[i] - m) / sum;
+  }
+  __syncthreads();
+  const int nch = H / VEC;
+  float acc[kMaxLd][CPT * VEC];
+#pragma unroll
+  for (int l = 0; l < kMaxLd; ++l)
+#pragma unroll
+    for (int e = 0; e < CPT * VEC; ++e) acc[l][e] = 0.f;
+  const T* base = hid + (int64_t)t * ts;
+  for (int i = 0; i < Lt; ++i) {
+    float wl[kMaxLd];
+#pragma unroll
+    for (int l = 0; l < kMaxLd; ++l) wl[l] = l < Ld ? w[l * Lt + i] : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 256;
+      if (ch < nch) {
+        T v[VEC];
+        *reinterpret_cast<u32x4*>(v) =
+            *reinterpret_cast<const u32x4*>(base + (int64_t)i * ls + ch * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float x = to_f(v[e]);
+#pragma unroll
+          for (int l = 0; l < kMaxLd; ++l) acc[l][c * VEC + e] += wl[l] * x;
+        }
+      }
+    }
+  }
+  float ss[kMaxLd];
+#pragma unroll
+  for (int l = 0; l < kMaxLd; ++l) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPT * VEC; ++e) s += acc[l][e] * acc[l][e];
+    ss[l] = wave_sum(s);
+  }
+  const int lane = tid & 63, wv = tid >> 6;
+  if (lane == 0)
+#pragma unroll
+    for (int l = 0; l < kMaxLd; ++l) red[l][wv] = ss[l];
+  __syncthreads();
+#pragma unroll
+  for (int l = 0; l < kMaxLd; ++l) {
+    if (l >= Ld) break;
+    const float ms = (red[l][0] + red[l][1] + red[l][2] + red[l][3]) / (float)H;
+    const float inv = rsqrtf(ms + eps);
+    T* o = out + ((int64_t)l * n_tok + t) * H;
+    const T* gl = g + (int64_t)l * H;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 256;
+      if (ch < nch) {
+        T gv[VEC], ov[VEC];
+        *reinterpret_cast<u32x4*>(gv) = *reinterpret_cast<const u32x4*>(gl + ch * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ov[e] = from_f<T>(acc[l][c * VEC + e] * inv * to_f(gv[e]));
+        *reinterpret_cast<u32x4*>(o + ch * VEC) = *reinterpret_cast<u32x4*>(ov);
+      }
+    }
+  }
+}
+
+template <typename T>
+static hipError_t mix_dispatch(const void* hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt,
+                               int Ld, const float* ml, const void* g, void* out, float eps,
+                               hipStream_t s) {
+  constexpr int VEC = Vec16<T>::n;
+  const int cpt = ceil_div(H / VEC, 256);
+  const T* h = (const T*)hid;
+  if (n_tok == 0) return hipSuccess;
+  if (cpt <= 1)
+    hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 1>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
+                       H, Lt, Ld, ml, (const T*)g, (T*)out, eps);
+  else if (cpt <= 2)
+    hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 2>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
+                       H, Lt, Ld, ml, (const T*)g, (T*)out, eps);
+  else if (cpt <= 4)
+    hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 4>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
+                       H, Lt, Ld, ml, (const T*)g, (T*)out, eps);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls, int n_tok,
+                              int H, int Lt, int Ld, const float* mix_logits, const void* g,
+                              void* out, float eps, hipStream_t s) {
+  return dtype == 1 ? mix_dispatch<bf16>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out, eps, s)
+                    : mix_dispatch<float>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out, eps,
+                                          s);
+}
+
+// ------------------------------------------------------------------ embedding gather
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
+                                                    const T* __restrict__ E, int H, int V,
+                                                    float* __restrict__ x) {
+  const int r = blockIdx.x;
+  int id = tok[r];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);       // out-of-range ids are clamped
+  const T* e = E + (int64_t)id * H;
+  float* o = x + (int64_t)r * H;
+  for (int i = threadIdx.x; i < H; i += 256) o[i] = to_f(e[i]);
+}
+
+hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H, int V,
+                        float* x, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(rows), dim3(256), 0, s, tokens, (const bf16*)E,
+                       H, V, x);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tokens,
+                       (const float*)E, H, V, x);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// out[r'] = T(x[r] / sqrt(mean(x[r]^2) + eps) * g).  With n_anchor > 0 only the mask rows of
+// each block are normalised and written compactly (r' = n*(B - n_anchor) + b - n_anchor).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+                                                      const T* __restrict__ g,
+                                                      T* __restrict__ out, int H, float eps,
+                                                      int block_len, int n_anchor) {
+  __shared__ float red[4];
+  const int ro = blockIdx.x;
+  int ri = ro;
+  if (n_anchor > 0) {
+    const int D = block_len - n_anchor;
+    ri = (ro / D) * block_len + n_anchor + ro % D;
+  }
+  const float* xr = x + (int64_t)ri * H;
+  float s = 0.f;
+  for (int i = threadIdx.x * 4; i < H; i += 256 * 4) {
+    float4 v = *reinterpret_cast<const float4*>(xr + i);
+    s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  T* o = out + (int64_t)ro * H;
+  for (int i = threadIdx.x * 4; i < H; i += 256 * 4) {
+    float4 v = *reinterpret_cast<const float4*>(xr + i);
+    o[i + 0] = from_f<T>(v.x * inv * to_f(g[i + 0]));
+    o[i + 1] = from_f<T>(v.y * inv * to_f(g[i + 1]));
+    o[i + 2] = from_f<T>(v.z * inv * to_f(g[i + 2]));
+    o[i + 3] = from_f<T>(v.w * inv * to_f(g[i + 3]));
+  }
+}
+
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, int rows, int H,
+                          float eps, int block_len, int n_anchor, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(rows), dim3(256), 0, s, x, (const bf16*)g,
+                       (bf16*)out, H, eps, block_len, n_anchor);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, (const float*)g,
+                       (float*)out, H, eps, block_len, n_anchor);
+  return hipGetLastError();
+}
+
+}  // namespace dbd

@@ -1,0 +1,728 @@
+// C ABI of libdbd.so: argument validation (host, before any launch), workspace carving and the
+// launch sequence of draft_block, verify_greedy and select_streak.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dbd.h"
+#include "dbd_internal.h"
+
+using namespace dbd;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                               \
+  do {                                                                              \
+    hipError_t e_ = (expr);                                                         \
+    if (e_ != hipSuccess)                                                           \
+      return fail(DBD_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_));             \
+  } while (0)
+
+// Launch the expression on stream `st`, bracketed by timing events when timing is enabled.
+#define HIP_STAGE(stage, st, expr)                                                  \
+  do {                                                                              \
+    Timing::Pair* tp_ = g_timing.begin(stage, st);                                  \
+    HIP_TRY(expr);                                                                  \
+    if (tp_) g_timing.end(tp_, st);                                                 \
+  } while (0)
+
+// Per-stage kernel timing (benchmarks only): event pairs recorded around every launch.
+struct Timing {
+  struct Pair {
+    hipEvent_t a, b;
+    int stage;
+  };
+  bool on = false;
+  std::vector<Pair> pool;     // created once, reused after reset
+  size_t used = 0;
+  Pair* begin(int stage, hipStream_t st) {
+    if (!on) return nullptr;
+    if (used == pool.size()) {
+      Pair p{};
+      if (hipEventCreate(&p.a) != hipSuccess || hipEventCreate(&p.b) != hipSuccess) return nullptr;
+      pool.push_back(p);
+    }
+    Pair* p = &pool[used++];
+    p->stage = stage;
+    if (hipEventRecord(p->a, st) != hipSuccess) { --used; return nullptr; }
+    return p;
+  }
+  void end(Pair* p, hipStream_t st) { (void)hipEventRecord(p->b, st); }
+};
+Timing g_timing;
+
+constexpr size_t kAlign = 256;
+
+// Bump allocator over the caller's workspace; with base == nullptr it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T) + (count == 0 ? 0 : 0);
+    return p;
+  }
+};
+
+int elem_size(int dtype) { return dtype == DBD_BF16 ? 2 : 4; }
+
+int attn_split(int dtype) { return dtype == DBD_BF16 ? 512 : 256; }
+
+struct DraftBufs {
+  RowMeta meta;
+  void* ctxfeat;
+  float* x;
+  void* xn;
+  void* q;
+  void* attn;
+  void* act;
+  float* part_o;
+  float2* part_ml;
+  float* lm_pv;
+  int32_t* lm_pi;
+  float* logits;
+  float* vpv;
+  int32_t* vpi;
+  int32_t* vflag;
+  uint64_t* zpart;
+  float* row_max;
+  int32_t* row_arg;
+  int s_max;
+  int split;
+  int ntiles;
+};
+
+size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, int K,
+                   float temperature, int cap, char* base, DraftBufs* b) {
+  Carver c{base};
+  DraftBufs t{};
+  const int es = elem_size(d.dtype);
+  const int64_t M = (int64_t)N * B, Md = (int64_t)N * (B - n_anchor);
+  const int half = d.head_dim / 2;
+  const int qd = d.n_q_heads * d.head_dim;
+  const int grp = d.n_q_heads / d.n_kv_heads;
+  const int R = B * grp;
+  const int Tn = T > 0 ? T : 1;
+  t.meta.blk_pos = c.take<int32_t>(M);
+  t.meta.ctx_seq = c.take<int32_t>(Tn);
+  t.meta.ctx_pos = c.take<int32_t>(Tn);
+  t.meta.seq_keys = c.take<int32_t>(N);
+  t.meta.rope_blk = c.take<float2>(M * half);
+  t.meta.rope_ctx = c.take<float2>((int64_t)Tn * half);
+  t.ctxfeat = d.n_target_layers > 0
+                  ? (void*)c.take<char>((int64_t)d.n_layers * Tn * d.hidden * es)
+                  : nullptr;
+  t.x = c.take<float>(M * d.hidden);
+  t.xn = c.take<char>(M * d.hidden * es);
+  t.q = c.take<char>(M * qd * es);
+  t.attn = c.take<char>(M * qd * es);
+  t.act = c.take<char>(M * d.ffn * es);
+  t.split = attn_split(d.dtype);
+  t.s_max = ceil_div(cap, t.split);
+  t.part_o = c.take<float>((int64_t)N * d.n_kv_heads * t.s_max * R * d.head_dim);
+  t.part_ml = c.take<float2>((int64_t)N * d.n_kv_heads * t.s_max * R);
+  t.ntiles = ceil_div(d.vocab, 128);
+  t.lm_pv = c.take<float>(Md * t.ntiles);
+  t.lm_pi = c.take<int32_t>(Md * t.ntiles);
+  if (temperature > 0.f) {
+    const int nch = ceil_div(d.vocab, vocab_chunk());
+    t.logits = c.take<float>(Md * d.vocab);
+    t.vpv = c.take<float>(Md * nch);
+    t.vpi = c.take<int32_t>(Md * nch);
+    t.vflag = c.take<int32_t>(Md * nch);
+    t.zpart = c.take<uint64_t>(Md * nch);
+    t.row_max = c.take<float>(Md);
+    t.row_arg = c.take<int32_t>(Md);
+  }
+  (void)K;
+  if (b) *b = t;
+  return (c.off + kAlign - 1) / kAlign * kAlign;
+}
+
+int check_desc(const dbd_model_desc* d) {
+  if (!d) return fail(DBD_ERR_ARG, "desc is NULL");
+  if (d->dtype != DBD_F32 && d->dtype != DBD_BF16)
+    return fail(DBD_ERR_ARG, "dtype %d is neither DBD_F32 nor DBD_BF16", d->dtype);
+  if (d->hidden <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->ffn <= 0 ||
+      d->n_layers <= 0 || d->vocab < 2 || d->n_target_layers < 0)
+    return fail(DBD_ERR_ARG, "non-positive model dimension");
+  if (d->vocab >= (1 << 18)) return fail(DBD_ERR_SHAPE, "vocab %d >= 2^18", d->vocab);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(DBD_ERR_SHAPE, "head_dim %d: only 64 and 128 are supported", d->head_dim);
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(DBD_ERR_SHAPE, "n_q_heads %d not a multiple of n_kv_heads %d", d->n_q_heads,
+                d->n_kv_heads);
+  const int qd = d->n_q_heads * d->head_dim, kd = d->n_kv_heads * d->head_dim;
+  if (qd % 128 || kd % 128)
+    return fail(DBD_ERR_SHAPE, "q_heads*head_dim (%d) and kv_heads*head_dim (%d) must be "
+                "multiples of 128", qd, kd);
+  if (d->hidden % 8) return fail(DBD_ERR_SHAPE, "hidden %d not a multiple of 8", d->hidden);
+  if (d->dtype == DBD_BF16) {
+    if (d->hidden % 64 || d->ffn % 64)
+      return fail(DBD_ERR_SHAPE, "bf16 path needs hidden (%d) and ffn (%d) multiples of 64",
+                  d->hidden, d->ffn);
+    if (d->hidden > 8192) return fail(DBD_ERR_UNSUPPORTED, "hidden %d > 8192", d->hidden);
+  } else if (d->hidden > 4096) {
+    return fail(DBD_ERR_UNSUPPORTED, "fp32 path: hidden %d > 4096", d->hidden);
+  }
+  if (d->n_target_layers > 16)
+    return fail(DBD_ERR_UNSUPPORTED, "n_target_layers %d > 16", d->n_target_layers);
+  if (d->n_target_layers > 0 && d->n_layers > 8)
+    return fail(DBD_ERR_UNSUPPORTED, "target mixing supports at most 8 draft layers (got %d)",
+                d->n_layers);
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.0))
+    return fail(DBD_ERR_ARG, "rms_eps must be >= 0 and rope_theta > 0");
+  return DBD_OK;
+}
+
+int check_draft_shape(const dbd_model_desc* d, int N, int B, int n_anchor, int T, int K,
+                      float temperature, int cap) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (N < 1) return fail(DBD_ERR_ARG, "batch %d < 1", N);
+  if (n_anchor != 0 && n_anchor != 1) return fail(DBD_ERR_ARG, "n_anchor must be 0 or 1");
+  if (B < 1 + n_anchor || B > 64) return fail(DBD_ERR_SHAPE, "block_len %d out of range", B);
+  const int grp = d->n_q_heads / d->n_kv_heads;
+  if (d->dtype == DBD_BF16 && B * grp > 256)
+    return fail(DBD_ERR_UNSUPPORTED, "block_len * (q_heads / kv_heads) = %d > 256", B * grp);
+  if (T < 0) return fail(DBD_ERR_ARG, "n_new_total %d < 0", T);
+  if (d->n_target_layers == 0 && T > 0)
+    return fail(DBD_ERR_ARG, "n_new_total must be 0 for a drafter without target mixing");
+  if (K < 1 || K > 64) return fail(DBD_ERR_ARG, "n_drafts %d out of [1, 64]", K);
+  if (!(temperature > 0.f) && K != 1)
+    return fail(DBD_ERR_ARG, "argmax drafting (temperature <= 0) needs n_drafts == 1");
+  if (!std::isfinite(temperature)) return fail(DBD_ERR_ARG, "temperature is not finite");
+  if (cap < B || cap % 64) return fail(DBD_ERR_CAPACITY, "ctx_capacity %d must be >= block_len "
+                                       "and a multiple of 64", cap);
+  return DBD_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dbd_last_error(void) { return g_err.c_str(); }
+
+int dbd_timing_enable(int on) {
+  g_err.clear();
+  g_timing.on = on != 0;
+  return DBD_OK;
+}
+
+int dbd_timing_reset(void) {
+  g_err.clear();
+  g_timing.used = 0;
+  return DBD_OK;
+}
+
+int dbd_timing_read(int stage, double* total_ms, int64_t* launches) {
+  g_err.clear();
+  if (!total_ms || !launches) return fail(DBD_ERR_ARG, "output pointer is NULL");
+  if (stage < 0 || stage >= DBD_STAGE_COUNT) return fail(DBD_ERR_ARG, "bad stage %d", stage);
+  double ms = 0.0;
+  int64_t n = 0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    Timing::Pair& p = g_timing.pool[i];
+    if (p.stage != stage) continue;
+    HIP_TRY(hipEventSynchronize(p.b));
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, p.a, p.b));
+    ms += t;
+    ++n;
+  }
+  *total_ms = ms;
+  *launches = n;
+  return DBD_OK;
+}
+
+int dbd_draft_workspace_bytes(const dbd_model_desc* desc, int32_t max_batch, int32_t block_len,
+                              int32_t n_anchor, int32_t max_new_tokens, int32_t n_drafts,
+                              float temperature, int32_t ctx_capacity, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  int rc = check_draft_shape(desc, max_batch, block_len, n_anchor, max_new_tokens, n_drafts,
+                             temperature, ctx_capacity);
+  if (rc) return rc;
+  *bytes = carve_draft(*desc, max_batch, block_len, n_anchor, max_new_tokens, n_drafts,
+                       temperature, ctx_capacity, nullptr, nullptr);
+  return DBD_OK;
+}
+
+int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
+                int32_t block_len, int32_t n_anchor, const int32_t* block_tokens,
+                const void* target_hidden_new, int64_t hid_token_stride,
+                int64_t hid_layer_stride, int32_t n_new_total, const int32_t* new_offsets,
+                const int32_t* ctx_len, void* kv_k, void* kv_v, int32_t ctx_capacity,
+                int32_t n_drafts, float temperature, uint64_t seed, int32_t* draft_tokens,
+                float* logits_out, int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  g_err.clear();
+  int rc = check_draft_shape(desc, batch, block_len, n_anchor, n_new_total, n_drafts,
+                             temperature, ctx_capacity);
+  if (rc) return rc;
+  const dbd_model_desc& d = *desc;
+  if (!w) return fail(DBD_ERR_ARG, "weights is NULL");
+  if (!block_tokens || !new_offsets || !ctx_len || !kv_k || !kv_v || !draft_tokens)
+    return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (!w->attn_norm_w || !w->wq || !w->wk_draft || !w->wv_draft || !w->wo || !w->mlp_norm_w ||
+      !w->w_gate || !w->w_up || !w->w_down || !w->final_norm_w || !w->embed || !w->lm_head)
+    return fail(DBD_ERR_ARG, "a required weight pointer is NULL");
+  const int es = elem_size(d.dtype);
+  const int vec = 16 / es;
+  if (d.n_target_layers > 0) {
+    if (!w->mix_logits || !w->mix_norm_w || !w->wk_ctx || !w->wv_ctx)
+      return fail(DBD_ERR_ARG, "mixing weights are NULL but n_target_layers > 0");
+    if (n_new_total > 0) {
+      if (!target_hidden_new) return fail(DBD_ERR_ARG, "target_hidden_new is NULL");
+      if (!aligned16(target_hidden_new) || hid_token_stride % vec || hid_layer_stride % vec)
+        return fail(DBD_ERR_SHAPE, "target_hidden_new must be 16-byte aligned with strides "
+                    "that are multiples of %d elements", vec);
+      if (hid_token_stride <= 0 || hid_layer_stride <= 0)
+        return fail(DBD_ERR_ARG, "hidden strides must be positive");
+    }
+  }
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const size_t need = carve_draft(d, batch, block_len, n_anchor, n_new_total, n_drafts,
+                                  temperature, ctx_capacity, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  DraftBufs b;
+  carve_draft(d, batch, block_len, n_anchor, n_new_total, n_drafts, temperature, ctx_capacity,
+              (char*)workspace, &b);
+  hipStream_t st = (hipStream_t)stream;
+
+  const int N = batch, B = block_len, T = n_new_total;
+  const int H = d.hidden, hd = d.head_dim, kvh = d.n_kv_heads;
+  const int qd = d.n_q_heads * hd, kd = kvh * hd, F = d.ffn, V = d.vocab;
+  const int M = N * B, D = B - n_anchor, Md = N * D;
+  const int64_t layer_elems = (int64_t)N * kvh * ctx_capacity * hd;
+
+  // rotary inverse frequencies theta^(-2i/hd), fp64
+  double inv_freq[64];
+  for (int i = 0; i < hd / 2; ++i) inv_freq[i] = std::pow(d.rope_theta, -2.0 * i / hd);
+  HIP_STAGE(DBD_STAGE_PREP, st, launch_prep(ctx_len, new_offsets, N, B, T, ctx_capacity, hd, inv_freq, b.meta,
+                      seq_status, st));
+
+  // 1. ingest: mix + RMSNorm, then context K/V for every draft layer (batched over layers)
+  if (d.n_target_layers > 0 && T > 0) {
+    HIP_STAGE(DBD_STAGE_MIX, st, launch_mix_rmsnorm(d.dtype, target_hidden_new, hid_token_stride, hid_layer_stride, T,
+                               H, d.n_target_layers, d.n_layers, w->mix_logits, w->mix_norm_w,
+                               b.ctxfeat, d.rms_eps, st));
+    GemmArgs g{};
+    g.A = b.ctxfeat;
+    g.lda = H;
+    g.a_bs = (int64_t)T * H;
+    g.seg[0] = BSeg{w->wk_ctx, 0, kd};
+    g.seg[1] = BSeg{w->wv_ctx, kd, 2 * kd};
+    g.nseg = 2;
+    g.ldb = H;
+    g.b_bs = (int64_t)kd * H;
+    g.M = T;
+    g.N = 2 * kd;
+    g.K = H;
+    EpiArgs e{};
+    e.kind = EPI_CTXKV;
+    e.kv_k = kv_k;
+    e.kv_v = kv_v;
+    e.layer_stride = layer_elems;
+    e.qd = qd;
+    e.kd = kd;
+    e.hd = hd;
+    e.kvh = kvh;
+    e.block_len = B;
+    e.batch = N;
+    e.cap = ctx_capacity;
+    e.row_seq = b.meta.ctx_seq;
+    e.row_pos = b.meta.ctx_pos;
+    e.rope = b.meta.rope_ctx;
+    HIP_STAGE(DBD_STAGE_GEMM_CTXKV, st, launch_gemm(d.dtype, g, e, d.n_layers, st));
+  }
+
+  // 2. block forward
+  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_embed(d.dtype, block_tokens, w->embed, M, H, V, b.x, st));
+  const char* cw = nullptr;
+  for (int l = 0; l < d.n_layers; ++l) {
+    auto lw = [&](const void* p, int64_t per_layer) {
+      return (const void*)((const char*)p + (int64_t)l * per_layer * es);
+    };
+    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->attn_norm_w, H), b.xn, M, H, d.rms_eps, B, 0, st));
+    {
+      GemmArgs g{};
+      g.A = b.xn;
+      g.lda = H;
+      g.seg[0] = BSeg{lw(w->wq, (int64_t)qd * H), 0, qd};
+      g.seg[1] = BSeg{lw(w->wk_draft, (int64_t)kd * H), qd, qd + kd};
+      g.seg[2] = BSeg{lw(w->wv_draft, (int64_t)kd * H), qd + kd, qd + 2 * kd};
+      g.nseg = 3;
+      g.ldb = H;
+      g.M = M;
+      g.N = qd + 2 * kd;
+      g.K = H;
+      EpiArgs e{};
+      e.kind = EPI_QKV;
+      e.q_out = b.q;
+      e.kv_k = kv_k;
+      e.kv_v = kv_v;
+      e.layer_off_k = (int64_t)l * layer_elems;
+      e.qd = qd;
+      e.kd = kd;
+      e.hd = hd;
+      e.kvh = kvh;
+      e.block_len = B;
+      e.batch = N;
+      e.cap = ctx_capacity;
+      e.row_pos = b.meta.blk_pos;
+      e.rope = b.meta.rope_blk;
+      HIP_STAGE(DBD_STAGE_GEMM_QKV, st, launch_gemm(d.dtype, g, e, 1, st));
+    }
+    {
+      AttnArgs a{};
+      a.q = b.q;
+      a.kv_k = (const char*)kv_k + (int64_t)l * layer_elems * es;
+      a.kv_v = (const char*)kv_v + (int64_t)l * layer_elems * es;
+      a.seq_keys = b.meta.seq_keys;
+      a.out = b.attn;
+      a.part_o = b.part_o;
+      a.part_ml = b.part_ml;
+      a.batch = N;
+      a.kvh = kvh;
+      a.grp = d.n_q_heads / kvh;
+      a.block_len = B;
+      a.cap = ctx_capacity;
+      a.qd = qd;
+      a.s_max = b.s_max;
+      a.split = b.split;
+      a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      HIP_STAGE(DBD_STAGE_ATTN, st, launch_attention(d.dtype, hd, a, st));
+    }
+    {
+      GemmArgs g{};
+      g.A = b.attn;
+      g.lda = qd;
+      g.seg[0] = BSeg{lw(w->wo, (int64_t)H * qd), 0, H};
+      g.nseg = 1;
+      g.ldb = qd;
+      g.M = M;
+      g.N = H;
+      g.K = qd;
+      EpiArgs e{};
+      e.kind = EPI_RESID;
+      e.C = b.x;
+      e.ldc = H;
+      HIP_STAGE(DBD_STAGE_GEMM_O, st, launch_gemm(d.dtype, g, e, 1, st));
+    }
+    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->mlp_norm_w, H), b.xn, M, H, d.rms_eps, B, 0, st));
+    {
+      GemmArgs g{};
+      g.A = b.xn;
+      g.lda = H;
+      g.seg[0] = BSeg{lw(w->w_gate, (int64_t)F * H), 0, F};
+      g.seg[1] = BSeg{lw(w->w_up, (int64_t)F * H), 0, F};
+      g.nseg = 2;
+      g.gateup = 1;
+      g.ldb = H;
+      g.M = M;
+      g.N = ceil_div(F, 64) * 128;
+      g.K = H;
+      EpiArgs e{};
+      e.kind = EPI_SWIGLU;
+      e.act = b.act;
+      e.F = F;
+      HIP_STAGE(DBD_STAGE_GEMM_GATEUP, st, launch_gemm(d.dtype, g, e, 1, st));
+    }
+    {
+      GemmArgs g{};
+      g.A = b.act;
+      g.lda = F;
+      g.seg[0] = BSeg{lw(w->w_down, (int64_t)H * F), 0, H};
+      g.nseg = 1;
+      g.ldb = F;
+      g.M = M;
+      g.N = H;
+      g.K = F;
+      EpiArgs e{};
+      e.kind = EPI_RESID;
+      e.C = b.x;
+      e.ldc = H;
+      HIP_STAGE(DBD_STAGE_GEMM_DOWN, st, launch_gemm(d.dtype, g, e, 1, st));
+    }
+  }
+  (void)cw;
+
+  // 3. final norm on the mask rows, LM head
+  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, w->final_norm_w, b.xn, Md, H, d.rms_eps, B, n_anchor, st));
+  const bool sampling = temperature > 0.f;
+  float* logits = logits_out ? logits_out : (sampling ? b.logits : nullptr);
+  {
+    GemmArgs g{};
+    g.A = b.xn;
+    g.lda = H;
+    g.seg[0] = BSeg{w->lm_head, 0, V};
+    g.nseg = 1;
+    g.ldb = H;
+    g.M = Md;
+    g.N = V;
+    g.K = H;
+    EpiArgs e{};
+    if (sampling) {
+      e.kind = EPI_STORE_F32;
+      e.C = logits;
+      e.ldc = V;
+    } else {
+      e.kind = EPI_ARGMAX;
+      e.part_val = b.lm_pv;
+      e.part_idx = b.lm_pi;
+      e.ntiles = b.ntiles;
+      e.logits = logits;
+      e.ldc = V;
+    }
+    HIP_STAGE(DBD_STAGE_GEMM_LMHEAD, st, launch_gemm(d.dtype, g, e, 1, st));
+  }
+  // 4. drafts
+  if (!sampling) {
+    HIP_STAGE(DBD_STAGE_DRAFT, st, launch_lm_argmax_final(b.lm_pv, b.lm_pi, Md, b.ntiles, b.meta.blk_pos, B, n_anchor,
+                                   D, draft_tokens, st));
+  } else {
+    const int ch = vocab_chunk();
+    const float inv_t = (float)(1.0 / (double)temperature);
+    HIP_STAGE(DBD_STAGE_DRAFT, st, launch_argmax_partial(logits, Md, V, ch, b.vpv, b.vpi,
+                                                         b.vflag, st));
+    HIP_STAGE(DBD_STAGE_DRAFT, st, launch_zsum_partial(logits, Md, V, ch, b.vpv, b.vpi, inv_t, b.zpart, b.row_max,
+                                b.row_arg, st));
+    HIP_STAGE(DBD_STAGE_DRAFT, st, launch_sample_pick(logits, Md, V, ch, b.zpart, b.row_max, inv_t, D, n_drafts, seed,
+                               b.meta.blk_pos, B, n_anchor, draft_tokens, st));
+  }
+  return DBD_OK;
+}
+
+// ------------------------------------------------------------------ verify / select
+static size_t carve_verify(int rows, int vocab, char* base, float** pv, int32_t** pi,
+                           int32_t** pf) {
+  Carver c{base};
+  const int nch = ceil_div(vocab, vocab_chunk());
+  float* a = c.take<float>((int64_t)rows * nch);
+  int32_t* b = c.take<int32_t>((int64_t)rows * nch);
+  int32_t* f = c.take<int32_t>((int64_t)rows * nch);
+  if (pv) { *pv = a; *pi = b; *pf = f; }
+  return (c.off + kAlign - 1) / kAlign * kAlign;
+}
+
+int dbd_verify_workspace_bytes(int32_t batch, int32_t n_rows, int32_t vocab, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (batch < 1 || n_rows < 1 || vocab < 2) return fail(DBD_ERR_ARG, "bad dimensions");
+  *bytes = carve_verify(batch * n_rows, vocab, nullptr, nullptr, nullptr, nullptr);
+  return DBD_OK;
+}
+
+int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32_t draft_stride,
+                  int32_t batch, int32_t n_draft, int32_t n_rows, int32_t vocab,
+                  int32_t* n_accepted, int32_t* bonus, int32_t* committed, int32_t* row_flags,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!target_logits || !draft_tokens || !n_accepted || !bonus || !committed)
+    return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2 || vocab >= (1 << 18))
+    return fail(DBD_ERR_ARG, "bad dimensions (batch %d, n_draft %d, vocab %d)", batch, n_draft,
+                vocab);
+  if (n_draft > 64) return fail(DBD_ERR_UNSUPPORTED, "n_draft %d > 64", n_draft);
+  if (n_rows != n_draft && n_rows != n_draft + 1)
+    return fail(DBD_ERR_SHAPE, "n_rows %d must be n_draft or n_draft + 1", n_rows);
+  if (draft_stride < n_draft) return fail(DBD_ERR_SHAPE, "draft_stride < n_draft");
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const int rows = batch * n_rows;
+  const size_t need = carve_verify(rows, vocab, nullptr, nullptr, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  float* pv;
+  int32_t *pi, *pf;
+  carve_verify(rows, vocab, (char*)workspace, &pv, &pi, &pf);
+  hipStream_t st = (hipStream_t)stream;
+  const int ch = vocab_chunk();
+  HIP_STAGE(DBD_STAGE_VERIFY, st, launch_argmax_partial(target_logits, rows, vocab, ch, pv, pi,
+                                                        pf, st));
+  HIP_STAGE(DBD_STAGE_VERIFY, st, launch_verify_finalize(pv, pi, pf, ceil_div(vocab, ch), draft_tokens, draft_stride,
+                                 batch, n_draft, n_rows, n_accepted, bonus, committed, row_flags,
+                                 st));
+  return DBD_OK;
+}
+
+static size_t carve_select(int rows, int vocab, char* base, float** pv, int32_t** pi,
+                           int32_t** pf, uint64_t** zp, float** rm, int32_t** ra) {
+  Carver c{base};
+  const int nch = ceil_div(vocab, vocab_chunk());
+  float* a = c.take<float>((int64_t)rows * nch);
+  int32_t* b = c.take<int32_t>((int64_t)rows * nch);
+  int32_t* f = c.take<int32_t>((int64_t)rows * nch);
+  uint64_t* z = c.take<uint64_t>((int64_t)rows * nch);
+  float* m = c.take<float>(rows);
+  int32_t* r = c.take<int32_t>(rows);
+  if (pv) { *pv = a; *pi = b; *pf = f; *zp = z; *rm = m; *ra = r; }
+  return (c.off + kAlign - 1) / kAlign * kAlign;
+}
+
+int dbd_select_workspace_bytes(int32_t batch, int32_t n_drafts, int32_t n_rows, int32_t vocab,
+                               size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (batch < 1 || n_drafts < 1 || n_rows < 1 || vocab < 2)
+    return fail(DBD_ERR_ARG, "bad dimensions");
+  *bytes = carve_select(batch * n_drafts * n_rows, vocab, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, nullptr, nullptr);
+  return DBD_OK;
+}
+
+int select_streak(const float* verifier_logits, const int32_t* drafts, int32_t batch,
+                  int32_t n_drafts, int32_t gamma, int32_t n_rows, int32_t vocab,
+                  int32_t* selected, double* scores, int32_t* n_accepted, int32_t* bonus,
+                  int32_t* committed, int32_t* row_flags, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!verifier_logits || !drafts || !selected || !n_accepted || !bonus || !committed)
+    return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (batch < 1 || n_drafts < 1 || gamma < 1 || vocab < 2 || vocab >= (1 << 18))
+    return fail(DBD_ERR_ARG, "bad dimensions");
+  if (n_drafts > 64) return fail(DBD_ERR_UNSUPPORTED, "n_drafts %d > 64", n_drafts);
+  if (gamma > 64) return fail(DBD_ERR_UNSUPPORTED, "gamma %d > 64", gamma);
+  if (n_rows != gamma && n_rows != gamma + 1)
+    return fail(DBD_ERR_SHAPE, "n_rows %d must be gamma or gamma + 1", n_rows);
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const int rows = batch * n_drafts * n_rows;
+  const size_t need = carve_select(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  float *pv, *rm;
+  int32_t *pi, *pf, *ra;
+  uint64_t* zp;
+  carve_select(rows, vocab, (char*)workspace, &pv, &pi, &pf, &zp, &rm, &ra);
+  hipStream_t st = (hipStream_t)stream;
+  const int ch = vocab_chunk();
+  HIP_STAGE(DBD_STAGE_SELECT, st, launch_argmax_partial(verifier_logits, rows, vocab, ch, pv, pi,
+                                                        pf, st));
+  HIP_STAGE(DBD_STAGE_SELECT, st, launch_zsum_partial(verifier_logits, rows, vocab, ch, pv, pi,
+                                                      1.0f, zp, rm, ra, st));
+  HIP_STAGE(DBD_STAGE_SELECT, st, launch_select_finalize(verifier_logits, vocab, ch, zp, rm, ra, pf, drafts, batch,
+                                 n_drafts, gamma, n_rows, selected, scores, n_accepted, bonus,
+                                 committed, row_flags, st));
+  return DBD_OK;
+}
+
+// ------------------------------------------------------------------ test hooks
+static size_t carve_sample(int rows, int vocab, char* base, float** pv, int32_t** pi,
+                           int32_t** pf, uint64_t** zp, float** rm, int32_t** ra) {
+  return carve_select(rows, vocab, base, pv, pi, pf, zp, rm, ra);
+}
+
+int dbd_sample_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2) return fail(DBD_ERR_ARG, "bad dimensions");
+  *bytes = carve_sample(batch * n_draft, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, nullptr);
+  return DBD_OK;
+}
+
+int dbd_sample_from_logits(const float* logits, int32_t batch, int32_t n_draft, int32_t vocab,
+                           int32_t n_drafts, float temperature, uint64_t seed, int32_t* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!logits || !out) return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2 || vocab >= (1 << 18))
+    return fail(DBD_ERR_ARG, "bad dimensions");
+  if (n_drafts < 1 || n_drafts > 64) return fail(DBD_ERR_ARG, "n_drafts out of [1, 64]");
+  if (!(temperature > 0.f) && n_drafts != 1)
+    return fail(DBD_ERR_ARG, "argmax drafting (temperature <= 0) needs n_drafts == 1");
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const int rows = batch * n_draft;
+  const size_t need = carve_sample(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  float *pv, *rm;
+  int32_t *pi, *pf, *ra;
+  uint64_t* zp;
+  carve_sample(rows, vocab, (char*)workspace, &pv, &pi, &pf, &zp, &rm, &ra);
+  hipStream_t st = (hipStream_t)stream;
+  const int ch = vocab_chunk();
+  HIP_TRY(launch_argmax_partial(logits, rows, vocab, ch, pv, pi, pf, st));
+  if (!(temperature > 0.f)) {
+    HIP_TRY(launch_argmax_final(pv, pi, rows, ceil_div(vocab, ch), out, nullptr, st));
+    return DBD_OK;
+  }
+  const float inv_t = (float)(1.0 / (double)temperature);
+  HIP_TRY(launch_zsum_partial(logits, rows, vocab, ch, pv, pi, inv_t, zp, rm, ra, st));
+  HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, zp, rm, inv_t, n_draft, n_drafts, seed,
+                             nullptr, 0, 0, out, st));
+  return DBD_OK;
+}
+
+int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const void* mix_norm_w,
+                    const void* hidden, int64_t hid_token_stride, int64_t hid_layer_stride,
+                    int32_t n_tokens, void* out, void* stream) {
+  g_err.clear();
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->n_target_layers < 1) return fail(DBD_ERR_ARG, "n_target_layers must be >= 1");
+  if (!mix_logits || !mix_norm_w || !hidden || !out)
+    return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  const int vec = 16 / elem_size(desc->dtype);
+  if (!aligned16(hidden) || hid_token_stride % vec || hid_layer_stride % vec || n_tokens < 0)
+    return fail(DBD_ERR_SHAPE, "hidden must be 16-byte aligned with strides multiple of %d",
+                vec);
+  HIP_TRY(launch_mix_rmsnorm(desc->dtype, hidden, hid_token_stride, hid_layer_stride, n_tokens,
+                             desc->hidden, desc->n_target_layers, desc->n_layers, mix_logits,
+                             mix_norm_w, out, desc->rms_eps, (hipStream_t)stream));
+  return DBD_OK;
+}
+
+int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t M, int32_t N,
+                int32_t K, int64_t lda, int64_t ldb, int64_t ldc, void* stream) {
+  g_err.clear();
+  if (dtype != DBD_F32 && dtype != DBD_BF16) return fail(DBD_ERR_ARG, "bad dtype");
+  if (!A || !Bm || !C) return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (M < 0 || N < 0 || K < 1 || lda < K || ldb < K || ldc < N)
+    return fail(DBD_ERR_SHAPE, "bad GEMM dimensions");
+  if (dtype == DBD_BF16 && (K % 64 || lda % 8 || ldb % 8 || !aligned16(A) || !aligned16(Bm)))
+    return fail(DBD_ERR_SHAPE, "bf16 GEMM needs K % 64 == 0, 16-byte aligned rows");
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.seg[0] = BSeg{Bm, 0, N};
+  g.nseg = 1;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  EpiArgs e{};
+  e.kind = EPI_STORE_F32;
+  e.C = C;
+  e.ldc = ldc;
+  HIP_TRY(launch_gemm(dtype, g, e, 1, (hipStream_t)stream));
+  return DBD_OK;
+}
+
+}  // extern "C"

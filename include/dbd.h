@@ -1,0 +1,263 @@
+/*
+ * dbd.h - C ABI of libdbd.so: the data-parallel hot path of block-diffusion speculative drafting
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method (the pages the library is built from):
+ *   [DFlare]     "DFlare: Scaling Up Draft Capacity for Block Diffusion Speculative Decoding", as
+ *                summarised on the iplexlaw blog page on DFlare block-diffusion drafting.
+ *   [SpecDiff-2] "SpecDiff-2: Scaling Diffusion Drafter Alignment For Faster Speculative
+ *                Decoding", MLSys 2026 talk notes.
+ *   [DFlash]     "DFlash: Block Diffusion for Flash Speculative Decoding", Qiita article.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and allocates every
+ *     buffer, including the workspace; the library allocates and frees nothing and keeps no
+ *     device state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  Calls return after
+ *     enqueueing; they never synchronise the device.
+ *   - Arguments are validated on the host before any launch; a non-zero return means nothing was
+ *     enqueued.  dbd_last_error() gives a message for the last failure on the calling thread.
+ *   - Dense tensors are row-major and contiguous unless a stride is given; "Linear" weights are
+ *     [out_features, in_features] (y = x W^T).
+ *   - Integer outputs (token ids, accepted lengths, selected drafts) are a pure function of the
+ *     inputs; ties in an argmax go to the lowest token index, ties between drafts to the lowest
+ *     draft index.
+ *   - Calls on different streams with disjoint output buffers are independent.
+ */
+#ifndef DBD_H
+#define DBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  DBD_OK = 0,
+  DBD_ERR_ARG = -1,          /* a required pointer is NULL or a scalar is out of range */
+  DBD_ERR_SHAPE = -2,        /* dimensions inconsistent or not supported by the kernels */
+  DBD_ERR_CAPACITY = -3,     /* KV-cache capacity too small for the requested work */
+  DBD_ERR_WORKSPACE = -4,    /* workspace NULL, misaligned (256 B) or smaller than required */
+  DBD_ERR_UNSUPPORTED = -5,  /* valid request outside what this build implements */
+  DBD_ERR_HIP = -6           /* a HIP runtime call failed (message has the HIP error) */
+};
+
+/* Element type of weights, target hidden states, KV cache and internal activations. */
+enum { DBD_F32 = 0, DBD_BF16 = 1 };
+
+/* Per-sequence status bits written by draft_block (seq_status) and the verify calls
+ * (row_flags). */
+enum {
+  DBD_SEQ_NONFINITE = 1,     /* a non-finite logit was seen in this sequence's rows */
+  DBD_SEQ_BAD_LENGTH = 2     /* ctx_len / new_offsets inconsistent or beyond capacity: the
+                                sequence was skipped and its outputs are -1 */
+};
+
+/* Drafter architecture (host struct).
+ * [DFlare], sections on per-draft-layer mixing and on splitting K/V projections by source:
+ * every draft layer mixes n_target_layers target hidden states with its own softmax weights and
+ * RMS-normalises the mix; context features and draft-block features have separate K/V
+ * projections; queries come from the draft block.  The block is one forward pass, attention is
+ * bidirectional inside the block and reaches the whole context ([DFlare] section on parallel
+ * drafting; [DFlash] section on writing a block in one forward pass).  The embedding and LM head
+ * are the target's, shared.  Layer form: pre-norm, RMSNorm y = x / sqrt(mean(x^2) + rms_eps) * g,
+ * rotate-half RoPE with base rope_theta on Q and on both kinds of K, SwiGLU MLP, no biases.
+ * n_target_layers = 0 describes a drafter with no target mixing ([SpecDiff-2] section 4: a
+ * standalone diffusion drafter) whose context K/V the caller supplies in the cache. */
+typedef struct {
+  int32_t hidden;            /* H */
+  int32_t n_q_heads;         /* qh */
+  int32_t n_kv_heads;        /* kvh; qh % kvh == 0 */
+  int32_t head_dim;          /* hd: 64 or 128 */
+  int32_t ffn;               /* F, SwiGLU inner size */
+  int32_t n_layers;          /* L_d, draft layers */
+  int32_t n_target_layers;   /* L_t, mixed target layers (0..16); 0 = context K/V in the cache */
+  int32_t vocab;             /* V < 2^18 */
+  int32_t mask_token_id;     /* id of [MASK] (informational: block_tokens carry the ids) */
+  int32_t dtype;             /* DBD_F32 or DBD_BF16 */
+  float rms_eps;             /* e.g. 1e-6 */
+  float reserved0;
+  double rope_theta;         /* e.g. 1e6 */
+} dbd_model_desc;
+
+/* Drafter weights (device pointers, element type desc.dtype unless noted).  Per-layer tensors
+ * are stacked over the L_d draft layers. */
+typedef struct {
+  const float* mix_logits;   /* [L_d, L_t] fp32 mixing logits (unused if L_t == 0) */
+  const void* mix_norm_w;    /* [L_d, H] RMSNorm gain after mixing (unused if L_t == 0) */
+  const void* wk_ctx;        /* [L_d, kvh*hd, H] context K projection (unused if L_t == 0) */
+  const void* wv_ctx;        /* [L_d, kvh*hd, H] context V projection (unused if L_t == 0) */
+  const void* attn_norm_w;   /* [L_d, H] */
+  const void* wq;            /* [L_d, qh*hd, H] */
+  const void* wk_draft;      /* [L_d, kvh*hd, H] draft-block K projection */
+  const void* wv_draft;      /* [L_d, kvh*hd, H] draft-block V projection */
+  const void* wo;            /* [L_d, H, qh*hd] */
+  const void* mlp_norm_w;    /* [L_d, H] */
+  const void* w_gate;        /* [L_d, F, H] */
+  const void* w_up;          /* [L_d, F, H] */
+  const void* w_down;        /* [L_d, H, F] */
+  const void* final_norm_w;  /* [H] */
+  const void* embed;         /* [V, H] shared token embedding */
+  const void* lm_head;       /* [V, H] shared LM head (may alias embed) */
+} dbd_weights;
+
+/* KV-cache layout (device, element type desc.dtype, caller-owned, persistent across calls):
+ *   kv_k: [L_d, N, kvh, ctx_capacity, hd]   rotated keys, one row of hd per position;
+ *   kv_v: [L_d, N, kvh, hd, ctx_capacity]   values stored position-minor (transposed) so that
+ *         the attention's P.V product reads contiguous runs of positions.
+ * ctx_capacity must be a multiple of 64. */
+
+/* Workspace size (host) for draft_block with at most `max_batch` sequences, block length
+ * `block_len`, `n_anchor` anchors, at most `max_new_tokens` ingested rows in total, `n_drafts`
+ * drafts per block, the given temperature (> 0: sampling) and cache capacity. */
+int dbd_draft_workspace_bytes(const dbd_model_desc* desc, int32_t max_batch, int32_t block_len,
+                              int32_t n_anchor, int32_t max_new_tokens, int32_t n_drafts,
+                              float temperature, int32_t ctx_capacity,
+                              size_t* bytes /* host out */);
+
+/* draft_block: one forward pass of the block-diffusion drafter for a batch of sequences,
+ * followed by drafting from its single-step marginals.
+ *
+ * Steps ([DFlare] mixing / K-V split / parallel drafting sections; [SpecDiff-2] sections 4
+ * and 5.2):
+ *   1. ingest: for the n_new[n] = new_offsets[n+1] - new_offsets[n] newly committed positions of
+ *      each sequence (rows new_offsets[n] .. new_offsets[n+1]-1 of target_hidden_new, positions
+ *      ctx_len[n] .. ctx_len[n]+n_new[n]-1), every draft layer l mixes the L_t target hidden
+ *      states with softmax(mix_logits[l]), applies RMSNorm * mix_norm_w[l], projects with
+ *      wk_ctx[l] / wv_ctx[l], rotates K and appends both to the cache;
+ *   2. block: x = embed[block_tokens] at positions P+b, P = ctx_len[n] + n_new[n]; each layer:
+ *      RMSNorm, Q/K/V from the block with wq/wk_draft/wv_draft (Q and K rotated); the block's K/V
+ *      are written into the cache at positions P .. P+B-1 (scratch: the next call's ingest
+ *      overwrites them); attention of every block row over cache positions 0 .. P+B-1 with no
+ *      mask; output projection and residual; RMSNorm, SwiGLU MLP and residual;
+ *   3. head: final RMSNorm and LM head on the D = B - n_anchor mask rows;
+ *   4. drafts: temperature <= 0 -> per-row argmax (n_drafts must be 1); temperature > 0 ->
+ *      n_drafts independent joint drafts, each position sampled from softmax(logits / T) with the
+ *      library's integer-exact sampler (counter RNG seeded by `seed`).
+ *
+ * block_tokens      [N, B] int32 (device): [anchor, MASK, ...] (n_anchor = 1) or all masks (0).
+ * target_hidden_new device, element type desc.dtype: row t, target layer i starts at element
+ *                   t*hid_token_stride + i*hid_layer_stride; H contiguous.  May be NULL when
+ *                   n_new_total == 0.  Ignored when L_t == 0.
+ * n_new_total       (host) total ingested rows = new_offsets[N] - new_offsets[0]; must be 0 when
+ *                   L_t == 0.
+ * new_offsets       [N+1] int32 (device), non-decreasing.
+ * ctx_len           [N] int32 (device): cached positions before this call.  Not modified; the
+ *                   caller advances it by n_new[n] after the call.
+ * kv_k, kv_v        the cache (layout above), read and written.
+ * draft_tokens      [N, n_drafts, D] int32 (device) out.
+ * logits_out        [N, D, V] fp32 (device) out, optional (NULL): the LM-head logits.
+ * seq_status        [N] int32 (device) out, optional: DBD_SEQ_* bits.
+ * workspace         device, 256-byte aligned, >= dbd_draft_workspace_bytes(...).
+ *
+ * Sequences whose lengths do not fit the capacity (P + B > ctx_capacity) are detected on the
+ * device: they get DBD_SEQ_BAD_LENGTH, their drafts are -1 and the cache is not touched for
+ * them. */
+int draft_block(const dbd_model_desc* desc, const dbd_weights* weights, int32_t batch,
+                int32_t block_len, int32_t n_anchor, const int32_t* block_tokens,
+                const void* target_hidden_new, int64_t hid_token_stride,
+                int64_t hid_layer_stride, int32_t n_new_total, const int32_t* new_offsets,
+                const int32_t* ctx_len, void* kv_k, void* kv_v, int32_t ctx_capacity,
+                int32_t n_drafts, float temperature, uint64_t seed, int32_t* draft_tokens,
+                float* logits_out, int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Workspace size (host) for verify_greedy. */
+int dbd_verify_workspace_bytes(int32_t batch, int32_t n_rows, int32_t vocab,
+                               size_t* bytes /* host out */);
+
+/* verify_greedy: greedy verification of one draft per sequence ([DFlare] section on parallel
+ * drafting and acceptance by the target: under greedy decoding the prefix up to the first
+ * mismatch is accepted and the target's next token is appended).
+ *
+ * target_logits [N, n_rows, V] fp32: row j is the target's distribution for draft position j;
+ *               n_rows is D or D+1 (the last row scores the token after a full accept).
+ * draft_tokens  [N, D] int32, row stride `draft_stride` elements (>= D).
+ * With t_j = argmax(row j): n_accepted[n] = first j with draft[j] != t_j (D if none);
+ * bonus[n] = t_{n_acc} if n_acc < n_rows else -1; committed[n] = draft[0..n_acc-1] followed by
+ * the bonus, padded with -1 to D+1 entries.  row_flags[n] (optional) gets DBD_SEQ_NONFINITE if a
+ * non-finite logit was seen (the argmax then ignores NaNs). */
+int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32_t draft_stride,
+                  int32_t batch, int32_t n_draft, int32_t n_rows, int32_t vocab,
+                  int32_t* n_accepted, int32_t* bonus, int32_t* committed, int32_t* row_flags,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace size (host) for select_streak. */
+int dbd_select_workspace_bytes(int32_t batch, int32_t n_drafts, int32_t n_rows, int32_t vocab,
+                               size_t* bytes /* host out */);
+
+/* select_streak: self-selection among K joint drafts by expected streak, then greedy acceptance
+ * on the chosen draft ([SpecDiff-2] section 5.2, with the streak equation of section 5.1).
+ *
+ * verifier_logits [N, K, n_rows, V] fp32: row (n, k, j) is the verifier's distribution for
+ *                 position j of draft k given that draft's prefix; n_rows is G or G+1.
+ * drafts          [N, K, G] int32.
+ * p_{k,j} = q(x_j) / Z of row (n,k,j) with the library's integer weights (temperature 1);
+ * S_k = sum_{m=1..G} prod_{j<=m} p_{k,j} accumulated in fp64 in position order;
+ * selected[n] = argmax_k S_k (lowest k on ties); scores [N, K] fp64 (optional);
+ * n_accepted / bonus / committed [N, G+1] / row_flags as in verify_greedy on rows (n, k*, .). */
+int select_streak(const float* verifier_logits, const int32_t* drafts, int32_t batch,
+                  int32_t n_drafts, int32_t gamma, int32_t n_rows, int32_t vocab,
+                  int32_t* selected, double* scores, int32_t* n_accepted, int32_t* bonus,
+                  int32_t* committed, int32_t* row_flags, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* ---- Test hooks: exported for parity tests of single stages; not part of the drafting API ---- */
+
+/* Workspace size (host) for dbd_sample_from_logits. */
+int dbd_sample_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab, size_t* bytes);
+
+/* The drafting stage of draft_block on given fp32 logits [N, D, V]: argmax (temperature <= 0,
+ * n_drafts == 1) or n_drafts samples per position; out [N, n_drafts, D] int32. */
+int dbd_sample_from_logits(const float* logits, int32_t batch, int32_t n_draft, int32_t vocab,
+                           int32_t n_drafts, float temperature, uint64_t seed, int32_t* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* The ingest mixing stage of draft_block ([DFlare] section on per-draft-layer mixing):
+ * out[l, t, :] = RMSNorm(sum_i softmax(mix_logits[l])_i * hidden[t, i, :]) * mix_norm_w[l],
+ * out [L_d, n_tokens, H] in desc.dtype. */
+int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const void* mix_norm_w,
+                    const void* hidden, int64_t hid_token_stride, int64_t hid_layer_stride,
+                    int32_t n_tokens, void* out, void* stream);
+
+/* The GEMM used for every projection: C[M, N] (fp32) = A[M, K] . B[N, K]^T with A, B in
+ * `dtype`; row strides lda, ldb, ldc in elements.  bf16 needs K % 64 == 0. */
+int dbd_gemm_nt(int32_t dtype, const void* A, const void* B, float* C, int32_t M, int32_t N,
+                int32_t K, int64_t lda, int64_t ldb, int64_t ldc, void* stream);
+
+/* Per-stage timing for benchmarks.  While enabled, every kernel launch of the library is
+ * bracketed by a pair of hipEvents recorded on the launch's stream and accounted to its stage
+ * (DBD_STAGE_*).  Enabling creates the events (hipEventCreate); it is not meant for production
+ * calls.  dbd_timing_read synchronises on the recorded events and returns, for one stage, the
+ * summed kernel milliseconds and the number of launches since the last reset. */
+enum {
+  DBD_STAGE_PREP = 0,        /* row metadata and rotary tables */
+  DBD_STAGE_MIX = 1,         /* ingest mix + RMSNorm */
+  DBD_STAGE_GEMM_CTXKV = 2,  /* context K/V projection + cache append */
+  DBD_STAGE_ROWNORM = 3,     /* embedding gather and RMSNorm */
+  DBD_STAGE_GEMM_QKV = 4,
+  DBD_STAGE_ATTN = 5,        /* attention + split combine */
+  DBD_STAGE_GEMM_O = 6,
+  DBD_STAGE_GEMM_GATEUP = 7,
+  DBD_STAGE_GEMM_DOWN = 8,
+  DBD_STAGE_GEMM_LMHEAD = 9,
+  DBD_STAGE_DRAFT = 10,      /* argmax reduction or sampling of the drafts */
+  DBD_STAGE_VERIFY = 11,     /* verify_greedy */
+  DBD_STAGE_SELECT = 12,     /* select_streak */
+  DBD_STAGE_COUNT = 13
+};
+int dbd_timing_enable(int on);
+int dbd_timing_reset(void);
+int dbd_timing_read(int stage, double* total_ms /* host out */, int64_t* launches /* host out */);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* dbd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBD_H */

@@ -1,0 +1,122 @@
+"""Build one synthetic workload on the GPU, run the library on it, and prepare the oracle's view
+of the same inputs.  Shared by the GPU parity tests (not collected itself)."""
+import numpy as np
+import torch
+
+import block_diffusion_drafter_draft_amd as dbd
+import synth
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class Case:
+    """Inputs of one draft_block step for workload ``wl`` plus the library's outputs.
+
+    The cache holds the cached context of every sequence: filled by a cold draft_block call that
+    ingests positions 0 .. C_n-1 (target-mixing drafters) or copied from synthetic rotated K/V
+    (drafters that take their context from a cache).  The measured step then ingests n_new
+    positions and drafts the block."""
+
+    def __init__(self, wl, seed=0, dev="cuda", ctx=None, new=None, seqs_hidden=None):
+        self.wl, self.dev, self.seed = wl, dev, seed
+        sh = wl.shape
+        self.shape = sh
+        self.desc = dbd.model_desc(sh)
+        self.W = synth.make_weights(sh, seed, dev)
+        self.wstruct = dbd.weights_struct(self.W)
+        c, n = synth.make_lengths(wl, seed)
+        self.ctx = np.asarray(ctx if ctx is not None else c, np.int64)
+        self.new = np.asarray(new if new is not None else n, np.int64)
+        self.cap = synth.capacity_for(wl, self.ctx, self.new)
+        N, B = wl.batch, wl.block_len
+        self.tokens = synth.make_block_tokens(wl, seed, dev)
+        L, kvh, hd = sh.n_layers, sh.n_kv_heads, sh.head_dim
+        dt = DT[sh.dtype]
+        self.kv_k = torch.zeros((L, N, kvh, self.cap, hd), dtype=dt, device=dev)
+        self.kv_v = torch.zeros((L, N, kvh, hd, self.cap), dtype=dt, device=dev)
+        self.D = B - wl.n_anchor
+        self.cache_kv = None
+        if wl.ctx_source == "hidden":
+            self.hidden = [synth.make_hidden(sh, int(self.ctx[i] + self.new[i]), seed, i, dev)
+                           for i in range(N)]
+        else:
+            K, V = synth.make_cache_kv(sh, N, int(self.ctx.max()), seed, dev)
+            self.cache_kv = (K, V)
+            for i in range(N):
+                C = int(self.ctx[i])
+                self.kv_k[:, i, :, :C, :] = K[:, i, :, :C, :]
+                self.kv_v[:, i, :, :, :C] = V[:, i, :, :C, :].transpose(-1, -2)
+
+    # ------------------------------------------------------------------ running the library
+    def _offsets(self, counts):
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        return torch.tensor(off, device=self.dev), int(off[-1])
+
+    def _hidden_rows(self, lo, hi):
+        rows = [self.hidden[i][int(lo[i]):int(hi[i])] for i in range(self.wl.batch)]
+        return torch.cat(rows, 0).contiguous()
+
+    def workspace(self, n_new_total, n_drafts, temperature):
+        nb = dbd.draft_workspace_bytes(self.desc, self.wl.batch, self.wl.block_len,
+                                       self.wl.n_anchor, n_new_total, n_drafts, temperature,
+                                       self.cap)
+        return torch.empty(nb, dtype=torch.uint8, device=self.dev)
+
+    def call(self, ctx_len, counts, hidden, n_drafts=None, temperature=None, seed=1234,
+             logits=True):
+        wl = self.wl
+        K = n_drafts if n_drafts is not None else wl.n_drafts
+        T = temperature if temperature is not None else wl.temperature
+        off, tot = self._offsets(counts)
+        ws = self.workspace(tot, K, T)
+        out = torch.full((wl.batch, K, self.D), -7, dtype=torch.int32, device=self.dev)
+        lg = (torch.empty((wl.batch, self.D, self.shape.vocab), dtype=torch.float32,
+                          device=self.dev) if logits else None)
+        st = torch.full((wl.batch,), -7, dtype=torch.int32, device=self.dev)
+        dbd.draft_block(self.desc, self.wstruct, self.tokens, hidden, off,
+                        torch.tensor(np.asarray(ctx_len, np.int32), device=self.dev), self.kv_k,
+                        self.kv_v, out, ws, tot, n_drafts=K, temperature=T, seed=seed,
+                        n_anchor=wl.n_anchor, logits_out=lg, seq_status=st)
+        return out, lg, st
+
+    def fill_cache(self):
+        """Cold ingest of positions 0 .. C_n-1 (target-mixing drafters only)."""
+        if self.wl.ctx_source != "hidden":
+            return
+        zeros = np.zeros(self.wl.batch, np.int64)
+        h = self._hidden_rows(zeros, self.ctx)
+        self.call(zeros, self.ctx, h if h.numel() else None, logits=False)
+
+    def step(self, **kw):
+        """The measured step: ingest n_new positions at C_n, draft the block."""
+        if self.wl.ctx_source == "hidden":
+            h = self._hidden_rows(self.ctx, self.ctx + self.new)
+            return self.call(self.ctx, self.new, h if h.numel() else None, **kw)
+        return self.call(self.ctx, np.zeros(self.wl.batch, np.int64), None, **kw)
+
+    # ------------------------------------------------------------------ the oracle's view
+    def cpu_weights(self):
+        return {k: v.detach().to("cpu") for k, v in self.W.items()}
+
+    def oracle_inputs(self, i):
+        """(block tokens, hidden [C+n, L_t, H] or None, ctx_kv or None) of sequence i on CPU."""
+        toks = self.tokens[i].to("cpu").numpy()
+        if self.wl.ctx_source == "hidden":
+            return toks, self.hidden[i].to("cpu"), None
+        K, V = self.cache_kv
+        C = int(self.ctx[i])
+        kv = [(K[l, i, :, :C, :].to("cpu"), V[l, i, :, :C, :].to("cpu"))
+              for l in range(self.shape.n_layers)]
+        return toks, None, kv
+
+    def gpu_cache(self, i, l, n_pos):
+        """GPU cache contents of sequence i, layer l, positions < n_pos as (K, V) [kvh, n, hd]."""
+        k = self.kv_k[l, i, :, :n_pos, :].float().cpu().numpy()
+        v = self.kv_v[l, i, :, :, :n_pos].float().cpu().numpy().transpose(0, 2, 1)
+        return k, v
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))

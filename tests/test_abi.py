@@ -1,0 +1,192 @@
+"""The C-ABI library loads, exports every function include/dbd.h declares, and rejects bad
+arguments on the host before any launch (no GPU needed: every call here returns before touching
+the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_drafter_draft_amd as dbd
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# These calls pass placeholder addresses that the host-side validation must reject before any
+# launch.  They are host-logic tests: where a GPU is visible they are not run at all, so that a
+# validation bug can never turn into a launch with a placeholder address.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-logic test; runs where no GPU is "
+                                "visible")
+HEADER = os.path.join(ROOT, "include", "dbd.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
+
+
+def test_header_declares_the_three_entry_points():
+    fns = header_functions()
+    for f in ("draft_block", "verify_greedy", "select_streak"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_function():
+    L = dbd.lib()
+    missing = [f for f in header_functions() if not hasattr(L, f)]
+    assert not missing, missing
+
+
+def test_struct_layouts_match_header():
+    # dbd_model_desc: 10 int32 + 2 float + 1 double = 56 bytes; dbd_weights: 16 pointers
+    assert ctypes.sizeof(dbd.ModelDesc) == 56
+    assert ctypes.sizeof(dbd.Weights) == 16 * 8
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = src[: src.index("} dbd_weights;")]
+    body = body[body.rindex("typedef struct {"):]
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == dbd.WEIGHT_FIELDS
+
+
+def _desc(name="qwen3-8b", **kw):
+    d = dbd.model_desc(synth.workload(name).shape)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _ws(desc, **kw):
+    args = dict(batch=32, block_len=16, n_anchor=1, max_new_tokens=256, n_drafts=1,
+                temperature=0.0, ctx_capacity=3136)
+    args.update(kw)
+    return dbd.draft_workspace_bytes(desc, **args)
+
+
+def test_workspace_query_is_positive_and_monotone():
+    d = _desc()
+    a = _ws(d)
+    b = _ws(d, batch=64)
+    c = _ws(d, temperature=1.0)
+    assert 0 < a < b and a < c
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, -2),            # only 64 / 128
+    ("n_kv_heads", 5, -2),           # 32 % 5 != 0
+    ("dtype", 7, -1),
+    ("vocab", 1 << 18, -2),
+    ("hidden", 4100, -2),            # bf16 needs multiples of 64
+    ("n_target_layers", 17, -5),
+])
+def test_bad_model_desc_rejected(field, value, code):
+    with pytest.raises(dbd.DbdError) as e:
+        _ws(_desc(**{field: value}))
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_len=65), -2),
+    (dict(n_anchor=2), -1),
+    (dict(n_drafts=2, temperature=0.0), -1),     # argmax drafting with K > 1
+    (dict(ctx_capacity=1000), -3),              # not a multiple of 64
+    (dict(ctx_capacity=8), -3),                 # smaller than the block
+    (dict(batch=0), -1),
+])
+def test_bad_draft_shape_rejected(kw, code):
+    with pytest.raises(dbd.DbdError) as e:
+        _ws(_desc(), **kw)
+    assert e.value.code == code
+
+
+def test_draft_block_null_pointers_rejected_before_launch():
+    L = dbd.lib()
+    d = _desc()
+    w = dbd.Weights()
+    rc = L.draft_block(ctypes.byref(d), ctypes.byref(w), 32, 16, 1, None, None, 0, 0, 0, None,
+                       None, None, None, 3136, 1, 0.0, 0, None, None, None, None, 0, None)
+    assert rc == -1 and b"NULL" in L.dbd_last_error()
+
+
+def test_draft_block_small_workspace_rejected():
+    L = dbd.lib()
+    d = _desc()
+    fake = 1 << 20                                  # never dereferenced: rejected on the host
+    w = dbd.Weights(*([fake] * 16))
+    rc = L.draft_block(ctypes.byref(d), ctypes.byref(w), 32, 16, 1, fake, fake, 8 * 9 * 4096,
+                       4096, 100, fake, fake, fake, fake, 3136, 1, 0.0, 0, fake, None, None,
+                       fake, 1024, None)
+    assert rc == -4 and b"workspace" in L.dbd_last_error()
+
+
+def test_draft_block_misaligned_hidden_rejected():
+    L = dbd.lib()
+    d = _desc()
+    fake = 1 << 20
+    w = dbd.Weights(*([fake] * 16))
+    rc = L.draft_block(ctypes.byref(d), ctypes.byref(w), 32, 16, 1, fake, fake + 2,
+                       8 * 9 * 4096, 4096, 100, fake, fake, fake, fake, 3136, 1, 0.0, 0, fake,
+                       None, None, fake, 1 << 40, None)
+    assert rc == -2
+
+
+def test_drafter_without_mixing_rejects_ingest():
+    d = dbd.model_desc(synth.workload("specdiff2-7b").shape)
+    with pytest.raises(dbd.DbdError) as e:
+        dbd.draft_workspace_bytes(d, 4, 32, 0, 10, 8, 1.5, 2112)
+    assert e.value.code == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    ((2, 3, 1, 4, 100), -2),       # n_rows not in {D, D+1}
+    ((2, 65, 65, 66, 100), -5),    # D > 64
+    ((2, 3, 3, 3, 1 << 18), -1),   # vocab too large
+    ((2, 3, 2, 4, 100), -2),       # draft_stride < D
+])
+def test_verify_validation(args, code):
+    L = dbd.lib()
+    fake = 1 << 20
+    batch, D, stride, R, V = args
+    rc = L.verify_greedy(fake, fake, stride, batch, D, R, V, fake, fake, fake, None, fake,
+                         1 << 30, None)
+    assert rc == code
+
+
+def test_select_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    rc = L.select_streak(fake, fake, 2, 8, 32, 34, 1000, fake, None, fake, fake, fake, None, fake,
+                         1 << 30, None)
+    assert rc == -2
+    rc = L.select_streak(fake, fake, 2, 8, 32, 32, 1000, fake, None, fake, fake, fake, None, fake,
+                         16, None)
+    assert rc == -4
+    rc = L.select_streak(fake, fake, 2, 65, 32, 32, 1000, fake, None, fake, fake, fake, None, fake,
+                         1 << 30, None)
+    assert rc == -5
+
+
+def test_sample_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    assert L.dbd_sample_from_logits(fake, 2, 3, 100, 2, 0.0, 0, fake, fake, 1 << 30, None) == -1
+    assert L.dbd_sample_from_logits(fake, 2, 3, 100, 1, 1.0, 0, fake, fake, 8, None) == -4
+
+
+def test_gemm_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, None) == -2   # K % 64
+    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, None) == -2      # lda < K
+    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, None) == -1

@@ -1,0 +1,74 @@
+"""GPU parity of single stages: the projection GEMM (bf16 MFMA and fp32 paths) and the ingest
+mix + RMSNorm, against the oracle's fp64 definitions on the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_drafter_draft_amd as dbd
+import synth
+from oracle import drafter as od
+from drafter_case import rel_l2
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (128, 128, 64), (200, 300, 192), (512, 640, 4096),
+                                   (480, 1000, 2560), (17, 2048, 1024), (235, 1024, 4096)])
+def test_gemm_nt(dtype, M, N, K):
+    print(f"gemm {dtype} M={M} N={N} K={K}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(M * 7 + N * 3 + K)
+    A = torch.randn((M, K), generator=g, device=DEV).to(dtype)
+    B = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(dtype)
+    C = torch.full((M, N), float("nan"), device=DEV)
+    dbd.gemm_nt(A, B, C)
+    torch.cuda.synchronize()
+    ref = od.f64(A) @ od.f64(B).T
+    # products of bf16 inputs are exact in fp32; only the fp32 accumulation rounds
+    assert rel_l2(C.cpu().numpy(), ref) < 1e-5
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "qwen3-8b", "gpt-oss-20b"])
+def test_mix_rmsnorm(name):
+    sh = synth.workload(name).shape
+    W = synth.make_weights(sh, 0, DEV)
+    T = 77
+    hid = synth.make_hidden(sh, T, 0, 0, DEV)
+    out = torch.empty((sh.n_layers, T, sh.hidden), dtype=hid.dtype, device=DEV)
+    dbd.mix_rmsnorm(dbd.model_desc(sh), W["mix_logits"], W["mix_norm_w"], hid, out)
+    torch.cuda.synchronize()
+    Wc = {k: W[k].cpu() for k in ("mix_logits", "mix_norm_w")}
+    tol = 1e-5 if sh.dtype == "f32" else 5e-3       # bf16 output rounding: 2^-9 relative
+    for l in range(sh.n_layers):
+        ref = od.context_features(sh, Wc, l, hid.cpu())
+        assert rel_l2(out[l].float().cpu().numpy(), ref) < tol
+
+
+def test_mix_rmsnorm_one_hot_selects_a_layer():
+    sh = synth.workload("qwen3-8b").shape
+    W = synth.make_weights(sh, 0, DEV)
+    lg = torch.zeros_like(W["mix_logits"])
+    lg[:, 4] = 1e4
+    hid = synth.make_hidden(sh, 9, 0, 0, DEV)
+    out = torch.empty((sh.n_layers, 9, sh.hidden), dtype=hid.dtype, device=DEV)
+    dbd.mix_rmsnorm(dbd.model_desc(sh), lg, W["mix_norm_w"], hid, out)
+    torch.cuda.synchronize()
+    for l in range(sh.n_layers):
+        ref = od.rmsnorm(od.f64(hid[:, 4, :]), od.f64(W["mix_norm_w"][l]), sh.rms_eps)
+        assert rel_l2(out[l].float().cpu().numpy(), ref) < 5e-3
+
+
+def test_mix_rmsnorm_strided_layer_major_input():
+    """Target hidden states stored layer-major [L_t, T, H] are read through the strides."""
+    sh = synth.workload("tiny-fp32").shape
+    W = synth.make_weights(sh, 0, DEV)
+    hid = synth.make_hidden(sh, 20, 0, 0, DEV)
+    lm = hid.permute(1, 0, 2).contiguous()          # [L_t, T, H]
+    view = lm.permute(1, 0, 2)                      # strides (H, T*H, 1)
+    out = torch.empty((sh.n_layers, 20, sh.hidden), device=DEV)
+    dbd.mix_rmsnorm(dbd.model_desc(sh), W["mix_logits"], W["mix_norm_w"], view, out)
+    torch.cuda.synchronize()
+    ref = od.context_features(sh, {k: W[k].cpu() for k in ("mix_logits", "mix_norm_w")}, 1,
+                              hid.cpu())
+    assert rel_l2(out[1].cpu().numpy(), ref) < 1e-5

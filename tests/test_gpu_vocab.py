@@ -1,0 +1,177 @@
+"""GPU parity of the vocabulary kernels against the oracle: greedy verification, streak
+selection and drafting from fp32 logits.  Integer outputs must be bit-exact; streak scores too
+(both sides use the same integer weights and the same fp64 operation order)."""
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_drafter_draft_amd as dbd
+import synth
+from oracle import accept, dnc
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _verify_gpu(logits, drafts):
+    N, R, V = logits.shape
+    D = drafts.shape[1]
+    ws = torch.empty(dbd.verify_workspace_bytes(N, R, V), dtype=torch.uint8, device=DEV)
+    n_acc = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    bonus = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    com = torch.full((N, D + 1), -7, dtype=torch.int32, device=DEV)
+    flags = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    dbd.verify_greedy(logits, drafts, n_acc, bonus, com, ws, row_flags=flags)
+    torch.cuda.synchronize()
+    return n_acc.cpu().numpy(), bonus.cpu().numpy(), com.cpu().numpy(), flags.cpu().numpy()
+
+
+def _check_verify(logits, drafts, planted=None):
+    print(f"verify_greedy shape={tuple(logits.shape)}", flush=True)
+    got = _verify_gpu(logits, drafts)
+    ref = accept.verify_greedy(logits.cpu().numpy(), drafts.cpu().numpy())
+    for g, r in zip(got[:3], ref):
+        assert np.array_equal(g, r)
+    assert np.all(got[3] == 0)
+    if planted is not None:
+        assert np.array_equal(got[0], planted)
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "qwen3-8b", "gpt-oss-20b"])
+def test_verify_greedy_workload_shapes(name):
+    wl = synth.workload(name)
+    V, D, N = wl.shape.vocab, wl.n_draft, wl.batch
+    drafts = synth.make_drafts(N, 1, D, V, seed=3, device=DEV)[:, 0].contiguous()
+    logits, a = synth.make_planted_verify_logits(drafts, wl.verify_rows, V, wl.planted_alpha,
+                                                 std=wl.logit_std, seed=3, device=DEV)
+    _check_verify(logits, drafts, a)
+
+
+@pytest.mark.parametrize("N,D,R,V", [(3, 5, 5, 37), (4, 7, 8, 4099), (2, 64, 65, 300),
+                                     (5, 1, 2, 8192), (1, 3, 4, 2)])
+def test_verify_greedy_ragged_and_ties(N, D, R, V):
+    g = torch.Generator(device=DEV).manual_seed(N * 1000 + V)
+    # small integer logits: exact ties everywhere, so the lowest-index rule decides
+    logits = torch.randint(-3, 4, (N, R, V), generator=g, device=DEV).float()
+    drafts = torch.randint(0, V, (N, D), generator=g, device=DEV, dtype=torch.int32)
+    # make a few prefixes match the target's argmax so acceptance lengths vary
+    t = logits.argmax(-1).to(torch.int32)
+    for n in range(N):
+        k = (n * 3) % (D + 1)
+        drafts[n, :k] = t[n, :k]
+    _check_verify(logits, drafts)
+
+
+def test_verify_greedy_identical_P_Q_accepts_all():
+    N, D, V = 4, 15, 5000
+    g = torch.Generator(device=DEV).manual_seed(5)
+    q = torch.randn((N, D + 1, V), generator=g, device=DEV)
+    drafts = q[:, :D].argmax(-1).to(torch.int32).contiguous()
+    n_acc, bonus, com, _ = _verify_gpu(q, drafts)
+    assert np.all(n_acc == D)
+    assert np.array_equal(bonus, q[:, D].argmax(-1).cpu().numpy())
+
+
+def test_verify_greedy_flags_non_finite():
+    N, D, V = 3, 4, 1000
+    logits = torch.randn((N, D + 1, V), device=DEV)
+    logits[1, 2, 17] = float("nan")
+    logits[2, 0, 5] = float("inf")
+    drafts = torch.zeros((N, D), dtype=torch.int32, device=DEV)
+    flags = _verify_gpu(logits, drafts)[3]
+    assert list(flags) == [0, 1, 1]
+
+
+def _select_gpu(logits, drafts):
+    N, K, R, V = logits.shape
+    G = drafts.shape[2]
+    ws = torch.empty(dbd.select_workspace_bytes(N, K, R, V), dtype=torch.uint8, device=DEV)
+    sel = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    sc = torch.zeros((N, K), dtype=torch.float64, device=DEV)
+    n_acc = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    bonus = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    com = torch.full((N, G + 1), -7, dtype=torch.int32, device=DEV)
+    flags = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    dbd.select_streak(logits, drafts, sel, n_acc, bonus, com, ws, scores=sc, row_flags=flags)
+    torch.cuda.synchronize()
+    return [x.cpu().numpy() for x in (sel, sc, n_acc, bonus, com, flags)]
+
+
+def _check_select(logits, drafts):
+    print(f"select_streak shape={tuple(logits.shape)}", flush=True)
+    got = _select_gpu(logits, drafts)
+    ref = accept.select_streak(logits.cpu().numpy(), drafts.cpu().numpy())
+    assert np.array_equal(got[0], ref[0])                  # selected draft
+    assert np.array_equal(got[1], ref[1])                  # fp64 streak scores, bit for bit
+    for g, r in zip(got[2:5], ref[2:]):
+        assert np.array_equal(g, r)
+    assert np.all(got[5] == 0)
+    return got
+
+
+def test_select_streak_tiny():
+    """[1, 4, 7, 1024] verifier logits N(0, 2) over 4 drafts of 7 tokens."""
+    drafts = synth.make_drafts(1, 4, 7, 1024, seed=9, device=DEV)
+    logits, _ = synth.make_planted_streak_logits(drafts, 7, 1024, 0.7, seed=9, device=DEV)
+    _check_select(logits, drafts)
+
+
+def test_select_streak_specdiff2_shape():
+    wl = synth.workload("specdiff2-7b")
+    N, K, G, V = wl.batch, wl.n_drafts, wl.n_draft, wl.shape.vocab
+    drafts = synth.make_drafts(N, K, G, V, seed=2, device=DEV)
+    logits, a = synth.make_planted_streak_logits(drafts, wl.verify_rows, V, wl.planted_alpha,
+                                                 std=wl.logit_std, seed=2, device=DEV)
+    got = _check_select(logits, drafts)
+    for n in range(N):
+        assert got[2][n] == a[n, got[0][n]]                # planted streak of the chosen draft
+
+
+@pytest.mark.parametrize("N,K,G,R,V", [(3, 5, 4, 5, 333), (2, 1, 6, 6, 9000), (2, 8, 32, 33, 2)])
+def test_select_streak_ragged(N, K, G, R, V):
+    g = torch.Generator(device=DEV).manual_seed(K * 100 + V)
+    logits = torch.randn((N, K, R, V), generator=g, device=DEV) * 2
+    drafts = torch.randint(0, V, (N, K, G), generator=g, device=DEV, dtype=torch.int32)
+    _check_select(logits, drafts)
+
+
+def test_select_streak_equal_scores_pick_lowest_draft():
+    V, G, K = 50, 4, 6
+    row = torch.randn((G, V), device=DEV)
+    logits = row.expand(1, K, G, V).contiguous()
+    drafts = torch.randint(0, V, (1, 1, G), device=DEV, dtype=torch.int32).expand(1, K, G)
+    got = _select_gpu(logits, drafts.contiguous())
+    assert got[0][0] == 0 and np.all(got[1][0] == got[1][0][0])
+
+
+def _sample_gpu(logits, K, T, seed):
+    N, D, V = logits.shape
+    ws = torch.empty(dbd.sample_workspace_bytes(N, D, V), dtype=torch.uint8, device=DEV)
+    out = torch.full((N, K, D), -7, dtype=torch.int32, device=DEV)
+    dbd.sample_from_logits(logits, K, T, seed, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,D,V,K,T", [(1, 7, 1024, 1, 0.0), (1, 7, 1024, 4, 1.0),
+                                       (3, 5, 4097, 3, 1.5), (2, 9, 64, 8, 2.0),
+                                       (16, 7, 201088, 1, 1.0), (4, 32, 152064, 8, 1.5),
+                                       (32, 15, 151936, 1, 0.0)])
+def test_drafting_from_fp32_logits_bit_exact(N, D, V, K, T):
+    print(f"sample N={N} D={D} V={V} K={K} T={T}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V + K)
+    logits = torch.randn((N, D, V), generator=g, device=DEV) * 2
+    if T <= 0:
+        logits[0, 0, 10] = logits[0, 0].max() + 1      # plant a tie at two indices
+        logits[0, 0, 3] = logits[0, 0, 10]
+    got = _sample_gpu(logits, K, T, seed=77)
+    ref = dnc.sample_drafts(logits.cpu().numpy(), K, T, 77)
+    assert np.array_equal(got, ref)
+
+
+def test_sampling_depends_on_seed_and_draft_index():
+    logits = torch.zeros((1, 4, 1000), device=DEV)       # uniform: draws differ freely
+    a = _sample_gpu(logits, 8, 1.0, 1)
+    b = _sample_gpu(logits, 8, 1.0, 2)
+    assert not np.array_equal(a, b)
+    assert len({tuple(a[0, k]) for k in range(8)}) > 1
