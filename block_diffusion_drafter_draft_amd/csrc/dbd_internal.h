@@ -72,6 +72,7 @@ struct BSeg {
 };
 struct GemmArgs {
   const void* A;
+  const void* A2;       // optional low part of A (bf16 pair split; same strides as A)
   int64_t lda, a_bs;    // row stride, batch (grid.z) stride, in elements
   BSeg seg[3];
   int nseg;
@@ -129,7 +130,7 @@ hipError_t launch_prep(const int32_t* ctx_len, const int32_t* new_offsets, int b
                        RowMeta meta, int32_t* seq_status, hipStream_t s);
 hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls, int n_tok,
                               int H, int Lt, int Ld, const float* mix_logits, const void* g,
-                              void* out, float eps, hipStream_t s);
+                              void* out, void* out_lo, float eps, hipStream_t s);
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H,
                         int V, float* x, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, int rows, int H,

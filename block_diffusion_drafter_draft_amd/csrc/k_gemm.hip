@@ -205,12 +205,22 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
 // ------------------------------------------------------------------ bf16 MFMA mainloop
 __device__ __forceinline__ int swz(int row, int kc) { return kc ^ ((row >> 1) & 7); }
 
-template <int KIND>
+// SPLITA: the A operand is given as two bf16 tensors, A (high part) and A2 = bf16(a - A) (low
+// part), and every MFMA is issued for both, so that the product sees A to about 16 significant
+// bits (the bf16 pair technique of Henry, Tang & Heinecke, "Leveraging the bfloat16 artificial
+// intelligence datatype for higher-precision computations", ARITH 2019).
+template <bool SPLITA>
+constexpr int gemm_smem_bytes() {
+  return SPLITA ? 3 * 2 * BM * BK * 2 : BM * CS_LD * 4;
+}
+
+template <int KIND, bool SPLITA>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, EpiArgs e) {
-  // LDS: two stages of A and B tiles (64 KB) reused as the fp32 output tile (66 KB)
-  __shared__ __attribute__((aligned(16))) char smem[BM * CS_LD * 4];
+  // LDS: two stages of the A (and A2) and B tiles, reused as the fp32 output tile (66 KB)
+  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<SPLITA>()];
   bf16* As = (bf16*)smem;                                   // [2][BM][BK]
   bf16* Bs = (bf16*)(smem + 2 * BM * BK * 2);              // [2][BN][BK]
+  bf16* A2s = (bf16*)(smem + 4 * BM * BK * 2);             // [2][BM][BK] (SPLITA)
   float* Cs = (float*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -222,13 +232,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, EpiArgs e) {
 
   const BMap bm = make_bmap(a);
   const bf16* ap[4];
+  const bf16* ap2[4];
   const bf16* bp[4];
   int so[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int id = tid + 256 * i, row = id >> 3, kc = id & 7;
     const int ar = min(m0 + row, M - 1);
-    ap[i] = (const bf16*)a.A + (int64_t)z * a.a_bs + (int64_t)ar * a.lda + kc * 8;
+    const int64_t aoff = (int64_t)z * a.a_bs + (int64_t)ar * a.lda + kc * 8;
+    ap[i] = (const bf16*)a.A + aoff;
+    ap2[i] = SPLITA ? (const bf16*)a.A2 + aoff : ap[i];
     bp[i] = brow_ptr<bf16>(bm, min(n0 + row, N - 1), z) + kc * 8;
     so[i] = row * BK + swz(row, kc) * 8;
   }
@@ -239,16 +252,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, EpiArgs e) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[4], rb[4], ra2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     ra[i] = *reinterpret_cast<const u32x4*>(ap[i]);
     rb[i] = *reinterpret_cast<const u32x4*>(bp[i]);
+    if constexpr (SPLITA) ra2[i] = *reinterpret_cast<const u32x4*>(ap2[i]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     *reinterpret_cast<u32x4*>(As + so[i]) = ra[i];
     *reinterpret_cast<u32x4*>(Bs + so[i]) = rb[i];
+    if constexpr (SPLITA) *reinterpret_cast<u32x4*>(A2s + so[i]) = ra2[i];
   }
   __syncthreads();
 
@@ -262,9 +277,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, EpiArgs e) {
       for (int i = 0; i < 4; ++i) {
         ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + koff);
         rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + koff);
+        if constexpr (SPLITA) ra2[i] = *reinterpret_cast<const u32x4*>(ap2[i] + koff);
       }
     }
     const bf16* Ac = As + cur * BM * BK;
+    const bf16* A2c = A2s + cur * BM * BK;
     const bf16* Bc = Bs + cur * BN * BK;
 #pragma unroll
     for (int s = 0; s < BK / 32; ++s) {
@@ -282,6 +299,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, EpiArgs e) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      if constexpr (SPLITA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ra_ = wm * 64 + i * 16 + (lane & 15);
+          af[i] = *reinterpret_cast<const bf16x8*>(A2c + ra_ * BK + swz(ra_, kc) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
     }
     if (more) {
       bf16* An = As + (cur ^ 1) * BM * BK;
@@ -290,6 +320,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a, EpiArgs e) {
       for (int i = 0; i < 4; ++i) {
         *reinterpret_cast<u32x4*>(An + so[i]) = ra[i];
         *reinterpret_cast<u32x4*>(Bn + so[i]) = rb[i];
+        if constexpr (SPLITA)
+          *reinterpret_cast<u32x4*>(A2s + (cur ^ 1) * BM * BK + so[i]) = ra2[i];
       }
     }
     __syncthreads();
@@ -373,7 +405,15 @@ static void launch_kind(int dtype, const GemmArgs& a, const EpiArgs& e, int batc
                         hipStream_t s) {
   if (dtype == 1) {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM), batch);
-    hipLaunchKernelGGL(gemm_bf16_kernel<KIND>, grid, dim3(256), 0, s, a, e);
+    bool split = false;
+    if constexpr (KIND == EPI_CTXKV) split = a.A2 != nullptr;   // only the context K/V GEMM
+    if constexpr (KIND == EPI_CTXKV) {
+      if (split) {
+        hipLaunchKernelGGL((gemm_bf16_kernel<KIND, true>), grid, dim3(256), 0, s, a, e);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((gemm_bf16_kernel<KIND, false>), grid, dim3(256), 0, s, a, e);
   } else {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, FM), batch);
     hipLaunchKernelGGL(gemm_f32_kernel<KIND>, grid, dim3(256), 0, s, a, e);

@@ -101,7 +101,7 @@ template <typename T, int CPT>
 __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
     const T* __restrict__ hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt, int Ld,
     const float* __restrict__ mix_logits, const T* __restrict__ g, T* __restrict__ out,
-    float eps) {
+    T* __restrict__ out_lo, float eps) {
   constexpr int VEC = Vec16<T>::n;
   __shared__ float w[kMaxLd * kMaxLt];
   __shared__ float red[kMaxLd][4];
@@ -167,11 +167,18 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * 256;
       if (ch < nch) {
-        T gv[VEC], ov[VEC];
+        T gv[VEC], ov[VEC], lv[VEC];
         *reinterpret_cast<u32x4*>(gv) = *reinterpret_cast<const u32x4*>(gl + ch * VEC);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) ov[e] = from_f<T>(acc[l][c * VEC + e] * inv * to_f(gv[e]));
+        for (int e = 0; e < VEC; ++e) {
+          const float y = acc[l][c * VEC + e] * inv * to_f(gv[e]);
+          ov[e] = from_f<T>(y);
+          lv[e] = from_f<T>(y - to_f(ov[e]));     // low part of the bf16 pair
+        }
         *reinterpret_cast<u32x4*>(o + ch * VEC) = *reinterpret_cast<u32x4*>(ov);
+        if (out_lo)
+          *reinterpret_cast<u32x4*>(out_lo + ((int64_t)l * n_tok + t) * H + ch * VEC) =
+              *reinterpret_cast<u32x4*>(lv);
       }
     }
   }
@@ -179,21 +186,21 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
 
 template <typename T>
 static hipError_t mix_dispatch(const void* hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt,
-                               int Ld, const float* ml, const void* g, void* out, float eps,
-                               hipStream_t s) {
+                               int Ld, const float* ml, const void* g, void* out, void* out_lo,
+                               float eps, hipStream_t s) {
   constexpr int VEC = Vec16<T>::n;
   const int cpt = ceil_div(H / VEC, 256);
   const T* h = (const T*)hid;
   if (n_tok == 0) return hipSuccess;
   if (cpt <= 1)
     hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 1>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, (const T*)g, (T*)out, eps);
+                       H, Lt, Ld, ml, (const T*)g, (T*)out, (T*)out_lo, eps);
   else if (cpt <= 2)
     hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 2>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, (const T*)g, (T*)out, eps);
+                       H, Lt, Ld, ml, (const T*)g, (T*)out, (T*)out_lo, eps);
   else if (cpt <= 4)
     hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 4>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, (const T*)g, (T*)out, eps);
+                       H, Lt, Ld, ml, (const T*)g, (T*)out, (T*)out_lo, eps);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -201,10 +208,11 @@ static hipError_t mix_dispatch(const void* hid, int64_t ts, int64_t ls, int n_to
 
 hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls, int n_tok,
                               int H, int Lt, int Ld, const float* mix_logits, const void* g,
-                              void* out, float eps, hipStream_t s) {
-  return dtype == 1 ? mix_dispatch<bf16>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out, eps, s)
-                    : mix_dispatch<float>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out, eps,
-                                          s);
+                              void* out, void* out_lo, float eps, hipStream_t s) {
+  return dtype == 1 ? mix_dispatch<bf16>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out,
+                                         out_lo, eps, s)
+                    : mix_dispatch<float>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out,
+                                          nullptr, eps, s);
 }
 
 // ------------------------------------------------------------------ embedding gather

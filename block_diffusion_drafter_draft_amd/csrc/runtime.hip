@@ -126,8 +126,10 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.meta.seq_keys = c.take<int32_t>(N);
   t.meta.rope_blk = c.take<float2>(M * half);
   t.meta.rope_ctx = c.take<float2>((int64_t)Tn * half);
+  // context features; bf16 keeps the (high, low) pair so the K/V projection sees ~16 bits
+  const int nparts = d.dtype == DBD_BF16 ? 2 : 1;
   t.ctxfeat = d.n_target_layers > 0
-                  ? (void*)c.take<char>((int64_t)d.n_layers * Tn * d.hidden * es)
+                  ? (void*)c.take<char>((int64_t)nparts * d.n_layers * Tn * d.hidden * es)
                   : nullptr;
   t.x = c.take<float>(M * d.hidden);
   t.xn = c.take<char>(M * d.hidden * es);
@@ -325,11 +327,17 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
 
   // 1. ingest: mix + RMSNorm, then context K/V for every draft layer (batched over layers)
   if (d.n_target_layers > 0 && T > 0) {
-    HIP_STAGE(DBD_STAGE_MIX, st, launch_mix_rmsnorm(d.dtype, target_hidden_new, hid_token_stride, hid_layer_stride, T,
-                               H, d.n_target_layers, d.n_layers, w->mix_logits, w->mix_norm_w,
-                               b.ctxfeat, d.rms_eps, st));
+    void* ctx_lo = d.dtype == DBD_BF16
+                       ? (void*)((char*)b.ctxfeat + (int64_t)d.n_layers * T * H * es)
+                       : nullptr;
+    HIP_STAGE(DBD_STAGE_MIX, st, launch_mix_rmsnorm(d.dtype, target_hidden_new,
+                                                    hid_token_stride, hid_layer_stride, T, H,
+                                                    d.n_target_layers, d.n_layers,
+                                                    w->mix_logits, w->mix_norm_w, b.ctxfeat,
+                                                    ctx_lo, d.rms_eps, st));
     GemmArgs g{};
     g.A = b.ctxfeat;
+    g.A2 = ctx_lo;
     g.lda = H;
     g.a_bs = (int64_t)T * H;
     g.seg[0] = BSeg{w->wk_ctx, 0, kd};
@@ -695,7 +703,7 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
                 vec);
   HIP_TRY(launch_mix_rmsnorm(desc->dtype, hidden, hid_token_stride, hid_layer_stride, n_tokens,
                              desc->hidden, desc->n_target_layers, desc->n_layers, mix_logits,
-                             mix_norm_w, out, desc->rms_eps, (hipStream_t)stream));
+                             mix_norm_w, out, nullptr, desc->rms_eps, (hipStream_t)stream));
   return DBD_OK;
 }
 
