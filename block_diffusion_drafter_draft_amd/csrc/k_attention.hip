@@ -25,9 +25,16 @@ __device__ __forceinline__ int kswz(int row, int c) {
 }
 __device__ __forceinline__ int vswz(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int HD>
-__global__ __launch_bounds__(1024) void attn_bf16_kernel(AttnArgs a) {
+// NW waves (a power of two, >= the 16-row query tiles of the group); every thread stages
+// 2 * KCH * HD * 2 / (64 * NW) bytes of the next chunk in registers while the current chunk is
+// consumed from LDS.
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KC = HD / 8;                    // 16-byte chunks per K row
+  constexpr int NT = 64 * NW;
+  constexpr int KT = KCH * KC, VT = HD * (KCH / 8);   // 16-byte chunks of K and V per stage
+  constexpr int KI = (KT + NT - 1) / NT;        // K chunks staged per thread
+  constexpr int VI = (VT + NT - 1) / NT;        // V chunks staged per thread
   __shared__ __attribute__((aligned(16))) bf16 Ks[KCH * HD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[HD * KCH];
   const int s = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
@@ -37,7 +44,6 @@ __global__ __launch_bounds__(1024) void attn_bf16_kernel(AttnArgs a) {
   const int k_end = min(L, k_begin + a.split);
   const int nsplit = (L + a.split - 1) / a.split;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthr = blockDim.x;
   const int R = a.block_len * a.grp;
 
   const bf16* Kg = (const bf16*)a.kv_k + ((int64_t)n * a.kvh + g) * a.cap * HD;
@@ -46,6 +52,7 @@ __global__ __launch_bounds__(1024) void attn_bf16_kernel(AttnArgs a) {
   // this lane's query row (column of S^T / O^T)
   const int r = wave * 16 + (lane & 15);
   const bool rvalid = r < R;
+  const bool wactive = wave * 16 < R;           // wave owns at least one query row
   const int b = rvalid ? r % a.block_len : 0, h = rvalid ? r / a.block_len : 0;
   const int64_t qrow = (int64_t)n * a.block_len + b;
   const int qcol = (g * a.grp + h) * HD;
@@ -68,71 +75,98 @@ __global__ __launch_bounds__(1024) void attn_bf16_kernel(AttnArgs a) {
   const int kr0 = 8 * (i16 >> 2) + (i16 & 3);
   const int kr1 = kr0 + 4;
 
-  for (int c0 = k_begin; c0 < k_end; c0 += KCH) {
-    // stage K rows [c0, c0+64) and V^T columns [c0, c0+64); positions >= k_end read as 0 in V
-    for (int idx = tid; idx < KCH * KC; idx += nthr) {
-      const int row = idx / KC, c = idx % KC;
-      u32x4 v = *reinterpret_cast<const u32x4*>(Kg + (int64_t)(c0 + row) * HD + c * 8);
-      *reinterpret_cast<u32x4*>(Ks + row * HD + kswz<HD>(row, c) * 8) = v;
+  u32x4 kreg[KI], vreg[VI];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < KI; ++j) {
+      const int idx = tid + j * NT, row = idx / KC, c = idx % KC;
+      if (KT % NT == 0 || idx < KT)
+        kreg[j] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)(c0 + row) * HD + c * 8);
     }
-    for (int idx = tid; idx < HD * (KCH / 8); idx += nthr) {
-      const int d = idx / (KCH / 8), c = idx % (KCH / 8);
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int idx = tid + j * NT, d = idx / (KCH / 8), c = idx % (KCH / 8);
+      if (VT % NT == 0 || idx < VT)
+        vreg[j] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)d * a.cap + c0 + c * 8);
+    }
+  };
+  auto store_chunk = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < KI; ++j) {
+      const int idx = tid + j * NT, row = idx / KC, c = idx % KC;
+      if (KT % NT == 0 || idx < KT)
+        *reinterpret_cast<u32x4*>(Ks + row * HD + kswz<HD>(row, c) * 8) = kreg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int idx = tid + j * NT, d = idx / (KCH / 8), c = idx % (KCH / 8);
+      if (!(VT % NT == 0 || idx < VT)) continue;
       const int k0 = c0 + c * 8;
-      u32x4 v = *reinterpret_cast<const u32x4*>(Vg + (int64_t)d * a.cap + k0);
-      if (k0 + 8 > k_end) {
+      u32x4 v = vreg[j];
+      if (k0 + 8 > k_end) {               // positions past the end read as 0
         bf16* e = reinterpret_cast<bf16*>(&v);
-        for (int j = 0; j < 8; ++j)
-          if (k0 + j >= k_end) e[j] = (bf16)0.f;
+        for (int q = 0; q < 8; ++q)
+          if (k0 + q >= k_end) e[q] = (bf16)0.f;
       }
       *reinterpret_cast<u32x4*>(Vs + d * KCH + vswz(d, c) * 8) = v;
     }
+  };
+
+  load_chunk(k_begin);
+  for (int c0 = k_begin; c0 < k_end; c0 += KCH) {
+    store_chunk(c0);
     __syncthreads();
+    if (c0 + KCH < k_end) load_chunk(c0 + KCH);     // in flight while this chunk is consumed
+    if (wactive) {
 #pragma unroll
-    for (int sub = 0; sub < KCH / 32; ++sub) {
-      const int key0 = c0 + sub * 32;
-      if (key0 < k_end) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        const int row0 = sub * 32 + kr0, row1 = sub * 32 + kr1;
+      for (int sub = 0; sub < KCH / 32; ++sub) {
+        const int key0 = c0 + sub * 32;
+        if (key0 < k_end) {
+          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+          const int row0 = sub * 32 + kr0, row1 = sub * 32 + kr1;
 #pragma unroll
-        for (int ks = 0; ks < HD / 32; ++ks) {
-          const int c = ks * 4 + (lane >> 4);
-          bf16x8 k0v = *reinterpret_cast<const bf16x8*>(Ks + row0 * HD + kswz<HD>(row0, c) * 8);
-          bf16x8 k1v = *reinterpret_cast<const bf16x8*>(Ks + row1 * HD + kswz<HD>(row1, c) * 8);
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks], s1, 0, 0, 0);
-        }
-        // lane holds S^T[key0 + 8*(lane/16) + e][query], e = 0..7
-        float sv[8];
-        const int kb = key0 + 8 * (lane >> 4);
+          for (int ks = 0; ks < HD / 32; ++ks) {
+            const int c = ks * 4 + (lane >> 4);
+            bf16x8 k0v =
+                *reinterpret_cast<const bf16x8*>(Ks + row0 * HD + kswz<HD>(row0, c) * 8);
+            bf16x8 k1v =
+                *reinterpret_cast<const bf16x8*>(Ks + row1 * HD + kswz<HD>(row1, c) * 8);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks], s1, 0, 0, 0);
+          }
+          // lane holds S^T[key0 + 8*(lane/16) + e][query], e = 0..7
+          float sv[8];
+          const int kb = key0 + 8 * (lane >> 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[e] = kb + e < k_end ? s0[e] * a.scale_log2 : -INFINITY;
-          sv[4 + e] = kb + 4 + e < k_end ? s1[e] * a.scale_log2 : -INFINITY;
-        }
-        float mx = sv[0];
+          for (int e = 0; e < 4; ++e) {
+            sv[e] = kb + e < k_end ? s0[e] * a.scale_log2 : -INFINITY;
+            sv[4 + e] = kb + 4 + e < k_end ? s1[e] * a.scale_log2 : -INFINITY;
+          }
+          float mx = sv[0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
-        bf16x8 pb;
-        float ps = 0.f;
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = exp2f(m_run - m_new);
+          bf16x8 pb;
+          float ps = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(sv[e] - m_new);
-          ps += p;
-          pb[e] = (bf16)p;
-        }
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
+          for (int e = 0; e < 8; ++e) {
+            const float p = exp2f(sv[e] - m_new);
+            ps += p;
+            pb[e] = (bf16)p;
+          }
+          l_run = l_run * alpha + ps;
+          m_run = m_new;
 #pragma unroll
-        for (int dt = 0; dt < HD / 16; ++dt) {
-          acc[dt] *= alpha;
-          const int d = dt * 16 + (lane & 15);
-          const int c = sub * 4 + (lane >> 4);
-          bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + d * KCH + vswz(d, c) * 8);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[dt], 0, 0, 0);
+          for (int dt = 0; dt < HD / 16; ++dt) {
+            acc[dt] *= alpha;
+            const int d = dt * 16 + (lane & 15);
+            const int c = sub * 4 + (lane >> 4);
+            bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + d * KCH + vswz(d, c) * 8);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[dt], 0, 0, 0);
+          }
         }
       }
     }
@@ -155,8 +189,7 @@ __global__ __launch_bounds__(1024) void attn_bf16_kernel(AttnArgs a) {
     float* po = a.part_o + pr * HD;
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) po[dt * 16 + (lane >> 4) * 4 + i] = acc[dt][i];
+      *reinterpret_cast<f32x4*>(po + dt * 16 + (lane >> 4) * 4) = acc[dt];
     if (lane < 16) a.part_ml[pr] = make_float2(m_run, l_run);
   }
 }
@@ -220,48 +253,81 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int HD) {
 }
 
 // ------------------------------------------------------------------ combine splits
+// grid (R / 4, kvh, N): each workgroup merges 4 query rows; thread = (row, 4 dimensions).  All
+// partial loads of a thread are independent of each other, so they are in flight together.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int HD) {
-  const int g = blockIdx.x, n = blockIdx.y;
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int HD) {
+  const int g = blockIdx.y, n = blockIdx.z;
   const int L = a.seq_keys[n];
   const int nsplit = (L + a.split - 1) / a.split;
   if (L <= 0 || nsplit <= 1) return;
   const int R = a.block_len * a.grp;
+  const int dq = HD / 4;                                  // float4 groups per row
+  const int r = blockIdx.x * 4 + threadIdx.x / dq;
+  const int d4 = threadIdx.x % dq;
+  if (r >= R || threadIdx.x >= 4 * dq) return;
   const int64_t base = ((int64_t)n * a.kvh + g) * a.s_max;
-  for (int idx = threadIdx.x; idx < R * HD; idx += blockDim.x) {
-    const int r = idx / HD, d = idx % HD;
-    float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.part_ml[(base + s) * R + r].x);
-    float l = 0.f, o = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = a.part_ml[(base + s) * R + r];
-      const float w = exp2f(ml.x - m);
-      l += w * ml.y;
-      o += w * a.part_o[((base + s) * R + r) * HD + d];
-    }
-    const int b = r % a.block_len, h = r / a.block_len;
-    const int64_t qrow = (int64_t)n * a.block_len + b;
-    ((T*)a.out)[qrow * a.qd + (g * a.grp + h) * HD + d] = from_f<T>(o / l);
+  constexpr int SU = 8;
+  float m = -INFINITY;
+  for (int s0 = 0; s0 < nsplit; s0 += SU) {
+    float2 ml[SU];
+#pragma unroll
+    for (int q = 0; q < SU; ++q)
+      ml[q] = s0 + q < nsplit ? a.part_ml[(base + s0 + q) * R + r] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int q = 0; q < SU; ++q) m = fmaxf(m, ml[q].x);
   }
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += SU) {
+    float2 ml[SU];
+    f32x4 po[SU];
+#pragma unroll
+    for (int q = 0; q < SU; ++q) {
+      const bool ok = s0 + q < nsplit;
+      const int64_t pr = (base + s0 + q) * R + r;
+      ml[q] = ok ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
+      po[q] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + pr * HD + 4 * d4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < SU; ++q) {
+      const float w = exp2f(ml[q].x - m);
+      l += w * ml[q].y;
+      o += w * po[q];
+    }
+  }
+  const float inv = 1.f / l;
+  const int b = r % a.block_len, h = r / a.block_len;
+  T* out = (T*)a.out + ((int64_t)n * a.block_len + b) * a.qd + (g * a.grp + h) * HD + 4 * d4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = from_f<T>(o[q] * inv);
+}
+
+template <int HD>
+static void launch_bf16(const AttnArgs& a, dim3 grid, int nw, hipStream_t s) {
+  if (nw <= 2) hipLaunchKernelGGL((attn_bf16_kernel<HD, 2>), grid, dim3(128), 0, s, a);
+  else if (nw <= 4) hipLaunchKernelGGL((attn_bf16_kernel<HD, 4>), grid, dim3(256), 0, s, a);
+  else if (nw <= 8) hipLaunchKernelGGL((attn_bf16_kernel<HD, 8>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((attn_bf16_kernel<HD, 16>), grid, dim3(1024), 0, s, a);
 }
 
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.s_max, a.kvh, a.batch);
   const int R = a.block_len * a.grp;
+  dim3 cgrid(ceil_div(R, 4), a.kvh, a.batch);
   if (dtype == 1) {
     const int nw = ceil_div(R, 16);
-    if (hd == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(64 * nw), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(64 * nw), 0, s, a);
+    if (hd == 128) launch_bf16<128>(a, grid, nw, s);
+    else launch_bf16<64>(a, grid, nw, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(attn_combine_kernel<bf16>, dim3(a.kvh, a.batch), dim3(256), 0, s, a, hd);
+    hipLaunchKernelGGL(attn_combine_kernel<bf16>, cgrid, dim3(128), 0, s, a, hd);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, a, hd);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.kvh, a.batch), dim3(256), 0, s, a, hd);
+    hipLaunchKernelGGL(attn_combine_kernel<float>, cgrid, dim3(128), 0, s, a, hd);
   }
   return hipGetLastError();
 }

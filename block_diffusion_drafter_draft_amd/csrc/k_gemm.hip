@@ -59,145 +59,180 @@ __device__ __forceinline__ const T* brow_ptr(const BMap& m, int v, int z) {
 }
 
 // ------------------------------------------------------------------ epilogues
+// The finished tile sits in LDS as fp32 (row stride CS_LD).  Each thread owns a contiguous
+// segment of one row (TPR threads per row, CPT columns each), issues all of its global loads
+// before any store (a store could alias a later load, so the compiler cannot hoist loads across
+// it), and stores 16-byte vectors where the layout is contiguous.
 template <typename T>
-__device__ __forceinline__ float rot(const float* row, int c, int hd, float2 cs) {
-  // rotate-half: pair (i, i + hd/2) of the head that column c belongs to
-  const int d = c % hd, base = c - d, half = hd / 2, i = d % half;
-  const float x1 = row[base + i], x2 = row[base + i + half];
-  return d < half ? x1 * cs.x - x2 * cs.y : x2 * cs.x + x1 * cs.y;
+__device__ __forceinline__ void store8(T* dst, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    *reinterpret_cast<bf16x8*>(dst) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// rotate-half RoPE of tile row `row` (LDS) at tile columns c .. c+7 (same head, same half);
+// cs = the 8 (cos, sin) pairs of the head-local pair indices of those columns.
+__device__ __forceinline__ void rope8(const float* row, int c, int hd, const float2* cs,
+                                      float* out) {
+  const int half = hd / 2, d = c % hd;
+  if (d < half) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      out[e] = row[c + e] * cs[e].x - row[c + e + half] * cs[e].y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      out[e] = row[c + e] * cs[e].x + row[c + e - half] * cs[e].y;
+  }
 }
 
 template <typename T, int TM, int KIND>
 __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, int m0, int n0,
                                              int tn, int z, int M, int N) {
+  constexpr int TPR = 256 / TM;                 // threads per tile row
+  constexpr int CPT = BN / TPR;                 // columns per thread
+  __shared__ int s_pos[TM], s_seq[TM];
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
   const int rows = min(TM, M - m0);
   const int cols = min(BN, N - n0);
-  switch (KIND) {
-    case EPI_STORE_F32: {
-      float* C = (float*)e.C + (int64_t)z * e.c_bs;
-      for (int idx = tid; idx < TM * BN; idx += nthr) {
-        const int r = idx / BN, c = idx % BN;
-        if (r < rows && c < cols) C[(int64_t)(m0 + r) * e.ldc + n0 + c] = Cs[r * CS_LD + c];
+  const int r = tid / TPR, cb = (tid % TPR) * CPT;
+  const int m = m0 + r;
+  const bool rok = r < rows;
+  const float* crow = Cs + r * CS_LD;
+
+  if constexpr (KIND == EPI_STORE_F32 || KIND == EPI_RESID || KIND == EPI_ARGMAX) {
+    float* C = KIND == EPI_ARGMAX ? e.logits : (float*)e.C + (int64_t)z * e.c_bs;
+    if (C && rok) {
+      float* dst = C + (int64_t)m * e.ldc + n0 + cb;
+      const bool vec = (e.ldc & 3) == 0 && cb + CPT <= cols && ((uintptr_t)dst & 15) == 0;
+      if (vec) {
+        f32x4 v[CPT / 4];
+        if constexpr (KIND == EPI_RESID) {
+#pragma unroll
+          for (int j = 0; j < CPT / 4; ++j) v[j] = *reinterpret_cast<const f32x4*>(dst + 4 * j);
+        }
+#pragma unroll
+        for (int j = 0; j < CPT / 4; ++j) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(crow + cb + 4 * j);
+          if constexpr (KIND == EPI_RESID) v[j] += a;
+          else v[j] = a;
+        }
+#pragma unroll
+        for (int j = 0; j < CPT / 4; ++j) *reinterpret_cast<f32x4*>(dst + 4 * j) = v[j];
+      } else {
+        for (int c = 0; c < CPT && cb + c < cols; ++c) {
+          if constexpr (KIND == EPI_RESID) dst[c] += crow[cb + c];
+          else dst[c] = crow[cb + c];
+        }
       }
-      break;
     }
-    case EPI_RESID: {
-      float* C = (float*)e.C;
-      for (int idx = tid; idx < TM * BN; idx += nthr) {
-        const int r = idx / BN, c = idx % BN;
-        if (r < rows && c < cols) C[(int64_t)(m0 + r) * e.ldc + n0 + c] += Cs[r * CS_LD + c];
+    if constexpr (KIND == EPI_ARGMAX) {
+      // TPR threads per row each scan their columns in increasing order, then combine
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      if (rok)
+        for (int c = cb; c < cb + CPT && c < cols; ++c) argmax_combine(bv, bi, crow[c], n0 + c);
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        argmax_combine(bv, bi, ov, oi);
       }
-      break;
+      if (rok && (tid % TPR) == 0) {
+        e.part_val[(int64_t)m * e.ntiles + tn] = bv;
+        e.part_idx[(int64_t)m * e.ntiles + tn] = bi;
+      }
     }
-    case EPI_QKV: {
-      const int half = e.hd / 2;
-      if (n0 < e.qd + e.kd) {
-        // queries (rotated) to q_out, or block keys (rotated) to the cache rows of the block
-        const bool isq = n0 < e.qd;
-        for (int idx = tid; idx < TM * BN; idx += nthr) {
-          const int r = idx / BN, c = idx % BN;
-          if (r >= rows || c >= cols) continue;
-          const int m = m0 + r;
-          const int pos = e.row_pos[m];
-          const int i = (c % e.hd) % half;
-          const float v = rot<T>(Cs + r * CS_LD, c, e.hd, e.rope[(int64_t)m * half + i]);
-          if (isq) {
-            ((T*)e.q_out)[(int64_t)m * e.qd + n0 + c] = from_f<T>(v);
-          } else if (pos >= 0) {
-            const int col = n0 - e.qd + c, g = col / e.hd, d = col % e.hd;
-            const int n = m / e.block_len;
-            const int64_t off = e.layer_off_k +
-                                (((int64_t)n * e.kvh + g) * e.cap + pos) * e.hd + d;
-            ((T*)e.kv_k)[off] = from_f<T>(v);
+  } else if constexpr (KIND == EPI_SWIGLU) {
+    // tile columns [0, BN/2) are gate, [BN/2, BN) up, for f = tn*BN/2 + c
+    constexpr int FPT = CPT / 2;
+    const int f0 = tn * (BN / 2) + (tid % TPR) * FPT;
+    const int fl = (tid % TPR) * FPT;
+    if (rok) {
+      T* dst = (T*)e.act + (int64_t)m * e.F + f0;
+      if (f0 + FPT <= e.F && (e.F & 7) == 0) {
+#pragma unroll
+        for (int j = 0; j < FPT / 8; ++j) {
+          float h[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float gt = crow[fl + 8 * j + q], up = crow[BN / 2 + fl + 8 * j + q];
+            h[q] = gt / (1.f + __expf(-gt)) * up;
+          }
+          store8<T>(dst + 8 * j, h);
+        }
+      } else {
+        for (int c = 0; c < FPT && f0 + c < e.F; ++c) {
+          const float gt = crow[fl + c], up = crow[BN / 2 + fl + c];
+          dst[c] = from_f<T>(gt / (1.f + __expf(-gt)) * up);
+        }
+      }
+    }
+  } else {
+    // EPI_QKV (block rows) and EPI_CTXKV (ingest rows): row metadata staged in LDS once
+    const bool ctx = KIND == EPI_CTXKV;
+    if (tid < TM) {
+      const int mm = m0 + tid;
+      const bool ok = tid < rows;
+      s_pos[tid] = ok ? e.row_pos[mm] : -1;
+      s_seq[tid] = ok ? (ctx ? e.row_seq[mm] : mm / e.block_len) : -1;
+    }
+    __syncthreads();
+    const int64_t lay = ctx ? (int64_t)z * e.layer_stride : e.layer_off_k;
+    const int kbeg = ctx ? 0 : e.qd;                    // first virtual column of K
+    const int vbeg = kbeg + e.kd;                       // first virtual column of V
+    const int half = e.hd / 2;
+    if (n0 < vbeg) {
+      // queries or keys: rotate, then store rows of 8
+      const bool isq = n0 < kbeg;
+      const int pos = rok ? s_pos[r] : -1;
+      const int n = rok ? s_seq[r] : 0;
+      if (rok && (isq || pos >= 0)) {
+#pragma unroll
+        for (int c8 = 0; c8 < CPT; c8 += 16) {
+          float2 cs[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int i = ((cb + c8 + q) % e.hd) % half;
+            cs[q] = e.rope[(int64_t)m * half + i];
+          }
+#pragma unroll
+          for (int h8 = 0; h8 < 16; h8 += 8) {
+            const int c = cb + c8 + h8;
+            if (c >= cols) continue;
+            float v[8];
+            rope8(crow, c, e.hd, cs + h8, v);
+            if (isq) {
+              store8<T>((T*)e.q_out + (int64_t)m * e.qd + n0 + c, v);
+            } else {
+              const int col = n0 - kbeg + c, g = col / e.hd, d = col % e.hd;
+              store8<T>((T*)e.kv_k + lay + (((int64_t)n * e.kvh + g) * e.cap + pos) * e.hd + d,
+                        v);
+            }
           }
         }
-      } else {
-        // block values to the transposed cache: consecutive threads walk positions
-        for (int idx = tid; idx < TM * BN; idx += nthr) {
-          const int c = idx / TM, r = idx % TM;
-          if (r >= rows || c >= cols) continue;
-          const int m = m0 + r;
-          const int pos = e.row_pos[m];
+      }
+    } else {
+      // values to the position-minor cache: thread = one column, a run of rows
+      constexpr int RPT = TM * BN / 256;     // rows per thread: 256 threads cover BN columns
+      const int c = tid % BN, rb = (tid / BN) * RPT;
+      if (c < cols) {
+        const int col = n0 - vbeg + c, g = col / e.hd, d = col % e.hd;
+        T* vbase = (T*)e.kv_v + lay + (int64_t)g * e.hd * e.cap + (int64_t)d * e.cap;
+        for (int q = 0; q < RPT; ++q) {
+          const int rr = rb + q;
+          if (rr >= rows) break;
+          const int pos = s_pos[rr];
           if (pos < 0) continue;
-          const int col = n0 - e.qd - e.kd + c, g = col / e.hd, d = col % e.hd;
-          const int n = m / e.block_len;
-          const int64_t off = e.layer_off_k +
-                              (((int64_t)n * e.kvh + g) * e.hd + d) * e.cap + pos;
-          ((T*)e.kv_v)[off] = from_f<T>(Cs[r * CS_LD + c]);
+          vbase[(int64_t)s_seq[rr] * e.kvh * e.hd * e.cap + pos] = from_f<T>(Cs[rr * CS_LD + c]);
         }
       }
-      break;
-    }
-    case EPI_CTXKV: {
-      const int half = e.hd / 2;
-      const int64_t lay = (int64_t)z * e.layer_stride;
-      if (n0 < e.kd) {
-        for (int idx = tid; idx < TM * BN; idx += nthr) {
-          const int r = idx / BN, c = idx % BN;
-          if (r >= rows || c >= cols) continue;
-          const int t = m0 + r;
-          const int pos = e.row_pos[t];
-          if (pos < 0) continue;
-          const int n = e.row_seq[t];
-          const int i = (c % e.hd) % half;
-          const float v = rot<T>(Cs + r * CS_LD, c, e.hd, e.rope[(int64_t)t * half + i]);
-          const int col = n0 + c, g = col / e.hd, d = col % e.hd;
-          ((T*)e.kv_k)[lay + (((int64_t)n * e.kvh + g) * e.cap + pos) * e.hd + d] = from_f<T>(v);
-        }
-      } else {
-        for (int idx = tid; idx < TM * BN; idx += nthr) {
-          const int c = idx / TM, r = idx % TM;
-          if (r >= rows || c >= cols) continue;
-          const int t = m0 + r;
-          const int pos = e.row_pos[t];
-          if (pos < 0) continue;
-          const int n = e.row_seq[t];
-          const int col = n0 - e.kd + c, g = col / e.hd, d = col % e.hd;
-          ((T*)e.kv_v)[lay + (((int64_t)n * e.kvh + g) * e.hd + d) * e.cap + pos] =
-              from_f<T>(Cs[r * CS_LD + c]);
-        }
-      }
-      break;
-    }
-    case EPI_SWIGLU: {
-      const int f0 = tn * (BN / 2);
-      for (int idx = tid; idx < TM * (BN / 2); idx += nthr) {
-        const int r = idx / (BN / 2), c = idx % (BN / 2);
-        if (r >= rows || f0 + c >= e.F) continue;
-        const float gt = Cs[r * CS_LD + c], up = Cs[r * CS_LD + BN / 2 + c];
-        const float h = gt / (1.f + __expf(-gt)) * up;
-        ((T*)e.act)[(int64_t)(m0 + r) * e.F + f0 + c] = from_f<T>(h);
-      }
-      break;
-    }
-    case EPI_ARGMAX: {
-      if (e.logits) {
-        for (int idx = tid; idx < TM * BN; idx += nthr) {
-          const int r = idx / BN, c = idx % BN;
-          if (r < rows && c < cols)
-            e.logits[(int64_t)(m0 + r) * e.ldc + n0 + c] = Cs[r * CS_LD + c];
-        }
-      }
-      // 2 threads per row, each scans half of the tile's columns in increasing order
-      for (int pr = tid; pr < TM * 2; pr += nthr) {
-        const int r = pr >> 1, h = pr & 1;
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        if (r < rows) {
-          for (int c = h * (BN / 2); c < (h + 1) * (BN / 2) && c < cols; ++c)
-            argmax_combine(bv, bi, Cs[r * CS_LD + c], n0 + c);
-        }
-        const float ov = __shfl_xor(bv, 1, 64);
-        const int oi = __shfl_xor(bi, 1, 64);
-        argmax_combine(bv, bi, ov, oi);
-        if (h == 0 && r < rows) {
-          e.part_val[(int64_t)(m0 + r) * e.ntiles + tn] = bv;
-          e.part_idx[(int64_t)(m0 + r) * e.ntiles + tn] = bi;
-        }
-      }
-      break;
     }
   }
 }
