@@ -86,8 +86,9 @@ def main():
     desc, ws_w = dbd.model_desc(sh), dbd.weights_struct(W)
     tokens = synth.make_block_tokens(wl, 0, dev)
     dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
-    kv_k = torch.zeros((sh.n_layers, N, sh.n_kv_heads, cap, sh.head_dim), dtype=dt, device=dev)
-    kv_v = torch.zeros((sh.n_layers, N, sh.n_kv_heads, sh.head_dim, cap), dtype=dt, device=dev)
+    ks, vs = dbd.kv_cache_shapes(sh, N, cap)
+    kv_k = torch.zeros(ks, dtype=dt, device=dev)
+    kv_v = torch.zeros(vs, dtype=dt, device=dev)
     hidden = [synth.make_hidden(sh, int(ctx[i] + new[i]), 0, i, dev) for i in range(N)]
     cold_rows = torch.cat([hidden[i][: int(ctx[i])] for i in range(N)], 0).contiguous()
     step_rows = torch.cat([hidden[i][int(ctx[i]):] for i in range(N)], 0).contiguous()

@@ -76,7 +76,8 @@ def lib():
                                               _sz, _vp]),
             "dbd_mix_rmsnorm": (_i32, [_c.POINTER(ModelDesc), _vp, _vp, _vp, _i64, _i64, _i32,
                                        _vp, _vp]),
-            "dbd_gemm_nt": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _vp]),
+            "dbd_gemm_nt": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
+                                   _vp]),
             "dbd_timing_enable": (_i32, [_i32]),
             "dbd_timing_reset": (_i32, []),
             "dbd_timing_read": (_i32, [_i32, _c.POINTER(_c.c_double), _c.POINTER(_i64)]),
@@ -117,6 +118,24 @@ def model_desc(shape, dtype=None) -> ModelDesc:
                      shape.vocab - 1 if not hasattr(shape, "mask_token_id")
                      else shape.mask_token_id, code, float(shape.rms_eps), 0.0,
                      float(shape.rope_theta))
+
+
+def kv_cache_shapes(shape, batch, ctx_capacity):
+    """Shapes of the K and V cache tensors (see the KV-cache layout in include/dbd.h)."""
+    L, kvh, hd = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    return (L, batch, kvh, ctx_capacity, hd), (L, batch, kvh, ctx_capacity // 8, hd, 8)
+
+
+def pack_values(v):
+    """[..., P, hd] values by position (P a multiple of 8) -> the cache's [..., P/8, hd, 8]."""
+    *lead, P, hd = v.shape
+    return v.reshape(*lead, P // 8, 8, hd).transpose(-1, -2)
+
+
+def unpack_values(vb):
+    """Inverse of pack_values: [..., P/8, hd, 8] -> [..., P, hd]."""
+    *lead, B8, hd, e = vb.shape
+    return vb.transpose(-1, -2).reshape(*lead, B8 * e, hd)
 
 
 def weights_struct(w: dict) -> Weights:
@@ -212,14 +231,15 @@ def mix_rmsnorm(desc, mix_logits, mix_norm_w, hidden, out, stream=None):
         hidden.stride(1), hidden.shape[0], _ptr(out), _stream(stream, hidden)))
 
 
-def gemm_nt(A, B, C, stream=None):
-    """C[M, N] fp32 = A[M, K] . B[N, K]^T with A, B both fp32 or both bf16."""
+def gemm_nt(A, B, C, tile_cfg=-1, stream=None):
+    """C[M, N] fp32 = A[M, K] . B[N, K]^T with A, B both fp32 or both bf16; tile_cfg picks the
+    bf16 block tile (-1: the library's choice)."""
     import torch
     dt = DBD_BF16 if A.dtype == torch.bfloat16 else DBD_F32
     M, K = A.shape
     N = B.shape[0]
     _check(lib().dbd_gemm_nt(dt, _ptr(A), _ptr(B), _ptr(C), M, N, K, A.stride(0), B.stride(0),
-                             C.stride(0), _stream(stream, A)))
+                             C.stride(0), int(tile_cfg), _stream(stream, A)))
 
 
 # Stage order of DBD_STAGE_* in include/dbd.h.

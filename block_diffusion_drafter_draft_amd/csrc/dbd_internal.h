@@ -135,8 +135,11 @@ hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int row
                         int V, float* x, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, int rows, int H,
                           float eps, int block_len, int n_anchor, hipStream_t s);
+// cfg: bf16 block-tile configuration index (see dbd_gemm_nt in dbd.h), -1 = pick for the shape
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
-                       hipStream_t s);
+                       hipStream_t s, int cfg = -1);
+// column tiles of the configuration launch_gemm picks for an (M, N) problem (argmax partials)
+int gemm_ntiles(int dtype, int cfg, int M, int N, int batch);
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
 hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,
                                   int ntiles, const int32_t* blk_pos, int block_len,

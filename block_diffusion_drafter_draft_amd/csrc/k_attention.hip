@@ -5,7 +5,7 @@
 //
 // Work item: (key split s, kv head g, sequence n); one wave per 16 query rows of the GQA group
 // (rows r = b + B*h over block positions b and the group's heads h).  Per 64-key chunk the K rows
-// and the transposed V are staged in LDS; each wave computes S^T = K.Q^T with the gfx950 MFMA
+// and V (kept in the cache in blocks of 8 positions, [cap/8][hd][8]) are staged in LDS; each wave computes S^T = K.Q^T with the gfx950 MFMA
 // 16x16x32 bf16, so that its lanes hold 8 consecutive keys of one query (keys are permuted inside
 // the MFMA tiles), runs the online softmax in fp32 (exp2 domain) and feeds P^T straight from
 // registers into O^T += V^T.P^T.  Splits of one (n, g) are merged by attn_combine_kernel.
@@ -47,6 +47,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   const int R = a.block_len * a.grp;
 
   const bf16* Kg = (const bf16*)a.kv_k + ((int64_t)n * a.kvh + g) * a.cap * HD;
+  // V cache of (n, g): blocks of 8 positions, [cap/8][HD][8]
   const bf16* Vg = (const bf16*)a.kv_v + ((int64_t)n * a.kvh + g) * HD * a.cap;
 
   // this lane's query row (column of S^T / O^T)
@@ -85,9 +86,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
-      const int idx = tid + j * NT, d = idx / (KCH / 8), c = idx % (KCH / 8);
+      const int idx = tid + j * NT, c = idx / HD, d = idx % HD;    // lanes: consecutive d
       if (VT % NT == 0 || idx < VT)
-        vreg[j] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)d * a.cap + c0 + c * 8);
+        vreg[j] = *reinterpret_cast<const u32x4*>(Vg + ((int64_t)(c0 / 8 + c) * HD + d) * 8);
     }
   };
   auto store_chunk = [&](int c0) {
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
-      const int idx = tid + j * NT, d = idx / (KCH / 8), c = idx % (KCH / 8);
+      const int idx = tid + j * NT, c = idx / HD, d = idx % HD;
       if (!(VT % NT == 0 || idx < VT)) continue;
       const int k0 = c0 + c * 8;
       u32x4 v = vreg[j];
@@ -238,9 +239,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int HD) {
     __syncthreads();
     l = red[4] + red[5] + red[6] + red[7];
     if (tid < HD) {
-      const float* vr = Vg + (int64_t)tid * a.cap + k_begin;
       float o = 0.f;
-      for (int k = 0; k < nk; ++k) o += p[k] * vr[k];
+      for (int k = 0; k < nk; ++k) {
+        const int kk = k_begin + k;                 // blocks of 8 positions [cap/8][HD][8]
+        o += p[k] * Vg[((int64_t)(kk >> 3) * HD + tid) * 8 + (kk & 7)];
+      }
       if (nsplit == 1) {
         ((float*)a.out)[qrow * a.qd + qcol + tid] = o / l;
       } else {

@@ -140,9 +140,10 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.s_max = ceil_div(cap, t.split);
   t.part_o = c.take<float>((int64_t)N * d.n_kv_heads * t.s_max * R * d.head_dim);
   t.part_ml = c.take<float2>((int64_t)N * d.n_kv_heads * t.s_max * R);
-  t.ntiles = ceil_div(d.vocab, 128);
-  t.lm_pv = c.take<float>(Md * t.ntiles);
-  t.lm_pi = c.take<int32_t>(Md * t.ntiles);
+  t.ntiles = gemm_ntiles(d.dtype, -1, (int)Md, d.vocab, 1);
+  const int64_t max_tiles = ceil_div(d.vocab, 128);          // any configuration fits
+  t.lm_pv = c.take<float>(Md * max_tiles);
+  t.lm_pi = c.take<int32_t>(Md * max_tiles);
   if (temperature > 0.f) {
     const int nch = ceil_div(d.vocab, vocab_chunk());
     t.logits = c.take<float>(Md * d.vocab);
@@ -450,7 +451,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       g.gateup = 1;
       g.ldb = H;
       g.M = M;
-      g.N = ceil_div(F, 64) * 128;
+      g.N = 2 * F;                      // padded to whole gate|up column tiles by the launcher
       g.K = H;
       EpiArgs e{};
       e.kind = EPI_SWIGLU;
@@ -708,7 +709,8 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
 }
 
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t M, int32_t N,
-                int32_t K, int64_t lda, int64_t ldb, int64_t ldc, void* stream) {
+                int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,
+                void* stream) {
   g_err.clear();
   if (dtype != DBD_F32 && dtype != DBD_BF16) return fail(DBD_ERR_ARG, "bad dtype");
   if (!A || !Bm || !C) return fail(DBD_ERR_ARG, "a required device pointer is NULL");
@@ -729,7 +731,8 @@ int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t 
   e.kind = EPI_STORE_F32;
   e.C = C;
   e.ldc = ldc;
-  HIP_TRY(launch_gemm(dtype, g, e, 1, (hipStream_t)stream));
+  if (tile_cfg < -1 || tile_cfg > 7) return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, 7]", tile_cfg);
+  HIP_TRY(launch_gemm(dtype, g, e, 1, (hipStream_t)stream, tile_cfg));
   return DBD_OK;
 }
 

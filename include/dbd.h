@@ -105,9 +105,10 @@ typedef struct {
 } dbd_weights;
 
 /* KV-cache layout (device, element type desc.dtype, caller-owned, persistent across calls):
- *   kv_k: [L_d, N, kvh, ctx_capacity, hd]   rotated keys, one row of hd per position;
- *   kv_v: [L_d, N, kvh, hd, ctx_capacity]   values stored position-minor (transposed) so that
- *         the attention's P.V product reads contiguous runs of positions.
+ *   kv_k: [L_d, N, kvh, ctx_capacity, hd]        rotated keys, one row of hd per position;
+ *   kv_v: [L_d, N, kvh, ctx_capacity/8, hd, 8]   values in blocks of 8 positions: value (p, d)
+ *         sits at [p/8][d][p%8], so the attention's P.V product reads 8 consecutive positions
+ *         of one dimension as one 16-byte vector and a 64-position chunk is contiguous.
  * ctx_capacity must be a multiple of 64. */
 
 /* Workspace size (host) for draft_block with at most `max_batch` sequences, block length
@@ -224,9 +225,13 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
                     int32_t n_tokens, void* out, void* stream);
 
 /* The GEMM used for every projection: C[M, N] (fp32) = A[M, K] . B[N, K]^T with A, B in
- * `dtype`; row strides lda, ldb, ldc in elements.  bf16 needs K % 64 == 0. */
+ * `dtype`; row strides lda, ldb, ldc in elements.  bf16 needs K % 64 == 0 and 16-byte aligned
+ * rows.  tile_cfg selects the bf16 block tile and pipeline depth (BM x BN / stages: 0: 256x256/2,
+ * 1: 256x128/3, 2: 128x128/3, 3: 64x128/4, 4: 128x128/2, 5: 64x128/3, 6: 256x128/2,
+ * 7: 128x256/2; -1: the library's choice for the shape). */
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* B, float* C, int32_t M, int32_t N,
-                int32_t K, int64_t lda, int64_t ldb, int64_t ldc, void* stream);
+                int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,
+                void* stream);
 
 /* Per-stage timing for benchmarks.  While enabled, every kernel launch of the library is
  * bracketed by a pair of hipEvents recorded on the launch's stream and accounted to its stage

@@ -32,8 +32,9 @@ class Case:
         self.tokens = synth.make_block_tokens(wl, seed, dev)
         L, kvh, hd = sh.n_layers, sh.n_kv_heads, sh.head_dim
         dt = DT[sh.dtype]
-        self.kv_k = torch.zeros((L, N, kvh, self.cap, hd), dtype=dt, device=dev)
-        self.kv_v = torch.zeros((L, N, kvh, hd, self.cap), dtype=dt, device=dev)
+        ks, vs = dbd.kv_cache_shapes(sh, N, self.cap)
+        self.kv_k = torch.zeros(ks, dtype=dt, device=dev)
+        self.kv_v = torch.zeros(vs, dtype=dt, device=dev)
         self.D = B - wl.n_anchor
         self.cache_kv = None
         if wl.ctx_source == "hidden":
@@ -44,8 +45,11 @@ class Case:
             self.cache_kv = (K, V)
             for i in range(N):
                 C = int(self.ctx[i])
+                C8 = (C + 7) // 8 * 8
                 self.kv_k[:, i, :, :C, :] = K[:, i, :, :C, :]
-                self.kv_v[:, i, :, :, :C] = V[:, i, :, :C, :].transpose(-1, -2)
+                vpad = torch.zeros((L, kvh, C8, hd), dtype=dt, device=dev)
+                vpad[:, :, :C] = V[:, i, :, :C, :]
+                self.kv_v[:, i, :, : C8 // 8] = dbd.pack_values(vpad)
 
     # ------------------------------------------------------------------ running the library
     def _offsets(self, counts):
@@ -112,7 +116,7 @@ class Case:
     def gpu_cache(self, i, l, n_pos):
         """GPU cache contents of sequence i, layer l, positions < n_pos as (K, V) [kvh, n, hd]."""
         k = self.kv_k[l, i, :, :n_pos, :].float().cpu().numpy()
-        v = self.kv_v[l, i, :, :, :n_pos].float().cpu().numpy().transpose(0, 2, 1)
+        v = dbd.unpack_values(self.kv_v[l, i]).float().cpu().numpy()[:, :n_pos, :]
         return k, v
 
 

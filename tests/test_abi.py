@@ -187,6 +187,7 @@ def test_sample_validation():
 def test_gemm_validation():
     L = dbd.lib()
     fake = 1 << 20
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, None) == -2   # K % 64
-    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, None) == -2      # lda < K
-    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, None) == -2   # K % 64
+    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, None) == -2      # lda < K
+    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 8, None) == -1    # tile_cfg
