@@ -83,7 +83,7 @@ def main():
     ctx, new = synth.make_lengths(wl, 0)
     cap = synth.capacity_for(wl, ctx, new)
     W = synth.make_weights(sh, 0, dev)
-    desc, ws_w = dbd.model_desc(sh), dbd.weights_struct(W)
+    desc, ws_w = dbd.model_desc(sh, act_pairs=wl.act_pairs), dbd.weights_struct(W)
     tokens = synth.make_block_tokens(wl, 0, dev)
     dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
     ks, vs = dbd.kv_cache_shapes(sh, N, cap)

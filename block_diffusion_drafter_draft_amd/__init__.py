@@ -29,7 +29,7 @@ class ModelDesc(_c.Structure):
     _fields_ = [("hidden", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
                 ("ffn", _i32), ("n_layers", _i32), ("n_target_layers", _i32), ("vocab", _i32),
                 ("mask_token_id", _i32), ("dtype", _i32), ("rms_eps", _f32),
-                ("reserved0", _f32), ("rope_theta", _c.c_double)]
+                ("act_pairs", _i32), ("rope_theta", _c.c_double)]
 
 
 WEIGHT_FIELDS = ["mix_logits", "mix_norm_w", "wk_ctx", "wv_ctx", "attn_norm_w", "wq", "wk_draft",
@@ -109,14 +109,15 @@ def _stream(stream, *tensors):
     return None
 
 
-def model_desc(shape, dtype=None) -> ModelDesc:
-    """ModelDesc from an object with the drafter's shape attributes (e.g. synth.DrafterShape)."""
+def model_desc(shape, dtype=None, act_pairs=0) -> ModelDesc:
+    """ModelDesc from an object with the drafter's shape attributes (e.g. synth.DrafterShape);
+    act_pairs=1 feeds the projection GEMMs bf16 (high, low) activation pairs."""
     dt = dtype if dtype is not None else shape.dtype
     code = {"f32": DBD_F32, "bf16": DBD_BF16, DBD_F32: DBD_F32, DBD_BF16: DBD_BF16}[dt]
     return ModelDesc(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
                      shape.n_layers, shape.n_target_layers, shape.vocab,
                      shape.vocab - 1 if not hasattr(shape, "mask_token_id")
-                     else shape.mask_token_id, code, float(shape.rms_eps), 0.0,
+                     else shape.mask_token_id, code, float(shape.rms_eps), int(act_pairs),
                      float(shape.rope_theta))
 
 

@@ -102,6 +102,7 @@ struct EpiArgs {
   const float2* rope;       // rope table for the rows
   // SwiGLU
   void* act;            // [M, F] element T
+  void* act_lo;         // optional low part of the bf16 pair of act
   int F;
   // LM-head argmax
   float* part_val;      // [M, ntiles]
@@ -118,6 +119,7 @@ struct AttnArgs {
   const void* kv_v;     // layer base: [N, kvh, hd, cap]
   const int32_t* seq_keys;
   void* out;            // [N*B, qd]
+  void* out_lo;         // optional low part of the bf16 pair of out
   float* part_o;        // [N, kvh, S_max, R, hd]
   float2* part_ml;      // [N, kvh, S_max, R] (running max in log2 units, sum)
   int batch, kvh, grp, block_len, cap, qd, s_max, split;
@@ -133,13 +135,14 @@ hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls
                               void* out, void* out_lo, float eps, hipStream_t s);
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H,
                         int V, float* x, hipStream_t s);
-hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, int rows, int H,
-                          float eps, int block_len, int n_anchor, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, void* out_lo,
+                          int rows, int H, float eps, int block_len, int n_anchor, hipStream_t s);
 // cfg: bf16 block-tile configuration index (see dbd_gemm_nt in dbd.h), -1 = pick for the shape
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
                        hipStream_t s, int cfg = -1);
-// column tiles of the configuration launch_gemm picks for an (M, N) problem (argmax partials)
-int gemm_ntiles(int dtype, int cfg, int M, int N, int batch);
+// column tiles of the configuration launch_gemm uses for an (M, N) problem of epilogue `kind`
+// (sizes the argmax partials); split = the A operand comes as a bf16 pair
+int gemm_ntiles(int dtype, int kind, int cfg, int M, int N, int batch, bool split);
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
 hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,
                                   int ntiles, const int32_t* blk_pos, int block_len,

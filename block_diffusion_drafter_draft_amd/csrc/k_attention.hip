@@ -181,10 +181,16 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   if (nsplit == 1) {
     const float inv = 1.f / l_run;
     bf16* o = (bf16*)a.out + qrow * a.qd + qcol;
+    bf16* ol = a.out_lo ? (bf16*)a.out_lo + qrow * a.qd + qcol : nullptr;
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[dt * 16 + (lane >> 4) * 4 + i] = (bf16)(acc[dt][i] * inv);
+      for (int i = 0; i < 4; ++i) {
+        const float y = acc[dt][i] * inv;
+        const bf16 hi = (bf16)y;
+        o[dt * 16 + (lane >> 4) * 4 + i] = hi;
+        if (ol) ol[dt * 16 + (lane >> 4) * 4 + i] = (bf16)(y - (float)hi);
+      }
   } else {
     const int64_t pr = (((int64_t)n * a.kvh + g) * a.s_max + s) * R + r;
     float* po = a.part_o + pr * HD;
@@ -302,9 +308,16 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int HD) {
   }
   const float inv = 1.f / l;
   const int b = r % a.block_len, h = r / a.block_len;
-  T* out = (T*)a.out + ((int64_t)n * a.block_len + b) * a.qd + (g * a.grp + h) * HD + 4 * d4;
+  const int64_t off = ((int64_t)n * a.block_len + b) * a.qd + (g * a.grp + h) * HD + 4 * d4;
+  T* out = (T*)a.out + off;
+  T* out_lo = a.out_lo ? (T*)a.out_lo + off : nullptr;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) out[q] = from_f<T>(o[q] * inv);
+  for (int q = 0; q < 4; ++q) {
+    const float y = o[q] * inv;
+    const T hi = from_f<T>(y);
+    out[q] = hi;
+    if (out_lo) out_lo[q] = from_f<T>(y - to_f(hi));
+  }
 }
 
 template <int HD>

@@ -160,6 +160,7 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
     const int fl = (tid % TPR) * FPT;
     if (rok) {
       T* dst = (T*)e.act + (int64_t)m * e.F + f0;
+      T* dlo = e.act_lo ? (T*)e.act_lo + (int64_t)m * e.F + f0 : nullptr;
       if (f0 + FPT <= e.F && (e.F & 7) == 0) {
 #pragma unroll
         for (int j = 0; j < FPT / 8; ++j) {
@@ -170,11 +171,18 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
             h[q] = gt / (1.f + __expf(-gt)) * up;
           }
           store8<T>(dst + 8 * j, h);
+          if (dlo) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) h[q] -= to_f(from_f<T>(h[q]));
+            store8<T>(dlo + 8 * j, h);
+          }
         }
       } else {
         for (int c = 0; c < FPT && f0 + c < e.F; ++c) {
           const float gt = crow[fl + c], up = crow[BN / 2 + fl + c];
-          dst[c] = from_f<T>(gt / (1.f + __expf(-gt)) * up);
+          const float h = gt / (1.f + __expf(-gt)) * up;
+          dst[c] = from_f<T>(h);
+          if (dlo) dlo[c] = from_f<T>(h - to_f(from_f<T>(h)));
         }
       }
     }
@@ -530,20 +538,26 @@ static void launch_cfg(int cfg, const GemmArgs& a, const EpiArgs& e, int batch, 
   }
 }
 
+// The bf16 configuration a launch really uses: the requested one (or the shape's choice), with
+// QKV / context K/V tiles kept at 128 columns (they must not straddle the Q/K/V segment
+// boundaries, multiples of 128) and bf16-pair launches on the tiles whose ring fits in LDS.
+static int resolve_cfg(int kind, int cfg, int M, int N, int batch, int gateup, int F,
+                       bool split) {
+  if (cfg < 0 || cfg >= kNumCfg) cfg = choose_cfg(M, N, batch, gateup, F);
+  if ((kind == EPI_QKV || kind == EPI_CTXKV) && kCfgBN[cfg] != 128)
+    cfg = kCfgBM[cfg] == 256 ? 1 : 4;
+  if (split) cfg = (cfg == 3 || cfg == 5) ? 5 : 4;
+  return cfg;
+}
+
 template <int KIND>
 static void launch_kind(int dtype, int cfg, GemmArgs a, const EpiArgs& e, int batch,
                         hipStream_t s) {
   if (dtype == 1) {
     const int F = a.seg[0].n1 - a.seg[0].n0;
-    if (cfg < 0 || cfg >= kNumCfg) cfg = choose_cfg(a.M, a.N, batch, a.gateup, F);
-    // QKV and context K/V tiles must not straddle the Q/K/V segment boundaries (multiples of
-    // 128): keep those at 128 columns.
-    if ((KIND == EPI_QKV || KIND == EPI_CTXKV) && kCfgBN[cfg] != 128)
-      cfg = kCfgBM[cfg] == 256 ? 1 : 4;
-    if constexpr (KIND == EPI_CTXKV) {
-      if (a.A2) { launch_cfg<KIND, true>(cfg, a, e, batch, s); return; }
-    }
-    launch_cfg<KIND, false>(cfg, a, e, batch, s);
+    cfg = resolve_cfg(KIND, cfg, a.M, a.N, batch, a.gateup, F, a.A2 != nullptr);
+    if (a.A2) launch_cfg<KIND, true>(cfg, a, e, batch, s);
+    else launch_cfg<KIND, false>(cfg, a, e, batch, s);
   } else {
     if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, FN / 2) * FN;
     dim3 grid(ceil_div(a.N, FN), ceil_div(a.M, FM), batch);
@@ -551,10 +565,9 @@ static void launch_kind(int dtype, int cfg, GemmArgs a, const EpiArgs& e, int ba
   }
 }
 
-int gemm_ntiles(int dtype, int cfg, int M, int N, int batch) {
+int gemm_ntiles(int dtype, int kind, int cfg, int M, int N, int batch, bool split) {
   if (dtype != 1) return ceil_div(N, FN);
-  if (cfg < 0 || cfg >= kNumCfg) cfg = choose_cfg(M, N, batch, 0, 0);
-  return ceil_div(N, kCfgBN[cfg]);
+  return ceil_div(N, kCfgBN[resolve_cfg(kind, cfg, M, N, batch, 0, 0, split)]);
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,

@@ -240,13 +240,15 @@ hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int row
 }
 
 // ------------------------------------------------------------------ RMSNorm
-// out[r'] = T(x[r] / sqrt(mean(x[r]^2) + eps) * g).  With n_anchor > 0 only the mask rows of
-// each block are normalised and written compactly (r' = n*(B - n_anchor) + b - n_anchor).
+// out[r'] = T(x[r] / sqrt(mean(x[r]^2) + eps) * g), and with out_lo the low part of the bf16
+// pair.  With n_anchor > 0 only the mask rows of each block are normalised and written
+// compactly (r' = n*(B - n_anchor) + b - n_anchor).
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
                                                       const T* __restrict__ g,
-                                                      T* __restrict__ out, int H, float eps,
-                                                      int block_len, int n_anchor) {
+                                                      T* __restrict__ out, T* __restrict__ out_lo,
+                                                      int H, float eps, int block_len,
+                                                      int n_anchor) {
   __shared__ float red[4];
   const int ro = blockIdx.x;
   int ri = ro;
@@ -265,24 +267,29 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   __syncthreads();
   const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
   T* o = out + (int64_t)ro * H;
+  T* ol = out_lo ? out_lo + (int64_t)ro * H : nullptr;
   for (int i = threadIdx.x * 4; i < H; i += 256 * 4) {
     float4 v = *reinterpret_cast<const float4*>(xr + i);
-    o[i + 0] = from_f<T>(v.x * inv * to_f(g[i + 0]));
-    o[i + 1] = from_f<T>(v.y * inv * to_f(g[i + 1]));
-    o[i + 2] = from_f<T>(v.z * inv * to_f(g[i + 2]));
-    o[i + 3] = from_f<T>(v.w * inv * to_f(g[i + 3]));
+    const float y[4] = {v.x * inv * to_f(g[i + 0]), v.y * inv * to_f(g[i + 1]),
+                        v.z * inv * to_f(g[i + 2]), v.w * inv * to_f(g[i + 3])};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const T hi = from_f<T>(y[q]);
+      o[i + q] = hi;
+      if (ol) ol[i + q] = from_f<T>(y[q] - to_f(hi));
+    }
   }
 }
 
-hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, int rows, int H,
-                          float eps, int block_len, int n_anchor, hipStream_t s) {
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, void* out_lo,
+                          int rows, int H, float eps, int block_len, int n_anchor, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (dtype == 1)
     hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(rows), dim3(256), 0, s, x, (const bf16*)g,
-                       (bf16*)out, H, eps, block_len, n_anchor);
+                       (bf16*)out, (bf16*)out_lo, H, eps, block_len, n_anchor);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, s, x, (const float*)g,
-                       (float*)out, H, eps, block_len, n_anchor);
+                       (float*)out, (float*)nullptr, H, eps, block_len, n_anchor);
   return hipGetLastError();
 }
 

@@ -93,6 +93,9 @@ struct DraftBufs {
   void* q;
   void* attn;
   void* act;
+  void* xn_lo;          // low parts of the bf16 pairs (act_pairs only, else null)
+  void* attn_lo;
+  void* act_lo;
   float* part_o;
   float2* part_ml;
   float* lm_pv;
@@ -136,11 +139,17 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.q = c.take<char>(M * qd * es);
   t.attn = c.take<char>(M * qd * es);
   t.act = c.take<char>(M * d.ffn * es);
+  if (d.dtype == DBD_BF16 && d.act_pairs) {
+    t.xn_lo = c.take<char>(M * d.hidden * es);
+    t.attn_lo = c.take<char>(M * qd * es);
+    t.act_lo = c.take<char>(M * d.ffn * es);
+  }
   t.split = attn_split(d.dtype);
   t.s_max = ceil_div(cap, t.split);
   t.part_o = c.take<float>((int64_t)N * d.n_kv_heads * t.s_max * R * d.head_dim);
   t.part_ml = c.take<float2>((int64_t)N * d.n_kv_heads * t.s_max * R);
-  t.ntiles = gemm_ntiles(d.dtype, -1, (int)Md, d.vocab, 1);
+  t.ntiles = gemm_ntiles(d.dtype, EPI_ARGMAX, -1, (int)Md, d.vocab, 1,
+                         d.dtype == DBD_BF16 && d.act_pairs);
   const int64_t max_tiles = ceil_div(d.vocab, 128);          // any configuration fits
   t.lm_pv = c.take<float>(Md * max_tiles);
   t.lm_pi = c.take<int32_t>(Md * max_tiles);
@@ -190,6 +199,8 @@ int check_desc(const dbd_model_desc* d) {
   if (d->n_target_layers > 0 && d->n_layers > 8)
     return fail(DBD_ERR_UNSUPPORTED, "target mixing supports at most 8 draft layers (got %d)",
                 d->n_layers);
+  if (d->act_pairs != 0 && d->act_pairs != 1)
+    return fail(DBD_ERR_ARG, "act_pairs must be 0 or 1");
   if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.0))
     return fail(DBD_ERR_ARG, "rms_eps must be >= 0 and rope_theta > 0");
   return DBD_OK;
@@ -374,10 +385,12 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     auto lw = [&](const void* p, int64_t per_layer) {
       return (const void*)((const char*)p + (int64_t)l * per_layer * es);
     };
-    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->attn_norm_w, H), b.xn, M, H, d.rms_eps, B, 0, st));
+    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->attn_norm_w, H), b.xn, b.xn_lo, M, H,
+                                                     d.rms_eps, B, 0, st));
     {
       GemmArgs g{};
       g.A = b.xn;
+      g.A2 = b.xn_lo;
       g.lda = H;
       g.seg[0] = BSeg{lw(w->wq, (int64_t)qd * H), 0, qd};
       g.seg[1] = BSeg{lw(w->wk_draft, (int64_t)kd * H), qd, qd + kd};
@@ -411,6 +424,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       a.kv_v = (const char*)kv_v + (int64_t)l * layer_elems * es;
       a.seq_keys = b.meta.seq_keys;
       a.out = b.attn;
+      a.out_lo = b.attn_lo;
       a.part_o = b.part_o;
       a.part_ml = b.part_ml;
       a.batch = N;
@@ -427,6 +441,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     {
       GemmArgs g{};
       g.A = b.attn;
+      g.A2 = b.attn_lo;
       g.lda = qd;
       g.seg[0] = BSeg{lw(w->wo, (int64_t)H * qd), 0, H};
       g.nseg = 1;
@@ -440,10 +455,12 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.ldc = H;
       HIP_STAGE(DBD_STAGE_GEMM_O, st, launch_gemm(d.dtype, g, e, 1, st));
     }
-    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->mlp_norm_w, H), b.xn, M, H, d.rms_eps, B, 0, st));
+    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->mlp_norm_w, H), b.xn, b.xn_lo, M, H,
+                                                     d.rms_eps, B, 0, st));
     {
       GemmArgs g{};
       g.A = b.xn;
+      g.A2 = b.xn_lo;
       g.lda = H;
       g.seg[0] = BSeg{lw(w->w_gate, (int64_t)F * H), 0, F};
       g.seg[1] = BSeg{lw(w->w_up, (int64_t)F * H), 0, F};
@@ -456,12 +473,14 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       EpiArgs e{};
       e.kind = EPI_SWIGLU;
       e.act = b.act;
+      e.act_lo = b.act_lo;
       e.F = F;
       HIP_STAGE(DBD_STAGE_GEMM_GATEUP, st, launch_gemm(d.dtype, g, e, 1, st));
     }
     {
       GemmArgs g{};
       g.A = b.act;
+      g.A2 = b.act_lo;
       g.lda = F;
       g.seg[0] = BSeg{lw(w->w_down, (int64_t)H * F), 0, H};
       g.nseg = 1;
@@ -479,12 +498,14 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   (void)cw;
 
   // 3. final norm on the mask rows, LM head
-  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, w->final_norm_w, b.xn, Md, H, d.rms_eps, B, n_anchor, st));
+  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, w->final_norm_w, b.xn, b.xn_lo, Md, H,
+                                                   d.rms_eps, B, n_anchor, st));
   const bool sampling = temperature > 0.f;
   float* logits = logits_out ? logits_out : (sampling ? b.logits : nullptr);
   {
     GemmArgs g{};
     g.A = b.xn;
+    g.A2 = b.xn_lo;
     g.lda = H;
     g.seg[0] = BSeg{w->lm_head, 0, V};
     g.nseg = 1;

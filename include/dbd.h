@@ -79,7 +79,10 @@ typedef struct {
   int32_t mask_token_id;     /* id of [MASK] (informational: block_tokens carry the ids) */
   int32_t dtype;             /* DBD_F32 or DBD_BF16 */
   float rms_eps;             /* e.g. 1e-6 */
-  float reserved0;
+  int32_t act_pairs;         /* bf16 only: 1 = feed every projection GEMM its activation as a
+                                bf16 (high, low) pair, ~16 significant bits, at twice the MFMA
+                                work; 0 = plain bf16 activations.  The mixed context features
+                                always use the pair. */
   double rope_theta;         /* e.g. 1e6 */
 } dbd_model_desc;
 

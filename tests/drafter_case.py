@@ -21,7 +21,7 @@ class Case:
         self.wl, self.dev, self.seed = wl, dev, seed
         sh = wl.shape
         self.shape = sh
-        self.desc = dbd.model_desc(sh)
+        self.desc = dbd.model_desc(sh, act_pairs=wl.act_pairs)
         self.W = synth.make_weights(sh, seed, dev)
         self.wstruct = dbd.weights_struct(self.W)
         c, n = synth.make_lengths(wl, seed)

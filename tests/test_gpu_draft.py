@@ -139,6 +139,24 @@ def test_qwen3_4b_matches_oracle():
     _run("qwen3-4b")
 
 
+def test_activation_pairs_are_more_accurate():
+    """The same Qwen3-4B-shaped step with bf16 activation pairs is closer to the oracle than with
+    plain bf16 activations, and still within tolerance."""
+    errs = {}
+    for pairs in (0, 1):
+        wl = synth.workload("qwen3-4b").with_(act_pairs=pairs)
+        case = Case(wl, dev=DEV)
+        case.fill_cache()
+        drafts, logits, status = case.step()
+        torch.cuda.synchronize()
+        _check_drafts_property(case, drafts, logits)
+        report = []
+        _compare(case, logits, [0], report)
+        errs[pairs] = report[0][1]
+    print(f"qwen3-4b logits rel-L2: plain bf16 {errs[0]:.3e}, pairs {errs[1]:.3e}", flush=True)
+    assert errs[1] < 0.75 * errs[0]          # the K/V cache and P stay bf16 in both modes
+
+
 @pytest.mark.timeout(600)
 def test_qwen3_8b_sampled_sequences_match_oracle():
     wl = synth.workload("qwen3-8b")
