@@ -7,6 +7,11 @@ context lengths uniform in [256, 3072]).  Inputs are synthetic and resident in H
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Prints one JSON line.
+
+Auxiliary modes for the HBM-traffic figure of the dominant kernel (rocprofv3 counter passes):
+  python bench.py --calibrate-copy           plain 1 GiB device copies (counter scale factor)
+  python bench.py --summarize-traffic DIR    FETCH_SIZE / WRITE_SIZE CSVs of the bench and of the
+                                             copy runs -> profiles/traffic_qwen3-8b_bs32.json
 """
 import argparse
 import json
@@ -14,6 +19,7 @@ import os
 import sys
 import time
 
+import hashlib
 import numpy as np
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X datasheet
@@ -30,7 +36,111 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps-only", action="store_true",
                     help="skip the instrumented pass and the cold-ingest timing")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-traffic", metavar="DIR")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3-8b_bs32.json")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: traffic counters are only valid for the build they came from."""
+    d = os.path.join(ROOT, "block_diffusion_drafter_draft_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def calibrate_copy():
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+
+
+def summarize_traffic(d):
+    """Per-launch HBM bytes of each library kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    runs (KiB per dispatch), scaled by what the same counters read for a plain copy of known
+    size.  Expects DIR/{fetch,write}/ (bench) and DIR/{copy_fetch,copy_write}/ (copy runs)."""
+    import csv
+    import glob
+
+    def per_kernel(sub, counter):
+        """Counter values per kernel name, restricted to dispatches with the grid of the last
+        dispatch of that kernel (the measured steps; the cold ingest runs other grids)."""
+        rows = {}
+        for f in glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows.setdefault(r["Kernel_Name"], []).append(
+                        (int(r["Dispatch_Id"]), r["Grid_Size"], float(r["Counter_Value"])))
+        vals = {}
+        for k, rs in rows.items():
+            rs.sort()
+            g = rs[-1][1]
+            vals[k] = [v for _, gs, v in rs if gs == g]
+        return vals
+
+    def copy_factor(sub, counter):
+        v = [x for k, xs in per_kernel(sub, counter).items() if "copy" in k.lower() or
+             "elementwise" in k.lower() for x in xs]
+        v = sorted(v)[-3:]                       # the three 1 GiB copies
+        return (sum(v) / len(v) * 1024.0) / COPY_BYTES   # KiB counted per byte moved
+    ff, fw = copy_factor("copy_fetch", "FETCH_SIZE"), copy_factor("copy_write", "WRITE_SIZE")
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    out = {"commands": [
+               "cd /tmp && export TMPDIR=/tmp",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/m/traffic/fetch"
+               " -o run -- python3 $REPO/bench.py --steps 3 --warmup 1 --profile-steps-only"
+               " --no-cpu-baseline",
+               "(the same with --pmc WRITE_SIZE into .../traffic/write)",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/m/traffic/copy_fetch"
+               " -o run -- python3 $REPO/bench.py --calibrate-copy",
+               "(the same with --pmc WRITE_SIZE into .../traffic/copy_write)",
+               "python3 bench.py --summarize-traffic gpurun_out/m/traffic"],
+           "source_hash": kernel_source_hash(), "copy_factor_fetch": round(ff, 4),
+           "copy_factor_write": round(fw, 4), "kernels": {}}
+    for k in fetch:
+        if "dbd::" not in k and not k.startswith("_ZN3dbd"):
+            continue
+        fb = sum(fetch[k]) / len(fetch[k]) * 1024.0 / ff
+        wb = (sum(write.get(k, [0])) / max(1, len(write.get(k, [0])))) * 1024.0 / fw
+        out["kernels"][k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                             "dispatches": len(fetch[k])}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps({"copy_factor_fetch": out["copy_factor_fetch"],
+                      "copy_factor_write": out["copy_factor_write"],
+                      "kernels": len(out["kernels"])}))
+
+
+# Library kernel (demangled name fragment) behind each timed stage whose launches all use one
+# kernel; the epilogue kind is a template argument of the GEMM kernel.
+STAGE_KERNEL = {"gemm_gateup": ", 4, false>", "gemm_lmhead": ", 5, false>",
+                "gemm_qkv": ", 2, false>", "gemm_ctxkv": ", 3, true>",
+                "attn": "attn_bf16_kernel", "mix": "mix_rmsnorm_kernel"}
+
+
+def measured_traffic(kernel_substr):
+    """HBM bytes per launch of the first library kernel whose name contains kernel_substr, from
+    the committed counter summary, or None when absent or taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    for k, v in t["kernels"].items():
+        if kernel_substr in k:
+            return v["fetch_bytes"] + v["write_bytes"]
+    return None
 
 
 def algorithmic_costs(wl, ctx, new):
@@ -65,6 +175,12 @@ def algorithmic_costs(wl, ctx, new):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path needs no inter-GPU exchange; see the sharding notes)",
@@ -186,8 +302,13 @@ def main():
             ach = b / n / avg_s / 1e9
             roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
                         "unit": "GB/s", "frac": round(ach * 1e9 / HBM_PEAK, 4)}
+        tr = measured_traffic(STAGE_KERNEL[dom]) if dom in STAGE_KERNEL else None
         roofline.update({"kernel": dom, "launches_per_step": n,
-                         "avg_launch_us": round(avg_s * 1e6, 2), "traffic": None})
+                         "avg_launch_us": round(avg_s * 1e6, 2),
+                         "algorithmic_bytes_per_launch": round(b / n),
+                         "traffic": tr,
+                         "traffic_source": None if tr is None else
+                         os.path.relpath(TRAFFIC_FILE, ROOT)})
     step_roof_s = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in costs.values())
 
     cpu = None
