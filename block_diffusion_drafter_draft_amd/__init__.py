@@ -76,8 +76,9 @@ def lib():
                                               _sz, _vp]),
             "dbd_mix_rmsnorm": (_i32, [_c.POINTER(ModelDesc), _vp, _vp, _vp, _i64, _i64, _i32,
                                        _vp, _vp]),
+            "dbd_gemm_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _c.POINTER(_sz)]),
             "dbd_gemm_nt": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
-                                   _vp]),
+                                   _vp, _sz, _vp]),
             "dbd_timing_enable": (_i32, [_i32]),
             "dbd_timing_reset": (_i32, []),
             "dbd_timing_read": (_i32, [_i32, _c.POINTER(_c.c_double), _c.POINTER(_i64)]),
@@ -232,15 +233,25 @@ def mix_rmsnorm(desc, mix_logits, mix_norm_w, hidden, out, stream=None):
         hidden.stride(1), hidden.shape[0], _ptr(out), _stream(stream, hidden)))
 
 
-def gemm_nt(A, B, C, tile_cfg=-1, stream=None):
+def gemm_workspace_bytes(dtype, M, N, K, tile_cfg=-1):
+    """Workspace bytes gemm_nt needs to split K for this shape and tile (0: it does not)."""
+    out = _sz(0)
+    _check(lib().dbd_gemm_workspace_bytes(dtype, M, N, K, int(tile_cfg), _c.byref(out)))
+    return out.value
+
+
+def gemm_nt(A, B, C, tile_cfg=-1, workspace=None, stream=None):
     """C[M, N] fp32 = A[M, K] . B[N, K]^T with A, B both fp32 or both bf16; tile_cfg picks the
-    bf16 block tile (-1: the library's choice)."""
+    bf16 block tile (-1: the library's choice).  With a workspace (gemm_workspace_bytes) the
+    deep-ring tiles may split K over several workgroups."""
     import torch
     dt = DBD_BF16 if A.dtype == torch.bfloat16 else DBD_F32
     M, K = A.shape
     N = B.shape[0]
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dbd_gemm_nt(dt, _ptr(A), _ptr(B), _ptr(C), M, N, K, A.stride(0), B.stride(0),
-                             C.stride(0), int(tile_cfg), _stream(stream, A)))
+                             C.stride(0), int(tile_cfg), _ptr(workspace), wb,
+                             _stream(stream, A)))
 
 
 # Stage order of DBD_STAGE_* in include/dbd.h.

@@ -27,6 +27,8 @@ COMMON = [
 SOURCES = {
     "k_rowops.hip": [],
     "k_gemm.hip": [],
+    # the deep-ring tiles keep their MFMA accumulators in VGPRs (see the file's header)
+    "k_gemm_deep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_attention.hip": [],
     "k_vocab.hip": ["-ffp-contract=off"],
     "runtime.hip": [],
@@ -48,11 +50,30 @@ def _compile(src, extra, verbose):
     return obj
 
 
+# Translation units whose kernels issue LDS reads as inline assembly: their device assembly is
+# kept in _build/ so that tests/test_asm_lds_reads.py can check every such read is waited for
+# before its registers are touched.
+ASM_LISTED = ["k_gemm_deep.hip"]
+
+
+def _device_asm(src, extra):
+    out = os.path.join(OBJ_DIR, src.replace(".hip", ".s"))
+    cmd = [HIPCC, *COMMON, *extra, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stdout}{r.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libdbd.so next to this file."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES) + len(ASM_LISTED),
+                                            os.cpu_count() or 4)) as ex:
+        asm = [ex.submit(_device_asm, s, SOURCES[s]) for s in ASM_LISTED]
         objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), SOURCES.items()))
+        for f in asm:
+            f.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

@@ -1,278 +1,23 @@
 // Projection GEMMs of the drafter: C = A[M,K] . W[N,K]^T (both operands K-contiguous), with the
-// epilogues that consume the tile: plain store, residual add, Q/K/V with rotation and cache
-// write, context K/V with rotation and cache append, SwiGLU, and the LM head's per-tile argmax.
+// epilogues that consume the tile (gemm_common.h), and the choice of kernel and tile per shape.
 //
-// bf16 path (gfx950): block tile BM x BN x 64 for 4 waves in a 2 x 2 grid, each wave a
+// bf16 pipelined path (gfx950): block tile BM x BN x 64 for 4 waves in a 2 x 2 grid, each wave a
 // (BM/2) x (BN/2) grid of 16x16x32 bf16 MFMA tiles with fp32 accumulation.  Tiles move from
 // global memory straight into LDS (global_load_lds_dwordx4, no register staging) through an
 // ST-stage ring; the 16-byte chunks of each 128-byte tile row are XOR-swizzled by choosing which
 // global chunk each lane fetches.  One barrier per k-tile.  Tiles sharing a weight column tile
-// are dispatched to the same XCD back to back so the weights come from HBM once.
+// are dispatched to the same XCD back to back so the weights come from HBM once.  The deep-ring
+// kernels (k_gemm_deep.hip) take the shapes where a deeper prefetch or split-K pays.
 // fp32 path: 64 x 128 x 16 block tile on the vector ALUs (exact fp32 products and sums).
-// Both paths stage the finished tile in LDS as fp32 and run the same epilogue code over it.
-#include "dbd_internal.h"
+// All paths stage the finished tile in LDS as fp32 and run the same epilogue code over it.
+#include <cmath>
+
+#include "gemm_common.h"
 
 namespace dbd {
 
 constexpr int BK = 64;
 
-// ------------------------------------------------------------------ B row addressing
-// Virtual column v (< N) -> pointer to the K-contiguous weight row that produces it.  The
-// segment base addresses are combined with integer arithmetic: a conditional choice between
-// members of the by-value argument struct is turned by the compiler into a load through a
-// selected address, which places the whole struct in private (scratch) memory.
-struct BMap {
-  uint64_t p0, d1, d2;   // base of segment 0, and offsets of segments 1, 2 from it (bytes)
-  int n1, n2, nseg, gateup, F;
-  int64_t ldb, b_bs;
-};
-__device__ __forceinline__ BMap make_bmap(const GemmArgs& a) {
-  BMap m;
-  m.p0 = (uint64_t)a.seg[0].ptr;
-  m.d1 = (uint64_t)a.seg[1].ptr - m.p0;
-  m.d2 = (uint64_t)a.seg[2].ptr - m.p0;
-  m.n1 = a.seg[1].n0;
-  m.n2 = a.seg[2].n0;
-  m.nseg = a.nseg;
-  m.gateup = a.gateup;
-  m.F = a.seg[0].n1 - a.seg[0].n0;
-  m.ldb = a.ldb;
-  m.b_bs = a.b_bs;
-  return m;
-}
-// Gate/up mode: column tile t of width BN holds gate rows [t*BN/2, (t+1)*BN/2) then the same up
-// rows, so the SwiGLU epilogue finds both halves of every output in one tile.
-template <typename T, int BN>
-__device__ __forceinline__ const T* brow_ptr(const BMap& m, int v, int z) {
-  uint64_t s1, s2;
-  int r;
-  if (m.gateup) {
-    const int t = v / BN, c = v % BN;
-    const int f = t * (BN / 2) + (c % (BN / 2));
-    r = f < m.F ? f : m.F - 1;
-    s1 = c >= BN / 2;
-    s2 = 0;
-  } else {
-    s2 = (m.nseg > 2 && v >= m.n2) ? 1 : 0;
-    s1 = (!s2 && m.nseg > 1 && v >= m.n1) ? 1 : 0;
-    r = v - (int)(s2 * m.n2 + s1 * m.n1);
-  }
-  const uint64_t base = m.p0 + s1 * m.d1 + s2 * m.d2;
-  return (const T*)base + (int64_t)z * m.b_bs + (int64_t)r * m.ldb;
-}
-
-// ------------------------------------------------------------------ epilogues
-// The finished tile (or a chunk of TM of its rows) sits in LDS as fp32, row stride BN + 4.  Each thread owns a contiguous
-// segment of one row (TPR threads per row, CPT columns each), issues all of its global loads
-// before any store (a store could alias a later load, so the compiler cannot hoist loads across
-// it), and stores 16-byte vectors where the layout is contiguous.
-template <typename T>
-__device__ __forceinline__ void store8(T* dst, const float* v) {
-  if constexpr (sizeof(T) == 2) {
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
-    *reinterpret_cast<bf16x8*>(dst) = o;
-  } else {
-    *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
-  }
-}
-
-// rotate-half RoPE of tile row `row` (LDS) at tile columns c .. c+7 (same head, same half);
-// cs = the 8 (cos, sin) pairs of the head-local pair indices of those columns.
-__device__ __forceinline__ void rope8(const float* row, int c, int hd, const float2* cs,
-                                      float* out) {
-  const int half = hd / 2, d = c % hd;
-  if (d < half) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      out[e] = row[c + e] * cs[e].x - row[c + e + half] * cs[e].y;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      out[e] = row[c + e] * cs[e].x + row[c + e - half] * cs[e].y;
-  }
-}
-
-template <typename T, int TM, int BN, int KIND>
-__device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, int m0, int n0,
-                                             int tn, int z, int M, int N) {
-  constexpr int CS_LD = BN + 4;                 // fp32 tile row stride in LDS
-  constexpr int TPR = 256 / TM;                 // threads per tile row
-  constexpr int CPT = BN / TPR;                 // columns per thread
-  __shared__ int s_pos[TM], s_seq[TM];
-  const int tid = threadIdx.x;
-  const int rows = min(TM, M - m0);
-  const int cols = min(BN, N - n0);
-  const int r = tid / TPR, cb = (tid % TPR) * CPT;
-  const int m = m0 + r;
-  const bool rok = r < rows;
-  const float* crow = Cs + r * CS_LD;
-
-  if constexpr (KIND == EPI_STORE_F32 || KIND == EPI_RESID || KIND == EPI_ARGMAX) {
-    float* C = KIND == EPI_ARGMAX ? e.logits : (float*)e.C + (int64_t)z * e.c_bs;
-    if (C && rok) {
-      float* dst = C + (int64_t)m * e.ldc + n0 + cb;
-      const bool vec = (e.ldc & 3) == 0 && cb + CPT <= cols && ((uintptr_t)dst & 15) == 0;
-      if (vec) {
-        f32x4 v[CPT / 4];
-        if constexpr (KIND == EPI_RESID) {
-#pragma unroll
-          for (int j = 0; j < CPT / 4; ++j) v[j] = *reinterpret_cast<const f32x4*>(dst + 4 * j);
-        }
-#pragma unroll
-        for (int j = 0; j < CPT / 4; ++j) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(crow + cb + 4 * j);
-          if constexpr (KIND == EPI_RESID) v[j] += a;
-          else v[j] = a;
-        }
-#pragma unroll
-        for (int j = 0; j < CPT / 4; ++j) *reinterpret_cast<f32x4*>(dst + 4 * j) = v[j];
-      } else {
-        for (int c = 0; c < CPT && cb + c < cols; ++c) {
-          if constexpr (KIND == EPI_RESID) dst[c] += crow[cb + c];
-          else dst[c] = crow[cb + c];
-        }
-      }
-    }
-    if constexpr (KIND == EPI_ARGMAX) {
-      // TPR threads per row each scan their columns in increasing order, then combine
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      if (rok)
-        for (int c = cb; c < cb + CPT && c < cols; ++c) argmax_combine(bv, bi, crow[c], n0 + c);
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        argmax_combine(bv, bi, ov, oi);
-      }
-      if (rok && (tid % TPR) == 0) {
-        e.part_val[(int64_t)m * e.ntiles + tn] = bv;
-        e.part_idx[(int64_t)m * e.ntiles + tn] = bi;
-      }
-    }
-  } else if constexpr (KIND == EPI_SWIGLU) {
-    // tile columns [0, BN/2) are gate, [BN/2, BN) up, for f = tn*BN/2 + c
-    constexpr int FPT = CPT / 2;
-    const int f0 = tn * (BN / 2) + (tid % TPR) * FPT;
-    const int fl = (tid % TPR) * FPT;
-    if (rok) {
-      T* dst = (T*)e.act + (int64_t)m * e.F + f0;
-      T* dlo = e.act_lo ? (T*)e.act_lo + (int64_t)m * e.F + f0 : nullptr;
-      if (f0 + FPT <= e.F && (e.F & 7) == 0) {
-#pragma unroll
-        for (int j = 0; j < FPT / 8; ++j) {
-          float h[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float gt = crow[fl + 8 * j + q], up = crow[BN / 2 + fl + 8 * j + q];
-            h[q] = gt / (1.f + __expf(-gt)) * up;
-          }
-          store8<T>(dst + 8 * j, h);
-          if (dlo) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) h[q] -= to_f(from_f<T>(h[q]));
-            store8<T>(dlo + 8 * j, h);
-          }
-        }
-      } else {
-        for (int c = 0; c < FPT && f0 + c < e.F; ++c) {
-          const float gt = crow[fl + c], up = crow[BN / 2 + fl + c];
-          const float h = gt / (1.f + __expf(-gt)) * up;
-          dst[c] = from_f<T>(h);
-          if (dlo) dlo[c] = from_f<T>(h - to_f(from_f<T>(h)));
-        }
-      }
-    }
-  } else {
-    // EPI_QKV (block rows) and EPI_CTXKV (ingest rows): row metadata staged in LDS once
-    const bool ctx = KIND == EPI_CTXKV;
-    if (tid < TM) {
-      const int mm = m0 + tid;
-      const bool ok = tid < rows;
-      s_pos[tid] = ok ? e.row_pos[mm] : -1;
-      s_seq[tid] = ok ? (ctx ? e.row_seq[mm] : mm / e.block_len) : -1;
-    }
-    __syncthreads();
-    const int64_t lay = ctx ? (int64_t)z * e.layer_stride : e.layer_off_k;
-    const int kbeg = ctx ? 0 : e.qd;                    // first virtual column of K
-    const int vbeg = kbeg + e.kd;                       // first virtual column of V
-    const int half = e.hd / 2;
-    if (n0 < vbeg) {
-      // queries or keys: rotate, then store rows of 8
-      const bool isq = n0 < kbeg;
-      const int pos = rok ? s_pos[r] : -1;
-      const int n = rok ? s_seq[r] : 0;
-      if (rok && (isq || pos >= 0)) {
-#pragma unroll
-        for (int c8 = 0; c8 < CPT; c8 += 16) {
-          float2 cs[16];
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int i = ((cb + c8 + q) % e.hd) % half;
-            cs[q] = e.rope[(int64_t)m * half + i];
-          }
-#pragma unroll
-          for (int h8 = 0; h8 < 16; h8 += 8) {
-            const int c = cb + c8 + h8;
-            if (c >= cols) continue;
-            float v[8];
-            rope8(crow, c, e.hd, cs + h8, v);
-            if (isq) {
-              store8<T>((T*)e.q_out + (int64_t)m * e.qd + n0 + c, v);
-            } else {
-              const int col = n0 - kbeg + c, g = col / e.hd, d = col % e.hd;
-              store8<T>((T*)e.kv_k + lay + (((int64_t)n * e.kvh + g) * e.cap + pos) * e.hd + d,
-                        v);
-            }
-          }
-        }
-      }
-    } else {
-      // values to the cache, stored in blocks of 8 positions [cap/8][hd][8]: lanes take
-      // consecutive dimensions, so one store instruction covers 1 KB of a block
-      constexpr int RPT = TM * BN / 256;     // rows per thread: 256 threads cover BN columns
-      const int c = tid % BN, rb = (tid / BN) * RPT;
-      if (c < cols) {
-        const int col = n0 - vbeg + c, g = col / e.hd, d = col % e.hd;
-        T* vbase = (T*)e.kv_v + lay + (int64_t)g * e.cap * e.hd + (int64_t)d * 8;
-        for (int q = 0; q < RPT; ++q) {
-          const int rr = rb + q;
-          if (rr >= rows) break;
-          const int pos = s_pos[rr];
-          if (pos < 0) continue;
-          vbase[(int64_t)s_seq[rr] * e.kvh * e.cap * e.hd + (int64_t)(pos >> 3) * e.hd * 8 +
-                (pos & 7)] = from_f<T>(Cs[rr * CS_LD + c]);
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ bf16 MFMA pipeline
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_block, 16,
-                                   0, 0);
-}
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-// Linear workgroup id -> (m tile, n tile): workgroups are handed to the 8 XCDs round robin, so
-// give each XCD a contiguous range of tiles, m fastest, and the m tiles of one weight column
-// tile run on one XCD at about the same time.
-__device__ __forceinline__ void tile_of(int bid, int total, int tiles_m, int* tm, int* tn) {
-  const int q = total >> 3;
-  const int t = bid < (q << 3) ? (bid & 7) * q + (bid >> 3) : bid;
-  *tm = t % tiles_m;
-  *tn = t / tiles_m;
-}
 
 // SPLITA: the A operand is given as two bf16 tensors, A (high part) and A2 = bf16(a - A) (low
 // part), and every MFMA is issued for both, so that the product sees A to about 16 significant
@@ -491,24 +236,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, EpiArgs e) {
 }
 
 // ------------------------------------------------------------------ launch
-// Block tile configurations of the bf16 path: (BM, BN, pipeline stages).
-constexpr int kNumCfg = 8;
-static const int kCfgBM[kNumCfg] = {256, 256, 128, 64, 128, 64, 256, 128};
-static const int kCfgBN[kNumCfg] = {256, 128, 128, 128, 128, 128, 128, 256};
-
-// Choose the largest tile that still gives every CU work in whole rounds: a tile count of at
-// least two per CU, else the configuration with the most tiles.
-static int choose_cfg(int M, int N, int batch, int gateup, int F) {
-  static const int order[4] = {0, 1, 4, 5};
-  int best = 5, best_tiles = 0;
-  for (int c : order) {
-    const int n = gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N;
-    const int tiles = ceil_div(M, kCfgBM[c]) * ceil_div(n, kCfgBN[c]) * batch;
-    if (tiles >= 512) return c;
-    if (tiles > best_tiles) { best = c; best_tiles = tiles; }
-  }
-  return best;
-}
+// Block tile configurations of the bf16 path: (BM, BN).  0-7: the pipelined ring of 64-wide k
+// tiles (stages per configuration in launch_cfg); 8-13: the deep rings of 32-wide k stages with
+// optional split-K (k_gemm_deep.hip; 8-10 four waves, 11-13 eight waves).
+constexpr int kNumCfg = kMaxGemmCfg + 1;
+static const int kCfgBM[kNumCfg] = {256, 256, 128, 64, 128, 64, 256, 128, 256, 128, 128,
+                                    256, 256, 256};
+static const int kCfgBN[kNumCfg] = {256, 128, 128, 128, 128, 128, 128, 256, 128, 256, 128,
+                                    256, 192, 128};
+static bool is_deep(int cfg) { return cfg >= 8; }
 
 template <int BM, int BN, int ST, int KIND, bool SPLITA>
 static void launch_pipe(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
@@ -520,6 +256,10 @@ static void launch_pipe(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) 
 
 template <int KIND, bool SPLITA>
 static void launch_cfg(int cfg, const GemmArgs& a, const EpiArgs& e, int batch, hipStream_t s) {
+  if (is_deep(cfg)) {
+    launch_deep_cfg<KIND, SPLITA>(cfg, a, e, batch, s);
+    return;
+  }
   if constexpr (SPLITA) {
     // the A2 stages double the A part of the ring: only the smaller tiles fit in LDS
     if (cfg == 3 || cfg == 5) launch_pipe<64, 128, 3, KIND, true>(a, e, batch, s);
@@ -538,16 +278,93 @@ static void launch_cfg(int cfg, const GemmArgs& a, const EpiArgs& e, int batch, 
   }
 }
 
-// The bf16 configuration a launch really uses: the requested one (or the shape's choice), with
-// QKV / context K/V tiles kept at 128 columns (they must not straddle the Q/K/V segment
-// boundaries, multiples of 128) and bf16-pair launches on the tiles whose ring fits in LDS.
-static int resolve_cfg(int kind, int cfg, int M, int N, int batch, int gateup, int F,
-                       bool split) {
-  if (cfg < 0 || cfg >= kNumCfg) cfg = choose_cfg(M, N, batch, gateup, F);
-  if ((kind == EPI_QKV || kind == EPI_CTXKV) && kCfgBN[cfg] != 128)
-    cfg = kCfgBM[cfg] == 256 ? 1 : 4;
-  if (split) cfg = (cfg == 3 || cfg == 5) ? 5 : 4;
-  return cfg;
+// The configuration a bf16-pair launch of `cfg` really uses (the pair doubles the A operand's
+// LDS and registers, so only the smaller tiles take it).
+static int pair_cfg(int cfg) {
+  if (is_deep(cfg)) return 10;
+  if (cfg == 3 || cfg == 5) return 5;
+  return 4;
+}
+
+// Split-K factor for a deep-ring tile, from a time estimate: rounds of 256 workgroups times the
+// time of one unit (a CU at about 1/256 of 1.9 PFLOP/s), plus the fp32 partials each split
+// writes and the last unit reads back (at about 5 TB/s), plus that last unit's own serial read
+// of the S partials of its tile (about 50 GB/s for one workgroup).  A unit keeps at least 4
+// k stages of 32.
+static int choose_split(int cfg, int M, int Nv, int K, int batch) {
+  const double BM = kCfgBM[cfg], BN = kCfgBN[cfg];
+  const double tiles = (double)ceil_div(M, kCfgBM[cfg]) * ceil_div(Nv, kCfgBN[cfg]) * batch;
+  const double cu_flops = 1.9e15 / 256, part_bw = 5e12, wg_bw = 50e9;
+  static const int cand[6] = {1, 2, 3, 4, 6, 8};
+  int best = 1;
+  double best_t = 0;
+  for (int S : cand) {
+    if (S > 1 && K / 32 / S < 4) break;
+    double t = std::ceil(tiles * S / 256.0) * 2.0 * BM * BN * ((double)K / S) / cu_flops;
+    if (S > 1) t += tiles * S * BM * BN * 4.0 * 2.0 / part_bw + S * BM * BN * 4.0 / wg_bw;
+    if (S == 1 || t < best_t) { best = S; best_t = t; }
+  }
+  return best;
+}
+
+// Default tile for a shape.  The eight-wave 256-row tiles when one of them covers the problem in
+// rounds of 256 workgroups that are at least 85% full; else the 64 x 128 pipelined tile when it
+// gives at most 320 tiles (small N: the most workgroups at one round); else the largest
+// pipelined tile that still gives every CU work in whole rounds (at least two tiles per CU), or
+// the one with the most tiles.
+static int choose_cfg(int M, int N, int batch, int gateup, int F, bool big_ok) {
+  auto tiles_of = [&](int c) {
+    const int n = gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N;
+    return ceil_div(M, kCfgBM[c]) * ceil_div(n, kCfgBN[c]) * batch;
+  };
+  if (big_ok && M >= 128) {
+    int best = -1;
+    double best_fill = 0.85;
+    for (int c : {11, 12}) {
+      const int t = tiles_of(c);
+      const double fill = (double)t / (256.0 * ceil_div(t, 256));
+      if (t >= 192 && fill > best_fill) { best = c; best_fill = fill; }
+    }
+    if (best >= 0) return best;
+  }
+  if (tiles_of(3) <= 320) return 3;
+  static const int order[4] = {0, 1, 4, 5};
+  int best = 5, best_tiles = 0;
+  for (int c : order) {
+    const int tiles = tiles_of(c);
+    if (tiles >= 512) return c;
+    if (tiles > best_tiles) { best = c; best_tiles = tiles; }
+  }
+  return best;
+}
+
+GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
+                   int F, bool pair, bool split_ok) {
+  GemmPlan p{};
+  p.split = 1;
+  if (dtype != 1) {
+    p.cfg = -1;
+    p.bn = FN;
+    return p;
+  }
+  // QKV / context K/V tiles stay at 128 columns: they must not straddle the Q/K/V segment
+  // boundaries (multiples of 128)
+  const bool n128 = kind == EPI_QKV || kind == EPI_CTXKV;
+  const bool chosen = cfg >= 0 && cfg < kNumCfg;
+  if (!chosen) cfg = choose_cfg(M, N, batch, gateup, F, !n128 && !pair);
+  if (n128 && kCfgBN[cfg] != 128)
+    cfg = cfg >= 11 ? 13 : is_deep(cfg) ? (kCfgBM[cfg] == 256 ? 8 : 10)
+                                        : (kCfgBM[cfg] == 256 ? 1 : 4);
+  if (pair) cfg = pair_cfg(cfg);
+  auto nvirt = [&](int c) { return gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N; };
+  p.cfg = cfg;
+  p.bn = kCfgBN[cfg];
+  // the library's own choice of an eight-wave tile already fills the chip: no split
+  if (is_deep(cfg) && split_ok && (chosen || cfg < 11))
+    p.split = choose_split(cfg, M, nvirt(cfg), K, batch);
+  p.tiles = ceil_div(M, kCfgBM[cfg]) * ceil_div(nvirt(cfg), kCfgBN[cfg]) * batch;
+  p.part_bytes = p.split > 1 ? (size_t)p.tiles * p.split * kCfgBM[cfg] * kCfgBN[cfg] * 4 : 0;
+  return p;
 }
 
 template <int KIND>
@@ -555,19 +372,17 @@ static void launch_kind(int dtype, int cfg, GemmArgs a, const EpiArgs& e, int ba
                         hipStream_t s) {
   if (dtype == 1) {
     const int F = a.seg[0].n1 - a.seg[0].n0;
-    cfg = resolve_cfg(KIND, cfg, a.M, a.N, batch, a.gateup, F, a.A2 != nullptr);
-    if (a.A2) launch_cfg<KIND, true>(cfg, a, e, batch, s);
-    else launch_cfg<KIND, false>(cfg, a, e, batch, s);
+    GemmPlan p = plan_gemm(dtype, KIND, cfg, a.M, a.N, a.K, batch, a.gateup, F,
+                           a.A2 != nullptr, a.part != nullptr && a.cnt != nullptr);
+    if (p.split > 1 && (p.part_bytes > a.part_cap || p.tiles > a.cnt_cap)) p.split = 1;
+    a.split = p.split;
+    if (a.A2) launch_cfg<KIND, true>(p.cfg, a, e, batch, s);
+    else launch_cfg<KIND, false>(p.cfg, a, e, batch, s);
   } else {
     if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, FN / 2) * FN;
     dim3 grid(ceil_div(a.N, FN), ceil_div(a.M, FM), batch);
     hipLaunchKernelGGL(gemm_f32_kernel<KIND>, grid, dim3(256), 0, s, a, e);
   }
-}
-
-int gemm_ntiles(int dtype, int kind, int cfg, int M, int N, int batch, bool split) {
-  if (dtype != 1) return ceil_div(N, FN);
-  return ceil_div(N, kCfgBN[resolve_cfg(kind, cfg, M, N, batch, 0, 0, split)]);
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,

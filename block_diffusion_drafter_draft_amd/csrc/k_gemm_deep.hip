@@ -1,0 +1,496 @@
+// Deep-ring bf16 GEMM (gfx950): block tile BM x BN, k stages of 32 bf16, an NS-deep LDS ring
+// filled by global->LDS DMA, 4 waves in a 2 x 2 grid, 16x16x32 bf16 MFMAs with fp32
+// accumulation, optional split-K over several workgroups.  This translation unit is compiled
+// with the MFMA accumulators in ordinary VGPRs (-mllvm -amdgpu-mfma-vgpr-form): the tiles here
+// fit in the 256 architectural VGPRs, and the accumulator form keeps the software-pipelined
+// loop free of accumulator copies.
+#include "gemm_common.h"
+
+namespace dbd {
+
+template <int BM_, int BN, int NS, int KIND, bool SPLITA>
+__global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a, EpiArgs e) {
+  using C = BigCfg<BM_, BN, NS, SPLITA>;
+  constexpr int BM = C::BM;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int z = blockIdx.z;
+  const int M = a.M, N = a.N, K = a.K;
+  const int S = a.split > 1 ? a.split : 1;
+  const int tiles_m = (M + BM - 1) / BM;
+  int tm, tn, sp;
+  unit_of(blockIdx.x, gridDim.x, tiles_m, S, &tm, &tn, &sp);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk_all = K / C::KS;
+  const int kb = (int)((int64_t)nk_all * sp / S), nk = (int)((int64_t)nk_all * (sp + 1) / S) - kb;
+
+  // Per-lane source of each 1 KB load: load j of a tile covers rows 16j .. 16j+15; lane l fills
+  // LDS slot (row 16j + l/4, chunk l%4) from global chunk (l%4) ^ swz32(row).
+  const int rr = lane >> 2, slot = lane & 3;
+  const BMap bm = make_bmap(a);
+  const bf16* asrc[C::LA];
+  const bf16* a2src[C::LA];
+  const bf16* bsrc[C::LB];
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) {
+    const int row = (wave + 4 * i) * 16 + rr;
+    const int64_t off = (int64_t)z * a.a_bs + (int64_t)min(m0 + row, M - 1) * a.lda +
+                        kb * C::KS + (slot ^ swz32(row)) * 8;
+    asrc[i] = (const bf16*)a.A + off;
+    a2src[i] = SPLITA ? (const bf16*)a.A2 + off : asrc[i];
+  }
+#pragma unroll
+  for (int j = 0; j < C::LB; ++j) {
+    const int row = (wave + 4 * j) * 16 + rr;
+    bsrc[j] = brow_ptr<bf16, BN>(bm, min(n0 + row, N - 1), z) + kb * C::KS +
+              (slot ^ swz32(row)) * 8;
+  }
+
+  // Fragment reads.  Lane l reads row (l%16) of each 16-row group at chunk l/16.  The reads are
+  // issued as inline ds_read_b128: a compiled LDS load after a global->LDS DMA makes the compiler
+  // wait for every DMA in flight (it cannot tell the ring slots apart), which would drain the
+  // ring each stage.  The kernel waits for the reads itself (lgkmcnt) and ties the fragment
+  // registers to that wait, so no MFMA can be scheduled before it.
+  const int fr = lane & 15, fk = lane >> 4;
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem +
+      (uint32_t)((fr * C::KS + ((fk ^ swz32(fr)) * 8)) * 2);
+  const uint32_t a_off = (uint32_t)(wm * C::WTM * C::KS * 2);
+  const uint32_t b_off = (uint32_t)((C::NA * BM * C::KS + wn * C::WTN * C::KS) * 2);
+  struct Frag {
+    bf16x8 a[C::MI], a2[SPLITA ? C::MI : 1], b[C::NI];
+  };
+  constexpr int NRD = C::MI * (SPLITA ? 2 : 1) + C::NI;     // reads per stage
+  // read r of the stage at LDS byte address `base`: A fragments, then A2, then B
+  auto read_one = [&](Frag& f, uint32_t base, int r) __attribute__((always_inline)) {
+    if (r < C::MI) {
+      ds_read16(f.a[r], base + a_off + (uint32_t)(r * 16 * C::KS * 2));
+    } else if (r < C::NA * C::MI) {
+      if constexpr (SPLITA)
+        ds_read16(f.a2[r - C::MI], base + a_off + (uint32_t)((BM + (r - C::MI) * 16) * C::KS * 2));
+    } else {
+      const int j = r - C::NA * C::MI;
+      ds_read16(f.b[j], base + b_off + (uint32_t)(j * 16 * C::KS * 2));
+    }
+  };
+  auto read_frags = [&](Frag& f, int st) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + (uint32_t)(st * C::STAGE);
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read_one(f, base, r);
+  };
+  // wait for every issued fragment read, then make the fragments depend on that wait
+  auto frags_ready = [&](Frag& f) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) asm volatile("" : "+v"(f.a[i]));
+    if constexpr (SPLITA) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) asm volatile("" : "+v"(f.a2[i]));
+    }
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) asm volatile("" : "+v"(f.b[j]));
+  };
+
+  f32x4 acc[C::MI][C::NI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int NMF = C::MI * C::NI * (SPLITA ? 2 : 1);      // MFMAs per stage
+  auto mfma_one = [&](const Frag& f, int q) __attribute__((always_inline)) {
+    const int h = SPLITA ? q & 1 : 0, ij = SPLITA ? q >> 1 : q;
+    const int i = ij / C::NI, j = ij % C::NI;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h ? f.a2[i] : f.a[i], f.b[j], acc[i][j],
+                                                        0, 0, 0);
+  };
+  // DMA load q of a stage (A, then A2, then B), into ring slot st from k stage kt
+  auto issue_one = [&](int st, int kt, int q) __attribute__((always_inline)) {
+    char* base = smem + st * C::STAGE;
+    const int k0 = kt * C::KS;
+    if (q < C::LA) {
+      lds_dma16(asrc[q] + k0, base + (wave + 4 * q) * 1024);
+    } else if (SPLITA && q < 2 * C::LA) {
+      const int i = q - C::LA;
+      lds_dma16(a2src[i] + k0, base + C::ABYTES + (wave + 4 * i) * 1024);
+    } else {
+      const int j = q - C::NA * C::LA;
+      lds_dma16(bsrc[j] + k0, base + C::NA * C::ABYTES + (wave + 4 * j) * 1024);
+    }
+  };
+  // One k stage.  Stage kt's fragments are in `cur`; after the vmcnt wait stage kt+1 has landed
+  // for this wave, and after the barrier for every wave, and stage kt's slot is free (every wave
+  // holds its fragments), so it is refilled with stage kt+NS.  The refill loads and the fragment
+  // reads of stage kt+1 are spread over the MFMAs of stage kt in a fixed order.
+  auto steady = [&](int kt, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+    wait_vmcnt<C::LPW * (NS - 2)>();
+    frags_ready(cur);
+    block_barrier();
+    const int sl = kt % NS;
+    const uint32_t base = lds0 + (uint32_t)(((kt + 1) % NS) * C::STAGE);
+    // MFMA q is followed by DMA load q (q < LPW), then by one fragment read after every other
+    // MFMA; reads that do not fit go after the last MFMA
+    constexpr int RSTEP = NMF - C::LPW >= 2 * NRD ? 2 : 1;
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      mfma_one(cur, q);
+      if (q < C::LPW) issue_one(sl, kt + NS, q);
+      if (q >= C::LPW && (q - C::LPW) % RSTEP == 0 && (q - C::LPW) / RSTEP < NRD)
+        read_one(nxt, base, (q - C::LPW) / RSTEP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = (NMF - C::LPW + RSTEP - 1) / RSTEP; r < NRD; ++r) read_one(nxt, base, r);
+  };
+  // the last stages: at most one left to issue
+  auto tail = [&](int kt, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+    wait_stages<C::LPW, NS>(min(NS - 2, nk - kt - 2));
+    frags_ready(cur);
+    block_barrier();
+    if (kt + NS < nk) {
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) issue_one(kt % NS, kt + NS, q);
+    }
+    if (kt + 1 < nk) read_frags(nxt, (kt + 1) % NS);
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) mfma_one(cur, q);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    if (st < nk) {
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) issue_one(st, st, q);
+    }
+  Frag f0, f1;
+  if (nk > 0) {
+    wait_stages<C::LPW, NS>(min(NS - 1, nk - 1));
+    block_barrier();
+    read_frags(f0, 0);
+  }
+  int kt = 0;
+  for (; kt + 1 + NS < nk; kt += 2) {
+    steady(kt, f0, f1);
+    steady(kt + 1, f1, f0);
+  }
+  // at most NS + 1 stages remain, taken in pairs so the fragment sets keep alternating
+  for (; kt < nk; kt += 2) {
+    tail(kt, f0, f1);
+    if (kt + 1 < nk) tail(kt + 1, f1, f0);
+  }
+  // no inline LDS read may still be in flight when the registers are reused below
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  // split-K: publish this unit's partial; the last unit of the tile to arrive adds all partials
+  // in split order (so the sum does not depend on arrival order) and runs the epilogue
+  if (S > 1) {
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tile = (z * tiles_n + tn) * tiles_m + tm;
+    constexpr int FR = C::MI * C::NI * 64;                      // f32x4 per wave
+    f32x4* part = reinterpret_cast<f32x4*>(a.part) + ((int64_t)tile * S * 4) * FR;
+    f32x4* mine = part + ((int64_t)sp * 4 + wave) * FR + lane;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j) mine[(i * C::NI + j) * 64] = acc[i][j];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const int old = atomicAdd(a.cnt + tile, 1);
+      s_last = old == S - 1;
+      if (old == S - 1) a.cnt[tile] = 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    // every partial, this unit's own included, is read back, so the sum is formed in split
+    // order whichever unit arrives last
+    const f32x4* base = part + (int64_t)wave * FR + lane;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j) {
+        const f32x4* p = base + (i * C::NI + j) * 64;
+        f32x4 t = p[0];
+        for (int q = 1; q < S; ++q) t += p[(int64_t)q * 4 * FR];
+        acc[i][j] = t;
+      }
+  }
+
+  // Output in rounds of 64 rows per wave row: round h stages accumulator rows [64h, 64h+64) of
+  // both wave rows (tile rows wm*BM/2 + 64h + ...) in LDS as 128 fp32 rows, then runs the
+  // epilogue over the two 64-row groups.  The accumulators a round uses are fixed at compile time.
+  block_barrier();       // every wave is done reading the ring: reuse it for the output tile
+  float* Cs = (float*)smem;
+  constexpr int CS_LD = BN + 4;
+#pragma unroll
+  for (int h = 0; h < C::MI / 4; ++h) {
+#pragma unroll
+    for (int i = 4 * h; i < 4 * h + 4; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * 64 + (i - 4 * h) * 16 + (lane >> 4) * 4 + r;
+          const int col = wn * C::WTN + j * 16 + (lane & 15);
+          Cs[row * CS_LD + col] = acc[i][j][r];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      run_epilogue<bf16, 64, BN, KIND>(e, Cs + g * 64 * CS_LD, m0 + g * C::WTM + 64 * h, n0, tn,
+                                       z, M, N);
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 8-wave ring
+// Block tile 256 x BN, k stages of KS (32 or 64) bf16, NS-slot LDS ring filled by global->LDS
+// DMA, 8 waves (two per SIMD) in a 2 x 4 grid: each wave owns a 128 x BN/4 sub-tile (8 x BN/64
+// MFMA tiles) and one fragment set.  Per stage a wave waits for its own DMA of the stage, the
+// workgroup synchronises once, the slot read in the previous stage is refilled, and the wave
+// reads its fragments and runs its MFMAs one 32-wide k step at a time; the second wave on the
+// SIMD runs MFMAs while the first waits for LDS.  With KS = 64 every DMA lane group reads whole
+// 128-byte lines (8 rows x 128 bytes per 1 KB load), half the L2 requests of 64-byte rows.
+// Stage rows are KS * 2 bytes; 16-byte chunk c of row r sits in slot c ^ swz(r) (swz32 for 64-byte
+// rows, swz for 128-byte rows; both measured conflict-free for the fragment reads).
+template <int BN, int NS, int KS_>
+struct W8Cfg {
+  static constexpr int BM = 256, KS = KS_, NT = 512, NW = 8;
+  static constexpr int ROWB = KS * 2, CPR = KS / 8;       // bytes and 16-byte chunks per row
+  static constexpr int RPL = 1024 / ROWB;                 // rows per 1 KB load
+  static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB;
+  static constexpr int STAGE = ABYTES + BBYTES;
+  static constexpr int NLA = ABYTES / 1024, NL = (ABYTES + BBYTES) / 1024;   // 1 KB loads / stage
+  static constexpr int LPW = (NL + NW - 1) / NW;          // loads of waves 0 .. NL%NW-1 (or all)
+  static constexpr int LPW_LO = NL % NW ? LPW - 1 : LPW;  // loads of the other waves
+  static constexpr int WTM = 128, WTN = BN / 4, MI = 8, NI = WTN / 16;
+  static constexpr int TM = BN == 192 ? 128 : 64;         // epilogue rows per round
+  static constexpr int CBYTES = TM * (BN + 4) * 4;
+  static constexpr int SMEM = NS * STAGE > CBYTES ? NS * STAGE : CBYTES;
+  static_assert(KS == 32 || KS == 64, "stage depth");
+  static_assert(BBYTES % 1024 == 0 && WTN % 16 == 0, "tile shape");
+  static_assert(LPW * (NS - 1) <= 63, "vmcnt range");
+  __device__ static int swizzle(int row) { return KS == 32 ? swz32(row) : swz(row); }
+};
+
+template <int BN, int NS, int KS, int KIND>
+__global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs a, EpiArgs e) {
+  using C = W8Cfg<BN, NS, KS>;
+  constexpr int BM = C::BM;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int z = blockIdx.z;
+  const int M = a.M, N = a.N, K = a.K;
+  const int S = a.split > 1 ? a.split : 1;
+  const int tiles_m = (M + BM - 1) / BM;
+  int tm, tn, sp;
+  unit_of(blockIdx.x, gridDim.x, tiles_m, S, &tm, &tn, &sp);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk_all = K / KS;
+  const int kb = (int)((int64_t)nk_all * sp / S), nk = (int)((int64_t)nk_all * (sp + 1) / S) - kb;
+
+  // DMA load l of a stage (l < NL) fills LDS [l KB, l+1 KB) of the stage: tile rows RPL l' ..
+  // RPL l' + RPL-1 of A (l' = l < NLA) or of B (l' = l - NLA); lane i fills row RPL l' + i/CPR,
+  // slot i%CPR from global chunk (i%CPR) ^ swizzle(row).  Wave w issues loads w, w+8, w+16, ...
+  const bool full = wave < (C::NL % C::NW ? C::NL % C::NW : C::NW);
+  const int rr = lane / C::CPR, slot = lane % C::CPR;
+  const BMap bm = make_bmap(a);
+  const bf16* src[C::LPW];
+#pragma unroll
+  for (int q = 0; q < C::LPW; ++q) {
+    int l = wave + C::NW * q;
+    if (l >= C::NL) l = C::NL - 1;            // not issued (see issue); any valid address
+    const bool isA = l < C::NLA;
+    const int row = (isA ? l : l - C::NLA) * C::RPL + rr;
+    const int chunk = (slot ^ C::swizzle(row)) * 8;
+    src[q] = isA ? (const bf16*)a.A + (int64_t)z * a.a_bs + (int64_t)min(m0 + row, M - 1) * a.lda +
+                       (int64_t)kb * KS + chunk
+                 : brow_ptr<bf16, BN>(bm, min(n0 + row, N - 1), z) + (int64_t)kb * KS + chunk;
+  }
+  auto issue = [&](int st, int kt) __attribute__((always_inline)) {
+    char* base = smem + st * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::LPW; ++q)
+      if (q < C::LPW_LO || full) lds_dma16(src[q] + kt * KS, base + (wave + C::NW * q) * 1024);
+  };
+  // wait until at most n stages of this wave's loads are in flight (n in [0, NS - 2])
+  auto wait_own = [&](int n) __attribute__((always_inline)) {
+    if (full) wait_stages<C::LPW, NS>(n);
+    else wait_stages<C::LPW_LO, NS>(n);
+  };
+
+  // fragment reads (inline ds_read_b128, see gemm_big_kernel): for k step s of a stage, lane l
+  // reads row l%16 of each 16-row group at chunk 4s + l/16
+  const int fr = lane & 15, fk = lane >> 4;
+  const uint32_t smem0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  uint32_t lds_k[KS / 32];
+#pragma unroll
+  for (int s2 = 0; s2 < KS / 32; ++s2)
+    lds_k[s2] = smem0 + (uint32_t)(fr * C::ROWB + (((4 * s2 + fk) ^ C::swizzle(fr)) * 16));
+  const uint32_t a_off = (uint32_t)(wm * C::WTM * C::ROWB);
+  const uint32_t b_off = (uint32_t)(C::ABYTES + wn * C::WTN * C::ROWB);
+  bf16x8 fa[C::MI], fb[C::NI];
+
+  f32x4 acc[C::MI][C::NI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_own(min(NS - 2, nk - 1 - kt));
+    block_barrier();
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+    const uint32_t stage = (uint32_t)((kt % NS) * C::STAGE);
+#pragma unroll
+    for (int s2 = 0; s2 < KS / 32; ++s2) {
+      const uint32_t base = lds_k[s2] + stage;
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+        ds_read16(fa[i], base + a_off + (uint32_t)(i * 16 * C::ROWB));
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+        ds_read16(fb[j], base + b_off + (uint32_t)(j * 16 * C::ROWB));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) asm volatile("" : "+v"(fa[i]));
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j) asm volatile("" : "+v"(fb[j]));
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Output: stage C::TM accumulator rows at a time in LDS as fp32, then the epilogue over them.
+  // Round h holds tile rows [TM h, TM h + TM); the waves whose rows fall there write them.
+  // `get(i, j)` yields accumulator tile (i, j) of this wave.
+  auto store_tile = [&](auto get) __attribute__((always_inline)) {
+    block_barrier();   // every wave is done reading the ring: reuse it for the output tile
+    float* Cs = (float*)smem;
+    constexpr int CS_LD = BN + 4;
+#pragma unroll
+    for (int h = 0; h < BM / C::TM; ++h) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int row0 = wm * C::WTM + i * 16;            // first tile row of acc tile (i, *)
+        if (row0 / C::TM != h) continue;
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) {
+          const f32x4 v = get(i, j);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = row0 - h * C::TM + (lane >> 4) * 4 + r;
+            const int col = wn * C::WTN + j * 16 + (lane & 15);
+            Cs[row * CS_LD + col] = v[r];
+          }
+        }
+      }
+      __syncthreads();
+      run_epilogue<bf16, C::TM, BN, KIND, C::NT>(e, Cs, m0 + h * C::TM, n0, tn, z, M, N);
+      __syncthreads();
+    }
+  };
+
+  if (S > 1) {
+    // split-K: publish this unit's partial; the last unit of the tile to arrive adds all
+    // partials in split order (the sum does not depend on arrival order) and writes the tile
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tile = (z * tiles_n + tn) * tiles_m + tm;
+    constexpr int FR = C::MI * C::NI * 64;                       // f32x4 per wave
+    f32x4* part = reinterpret_cast<f32x4*>(a.part) + (int64_t)tile * S * C::NW * FR;
+    f32x4* mine = part + ((int64_t)sp * C::NW + wave) * FR + lane;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j) mine[(i * C::NI + j) * 64] = acc[i][j];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const int old = atomicAdd(a.cnt + tile, 1);
+      s_last = old == S - 1;
+      if (old == S - 1) a.cnt[tile] = 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const f32x4* mybase = part + (int64_t)wave * FR + lane;
+    store_tile([&](int i, int j) {
+      const f32x4* p = mybase + (i * C::NI + j) * 64;
+      f32x4 t = p[0];
+      for (int q = 1; q < S; ++q) t += p[(int64_t)q * C::NW * FR];
+      return t;
+    });
+    return;
+  }
+  store_tile([&](int i, int j) { return acc[i][j]; });
+}
+
+template <int BN, int NS, int KS, int KIND>
+static void launch_w8(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
+  if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, BN / 2) * BN;
+  const int S = a.split > 1 ? a.split : 1;
+  const int units = ceil_div(a.M, 256) * ceil_div(a.N, BN) * S;
+  hipLaunchKernelGGL((gemm_w8_kernel<BN, NS, KS, KIND>), dim3(units, 1, batch), dim3(512), 0, s,
+                     a, e);
+}
+
+template <int BM, int BN, int NS, int KIND, bool SPLITA>
+static void launch_deep(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
+  if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, BN / 2) * BN;
+  const int S = a.split > 1 ? a.split : 1;
+  const int units = ceil_div(a.M, BM) * ceil_div(a.N, BN) * S;
+  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, NS, KIND, SPLITA>), dim3(units, 1, batch),
+                     dim3(256), 0, s, a, e);
+}
+
+// 8: 256 x 128 (3 stages), 9: 128 x 256 (3), 10: 128 x 128 (4): four waves, 32-wide k stages;
+// 11: 256 x 256 (2), 12: 256 x 192 (2), 13: 256 x 128 (3): eight waves, 64-wide k stages.  The bf16-pair A operand doubles the A part
+// of a stage and the A fragments: pairs always take the four-wave 128 x 128 tile with 6 stages.
+// The value-cache epilogues (QKV, context K/V) need 128-column tiles.
+template <int KIND, bool SPLITA>
+void launch_deep_cfg(int cfg, GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
+  if constexpr (SPLITA) {
+    launch_deep<128, 128, 6, KIND, true>(a, e, batch, s);
+  } else if constexpr (KIND == EPI_QKV || KIND == EPI_CTXKV) {
+    switch (cfg) {
+      case 8: launch_deep<256, 128, 3, KIND, false>(a, e, batch, s); break;
+      case 11: case 12: case 13: launch_w8<128, 3, 64, KIND>(a, e, batch, s); break;
+      default: launch_deep<128, 128, 4, KIND, false>(a, e, batch, s); break;
+    }
+  } else {
+    switch (cfg) {
+      case 8: launch_deep<256, 128, 3, KIND, false>(a, e, batch, s); break;
+      case 9: launch_deep<128, 256, 3, KIND, false>(a, e, batch, s); break;
+      case 11: launch_w8<256, 2, 64, KIND>(a, e, batch, s); break;
+      case 12: launch_w8<192, 2, 64, KIND>(a, e, batch, s); break;
+      case 13: launch_w8<128, 3, 64, KIND>(a, e, batch, s); break;
+      default: launch_deep<128, 128, 4, KIND, false>(a, e, batch, s); break;
+    }
+  }
+}
+
+#define DBD_DEEP(K)                                                                         \
+  template void launch_deep_cfg<K, false>(int, GemmArgs, const EpiArgs&, int, hipStream_t); \
+  template void launch_deep_cfg<K, true>(int, GemmArgs, const EpiArgs&, int, hipStream_t);
+DBD_DEEP(EPI_STORE_F32)
+DBD_DEEP(EPI_RESID)
+DBD_DEEP(EPI_QKV)
+DBD_DEEP(EPI_CTXKV)
+DBD_DEEP(EPI_SWIGLU)
+DBD_DEEP(EPI_ARGMAX)
+#undef DBD_DEEP
+
+}  // namespace dbd

@@ -110,6 +110,8 @@ struct DraftBufs {
   int s_max;
   int split;
   int ntiles;
+  float* gemm_part;
+  size_t gemm_part_bytes;
 };
 
 size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, int K,
@@ -148,8 +150,35 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.s_max = ceil_div(cap, t.split);
   t.part_o = c.take<float>((int64_t)N * d.n_kv_heads * t.s_max * R * d.head_dim);
   t.part_ml = c.take<float2>((int64_t)N * d.n_kv_heads * t.s_max * R);
-  t.ntiles = gemm_ntiles(d.dtype, EPI_ARGMAX, -1, (int)Md, d.vocab, 1,
-                         d.dtype == DBD_BF16 && d.act_pairs);
+  // split-K partials and tile counters: the largest need over the step's GEMMs
+  {
+    const bool pr = d.dtype == DBD_BF16 && d.act_pairs;
+    const int kd = d.n_kv_heads * d.head_dim;
+    GemmPlan pl[6];
+    int np = 0;
+    pl[np++] = plan_gemm(d.dtype, EPI_QKV, -1, (int)M, qd + 2 * kd, d.hidden, 1, 0, 0, pr, true);
+    pl[np++] = plan_gemm(d.dtype, EPI_RESID, -1, (int)M, d.hidden, qd, 1, 0, 0, pr, true);
+    pl[np++] = plan_gemm(d.dtype, EPI_SWIGLU, -1, (int)M, 2 * d.ffn, d.hidden, 1, 1, d.ffn, pr,
+                         true);
+    pl[np++] = plan_gemm(d.dtype, EPI_RESID, -1, (int)M, d.hidden, d.ffn, 1, 0, 0, pr, true);
+    pl[np++] = plan_gemm(d.dtype, temperature > 0.f ? EPI_STORE_F32 : EPI_ARGMAX, -1, (int)Md,
+                         d.vocab, d.hidden, 1, 0, 0, pr, true);
+    if (d.n_target_layers > 0 && T > 0)
+      pl[np++] = plan_gemm(d.dtype, EPI_CTXKV, -1, T, 2 * kd, d.hidden, d.n_layers, 0, 0,
+                           d.dtype == DBD_BF16, true);
+    size_t part = 0;
+    int cnt = 0;
+    for (int i = 0; i < np; ++i)
+      if (pl[i].split > 1) {
+        part = part > pl[i].part_bytes ? part : pl[i].part_bytes;
+        cnt = cnt > pl[i].tiles ? cnt : pl[i].tiles;
+      }
+    t.gemm_part = part ? (float*)c.take<char>((int64_t)part) : nullptr;
+    t.gemm_part_bytes = part;
+    t.meta.gemm_cnt = cnt ? c.take<int32_t>(cnt) : nullptr;
+    t.meta.n_gemm_cnt = cnt;
+    t.ntiles = ceil_div(d.vocab, pl[4].bn);
+  }
   const int64_t max_tiles = ceil_div(d.vocab, 128);          // any configuration fits
   t.lm_pv = c.take<float>(Md * max_tiles);
   t.lm_pi = c.take<int32_t>(Md * max_tiles);
@@ -348,6 +377,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
                                                     w->mix_logits, w->mix_norm_w, b.ctxfeat,
                                                     ctx_lo, d.rms_eps, st));
     GemmArgs g{};
+    g.part = b.gemm_part;
+    g.cnt = b.meta.gemm_cnt;
+    g.part_cap = b.gemm_part_bytes;
+    g.cnt_cap = b.meta.n_gemm_cnt;
     g.A = b.ctxfeat;
     g.A2 = ctx_lo;
     g.lda = H;
@@ -389,6 +422,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
                                                      d.rms_eps, B, 0, st));
     {
       GemmArgs g{};
+      g.part = b.gemm_part;
+      g.cnt = b.meta.gemm_cnt;
+      g.part_cap = b.gemm_part_bytes;
+      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.xn;
       g.A2 = b.xn_lo;
       g.lda = H;
@@ -440,6 +477,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     }
     {
       GemmArgs g{};
+      g.part = b.gemm_part;
+      g.cnt = b.meta.gemm_cnt;
+      g.part_cap = b.gemm_part_bytes;
+      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.attn;
       g.A2 = b.attn_lo;
       g.lda = qd;
@@ -459,6 +500,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
                                                      d.rms_eps, B, 0, st));
     {
       GemmArgs g{};
+      g.part = b.gemm_part;
+      g.cnt = b.meta.gemm_cnt;
+      g.part_cap = b.gemm_part_bytes;
+      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.xn;
       g.A2 = b.xn_lo;
       g.lda = H;
@@ -479,6 +524,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     }
     {
       GemmArgs g{};
+      g.part = b.gemm_part;
+      g.cnt = b.meta.gemm_cnt;
+      g.part_cap = b.gemm_part_bytes;
+      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.act;
       g.A2 = b.act_lo;
       g.lda = F;
@@ -504,6 +553,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   float* logits = logits_out ? logits_out : (sampling ? b.logits : nullptr);
   {
     GemmArgs g{};
+    g.part = b.gemm_part;
+    g.cnt = b.meta.gemm_cnt;
+    g.part_cap = b.gemm_part_bytes;
+    g.cnt_cap = b.meta.n_gemm_cnt;
     g.A = b.xn;
     g.A2 = b.xn_lo;
     g.lda = H;
@@ -729,9 +782,32 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
   return DBD_OK;
 }
 
+static size_t gemm_ws_layout(int dtype, int M, int N, int K, int cfg, size_t* part_off,
+                             int* ncnt) {
+  const GemmPlan p = plan_gemm(dtype, EPI_STORE_F32, cfg, M, N, K, 1, 0, 0, false, true);
+  if (p.split <= 1) { *ncnt = 0; *part_off = 0; return 0; }
+  *ncnt = p.tiles;
+  *part_off = ((size_t)p.tiles * 4 + kAlign - 1) / kAlign * kAlign;
+  return *part_off + p.part_bytes;
+}
+
+int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t tile_cfg,
+                             size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (dtype != DBD_F32 && dtype != DBD_BF16) return fail(DBD_ERR_ARG, "bad dtype");
+  if (M < 0 || N < 0 || K < 1) return fail(DBD_ERR_SHAPE, "bad GEMM dimensions");
+  if (tile_cfg < -1 || tile_cfg > kMaxGemmCfg)
+    return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, %d]", tile_cfg, kMaxGemmCfg);
+  size_t off;
+  int ncnt;
+  *bytes = M > 0 && N > 0 ? gemm_ws_layout(dtype, M, N, K, tile_cfg, &off, &ncnt) : 0;
+  return DBD_OK;
+}
+
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t M, int32_t N,
                 int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,
-                void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (dtype != DBD_F32 && dtype != DBD_BF16) return fail(DBD_ERR_ARG, "bad dtype");
   if (!A || !Bm || !C) return fail(DBD_ERR_ARG, "a required device pointer is NULL");
@@ -739,6 +815,8 @@ int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t 
     return fail(DBD_ERR_SHAPE, "bad GEMM dimensions");
   if (dtype == DBD_BF16 && (K % 64 || lda % 8 || ldb % 8 || !aligned16(A) || !aligned16(Bm)))
     return fail(DBD_ERR_SHAPE, "bf16 GEMM needs K % 64 == 0, 16-byte aligned rows");
+  if (tile_cfg < -1 || tile_cfg > kMaxGemmCfg)
+    return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, %d]", tile_cfg, kMaxGemmCfg);
   GemmArgs g{};
   g.A = A;
   g.lda = lda;
@@ -752,8 +830,25 @@ int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t 
   e.kind = EPI_STORE_F32;
   e.C = C;
   e.ldc = ldc;
-  if (tile_cfg < -1 || tile_cfg > 7) return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, 7]", tile_cfg);
-  HIP_TRY(launch_gemm(dtype, g, e, 1, (hipStream_t)stream, tile_cfg));
+  hipStream_t st = (hipStream_t)stream;
+  if (workspace && M > 0 && N > 0) {
+    size_t off;
+    int ncnt;
+    const size_t need = gemm_ws_layout(dtype, M, N, K, tile_cfg, &off, &ncnt);
+    if ((uintptr_t)workspace % kAlign)
+      return fail(DBD_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                  need);
+    if (ncnt > 0) {
+      g.cnt = (int*)workspace;
+      g.part = (float*)((char*)workspace + off);
+      g.cnt_cap = ncnt;
+      g.part_cap = need - off;
+      HIP_TRY(launch_fill_i32(g.cnt, ncnt, 0, st));
+    }
+  }
+  HIP_TRY(launch_gemm(dtype, g, e, 1, st, tile_cfg));
   return DBD_OK;
 }
 

@@ -227,14 +227,23 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
                     const void* hidden, int64_t hid_token_stride, int64_t hid_layer_stride,
                     int32_t n_tokens, void* out, void* stream);
 
+/* Workspace size (host) for dbd_gemm_nt with the same dtype, shape and tile_cfg: the split-K
+ * partials and tile counters of the configuration (0 when it does not split K). */
+int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t tile_cfg,
+                             size_t* bytes);
+
 /* The GEMM used for every projection: C[M, N] (fp32) = A[M, K] . B[N, K]^T with A, B in
  * `dtype`; row strides lda, ldb, ldc in elements.  bf16 needs K % 64 == 0 and 16-byte aligned
- * rows.  tile_cfg selects the bf16 block tile and pipeline depth (BM x BN / stages: 0: 256x256/2,
- * 1: 256x128/3, 2: 128x128/3, 3: 64x128/4, 4: 128x128/2, 5: 64x128/3, 6: 256x128/2,
- * 7: 128x256/2; -1: the library's choice for the shape). */
+ * rows.  tile_cfg selects the bf16 block tile (BM x BN): 0-7 a ring of 64-wide k tiles
+ * (0: 256x256/2 stages, 1: 256x128/3, 2: 128x128/3, 3: 64x128/4, 4: 128x128/2, 5: 64x128/3,
+ * 6: 256x128/2, 7: 128x256/2); 8-13 a deep ring of 32-wide k stages (4 waves: 8: 256x128/3,
+ * 9: 128x256/3, 10: 128x128/4; 8 waves: 11: 256x256/4, 12: 256x192/5, 13: 256x128/6) which
+ * splits K over several workgroups when `workspace` is given (NULL: no split); -1: the
+ * library's choice.  The
+ * workspace (dbd_gemm_workspace_bytes, 256-byte aligned) is used only by this call. */
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* B, float* C, int32_t M, int32_t N,
                 int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,
-                void* stream);
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-stage timing for benchmarks.  While enabled, every kernel launch of the library is
  * bracketed by a pair of hipEvents recorded on the launch's stream and accounted to its stage

@@ -187,7 +187,26 @@ def test_sample_validation():
 def test_gemm_validation():
     L = dbd.lib()
     fake = 1 << 20
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, None) == -2   # K % 64
-    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, None) == -2      # lda < K
-    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, None) == -1
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 8, None) == -1    # tile_cfg
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, None, 0, None) == -2
+    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, None, 0, None) == -2  # lda<K
+    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, None, 0, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 14, None, 0, None) == -1
+    # a split-K shape with a workspace that is too small, or misaligned
+    need = dbd.gemm_workspace_bytes(dbd.DBD_BF16, 512, 4096, 4096, 8)
+    assert need > 0
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 512, 4096, 4096, 4096, 4096, 4096, 8, fake,
+                         need - 1, None) == -4
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 512, 4096, 4096, 4096, 4096, 4096, 8, fake + 16,
+                         need, None) == -4
+    assert dbd.gemm_workspace_bytes(dbd.DBD_F32, 512, 4096, 4096) == 0
+
+
+def test_gemm_split_plan_fits_workspace():
+    """Split-K partials are sized by the same plan the launch uses: for every deep tile the
+    workspace holds one fp32 tile per (output tile, split) and one counter per tile."""
+    for M, N, K in [(512, 4096, 4096), (512, 4096, 12288), (128, 2048, 4096), (16, 6144, 4096)]:
+        for cfg in range(8, 14):
+            b = dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, cfg)
+            assert b % 4 == 0
+            if b:
+                assert b >= 128 * 128 * 4 * 2

@@ -1,0 +1,162 @@
+"""Static check of the inline-assembly LDS reads in the deep-ring GEMM kernels.
+
+The kernels issue ds_read_b128 as inline assembly (so that the compiler does not drain the
+global->LDS DMA ring before every LDS read) and wait for them themselves with
+s_waitcnt lgkmcnt(0).  The compiler does not know that such a read writes its destination
+registers later, so any instruction that reads or writes those registers before the wait would
+see stale data or be overwritten.  This test walks the device assembly of the translation unit
+(written by build()) and checks, for every such read, that nothing but further inline LDS reads
+touches its destination registers before an lgkmcnt(0) wait, and that no read is still pending
+at a label or branch.  It needs no GPU."""
+import os
+import re
+
+import pytest
+
+ASM = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "block_diffusion_drafter_draft_amd", "_build", "k_gemm_deep.s")
+
+REG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def regs_of(text):
+    out = set()
+    for m in REG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _functions(lines):
+    """Split device assembly into functions: name -> list of (line number, text, in_asm)."""
+    fns, cur, in_asm = {}, None, False
+    for no, raw in enumerate(lines, 1):
+        t = raw.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        code = t.split(";")[0].strip()
+        if not code:
+            continue
+        if code.endswith(":") and not code.startswith(".L") and not code.startswith("."):
+            cur = code[:-1]
+            fns[cur] = []
+            continue
+        if code.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if cur is None or (code.startswith(".") and not code.endswith(":")):
+            continue
+        fns[cur].append((no, code, in_asm))
+    return fns
+
+
+def _blocks(body):
+    """Basic blocks of one function: list of (label or None, instructions, successor labels,
+    falls through)."""
+    blocks, cur = [], [None, []]
+    for no, code, in_asm in body:
+        if code.endswith(":"):
+            if cur[1] or cur[0] is not None:
+                blocks.append(cur)
+            cur = [code[:-1], []]
+            continue
+        cur[1].append((no, code, in_asm))
+        op = code.split()[0]
+        if op.startswith("s_cbranch") or op in ("s_branch", "s_endpgm", "s_setpc_b64"):
+            blocks.append(cur)
+            cur = [None, []]
+    if cur[1] or cur[0] is not None:
+        blocks.append(cur)
+    out = []
+    for lab, ins in blocks:
+        succ, falls = [], True
+        if ins:
+            last = ins[-1][1].split()
+            if last[0].startswith("s_cbranch"):
+                succ.append(last[1])
+            elif last[0] == "s_branch":
+                succ.append(last[1])
+                falls = False
+            elif last[0] in ("s_endpgm", "s_setpc_b64"):
+                falls = False
+        out.append((lab, ins, succ, falls))
+    return out
+
+
+def _step(pending, no, code, in_asm, fn, bad):
+    op = code.split()[0]
+    if op == "s_waitcnt":
+        return set() if "lgkmcnt(0)" in code else pending
+    args = code.split(None, 1)[1] if " " in code else ""
+    if in_asm and op == "ds_read_b128":
+        dst, addr = args.split(",", 1)
+        if regs_of(addr) & pending:
+            bad.add((fn, no, "address register of a pending read"))
+        d = regs_of(dst)
+        if d & pending:
+            bad.add((fn, no, "destination overlaps a pending read"))
+        return pending | d
+    if pending and regs_of(args) & pending:
+        bad.add((fn, no, f"'{code[:60]}' touches a pending read's registers"))
+    return pending
+
+
+def check(lines):
+    """Dataflow over each function's control-flow graph: the registers of inline ds_read_b128
+    not yet covered by an lgkmcnt(0) wait, on any path, must not be read or written.  Returns a
+    list of (function, line number, message)."""
+    bad = set()
+    for fn, body in _functions(lines).items():
+        blocks = _blocks(body)
+        index = {lab: k for k, (lab, _, _, _) in enumerate(blocks) if lab is not None}
+        entry = [set() for _ in blocks]
+        work = list(range(len(blocks)))
+        while work:
+            k = work.pop(0)
+            lab, ins, succ, falls = blocks[k]
+            pend = set(entry[k])
+            for no, code, in_asm in ins:
+                pend = _step(pend, no, code, in_asm, fn, bad)
+            nxt = [index[l] for l in succ if l in index]
+            if falls and k + 1 < len(blocks):
+                nxt.append(k + 1)
+            for t in nxt:
+                if not pend <= entry[t]:
+                    entry[t] |= pend
+                    if t not in work:
+                        work.append(t)
+            if pend and not nxt and ins and ins[-1][1].split()[0] == "s_endpgm":
+                bad.add((fn, ins[-1][0], "program ends with pending reads"))
+    return sorted(bad)
+
+
+def test_checker_flags_a_planted_hazard():
+    planted = ["kern:", ";;#ASMSTART", "ds_read_b128 v[4:7], v1", ";;#ASMEND",
+               "v_add_u32_e32 v8, v5, v2", "s_waitcnt lgkmcnt(0)", "s_endpgm"]
+    assert check(planted)
+    # a hazard reached only through a branch
+    branchy = ["kern:", ";;#ASMSTART", "ds_read_b128 v[4:7], v1", ";;#ASMEND",
+               "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)", "s_endpgm", ".LBB0_2:",
+               "v_mov_b32_e32 v6, 0", "s_waitcnt lgkmcnt(0)", "s_endpgm"]
+    assert check(branchy)
+    clean = ["kern:", ";;#ASMSTART", "ds_read_b128 v[4:7], v1", ";;#ASMEND",
+             "v_add_u32_e32 v8, v9, v2", "s_waitcnt lgkmcnt(0)", "v_add_u32_e32 v8, v5, v2",
+             "s_endpgm"]
+    assert not check(clean)
+
+
+def test_deep_gemm_lds_reads_are_waited_for():
+    if not os.path.exists(ASM):
+        pytest.skip("device assembly not built (run __graft_entry__.build())")
+    lines = open(ASM).read().splitlines()
+    n_reads = sum(1 for i, l in enumerate(lines) if "ds_read_b128" in l and i > 0
+                  and lines[i - 1].strip().startswith(";;#ASMSTART"))
+    assert n_reads > 0
+    bad = check(lines)
+    assert not bad, bad[:10]

@@ -29,6 +29,29 @@ def test_gemm_nt(dtype, M, N, K):
     assert rel_l2(C.cpu().numpy(), ref) < 1e-5
 
 
+@pytest.mark.parametrize("cfg", list(range(14)))
+@pytest.mark.parametrize("M,N,K", [(200, 300, 192), (512, 640, 4096), (235, 1000, 2560),
+                                   (16, 384, 4096)])
+def test_gemm_nt_tile_configs(cfg, M, N, K):
+    """Every bf16 tile configuration, with a workspace so the deep-ring tiles split K where
+    their plan does; two calls in a row must agree bit for bit (the split partials are summed in
+    split order and the tile counters are left at zero)."""
+    print(f"gemm cfg={cfg} M={M} N={N} K={K}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(cfg * 131 + M + N + K)
+    A = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
+    B = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    wb = dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, cfg)
+    ws = torch.empty(max(wb, 1), dtype=torch.uint8, device=DEV) if wb else None
+    C1 = torch.full((M, N), float("nan"), device=DEV)
+    C2 = torch.full((M, N), float("nan"), device=DEV)
+    dbd.gemm_nt(A, B, C1, tile_cfg=cfg, workspace=ws)
+    dbd.gemm_nt(A, B, C2, tile_cfg=cfg, workspace=ws)
+    torch.cuda.synchronize()
+    ref = od.f64(A) @ od.f64(B).T
+    assert rel_l2(C1.cpu().numpy(), ref) < 1e-5
+    assert torch.equal(C1, C2)
+
+
 @pytest.mark.parametrize("name", ["tiny-fp32", "qwen3-8b", "gpt-oss-20b"])
 def test_mix_rmsnorm(name):
     sh = synth.workload(name).shape
