@@ -29,7 +29,8 @@ SOURCES = {
     "k_gemm.hip": [],
     # the deep-ring tiles keep their MFMA accumulators in VGPRs (see the file's header)
     "k_gemm_deep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "k_attention.hip": [],
+    # the attention accumulators are rescaled by the online softmax: keep them in VGPRs
+    "k_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_vocab.hip": ["-ffp-contract=off"],
     "runtime.hip": [],
 }

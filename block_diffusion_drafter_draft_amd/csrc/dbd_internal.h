@@ -162,7 +162,7 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
                    int F, bool pair, bool split_ok);
-constexpr int kMaxGemmCfg = 13;
+constexpr int kMaxGemmCfg = 16;
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
 hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,
                                   int ntiles, const int32_t* blk_pos, int block_len,

@@ -241,9 +241,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, EpiArgs e) {
 // optional split-K (k_gemm_deep.hip; 8-10 four waves, 11-13 eight waves).
 constexpr int kNumCfg = kMaxGemmCfg + 1;
 static const int kCfgBM[kNumCfg] = {256, 256, 128, 64, 128, 64, 256, 128, 256, 128, 128,
-                                    256, 256, 256};
+                                    256, 256, 256, 256, 256, 256};
 static const int kCfgBN[kNumCfg] = {256, 128, 128, 128, 128, 128, 128, 256, 128, 256, 128,
-                                    256, 192, 128};
+                                    256, 192, 128, 256, 192, 128};
 static bool is_deep(int cfg) { return cfg >= 8; }
 
 template <int BM, int BN, int ST, int KIND, bool SPLITA>
@@ -307,17 +307,26 @@ static int choose_split(int cfg, int M, int Nv, int K, int batch) {
   return best;
 }
 
-// Default tile for a shape.  The eight-wave 256-row tiles when one of them covers the problem in
-// rounds of 256 workgroups that are at least 85% full; else the 64 x 128 pipelined tile when it
-// gives at most 320 tiles (small N: the most workgroups at one round); else the largest
-// pipelined tile that still gives every CU work in whole rounds (at least two tiles per CU), or
-// the one with the most tiles.
-static int choose_cfg(int M, int N, int batch, int gateup, int F, bool big_ok) {
+// Default tile for a problem, from timings of every configuration on the drafter's shapes with
+// their own epilogues (MI355X, weights streamed from HBM):
+//  - bf16-pair A operands, and the Q/K/V and context K/V epilogues (rotation, scattered cache
+//    writes) when M >= 64: the four-wave deep 128 x 128 tile.  Two of its workgroups share a
+//    CU, so one's epilogue overlaps the other's main loop (QKV 4096+2048 x 4096, M = 512:
+//    58.8 us against 78.1 us for the pipelined 64 x 128 tile; context K/V with pairs: 147 us
+//    against 230 us);
+//  - the eight-wave 256-row tiles when one of them covers the problem in rounds of 256
+//    workgroups that are at least 85% full (gate/up, LM head);
+//  - M <= 128 with K >= 8192: the deep 128 x 128 tile, which may split K;
+//  - else the pipelined 64 x 128 tile when it gives at most 320 tiles (small N); else the
+//    largest pipelined tile that still gives every CU work in whole rounds (at least two tiles
+//    per CU), or the one with the most tiles.
+static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int F, bool pair) {
   auto tiles_of = [&](int c) {
     const int n = gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N;
     return ceil_div(M, kCfgBM[c]) * ceil_div(n, kCfgBN[c]) * batch;
   };
-  if (big_ok && M >= 128) {
+  if (M >= 64 && (pair || kind == EPI_QKV || kind == EPI_CTXKV)) return 10;
+  if (!pair && kind != EPI_QKV && kind != EPI_CTXKV && M >= 128) {
     int best = -1;
     double best_fill = 0.85;
     for (int c : {11, 12}) {
@@ -327,6 +336,7 @@ static int choose_cfg(int M, int N, int batch, int gateup, int F, bool big_ok) {
     }
     if (best >= 0) return best;
   }
+  if (M <= 128 && K >= 8192) return 10;
   if (tiles_of(3) <= 320) return 3;
   static const int order[4] = {0, 1, 4, 5};
   int best = 5, best_tiles = 0;
@@ -351,9 +361,9 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
   // boundaries (multiples of 128)
   const bool n128 = kind == EPI_QKV || kind == EPI_CTXKV;
   const bool chosen = cfg >= 0 && cfg < kNumCfg;
-  if (!chosen) cfg = choose_cfg(M, N, batch, gateup, F, !n128 && !pair);
+  if (!chosen) cfg = choose_cfg(kind, M, N, K, batch, gateup, F, pair);
   if (n128 && kCfgBN[cfg] != 128)
-    cfg = cfg >= 11 ? 13 : is_deep(cfg) ? (kCfgBM[cfg] == 256 ? 8 : 10)
+    cfg = cfg >= 14 ? 16 : cfg >= 11 ? 13 : is_deep(cfg) ? (kCfgBM[cfg] == 256 ? 8 : 10)
                                         : (kCfgBM[cfg] == 256 ? 1 : 4);
   if (pair) cfg = pair_cfg(cfg);
   auto nvirt = [&](int c) { return gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N; };

@@ -438,6 +438,178 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs a, EpiArgs e) {
   store_tile([&](int i, int j) { return acc[i][j]; });
 }
 
+// ------------------------------------------------------------------ 8-wave, register-staged
+// The same 256 x BN tile, 8-wave grid, 64-wide k stages and epilogue as gemm_w8_kernel, but the
+// tiles travel global -> VGPRs -> LDS (global_load_dwordx4, then ds_write_b128 into a two-slot
+// ring) instead of global->LDS DMA: measured on gfx950, ordinary loads stream about 1.4x the
+// bytes per CU that the DMA path does.  Stage kt+2 is loaded into registers while stage kt is
+// computed and written to LDS at the start of the next stage.  All LDS traffic is ordinary
+// compiled code, so the compiler places every wait.
+template <int BN>
+struct W8RCfg {
+  static constexpr int BM = 256, KS = 64, NT = 512, NW = 8, ROWB = 128;
+  static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB, STAGE = ABYTES + BBYTES;
+  static constexpr int CH = STAGE / 16 / NT;              // 16-byte chunks per thread per stage
+  static constexpr int WTM = 128, WTN = BN / 4, MI = 8, NI = WTN / 16;
+  static constexpr int TM = BN == 192 ? 128 : 64;
+  static constexpr int CBYTES = TM * (BN + 4) * 4;
+  static constexpr int SMEM = 2 * STAGE > CBYTES ? 2 * STAGE : CBYTES;
+  static_assert(STAGE % (16 * NT) == 0 && WTN % 16 == 0, "tile shape");
+};
+
+template <int BN, int KIND>
+__global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
+  using C = W8RCfg<BN>;
+  constexpr int BM = C::BM, KS = C::KS;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int z = blockIdx.z;
+  const int M = a.M, N = a.N, K = a.K;
+  const int S = a.split > 1 ? a.split : 1;
+  const int tiles_m = (M + BM - 1) / BM;
+  int tm, tn, sp;
+  unit_of(blockIdx.x, gridDim.x, tiles_m, S, &tm, &tn, &sp);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk_all = K / KS;
+  const int kb = (int)((int64_t)nk_all * sp / S), nk = (int)((int64_t)nk_all * (sp + 1) / S) - kb;
+
+  // chunk c = tid + 512 q of a stage: tile row c / 8 (A rows first, then B rows), 16-byte chunk
+  // c % 8 of the row's 128 bytes; eight consecutive threads read one 128-byte line.  It is
+  // stored in LDS slot (c % 8) ^ swz(row) of the row.
+  const BMap bm = make_bmap(a);
+  const bf16* src[C::CH];
+  uint32_t dst[C::CH];
+#pragma unroll
+  for (int q = 0; q < C::CH; ++q) {
+    const int c = tid + C::NT * q, row = c >> 3, ch = c & 7;
+    const bool isA = row < BM;
+    const int r = isA ? row : row - BM;
+    src[q] = (isA ? (const bf16*)a.A + (int64_t)z * a.a_bs + (int64_t)min(m0 + r, M - 1) * a.lda
+                  : brow_ptr<bf16, BN>(bm, min(n0 + r, N - 1), z)) +
+             (int64_t)kb * KS + ch * 8;
+    dst[q] = (uint32_t)(row * C::ROWB + ((ch ^ swz(row)) * 16));
+  }
+  u32x4 stg[C::CH];
+  auto load = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < C::CH; ++q) stg[q] = *reinterpret_cast<const u32x4*>(src[q] + kt * KS);
+  };
+  auto store = [&](int slot) __attribute__((always_inline)) {
+    char* base = smem + slot * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::CH; ++q) *reinterpret_cast<u32x4*>(base + dst[q]) = stg[q];
+  };
+
+  const int fr = lane & 15, fk = lane >> 4;
+  int rd[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) rd[s2] = fr * C::ROWB + (((4 * s2 + fk) ^ swz(fr)) * 16);
+  const int a_off = wm * C::WTM * C::ROWB, b_off = C::ABYTES + wn * C::WTN * C::ROWB;
+
+  f32x4 acc[C::MI][C::NI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) {
+    load(0);
+    store(0);
+    if (nk > 1) load(1);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    // slot kt&1 holds stage kt; the registers hold stage kt+1 (in flight); slot (kt+1)&1 was
+    // last read in stage kt-1, which every wave finished before the barrier ending it
+    if (kt + 1 < nk) store((kt + 1) & 1);
+    if (kt + 2 < nk) load(kt + 2);
+    const char* st = smem + (kt & 1) * C::STAGE;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 fa[C::MI], fb[C::NI];
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(st + a_off + rd[s2] + i * 16 * C::ROWB);
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(st + b_off + rd[s2] + j * 16 * C::ROWB);
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  auto store_tile = [&](auto get) __attribute__((always_inline)) {
+    float* Cs = (float*)smem;
+    constexpr int CS_LD = BN + 4;
+#pragma unroll
+    for (int h = 0; h < BM / C::TM; ++h) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int row0 = wm * C::WTM + i * 16;
+        if (row0 / C::TM != h) continue;
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) {
+          const f32x4 v = get(i, j);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = row0 - h * C::TM + (lane >> 4) * 4 + r;
+            const int col = wn * C::WTN + j * 16 + (lane & 15);
+            Cs[row * CS_LD + col] = v[r];
+          }
+        }
+      }
+      __syncthreads();
+      run_epilogue<bf16, C::TM, BN, KIND, C::NT>(e, Cs, m0 + h * C::TM, n0, tn, z, M, N);
+      __syncthreads();
+    }
+  };
+
+  if (S > 1) {
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tile = (z * tiles_n + tn) * tiles_m + tm;
+    constexpr int FR = C::MI * C::NI * 64;
+    f32x4* part = reinterpret_cast<f32x4*>(a.part) + (int64_t)tile * S * C::NW * FR;
+    f32x4* mine = part + ((int64_t)sp * C::NW + wave) * FR + lane;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j) mine[(i * C::NI + j) * 64] = acc[i][j];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const int old = atomicAdd(a.cnt + tile, 1);
+      s_last = old == S - 1;
+      if (old == S - 1) a.cnt[tile] = 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const f32x4* mybase = part + (int64_t)wave * FR + lane;
+    store_tile([&](int i, int j) {
+      const f32x4* p = mybase + (i * C::NI + j) * 64;
+      f32x4 t = p[0];
+      for (int q = 1; q < S; ++q) t += p[(int64_t)q * C::NW * FR];
+      return t;
+    });
+    return;
+  }
+  store_tile([&](int i, int j) { return acc[i][j]; });
+}
+
+template <int BN, int KIND>
+static void launch_w8r(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
+  if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, BN / 2) * BN;
+  const int S = a.split > 1 ? a.split : 1;
+  const int units = ceil_div(a.M, 256) * ceil_div(a.N, BN) * S;
+  hipLaunchKernelGGL((gemm_w8r_kernel<BN, KIND>), dim3(units, 1, batch), dim3(512), 0, s, a, e);
+}
+
 template <int BN, int NS, int KS, int KIND>
 static void launch_w8(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, BN / 2) * BN;
@@ -457,7 +629,8 @@ static void launch_deep(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) 
 }
 
 // 8: 256 x 128 (3 stages), 9: 128 x 256 (3), 10: 128 x 128 (4): four waves, 32-wide k stages;
-// 11: 256 x 256 (2), 12: 256 x 192 (2), 13: 256 x 128 (3): eight waves, 64-wide k stages.  The bf16-pair A operand doubles the A part
+// 11: 256 x 256 (2), 12: 256 x 192 (2), 13: 256 x 128 (3): eight waves, 64-wide k stages;
+// 14: 256 x 256, 15: 256 x 192, 16: 256 x 128: eight waves, register-staged two-slot ring.  The bf16-pair A operand doubles the A part
 // of a stage and the A fragments: pairs always take the four-wave 128 x 128 tile with 6 stages.
 // The value-cache epilogues (QKV, context K/V) need 128-column tiles.
 template <int KIND, bool SPLITA>
@@ -468,6 +641,7 @@ void launch_deep_cfg(int cfg, GemmArgs a, const EpiArgs& e, int batch, hipStream
     switch (cfg) {
       case 8: launch_deep<256, 128, 3, KIND, false>(a, e, batch, s); break;
       case 11: case 12: case 13: launch_w8<128, 3, 64, KIND>(a, e, batch, s); break;
+      case 14: case 15: case 16: launch_w8r<128, KIND>(a, e, batch, s); break;
       default: launch_deep<128, 128, 4, KIND, false>(a, e, batch, s); break;
     }
   } else {
@@ -477,6 +651,9 @@ void launch_deep_cfg(int cfg, GemmArgs a, const EpiArgs& e, int batch, hipStream
       case 11: launch_w8<256, 2, 64, KIND>(a, e, batch, s); break;
       case 12: launch_w8<192, 2, 64, KIND>(a, e, batch, s); break;
       case 13: launch_w8<128, 3, 64, KIND>(a, e, batch, s); break;
+      case 14: launch_w8r<256, KIND>(a, e, batch, s); break;
+      case 15: launch_w8r<192, KIND>(a, e, batch, s); break;
+      case 16: launch_w8r<128, KIND>(a, e, batch, s); break;
       default: launch_deep<128, 128, 4, KIND, false>(a, e, batch, s); break;
     }
   }

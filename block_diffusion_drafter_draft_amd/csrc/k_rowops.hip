@@ -262,6 +262,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
                                                       T* __restrict__ out, T* __restrict__ out_lo,
                                                       int H, float eps, int block_len,
                                                       int n_anchor) {
+  // thread t owns the groups of 4 columns t, t + 256, ... (coalesced); the row stays in registers
+  // between the sum of squares and the scaling (H <= 8192)
+  constexpr int MAXG = 8;
   __shared__ float red[4];
   const int ro = blockIdx.x;
   int ri = ro;
@@ -270,10 +273,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     ri = (ro / D) * block_len + n_anchor + ro % D;
   }
   const float* xr = x + (int64_t)ri * H;
+  float4 v[MAXG];
   float s = 0.f;
-  for (int i = threadIdx.x * 4; i < H; i += 256 * 4) {
-    float4 v = *reinterpret_cast<const float4*>(xr + i);
-    s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int q = 0; q < MAXG; ++q) {
+    const int i = (threadIdx.x + q * 256) * 4;
+    if (i < H) {
+      v[q] = *reinterpret_cast<const float4*>(xr + i);
+      s += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
+    }
   }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -281,15 +289,25 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
   T* o = out + (int64_t)ro * H;
   T* ol = out_lo ? out_lo + (int64_t)ro * H : nullptr;
-  for (int i = threadIdx.x * 4; i < H; i += 256 * 4) {
-    float4 v = *reinterpret_cast<const float4*>(xr + i);
-    const float y[4] = {v.x * inv * to_f(g[i + 0]), v.y * inv * to_f(g[i + 1]),
-                        v.z * inv * to_f(g[i + 2]), v.w * inv * to_f(g[i + 3])};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const T hi = from_f<T>(y[q]);
-      o[i + q] = hi;
-      if (ol) ol[i + q] = from_f<T>(y[q] - to_f(hi));
+  for (int q = 0; q < MAXG; ++q) {
+    const int i = (threadIdx.x + q * 256) * 4;
+    if (i >= H) continue;
+    T gv[4], hi[4], lo[4];
+    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(gv) = *reinterpret_cast<const uint2*>(g + i);
+    else *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(g + i);
+    const float y[4] = {v[q].x * inv * to_f(gv[0]), v[q].y * inv * to_f(gv[1]),
+                        v[q].z * inv * to_f(gv[2]), v[q].w * inv * to_f(gv[3])};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = from_f<T>(y[e]);
+      lo[e] = from_f<T>(y[e] - to_f(hi[e]));
+    }
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint2*>(o + i) = *reinterpret_cast<uint2*>(hi);
+      if (ol) *reinterpret_cast<uint2*>(ol + i) = *reinterpret_cast<uint2*>(lo);
+    } else {
+      *reinterpret_cast<float4*>(o + i) = *reinterpret_cast<float4*>(hi);
     }
   }
 }

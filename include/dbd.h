@@ -237,9 +237,10 @@ int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int
  * rows.  tile_cfg selects the bf16 block tile (BM x BN): 0-7 a ring of 64-wide k tiles
  * (0: 256x256/2 stages, 1: 256x128/3, 2: 128x128/3, 3: 64x128/4, 4: 128x128/2, 5: 64x128/3,
  * 6: 256x128/2, 7: 128x256/2); 8-13 a deep ring of 32-wide k stages (4 waves: 8: 256x128/3,
- * 9: 128x256/3, 10: 128x128/4; 8 waves: 11: 256x256/4, 12: 256x192/5, 13: 256x128/6) which
- * splits K over several workgroups when `workspace` is given (NULL: no split); -1: the
- * library's choice.  The
+ * 9: 128x256/3, 10: 128x128/4; 8 waves, 64-wide k stages: 11: 256x256/2, 12: 256x192/2,
+ * 13: 256x128/3) which splits K over several workgroups when `workspace` is given (NULL: no
+ * split); 14-16 the 8-wave tiles 256x256, 256x192, 256x128 staged through registers instead of
+ * global->LDS DMA (same split rule); -1: the library's choice.  The
  * workspace (dbd_gemm_workspace_bytes, 256-byte aligned) is used only by this call. */
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* B, float* C, int32_t M, int32_t N,
                 int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,

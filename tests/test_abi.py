@@ -190,7 +190,7 @@ def test_gemm_validation():
     assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, None, 0, None) == -2
     assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, None, 0, None) == -2  # lda<K
     assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, None, 0, None) == -1
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 14, None, 0, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 17, None, 0, None) == -1
     # a split-K shape with a workspace that is too small, or misaligned
     need = dbd.gemm_workspace_bytes(dbd.DBD_BF16, 512, 4096, 4096, 8)
     assert need > 0
@@ -205,7 +205,7 @@ def test_gemm_split_plan_fits_workspace():
     """Split-K partials are sized by the same plan the launch uses: for every deep tile the
     workspace holds one fp32 tile per (output tile, split) and one counter per tile."""
     for M, N, K in [(512, 4096, 4096), (512, 4096, 12288), (128, 2048, 4096), (16, 6144, 4096)]:
-        for cfg in range(8, 14):
+        for cfg in range(8, 17):
             b = dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, cfg)
             assert b % 4 == 0
             if b:

@@ -5,7 +5,7 @@ global->LDS DMA ring before every LDS read) and wait for them themselves with
 s_waitcnt lgkmcnt(0).  The compiler does not know that such a read writes its destination
 registers later, so any instruction that reads or writes those registers before the wait would
 see stale data or be overwritten.  This test walks the device assembly of the translation unit
-(written by build()) and checks, for every such read, that nothing but further inline LDS reads
+(written by build() for every unit that has such reads) and checks, for every such read, that nothing but further inline LDS reads
 touches its destination registers before an lgkmcnt(0) wait, and that no read is still pending
 at a label or branch.  It needs no GPU."""
 import os
@@ -13,8 +13,9 @@ import re
 
 import pytest
 
-ASM = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "block_diffusion_drafter_draft_amd", "_build", "k_gemm_deep.s")
+BUILD = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                     "block_diffusion_drafter_draft_amd", "_build")
+UNITS = ["k_gemm_deep.s"]
 
 REG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
 
@@ -151,10 +152,12 @@ def test_checker_flags_a_planted_hazard():
     assert not check(clean)
 
 
-def test_deep_gemm_lds_reads_are_waited_for():
-    if not os.path.exists(ASM):
+@pytest.mark.parametrize("unit", UNITS)
+def test_inline_lds_reads_are_waited_for(unit):
+    path = os.path.join(BUILD, unit)
+    if not os.path.exists(path):
         pytest.skip("device assembly not built (run __graft_entry__.build())")
-    lines = open(ASM).read().splitlines()
+    lines = open(path).read().splitlines()
     n_reads = sum(1 for i, l in enumerate(lines) if "ds_read_b128" in l and i > 0
                   and lines[i - 1].strip().startswith(";;#ASMSTART"))
     assert n_reads > 0
