@@ -53,6 +53,14 @@ __device__ __forceinline__ const T* brow_ptr(const BMap& m, int v, int z) {
   return (const T*)base + (int64_t)z * m.b_bs + (int64_t)r * m.ldb;
 }
 
+// A 16-byte load through a global (address space 1) pointer.  The weight-row pointers are built
+// from integer arithmetic, so the compiler cannot prove them global and would emit a flat load,
+// which also counts on lgkmcnt: every wait for an LDS read would then wait for the global
+// prefetches as well.
+__device__ __forceinline__ u32x4 load_global16(const void* p) {
+  return *(const __attribute__((address_space(1))) u32x4*)(p);
+}
+
 // ------------------------------------------------------------------ epilogues
 // The finished tile (or a chunk of TM of its rows) sits in LDS as fp32, row stride BN + 4.  Each thread owns a contiguous
 // segment of one row (TPR threads per row, CPT columns each), issues all of its global loads

@@ -442,8 +442,8 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs a, EpiArgs e) {
 // The same 256 x BN tile, 8-wave grid, 64-wide k stages and epilogue as gemm_w8_kernel, but the
 // tiles travel global -> VGPRs -> LDS (global_load_dwordx4, then ds_write_b128 into a two-slot
 // ring) instead of global->LDS DMA: measured on gfx950, ordinary loads stream about 1.4x the
-// bytes per CU that the DMA path does.  Stage kt+2 is loaded into registers while stage kt is
-// computed and written to LDS at the start of the next stage.  All LDS traffic is ordinary
+// bytes per CU that the DMA path does.  Two register sets alternate: stage kt+2 is loaded while
+// stage kt is computed and stage kt+1 is written to LDS after it.  All LDS traffic is ordinary
 // compiled code, so the compiler places every wait.
 template <int BN>
 struct W8RCfg {
@@ -491,12 +491,12 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
              (int64_t)kb * KS + ch * 8;
     dst[q] = (uint32_t)(row * C::ROWB + ((ch ^ swz(row)) * 16));
   }
-  u32x4 stg[C::CH];
-  auto load = [&](int kt) __attribute__((always_inline)) {
+  u32x4 stA[C::CH], stB[C::CH];
+  auto load = [&](u32x4* stg, int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < C::CH; ++q) stg[q] = *reinterpret_cast<const u32x4*>(src[q] + kt * KS);
+    for (int q = 0; q < C::CH; ++q) stg[q] = load_global16(src[q] + kt * KS);
   };
-  auto store = [&](int slot) __attribute__((always_inline)) {
+  auto store = [&](const u32x4* stg, int slot) __attribute__((always_inline)) {
     char* base = smem + slot * C::STAGE;
 #pragma unroll
     for (int q = 0; q < C::CH; ++q) *reinterpret_cast<u32x4*>(base + dst[q]) = stg[q];
@@ -514,18 +514,8 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) {
-    load(0);
-    store(0);
-    if (nk > 1) load(1);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    // slot kt&1 holds stage kt; the registers hold stage kt+1 (in flight); slot (kt+1)&1 was
-    // last read in stage kt-1, which every wave finished before the barrier ending it
-    if (kt + 1 < nk) store((kt + 1) & 1);
-    if (kt + 2 < nk) load(kt + 2);
-    const char* st = smem + (kt & 1) * C::STAGE;
+  auto compute = [&](int slot) __attribute__((always_inline)) {
+    const char* st = smem + slot * C::STAGE;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       bf16x8 fa[C::MI], fb[C::NI];
@@ -541,8 +531,31 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
         for (int j = 0; j < C::NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
+  };
+  // Stage kt: slot kt&1 holds stage kt; the register set `nxt` holds stage kt+1 (loaded two
+  // stages ago) and `fre` is free (its stage is in LDS).  Stage kt+2 is loaded into `fre`
+  // first, so it has two stages of compute to land; after the MFMAs stage kt+1 goes from `nxt`
+  // into the other slot, last read in stage kt-1 (before the barrier ending it).  Every step
+  // loads and stores unconditionally (past the last stage it reloads and rewrites the last
+  // one, which is never read again), so the order of the loads in flight is the same on every
+  // path and the waits before the LDS writes cover only the older register set.
+  auto step = [&](int kt, u32x4* nxt, u32x4* fre) __attribute__((always_inline)) {
+    load(fre, min(kt + 2, nk - 1));
+    compute(kt & 1);
+    store(nxt, (kt + 1) & 1);
     __syncthreads();
+  };
+
+  load(stA, 0);
+  store(stA, 0);
+  load(stB, min(1, nk - 1));
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, stB, stA);
+    step(kt + 1, stA, stB);
   }
+  if (kt < nk) step(kt, stB, stA);
 
   auto store_tile = [&](auto get) __attribute__((always_inline)) {
     float* Cs = (float*)smem;

@@ -1,4 +1,4 @@
-"""Static check of the inline-assembly LDS reads in the deep-ring GEMM kernels.
+"""Static check of the inline-assembly LDS reads in the deep-ring and four-wave GEMM kernels.
 
 The kernels issue ds_read_b128 as inline assembly (so that the compiler does not drain the
 global->LDS DMA ring before every LDS read) and wait for them themselves with
@@ -90,49 +90,81 @@ def _blocks(body):
     return out
 
 
-def _step(pending, no, code, in_asm, fn, bad):
+# The pending state is a map register -> age: the number of LDS operations issued after the
+# read that writes it.  LDS operations complete in order, so s_waitcnt lgkmcnt(N) completes
+# every read with N or more younger LDS operations.  Scalar memory operations also count on
+# lgkmcnt but complete out of order: they never make a read older, so they are not counted.
+MAX_AGE = 64
+
+
+def _pending(state):
+    return set(state)
+
+
+def _age(state):
+    return {r: min(a + 1, MAX_AGE) for r, a in state.items()}
+
+
+def _step(state, no, code, in_asm, fn, bad):
     op = code.split()[0]
     if op == "s_waitcnt":
-        return set() if "lgkmcnt(0)" in code else pending
+        m = re.search(r"lgkmcnt\((\d+)\)", code)
+        if m:
+            n = int(m.group(1))
+            state = {r: a for r, a in state.items() if a < n}
+        return state
     args = code.split(None, 1)[1] if " " in code else ""
     if in_asm and op == "ds_read_b128":
         dst, addr = args.split(",", 1)
-        if regs_of(addr) & pending:
+        if regs_of(addr) & _pending(state):
             bad.add((fn, no, "address register of a pending read"))
         d = regs_of(dst)
-        if d & pending:
+        if d & _pending(state):
             bad.add((fn, no, "destination overlaps a pending read"))
-        return pending | d
-    if pending and regs_of(args) & pending:
+        state = _age(state)
+        for r in d:
+            state[r] = 0
+        return state
+    if state and regs_of(args) & _pending(state):
         bad.add((fn, no, f"'{code[:60]}' touches a pending read's registers"))
-    return pending
+    if op.startswith("ds_"):
+        state = _age(state)          # any other LDS operation is younger than the reads
+    return state
+
+
+def _merge(into, new):
+    """Join of two states: a register is pending if it is on either path, at the younger age."""
+    changed = False
+    for r, a in new.items():
+        if r not in into or a < into[r]:
+            into[r] = a
+            changed = True
+    return changed
 
 
 def check(lines):
     """Dataflow over each function's control-flow graph: the registers of inline ds_read_b128
-    not yet covered by an lgkmcnt(0) wait, on any path, must not be read or written.  Returns a
+    not yet covered by an lgkmcnt wait, on any path, must not be read or written.  Returns a
     list of (function, line number, message)."""
     bad = set()
     for fn, body in _functions(lines).items():
         blocks = _blocks(body)
         index = {lab: k for k, (lab, _, _, _) in enumerate(blocks) if lab is not None}
-        entry = [set() for _ in blocks]
+        entry = [dict() for _ in blocks]
         work = list(range(len(blocks)))
         while work:
             k = work.pop(0)
             lab, ins, succ, falls = blocks[k]
-            pend = set(entry[k])
+            st = dict(entry[k])
             for no, code, in_asm in ins:
-                pend = _step(pend, no, code, in_asm, fn, bad)
+                st = _step(st, no, code, in_asm, fn, bad)
             nxt = [index[l] for l in succ if l in index]
             if falls and k + 1 < len(blocks):
                 nxt.append(k + 1)
             for t in nxt:
-                if not pend <= entry[t]:
-                    entry[t] |= pend
-                    if t not in work:
-                        work.append(t)
-            if pend and not nxt and ins and ins[-1][1].split()[0] == "s_endpgm":
+                if _merge(entry[t], st) and t not in work:
+                    work.append(t)
+            if st and not nxt and ins and ins[-1][1].split()[0] == "s_endpgm":
                 bad.add((fn, ins[-1][0], "program ends with pending reads"))
     return sorted(bad)
 
@@ -146,6 +178,13 @@ def test_checker_flags_a_planted_hazard():
                "s_cbranch_scc1 .LBB0_2", "s_waitcnt lgkmcnt(0)", "s_endpgm", ".LBB0_2:",
                "v_mov_b32_e32 v6, 0", "s_waitcnt lgkmcnt(0)", "s_endpgm"]
     assert check(branchy)
+    # a partial wait covers the older read only
+    partial = ["kern:", ";;#ASMSTART", "ds_read_b128 v[4:7], v1", ";;#ASMEND", ";;#ASMSTART",
+               "ds_read_b128 v[8:11], v2", ";;#ASMEND", "s_waitcnt lgkmcnt(1)",
+               "v_add_u32_e32 v20, v5, v2", "v_add_u32_e32 v21, v9, v2", "s_waitcnt lgkmcnt(0)",
+               "s_endpgm"]
+    bad = check(partial)
+    assert len(bad) == 1 and bad[0][1] == 10
     clean = ["kern:", ";;#ASMSTART", "ds_read_b128 v[4:7], v1", ";;#ASMEND",
              "v_add_u32_e32 v8, v9, v2", "s_waitcnt lgkmcnt(0)", "v_add_u32_e32 v8, v5, v2",
              "s_endpgm"]
