@@ -15,6 +15,7 @@ Auxiliary modes for the HBM-traffic figure of the dominant kernel (rocprofv3 cou
 """
 import argparse
 import json
+import re
 import os
 import sys
 import time
@@ -122,25 +123,45 @@ def summarize_traffic(d):
                       "kernels": len(out["kernels"])}))
 
 
-# Library kernel (demangled name fragment) behind each timed stage whose launches all use one
-# kernel; the epilogue kind is a template argument of the GEMM kernel.
-STAGE_KERNEL = {"gemm_gateup": ", 4, false>", "gemm_lmhead": ", 5, false>",
-                "gemm_qkv": ", 2, false>", "gemm_ctxkv": ", 3, true>",
-                "attn": "attn_bf16_kernel", "mix": "mix_rmsnorm_kernel"}
+# Epilogue kind (a template argument of every GEMM kernel) of each timed GEMM stage whose
+# launches all use one epilogue, and the kernel name fragment of the other stages.
+STAGE_EPILOGUE = {"gemm_gateup": 4, "gemm_lmhead": 5, "gemm_qkv": 2, "gemm_ctxkv": 3}
+STAGE_KERNEL = {"attn": "attn_bf16_kernel", "mix": "mix_rmsnorm_kernel"}
+# position of the epilogue kind in each GEMM kernel's template argument list
+KIND_ARG = {"gemm_bf16_kernel": 3, "gemm_big_kernel": 3, "gemm_w8_kernel": 3,
+            "gemm_w8r_kernel": 1}
 
 
-def measured_traffic(kernel_substr):
-    """HBM bytes per launch of the first library kernel whose name contains kernel_substr, from
-    the committed counter summary, or None when absent or taken on other kernel sources."""
+def gemm_epilogue(name):
+    """Epilogue kind of a demangled library GEMM kernel name, or None."""
+    m = re.search(r"dbd::(gemm_\w+_kernel)<([^>]*)>", name)
+    if not m or m.group(1) not in KIND_ARG:
+        return None
+    return int(m.group(2).split(",")[KIND_ARG[m.group(1)]])
+
+
+def stage_kernels(stage, names):
+    """The kernel names among `names` that the timed stage launches."""
+    if stage in STAGE_EPILOGUE:
+        return [k for k in names if gemm_epilogue(k) == STAGE_EPILOGUE[stage]]
+    if stage in STAGE_KERNEL:
+        return [k for k in names if STAGE_KERNEL[stage] in k]
+    return []
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of the one library kernel the stage launches, from the committed
+    counter summary, or None when absent, ambiguous or taken on other kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     t = json.load(open(TRAFFIC_FILE))
     if t.get("source_hash") != kernel_source_hash():
         return None
-    for k, v in t["kernels"].items():
-        if kernel_substr in k:
-            return v["fetch_bytes"] + v["write_bytes"]
-    return None
+    ks = stage_kernels(stage, t["kernels"])
+    if len(ks) != 1:
+        return None
+    v = t["kernels"][ks[0]]
+    return {"bytes": v["fetch_bytes"] + v["write_bytes"], "kernel": ks[0]}
 
 
 def algorithmic_costs(wl, ctx, new):
@@ -302,11 +323,12 @@ def main():
             ach = b / n / avg_s / 1e9
             roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
                         "unit": "GB/s", "frac": round(ach * 1e9 / HBM_PEAK, 4)}
-        tr = measured_traffic(STAGE_KERNEL[dom]) if dom in STAGE_KERNEL else None
+        tr = measured_traffic(dom)
         roofline.update({"kernel": dom, "launches_per_step": n,
                          "avg_launch_us": round(avg_s * 1e6, 2),
                          "algorithmic_bytes_per_launch": round(b / n),
-                         "traffic": tr,
+                         "traffic": None if tr is None else tr["bytes"],
+                         "traffic_kernel": None if tr is None else tr["kernel"],
                          "traffic_source": None if tr is None else
                          os.path.relpath(TRAFFIC_FILE, ROOT)})
     step_roof_s = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in costs.values())

@@ -76,9 +76,11 @@ def lib():
                                               _sz, _vp]),
             "dbd_mix_rmsnorm": (_i32, [_c.POINTER(ModelDesc), _vp, _vp, _vp, _i64, _i64, _i32,
                                        _vp, _vp]),
-            "dbd_gemm_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _c.POINTER(_sz)]),
+            "dbd_gemm_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                _c.POINTER(_sz)]),
             "dbd_gemm_nt": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
-                                   _vp, _sz, _vp]),
+                                   _i32, _vp, _sz, _vp]),
+            "dbd_gemm_override": (_i32, [_i32, _i32, _i32]),
             "dbd_timing_enable": (_i32, [_i32]),
             "dbd_timing_reset": (_i32, []),
             "dbd_timing_read": (_i32, [_i32, _c.POINTER(_c.c_double), _c.POINTER(_i64)]),
@@ -233,25 +235,33 @@ def mix_rmsnorm(desc, mix_logits, mix_norm_w, hidden, out, stream=None):
         hidden.stride(1), hidden.shape[0], _ptr(out), _stream(stream, hidden)))
 
 
-def gemm_workspace_bytes(dtype, M, N, K, tile_cfg=-1):
-    """Workspace bytes gemm_nt needs to split K for this shape and tile (0: it does not)."""
+def gemm_workspace_bytes(dtype, M, N, K, tile_cfg=-1, split=0):
+    """Workspace bytes gemm_nt needs to split K for this shape, tile and split (0: it does not)."""
     out = _sz(0)
-    _check(lib().dbd_gemm_workspace_bytes(dtype, M, N, K, int(tile_cfg), _c.byref(out)))
+    _check(lib().dbd_gemm_workspace_bytes(dtype, M, N, K, int(tile_cfg), int(split),
+                                          _c.byref(out)))
     return out.value
 
 
-def gemm_nt(A, B, C, tile_cfg=-1, workspace=None, stream=None):
+def gemm_nt(A, B, C, tile_cfg=-1, workspace=None, stream=None, split=0):
     """C[M, N] fp32 = A[M, K] . B[N, K]^T with A, B both fp32 or both bf16; tile_cfg picks the
     bf16 block tile (-1: the library's choice).  With a workspace (gemm_workspace_bytes) the
-    deep-ring tiles may split K over several workgroups."""
+    deep-ring tiles may split K over several workgroups: split 0 lets the library choose, 1 does
+    not split, S > 1 splits S ways (a second kernel adds the partials in split order)."""
     import torch
     dt = DBD_BF16 if A.dtype == torch.bfloat16 else DBD_F32
     M, K = A.shape
     N = B.shape[0]
     wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dbd_gemm_nt(dt, _ptr(A), _ptr(B), _ptr(C), M, N, K, A.stride(0), B.stride(0),
-                             C.stride(0), int(tile_cfg), _ptr(workspace), wb,
+                             C.stride(0), int(tile_cfg), int(split), _ptr(workspace), wb,
                              _stream(stream, A)))
+
+
+def gemm_override(stage, tile_cfg=-1, split=0):
+    """Replace the tile / split-K choice of one draft_block GEMM stage (a name of STAGES starting
+    with "gemm_"); -1 / 0 restore the library's choice.  Set before sizing the workspace."""
+    _check(lib().dbd_gemm_override(STAGES.index(stage), int(tile_cfg), int(split)))
 
 
 # Stage order of DBD_STAGE_* in include/dbd.h.

@@ -62,8 +62,6 @@ struct RowMeta {
   int32_t* seq_keys;    // [N]     keys the block attends to (P + B), 0 if invalid
   float2* rope_blk;     // [N*B][hd/2] (cos, sin)
   float2* rope_ctx;     // [T_new][hd/2]
-  int32_t* gemm_cnt;    // [n_gemm_cnt] split-K tile counters, zeroed by the prep kernel
-  int n_gemm_cnt;
 };
 
 // GEMM: C = A[M,K] . Bv[N,K]^T where the virtual B rows come from up to three weight tensors
@@ -82,15 +80,13 @@ struct GemmArgs {
   int gateup;           // 1: tile t holds gate rows [t*BN/2, +BN/2) then up rows; seg0 = gate,
                         //    seg1 = up, both with n1 - n0 = F
   int M, N, K;          // N = virtual columns
-  // split-K (deep-ring tiles only): `split` workgroups share one output tile, each over K/split;
-  // each writes its fp32 partial to part[(tile*split + s) * BM*BN] and the last to arrive (per
-  // cnt[tile], zero on entry and left zero) sums the partials in split order and runs the epilogue.
-  // part_cap / cnt_cap: bytes and counters available; a split that does not fit runs unsplit.
+  // split-K (deep-ring tiles only): `split` workgroups share one output tile, each over its
+  // share of K, and write fp32 partials to part[(tile*split + s) * BM*BN] (fragment order); a
+  // second kernel adds them in split order and runs the epilogue.  part_cap: bytes available; a
+  // split that does not fit runs unsplit.
   int split;
   float* part;
-  int* cnt;
   size_t part_cap;
-  int cnt_cap;
 };
 
 // Epilogue selectors and their parameters.
@@ -151,18 +147,20 @@ hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, v
                           int rows, int H, float eps, int block_len, int n_anchor, hipStream_t s);
 // cfg: bf16 block-tile configuration index (see dbd_gemm_nt in dbd.h), -1 = pick for the shape
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
-                       hipStream_t s, int cfg = -1);
+                       hipStream_t s, int cfg = -1, int split = 0);
 // What launch_gemm does for a problem: the tile configuration (-1 on the fp32 path), its column
 // tile width, the split-K factor (1 unless split_ok: a partial buffer and counters are given),
 // the output tiles over the batch and the partial-buffer bytes.  pair = the A operand comes as a
 // bf16 pair.  The workspace sizing and the launch both use it, so they agree.
+// split_req: 0 = the library's choice, 1 = no split, S > 1 = S-way split.
 struct GemmPlan {
   int cfg, bn, split, tiles;
   size_t part_bytes;
 };
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
-                   int F, bool pair, bool split_ok);
+                   int F, bool pair, bool split_ok, int split_req = 0);
 constexpr int kMaxGemmCfg = 16;
+constexpr int kMaxGemmSplit = 16;
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
 hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,
                                   int ntiles, const int32_t* blk_pos, int block_len,

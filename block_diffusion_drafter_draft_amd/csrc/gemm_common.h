@@ -102,6 +102,9 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
   constexpr int TPR = NT / TM;                  // threads per tile row
   static_assert(NT % TM == 0 && BN % TPR == 0, "epilogue thread layout");
   constexpr int CPT = BN / TPR;                 // columns per thread
+  // SwiGLU stores 8 outputs from 16 columns, the rotations work on 16 columns at a time
+  static_assert((KIND != EPI_SWIGLU && KIND != EPI_QKV && KIND != EPI_CTXKV) || CPT % 16 == 0,
+                "epilogue columns per thread");
   __shared__ int s_pos[TM], s_seq[TM];
   const int tid = threadIdx.x;
   const int rows = min(TM, M - m0);

@@ -10,6 +10,7 @@
 // kernels (k_gemm_deep.hip) take the shapes where a deeper prefetch or split-K pays.
 // fp32 path: 64 x 128 x 16 block tile on the vector ALUs (exact fp32 products and sums).
 // All paths stage the finished tile in LDS as fp32 and run the same epilogue code over it.
+#include <algorithm>
 #include <cmath>
 
 #include "gemm_common.h"
@@ -287,21 +288,20 @@ static int pair_cfg(int cfg) {
 }
 
 // Split-K factor for a deep-ring tile, from a time estimate: rounds of 256 workgroups times the
-// time of one unit (a CU at about 1/256 of 1.9 PFLOP/s), plus the fp32 partials each split
-// writes and the last unit reads back (at about 5 TB/s), plus that last unit's own serial read
-// of the S partials of its tile (about 50 GB/s for one workgroup).  A unit keeps at least 4
-// k stages of 32.
+// time of one unit (a CU at about 1/256 of 1.9 PFLOP/s), plus the fp32 partials written and
+// read back (at about 5 TB/s) and the reduction kernel's launch (about 4 us).  A unit keeps at
+// least 4 k stages of 32.
 static int choose_split(int cfg, int M, int Nv, int K, int batch) {
   const double BM = kCfgBM[cfg], BN = kCfgBN[cfg];
   const double tiles = (double)ceil_div(M, kCfgBM[cfg]) * ceil_div(Nv, kCfgBN[cfg]) * batch;
-  const double cu_flops = 1.9e15 / 256, part_bw = 5e12, wg_bw = 50e9;
+  const double cu_flops = 1.9e15 / 256, part_bw = 5e12, launch_s = 4e-6;
   static const int cand[6] = {1, 2, 3, 4, 6, 8};
   int best = 1;
   double best_t = 0;
   for (int S : cand) {
     if (S > 1 && K / 32 / S < 4) break;
     double t = std::ceil(tiles * S / 256.0) * 2.0 * BM * BN * ((double)K / S) / cu_flops;
-    if (S > 1) t += tiles * S * BM * BN * 4.0 * 2.0 / part_bw + S * BM * BN * 4.0 / wg_bw;
+    if (S > 1) t += tiles * S * BM * BN * 4.0 * 2.0 / part_bw + launch_s;
     if (S == 1 || t < best_t) { best = S; best_t = t; }
   }
   return best;
@@ -348,8 +348,63 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
   return best;
 }
 
+// Time (us) of a tile choice, a model fitted to measurements on MI355X of the drafter's shapes
+// (M = 128 .. 512 rows, N = 2k .. 6k, K = 3.5k .. 19k, weights streamed from HBM, store and
+// residual epilogues; within about 10% of the measured time).  A unit (one workgroup) costs a
+// fixed start plus a time per k stage; the stage time is set by the bytes each CU pulls from L2
+// per stage, and units beyond one per CU share it: in whole rounds for the one-per-CU tiles (3,
+// 16), proportionally past 192 units for the 128 x 128 tile, two of which fit on a CU.  A split
+// adds the reduction kernel (its launch plus writing and reading the fp32 partials); without a
+// split the rotation and cache-scatter epilogues run inside the main kernel (about 4.2 us per
+// million outputs for Q/K/V, 1.3 for the context K/V).
+//   3: pipelined 64 x 128, 64-wide stages: 6.7 + 0.455 per stage
+//   10: four-wave 128 x 128, 32-wide stages: 5.3 + 0.356 per stage (x 1.5 with a bf16 pair A)
+//   16: register-staged eight-wave 256 x 128, 64-wide stages: 10.4 + 0.88 per stage
+static double model_us(int kind, int cfg, int M, int Nv, int K, int batch, int S, bool pair) {
+  const double units = (double)ceil_div(M, kCfgBM[cfg]) * ceil_div(Nv, kCfgBN[cfg]) * batch * S;
+  double t;
+  if (cfg == 10)
+    t = 5.3 + 0.356 * (pair ? 1.5 : 1.0) * (K / 32.0 / S) * std::max(1.0, units / 192.0);
+  else if (cfg == 16)
+    t = 10.4 + 0.88 * (K / 64.0 / S) * std::ceil(units / 256.0);
+  else
+    t = 6.7 + 0.455 * (K / 64.0) * std::ceil(units / 256.0);
+  if (S > 1)
+    t += 1.5 + 0.36e-6 * units * kCfgBM[cfg] * kCfgBN[cfg] * 4.0;
+  else if (kind == EPI_QKV && is_deep(cfg))
+    t += 4.2e-6 * (double)M * Nv * batch;
+  else if (kind == EPI_CTXKV && is_deep(cfg))
+    t += 1.3e-6 * (double)M * Nv * batch;
+  return t;
+}
+
+// The library's tile and split: the heuristic tile of choose_cfg, and where that is the 64 x 128
+// or the 128 x 128 tile, the fastest under model_us of it and of the 128 x 128 and 256 x 128
+// (M >= 192, no bf16 pair) tiles with splits of 2 .. 8 (each unit keeps at least 4 stages of
+// 32, or 2 of 64).
+struct TileChoice {
+  int cfg, split;
+};
+static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gateup, int F,
+                              bool pair) {
+  const int base = choose_cfg(kind, M, N, K, batch, gateup, F, pair);
+  if (gateup || (base != 3 && base != 10)) return {base, 1};
+  TileChoice best{base, 1};
+  double best_t = model_us(kind, base, M, N, K, batch, 1, pair);
+  static const int cand[6] = {1, 2, 3, 4, 6, 8};
+  for (int cfg : {10, 16}) {
+    if (cfg == 16 && (pair || M < 192)) continue;
+    for (int S : cand) {
+      if (cfg == 10 ? K / 32 / S < 4 : K / 64 / S < 2) break;
+      const double t = model_us(kind, cfg, M, N, K, batch, S, pair);
+      if (t < best_t) { best = {cfg, S}; best_t = t; }
+    }
+  }
+  return best;
+}
+
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
-                   int F, bool pair, bool split_ok) {
+                   int F, bool pair, bool split_ok, int split_req) {
   GemmPlan p{};
   p.split = 1;
   if (dtype != 1) {
@@ -361,7 +416,12 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
   // boundaries (multiples of 128)
   const bool n128 = kind == EPI_QKV || kind == EPI_CTXKV;
   const bool chosen = cfg >= 0 && cfg < kNumCfg;
-  if (!chosen) cfg = choose_cfg(kind, M, N, K, batch, gateup, F, pair);
+  int lib_split = 1;
+  if (!chosen) {
+    const TileChoice c = choose_tile(kind, M, N, K, batch, gateup, F, pair);
+    cfg = c.cfg;
+    lib_split = c.split;
+  }
   if (n128 && kCfgBN[cfg] != 128)
     cfg = cfg >= 14 ? 16 : cfg >= 11 ? 13 : is_deep(cfg) ? (kCfgBM[cfg] == 256 ? 8 : 10)
                                         : (kCfgBM[cfg] == 256 ? 1 : 4);
@@ -369,22 +429,28 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
   auto nvirt = [&](int c) { return gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N; };
   p.cfg = cfg;
   p.bn = kCfgBN[cfg];
-  // the library's own choice of an eight-wave tile already fills the chip: no split
-  if (is_deep(cfg) && split_ok && (chosen || cfg < 11))
-    p.split = choose_split(cfg, M, nvirt(cfg), K, batch);
+  if (is_deep(cfg) && split_ok) {
+    if (split_req > 1) {
+      // a requested split keeps each unit at least one k stage
+      p.split = std::min(split_req, std::max(1, K / 64));
+    } else if (split_req == 0) {
+      // the library's own tile comes with its split; a caller's tile gets the generic estimate
+      p.split = chosen ? choose_split(cfg, M, nvirt(cfg), K, batch) : lib_split;
+    }
+  }
   p.tiles = ceil_div(M, kCfgBM[cfg]) * ceil_div(nvirt(cfg), kCfgBN[cfg]) * batch;
   p.part_bytes = p.split > 1 ? (size_t)p.tiles * p.split * kCfgBM[cfg] * kCfgBN[cfg] * 4 : 0;
   return p;
 }
 
 template <int KIND>
-static void launch_kind(int dtype, int cfg, GemmArgs a, const EpiArgs& e, int batch,
+static void launch_kind(int dtype, int cfg, int split, GemmArgs a, const EpiArgs& e, int batch,
                         hipStream_t s) {
   if (dtype == 1) {
     const int F = a.seg[0].n1 - a.seg[0].n0;
     GemmPlan p = plan_gemm(dtype, KIND, cfg, a.M, a.N, a.K, batch, a.gateup, F,
-                           a.A2 != nullptr, a.part != nullptr && a.cnt != nullptr);
-    if (p.split > 1 && (p.part_bytes > a.part_cap || p.tiles > a.cnt_cap)) p.split = 1;
+                           a.A2 != nullptr, a.part != nullptr, split);
+    if (p.split > 1 && p.part_bytes > a.part_cap) p.split = 1;
     a.split = p.split;
     if (a.A2) launch_cfg<KIND, true>(p.cfg, a, e, batch, s);
     else launch_cfg<KIND, false>(p.cfg, a, e, batch, s);
@@ -396,15 +462,15 @@ static void launch_kind(int dtype, int cfg, GemmArgs a, const EpiArgs& e, int ba
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
-                       hipStream_t s, int cfg) {
+                       hipStream_t s, int cfg, int split) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   switch (e.kind) {
-    case EPI_STORE_F32: launch_kind<EPI_STORE_F32>(dtype, cfg, a, e, batch, s); break;
-    case EPI_RESID: launch_kind<EPI_RESID>(dtype, cfg, a, e, batch, s); break;
-    case EPI_QKV: launch_kind<EPI_QKV>(dtype, cfg, a, e, batch, s); break;
-    case EPI_CTXKV: launch_kind<EPI_CTXKV>(dtype, cfg, a, e, batch, s); break;
-    case EPI_SWIGLU: launch_kind<EPI_SWIGLU>(dtype, cfg, a, e, batch, s); break;
-    case EPI_ARGMAX: launch_kind<EPI_ARGMAX>(dtype, cfg, a, e, batch, s); break;
+    case EPI_STORE_F32: launch_kind<EPI_STORE_F32>(dtype, cfg, split, a, e, batch, s); break;
+    case EPI_RESID: launch_kind<EPI_RESID>(dtype, cfg, split, a, e, batch, s); break;
+    case EPI_QKV: launch_kind<EPI_QKV>(dtype, cfg, split, a, e, batch, s); break;
+    case EPI_CTXKV: launch_kind<EPI_CTXKV>(dtype, cfg, split, a, e, batch, s); break;
+    case EPI_SWIGLU: launch_kind<EPI_SWIGLU>(dtype, cfg, split, a, e, batch, s); break;
+    case EPI_ARGMAX: launch_kind<EPI_ARGMAX>(dtype, cfg, split, a, e, batch, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -28,7 +28,6 @@ __global__ void prep_kernel(const int32_t* __restrict__ ctx_len,
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int nblk = batch * block_len;
   const int64_t total = (int64_t)(nblk + n_new_total) * half;
-  if (gid < meta.n_gemm_cnt) meta.gemm_cnt[gid] = 0;
   if (gid < batch) {
     int P;
     bool ok = seq_ok(ctx_len, off, (int)gid, block_len, n_new_total, cap, &P);
@@ -80,7 +79,6 @@ hipError_t launch_prep(const int32_t* ctx_len, const int32_t* new_offsets, int b
   for (int i = 0; i < 64; ++i) fq.v[i] = i < half ? inv_freq[i] : 0.0;
   int64_t total = (int64_t)(batch * block_len + n_new_total) * half;
   if (total < batch) total = batch;
-  if (total < meta.n_gemm_cnt) total = meta.n_gemm_cnt;
   const int threads = 256;
   const int blocks = (int)ceil_div64(total, threads);
   hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(threads), 0, s, ctx_len, new_offsets, batch,

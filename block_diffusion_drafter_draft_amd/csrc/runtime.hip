@@ -85,6 +85,12 @@ int elem_size(int dtype) { return dtype == DBD_BF16 ? 2 : 4; }
 
 int attn_split(int dtype) { return dtype == DBD_BF16 ? 512 : 256; }
 
+// Per-stage GEMM tile / split overrides (dbd_gemm_override), indexed by DBD_STAGE_*: -1 / 0 =
+// the library's choice.
+static int g_ov_cfg[DBD_STAGE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+static int g_ov_split[DBD_STAGE_COUNT] = {};
+static bool bad_split(int32_t split) { return split < 0 || split > kMaxGemmSplit; }
+
 struct DraftBufs {
   RowMeta meta;
   void* ctxfeat;
@@ -150,33 +156,32 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.s_max = ceil_div(cap, t.split);
   t.part_o = c.take<float>((int64_t)N * d.n_kv_heads * t.s_max * R * d.head_dim);
   t.part_ml = c.take<float2>((int64_t)N * d.n_kv_heads * t.s_max * R);
-  // split-K partials and tile counters: the largest need over the step's GEMMs
+  // split-K partials: the largest need over the step's GEMMs
   {
     const bool pr = d.dtype == DBD_BF16 && d.act_pairs;
     const int kd = d.n_kv_heads * d.head_dim;
     GemmPlan pl[6];
     int np = 0;
-    pl[np++] = plan_gemm(d.dtype, EPI_QKV, -1, (int)M, qd + 2 * kd, d.hidden, 1, 0, 0, pr, true);
-    pl[np++] = plan_gemm(d.dtype, EPI_RESID, -1, (int)M, d.hidden, qd, 1, 0, 0, pr, true);
-    pl[np++] = plan_gemm(d.dtype, EPI_SWIGLU, -1, (int)M, 2 * d.ffn, d.hidden, 1, 1, d.ffn, pr,
-                         true);
-    pl[np++] = plan_gemm(d.dtype, EPI_RESID, -1, (int)M, d.hidden, d.ffn, 1, 0, 0, pr, true);
-    pl[np++] = plan_gemm(d.dtype, temperature > 0.f ? EPI_STORE_F32 : EPI_ARGMAX, -1, (int)Md,
-                         d.vocab, d.hidden, 1, 0, 0, pr, true);
+    pl[np++] = plan_gemm(d.dtype, EPI_QKV, g_ov_cfg[DBD_STAGE_GEMM_QKV], (int)M, qd + 2 * kd,
+                         d.hidden, 1, 0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_QKV]);
+    pl[np++] = plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_O], (int)M, d.hidden, qd, 1,
+                         0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_O]);
+    pl[np++] = plan_gemm(d.dtype, EPI_SWIGLU, g_ov_cfg[DBD_STAGE_GEMM_GATEUP], (int)M, 2 * d.ffn,
+                         d.hidden, 1, 1, d.ffn, pr, true, g_ov_split[DBD_STAGE_GEMM_GATEUP]);
+    pl[np++] = plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_DOWN], (int)M, d.hidden, d.ffn,
+                         1, 0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_DOWN]);
+    pl[np++] = plan_gemm(d.dtype, temperature > 0.f ? EPI_STORE_F32 : EPI_ARGMAX,
+                         g_ov_cfg[DBD_STAGE_GEMM_LMHEAD], (int)Md, d.vocab, d.hidden, 1, 0, 0,
+                         pr, true, g_ov_split[DBD_STAGE_GEMM_LMHEAD]);
     if (d.n_target_layers > 0 && T > 0)
-      pl[np++] = plan_gemm(d.dtype, EPI_CTXKV, -1, T, 2 * kd, d.hidden, d.n_layers, 0, 0,
-                           d.dtype == DBD_BF16, true);
+      pl[np++] = plan_gemm(d.dtype, EPI_CTXKV, g_ov_cfg[DBD_STAGE_GEMM_CTXKV], T, 2 * kd,
+                           d.hidden, d.n_layers, 0, 0, d.dtype == DBD_BF16, true,
+                           g_ov_split[DBD_STAGE_GEMM_CTXKV]);
     size_t part = 0;
-    int cnt = 0;
     for (int i = 0; i < np; ++i)
-      if (pl[i].split > 1) {
-        part = part > pl[i].part_bytes ? part : pl[i].part_bytes;
-        cnt = cnt > pl[i].tiles ? cnt : pl[i].tiles;
-      }
+      if (pl[i].split > 1) part = part > pl[i].part_bytes ? part : pl[i].part_bytes;
     t.gemm_part = part ? (float*)c.take<char>((int64_t)part) : nullptr;
     t.gemm_part_bytes = part;
-    t.meta.gemm_cnt = cnt ? c.take<int32_t>(cnt) : nullptr;
-    t.meta.n_gemm_cnt = cnt;
     t.ntiles = ceil_div(d.vocab, pl[4].bn);
   }
   const int64_t max_tiles = ceil_div(d.vocab, 128);          // any configuration fits
@@ -264,6 +269,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 extern "C" {
 
 const char* dbd_last_error(void) { return g_err.c_str(); }
+
+int dbd_gemm_override(int32_t stage, int32_t tile_cfg, int32_t split) {
+  g_err.clear();
+  const bool gemm = stage == DBD_STAGE_GEMM_CTXKV || stage == DBD_STAGE_GEMM_QKV ||
+                    stage == DBD_STAGE_GEMM_O || stage == DBD_STAGE_GEMM_GATEUP ||
+                    stage == DBD_STAGE_GEMM_DOWN || stage == DBD_STAGE_GEMM_LMHEAD;
+  if (!gemm) return fail(DBD_ERR_ARG, "stage %d is not a GEMM stage", stage);
+  if (tile_cfg < -1 || tile_cfg > kMaxGemmCfg)
+    return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, %d]", tile_cfg, kMaxGemmCfg);
+  if (bad_split(split))
+    return fail(DBD_ERR_ARG, "split %d out of [0, %d]", split, kMaxGemmSplit);
+  g_ov_cfg[stage] = tile_cfg;
+  g_ov_split[stage] = split;
+  return DBD_OK;
+}
 
 int dbd_timing_enable(int on) {
   g_err.clear();
@@ -378,9 +398,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
                                                     ctx_lo, d.rms_eps, st));
     GemmArgs g{};
     g.part = b.gemm_part;
-    g.cnt = b.meta.gemm_cnt;
     g.part_cap = b.gemm_part_bytes;
-    g.cnt_cap = b.meta.n_gemm_cnt;
     g.A = b.ctxfeat;
     g.A2 = ctx_lo;
     g.lda = H;
@@ -408,7 +426,8 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     e.row_seq = b.meta.ctx_seq;
     e.row_pos = b.meta.ctx_pos;
     e.rope = b.meta.rope_ctx;
-    HIP_STAGE(DBD_STAGE_GEMM_CTXKV, st, launch_gemm(d.dtype, g, e, d.n_layers, st));
+    HIP_STAGE(DBD_STAGE_GEMM_CTXKV, st, launch_gemm(d.dtype, g, e, d.n_layers, st, g_ov_cfg[DBD_STAGE_GEMM_CTXKV],
+                                                  g_ov_split[DBD_STAGE_GEMM_CTXKV]));
   }
 
   // 2. block forward
@@ -423,9 +442,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     {
       GemmArgs g{};
       g.part = b.gemm_part;
-      g.cnt = b.meta.gemm_cnt;
       g.part_cap = b.gemm_part_bytes;
-      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.xn;
       g.A2 = b.xn_lo;
       g.lda = H;
@@ -452,7 +469,8 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.cap = ctx_capacity;
       e.row_pos = b.meta.blk_pos;
       e.rope = b.meta.rope_blk;
-      HIP_STAGE(DBD_STAGE_GEMM_QKV, st, launch_gemm(d.dtype, g, e, 1, st));
+      HIP_STAGE(DBD_STAGE_GEMM_QKV, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_QKV],
+                                                  g_ov_split[DBD_STAGE_GEMM_QKV]));
     }
     {
       AttnArgs a{};
@@ -478,9 +496,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     {
       GemmArgs g{};
       g.part = b.gemm_part;
-      g.cnt = b.meta.gemm_cnt;
       g.part_cap = b.gemm_part_bytes;
-      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.attn;
       g.A2 = b.attn_lo;
       g.lda = qd;
@@ -494,16 +510,15 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.kind = EPI_RESID;
       e.C = b.x;
       e.ldc = H;
-      HIP_STAGE(DBD_STAGE_GEMM_O, st, launch_gemm(d.dtype, g, e, 1, st));
+      HIP_STAGE(DBD_STAGE_GEMM_O, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_O],
+                                                  g_ov_split[DBD_STAGE_GEMM_O]));
     }
     HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->mlp_norm_w, H), b.xn, b.xn_lo, M, H,
                                                      d.rms_eps, B, 0, st));
     {
       GemmArgs g{};
       g.part = b.gemm_part;
-      g.cnt = b.meta.gemm_cnt;
       g.part_cap = b.gemm_part_bytes;
-      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.xn;
       g.A2 = b.xn_lo;
       g.lda = H;
@@ -520,14 +535,13 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.act = b.act;
       e.act_lo = b.act_lo;
       e.F = F;
-      HIP_STAGE(DBD_STAGE_GEMM_GATEUP, st, launch_gemm(d.dtype, g, e, 1, st));
+      HIP_STAGE(DBD_STAGE_GEMM_GATEUP, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_GATEUP],
+                                                  g_ov_split[DBD_STAGE_GEMM_GATEUP]));
     }
     {
       GemmArgs g{};
       g.part = b.gemm_part;
-      g.cnt = b.meta.gemm_cnt;
       g.part_cap = b.gemm_part_bytes;
-      g.cnt_cap = b.meta.n_gemm_cnt;
       g.A = b.act;
       g.A2 = b.act_lo;
       g.lda = F;
@@ -541,7 +555,8 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.kind = EPI_RESID;
       e.C = b.x;
       e.ldc = H;
-      HIP_STAGE(DBD_STAGE_GEMM_DOWN, st, launch_gemm(d.dtype, g, e, 1, st));
+      HIP_STAGE(DBD_STAGE_GEMM_DOWN, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_DOWN],
+                                                  g_ov_split[DBD_STAGE_GEMM_DOWN]));
     }
   }
   (void)cw;
@@ -554,9 +569,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   {
     GemmArgs g{};
     g.part = b.gemm_part;
-    g.cnt = b.meta.gemm_cnt;
     g.part_cap = b.gemm_part_bytes;
-    g.cnt_cap = b.meta.n_gemm_cnt;
     g.A = b.xn;
     g.A2 = b.xn_lo;
     g.lda = H;
@@ -579,7 +592,8 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.logits = logits;
       e.ldc = V;
     }
-    HIP_STAGE(DBD_STAGE_GEMM_LMHEAD, st, launch_gemm(d.dtype, g, e, 1, st));
+    HIP_STAGE(DBD_STAGE_GEMM_LMHEAD, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_LMHEAD],
+                                                  g_ov_split[DBD_STAGE_GEMM_LMHEAD]));
   }
   // 4. drafts
   if (!sampling) {
@@ -782,32 +796,28 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
   return DBD_OK;
 }
 
-static size_t gemm_ws_layout(int dtype, int M, int N, int K, int cfg, size_t* part_off,
-                             int* ncnt) {
-  const GemmPlan p = plan_gemm(dtype, EPI_STORE_F32, cfg, M, N, K, 1, 0, 0, false, true);
-  if (p.split <= 1) { *ncnt = 0; *part_off = 0; return 0; }
-  *ncnt = p.tiles;
-  *part_off = ((size_t)p.tiles * 4 + kAlign - 1) / kAlign * kAlign;
-  return *part_off + p.part_bytes;
+static size_t gemm_ws_bytes(int dtype, int M, int N, int K, int cfg, int split) {
+  const GemmPlan p = plan_gemm(dtype, EPI_STORE_F32, cfg, M, N, K, 1, 0, 0, false, true, split);
+  return p.split > 1 ? p.part_bytes : 0;
 }
 
 int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t tile_cfg,
-                             size_t* bytes) {
+                             int32_t split, size_t* bytes) {
   g_err.clear();
   if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
   if (dtype != DBD_F32 && dtype != DBD_BF16) return fail(DBD_ERR_ARG, "bad dtype");
   if (M < 0 || N < 0 || K < 1) return fail(DBD_ERR_SHAPE, "bad GEMM dimensions");
   if (tile_cfg < -1 || tile_cfg > kMaxGemmCfg)
     return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, %d]", tile_cfg, kMaxGemmCfg);
-  size_t off;
-  int ncnt;
-  *bytes = M > 0 && N > 0 ? gemm_ws_layout(dtype, M, N, K, tile_cfg, &off, &ncnt) : 0;
+  if (bad_split(split))
+    return fail(DBD_ERR_ARG, "split %d out of [0, %d]", split, kMaxGemmSplit);
+  *bytes = M > 0 && N > 0 ? gemm_ws_bytes(dtype, M, N, K, tile_cfg, split) : 0;
   return DBD_OK;
 }
 
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t M, int32_t N,
                 int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                int32_t split, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (dtype != DBD_F32 && dtype != DBD_BF16) return fail(DBD_ERR_ARG, "bad dtype");
   if (!A || !Bm || !C) return fail(DBD_ERR_ARG, "a required device pointer is NULL");
@@ -817,6 +827,8 @@ int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t 
     return fail(DBD_ERR_SHAPE, "bf16 GEMM needs K % 64 == 0, 16-byte aligned rows");
   if (tile_cfg < -1 || tile_cfg > kMaxGemmCfg)
     return fail(DBD_ERR_ARG, "tile_cfg %d out of [-1, %d]", tile_cfg, kMaxGemmCfg);
+  if (bad_split(split))
+    return fail(DBD_ERR_ARG, "split %d out of [0, %d]", split, kMaxGemmSplit);
   GemmArgs g{};
   g.A = A;
   g.lda = lda;
@@ -832,23 +844,16 @@ int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t 
   e.ldc = ldc;
   hipStream_t st = (hipStream_t)stream;
   if (workspace && M > 0 && N > 0) {
-    size_t off;
-    int ncnt;
-    const size_t need = gemm_ws_layout(dtype, M, N, K, tile_cfg, &off, &ncnt);
+    const size_t need = gemm_ws_bytes(dtype, M, N, K, tile_cfg, split);
     if ((uintptr_t)workspace % kAlign)
       return fail(DBD_ERR_WORKSPACE, "workspace not 256-byte aligned");
     if (workspace_bytes < need)
       return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
                   need);
-    if (ncnt > 0) {
-      g.cnt = (int*)workspace;
-      g.part = (float*)((char*)workspace + off);
-      g.cnt_cap = ncnt;
-      g.part_cap = need - off;
-      HIP_TRY(launch_fill_i32(g.cnt, ncnt, 0, st));
-    }
+    g.part = (float*)workspace;
+    g.part_cap = workspace_bytes;
   }
-  HIP_TRY(launch_gemm(dtype, g, e, 1, st, tile_cfg));
+  HIP_TRY(launch_gemm(dtype, g, e, 1, st, tile_cfg, split));
   return DBD_OK;
 }
 

@@ -227,10 +227,10 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
                     const void* hidden, int64_t hid_token_stride, int64_t hid_layer_stride,
                     int32_t n_tokens, void* out, void* stream);
 
-/* Workspace size (host) for dbd_gemm_nt with the same dtype, shape and tile_cfg: the split-K
- * partials and tile counters of the configuration (0 when it does not split K). */
+/* Workspace size (host) for dbd_gemm_nt with the same dtype, shape, tile_cfg and split: the
+ * split-K partials of the configuration (0 when it does not split K). */
 int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t tile_cfg,
-                             size_t* bytes);
+                             int32_t split, size_t* bytes);
 
 /* The GEMM used for every projection: C[M, N] (fp32) = A[M, K] . B[N, K]^T with A, B in
  * `dtype`; row strides lda, ldb, ldc in elements.  bf16 needs K % 64 == 0 and 16-byte aligned
@@ -240,11 +240,14 @@ int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int
  * 9: 128x256/3, 10: 128x128/4; 8 waves, 64-wide k stages: 11: 256x256/2, 12: 256x192/2,
  * 13: 256x128/3) which splits K over several workgroups when `workspace` is given (NULL: no
  * split); 14-16 the 8-wave tiles 256x256, 256x192, 256x128 staged through registers instead of
- * global->LDS DMA (same split rule); -1: the library's choice.  The
- * workspace (dbd_gemm_workspace_bytes, 256-byte aligned) is used only by this call. */
+ * global->LDS DMA (same split rule); -1: the library's choice.  split (deep-ring tiles with a
+ * workspace only; in [0, 16]): 0 the library's choice, 1 no split, S > 1 K split over S
+ * workgroups per output tile whose fp32 partials a second kernel adds, in split order, with
+ * several workgroups per tile; a split is capped at K / 64.  The workspace
+ * (dbd_gemm_workspace_bytes, 256-byte aligned) is used only by this call. */
 int dbd_gemm_nt(int32_t dtype, const void* A, const void* B, float* C, int32_t M, int32_t N,
                 int32_t K, int64_t lda, int64_t ldb, int64_t ldc, int32_t tile_cfg,
-                void* workspace, size_t workspace_bytes, void* stream);
+                int32_t split, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-stage timing for benchmarks.  While enabled, every kernel launch of the library is
  * bracketed by a pair of hipEvents recorded on the launch's stream and accounted to its stage
@@ -270,6 +273,14 @@ enum {
 int dbd_timing_enable(int on);
 int dbd_timing_reset(void);
 int dbd_timing_read(int stage, double* total_ms /* host out */, int64_t* launches /* host out */);
+
+/* Tile tuning: replaces the library's choice of bf16 block tile and split-K (tile_cfg and split
+ * as in dbd_gemm_nt; -1 and 0 restore the library's choice) for one GEMM stage of draft_block
+ * (DBD_STAGE_GEMM_*), process-wide.  dbd_draft_workspace_bytes sizes the split partials from
+ * the same choice, so set it before sizing a workspace; a workspace sized before the change may
+ * run the stage unsplit.  Not thread-safe; meant for benchmarks.  Returns DBD_ERR_ARG for a
+ * stage that is not a GEMM or an out-of-range tile_cfg / split. */
+int dbd_gemm_override(int32_t stage, int32_t tile_cfg, int32_t split);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* dbd_last_error(void);

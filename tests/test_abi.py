@@ -187,26 +187,59 @@ def test_sample_validation():
 def test_gemm_validation():
     L = dbd.lib()
     fake = 1 << 20
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, None, 0, None) == -2
-    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, None, 0, None) == -2  # lda<K
-    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, None, 0, None) == -1
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 17, None, 0, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, 0, None, 0, None) == -2
+    assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, 0, None, 0, None) == -2
+    assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, 0, None, 0, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 17, 0, None, 0, None) == -1
+    for bad in (17, -1):
+        assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 8, bad, None, 0, None) == -1
+        with pytest.raises(dbd.DbdError):
+            dbd.gemm_workspace_bytes(dbd.DBD_BF16, 4, 4, 64, 8, bad)
     # a split-K shape with a workspace that is too small, or misaligned
     need = dbd.gemm_workspace_bytes(dbd.DBD_BF16, 512, 4096, 4096, 8)
     assert need > 0
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 512, 4096, 4096, 4096, 4096, 4096, 8, fake,
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 512, 4096, 4096, 4096, 4096, 4096, 8, 0, fake,
                          need - 1, None) == -4
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 512, 4096, 4096, 4096, 4096, 4096, 8, fake + 16,
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 512, 4096, 4096, 4096, 4096, 4096, 8, 0, fake + 16,
                          need, None) == -4
     assert dbd.gemm_workspace_bytes(dbd.DBD_F32, 512, 4096, 4096) == 0
 
 
+def test_gemm_requested_split_sizes_workspace():
+    """A requested split S sizes one fp32 tile per (output tile, split); no split and the
+    pipelined tiles need nothing; a split is capped at K / 64."""
+    M, N, K = 512, 4096, 12288
+    for S in (2, 3, 4, 8, 16):
+        assert dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, 11, S) == 2 * 16 * S * 256 * 256 * 4
+    assert dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, 11, 1) == 0
+    assert dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, 3, 4) == 0
+    assert dbd.gemm_workspace_bytes(dbd.DBD_BF16, 256, 256, 128, 11, 8) == 2 * 256 * 256 * 4
+
+
 def test_gemm_split_plan_fits_workspace():
     """Split-K partials are sized by the same plan the launch uses: for every deep tile the
-    workspace holds one fp32 tile per (output tile, split) and one counter per tile."""
+    workspace holds one fp32 tile per (output tile, split)."""
     for M, N, K in [(512, 4096, 4096), (512, 4096, 12288), (128, 2048, 4096), (16, 6144, 4096)]:
         for cfg in range(8, 17):
             b = dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, cfg)
             assert b % 4 == 0
             if b:
                 assert b >= 128 * 128 * 4 * 2
+
+
+def test_gemm_override_validation():
+    L = dbd.lib()
+    assert L.dbd_gemm_override(5, -1, 0) == -1          # attention is not a GEMM stage
+    assert L.dbd_gemm_override(4, 17, 0) == -1
+    assert L.dbd_gemm_override(4, 10, 17) == -1
+    # an override changes the planned split partials, and -1 / 0 restore the default
+    sh = synth.workload("qwen3-8b").shape
+    desc = dbd.model_desc(sh)
+    base = dbd.draft_workspace_bytes(desc, 32, 16, 1, 64, 1, 0.0, 4096)
+    dbd.gemm_override("gemm_down", 11, 8)
+    try:
+        # 2 x 16 output tiles of 256 x 256, 8 fp32 partials each: more than any default plan
+        assert dbd.draft_workspace_bytes(desc, 32, 16, 1, 64, 1, 0.0, 4096) > base
+    finally:
+        dbd.gemm_override("gemm_down")
+    assert dbd.draft_workspace_bytes(desc, 32, 16, 1, 64, 1, 0.0, 4096) == base

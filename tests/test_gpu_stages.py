@@ -35,7 +35,7 @@ def test_gemm_nt(dtype, M, N, K):
 def test_gemm_nt_tile_configs(cfg, M, N, K):
     """Every bf16 tile configuration, with a workspace so the deep-ring tiles split K where
     their plan does; two calls in a row must agree bit for bit (the split partials are summed in
-    split order and the tile counters are left at zero)."""
+    split order)."""
     print(f"gemm cfg={cfg} M={M} N={N} K={K}", flush=True)
     g = torch.Generator(device=DEV).manual_seed(cfg * 131 + M + N + K)
     A = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
@@ -46,6 +46,29 @@ def test_gemm_nt_tile_configs(cfg, M, N, K):
     C2 = torch.full((M, N), float("nan"), device=DEV)
     dbd.gemm_nt(A, B, C1, tile_cfg=cfg, workspace=ws)
     dbd.gemm_nt(A, B, C2, tile_cfg=cfg, workspace=ws)
+    torch.cuda.synchronize()
+    ref = od.f64(A) @ od.f64(B).T
+    assert rel_l2(C1.cpu().numpy(), ref) < 1e-5
+    assert torch.equal(C1, C2)
+
+
+@pytest.mark.parametrize("cfg", list(range(8, 17)))
+@pytest.mark.parametrize("split", [2, 3, 5, 16])
+@pytest.mark.parametrize("M,N,K", [(235, 1000, 2560), (512, 640, 4096)])
+def test_gemm_nt_requested_split(cfg, split, M, N, K):
+    """A requested split-K (partials added by the second kernel) over ragged M, N and k ranges
+    that do not divide evenly; two calls in a row agree bit for bit."""
+    print(f"gemm cfg={cfg} split={split} M={M} N={N} K={K}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(cfg * 37 + split * 5 + M + K)
+    A = torch.randn((M, K), generator=g, device=DEV).to(torch.bfloat16)
+    B = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    wb = dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, cfg, split)
+    assert wb > 0
+    ws = torch.empty(wb, dtype=torch.uint8, device=DEV)
+    C1 = torch.full((M, N), float("nan"), device=DEV)
+    C2 = torch.full((M, N), float("nan"), device=DEV)
+    dbd.gemm_nt(A, B, C1, tile_cfg=cfg, workspace=ws, split=split)
+    dbd.gemm_nt(A, B, C2, tile_cfg=cfg, workspace=ws, split=split)
     torch.cuda.synchronize()
     ref = od.f64(A) @ od.f64(B).T
     assert rel_l2(C1.cpu().numpy(), ref) < 1e-5
