@@ -341,28 +341,34 @@ __device__ void greedy_accept(const int32_t* t_s, const int32_t* draft, int D, i
     committed[j] = j < first ? draft[j] : (j == first ? b : -1);
 }
 
-__global__ __launch_bounds__(64) void verify_finalize_kernel(
+// One workgroup per sequence; wave w reduces rows w, w + VF_WAVES, ... (the rows' partial
+// reductions are independent, so they overlap instead of queueing behind each other's loads),
+// then wave 0 runs the acceptance.
+constexpr int VF_WAVES = 16;
+__global__ __launch_bounds__(64 * VF_WAVES) void verify_finalize_kernel(
     const float* pv, const int32_t* pi, const int32_t* pflag, int nch, const int32_t* drafts,
     int draft_stride, int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,
     int32_t* committed, int32_t* row_flags) {
   __shared__ int32_t t_s[128];
-  const int n = blockIdx.x;
+  __shared__ int s_bad;
+  const int n = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
   int bad = 0;
-  for (int j = 0; j < n_rows; ++j) {
+  for (int j = wave; j < n_rows; j += VF_WAVES) {
     float bv;
     int bi;
     const int64_t row = (int64_t)n * n_rows + j;
     reduce_partials(pv, pi, row, nch, bv, bi);
-    for (int c = threadIdx.x; c < nch; c += 64) bad |= pflag[row * nch + c];
-    if (threadIdx.x == 0) t_s[j] = bi;
+    for (int c = lane; c < nch; c += 64) bad |= pflag[row * nch + c];
+    if (lane == 0) t_s[j] = bi;
   }
+  if (__ballot(bad != 0) && lane == 0) atomicOr(&s_bad, 1);
   __syncthreads();
+  if (wave != 0) return;
   greedy_accept(t_s, drafts + (int64_t)n * draft_stride, n_draft, n_rows, n_acc + n, bonus + n,
                 committed + (int64_t)n * (n_draft + 1));
-  if (row_flags) {
-    const uint64_t m = __ballot(bad != 0);
-    if (threadIdx.x == 0) row_flags[n] = m ? 1 : 0;
-  }
+  if (row_flags && lane == 0) row_flags[n] = s_bad ? 1 : 0;
 }
 
 hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int32_t* pflag,
@@ -370,8 +376,9 @@ hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int3
                                   int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,
                                   int32_t* committed, int32_t* row_flags, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(verify_finalize_kernel, dim3(batch), dim3(64), 0, s, pv, pi, pflag, nch,
-                     drafts, draft_stride, n_draft, n_rows, n_acc, bonus, committed, row_flags);
+  hipLaunchKernelGGL(verify_finalize_kernel, dim3(batch), dim3(64 * VF_WAVES), 0, s, pv, pi,
+                     pflag, nch, drafts, draft_stride, n_draft, n_rows, n_acc, bonus, committed,
+                     row_flags);
   return hipGetLastError();
 }
 
