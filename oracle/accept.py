@@ -10,6 +10,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   greedy acceptance runs on it, reusing the cached verifier outputs.
 * Streak equation and acceptance rate (SpecDiff-2 notes, section 5.1): the expected accepted
   tokens per draft is E[sum_m prod_{j<=m} alpha_j]; alpha = 1 - (1/2)||P - Q||_1.
+* Lossless stochastic verification (SpecDiff-2 notes, sections 4 and 5.1): the
+  speculative-sampling rule on the integer weights, ``verify_sample``.
 
 Readings where the pages are silent (each listed with its reason in the design notes):
 * target row j scores the token at draft position j; with D+1 rows the last one gives the bonus
@@ -99,6 +101,90 @@ def select_streak(verifier_logits, drafts):
         a, b, c = greedy_accept_row_tokens(t, drafts[n, best], R)
         n_acc[n], bonus[n], committed[n] = a, b, c
     return selected, scores, n_acc, bonus, committed
+
+
+def spec_accept_token(qP, ZP: int, qQ, ZQ: int, x: int, u: int) -> bool:
+    """Accept draft token x with probability min(1, P(x)/Q(x)), P(x) = qP[x]/ZP, Q(x) = qQ[x]/ZQ,
+    for a uniform 32-bit draw u: accepted iff u/2^32 < P(x)/Q(x), i.e. in integers
+    u * qQ[x] * ZP < qP[x] * ZQ * 2^32.  A token outside the vocabulary has P = Q = 0 and is
+    rejected."""
+    V = len(qP)
+    px = int(qP[x]) if 0 <= x < V else 0
+    qx = int(qQ[x]) if 0 <= x < V else 0
+    return int(u) * qx * int(ZP) < px * int(ZQ) * (1 << 32)
+
+
+def residual_weights(qP, ZP: int, qQ, ZQ: int):
+    """Integer weights of norm(max(0, P - Q)): w_v = max(0, qP[v]*ZQ - qQ[v]*ZP), a common
+    multiple ZP*ZQ of P - Q (Python ints, exact)."""
+    return [max(0, int(a) * int(ZQ) - int(b) * int(ZP)) for a, b in zip(qP, qQ)]
+
+
+def sample_from_weights(w, u: int) -> int:
+    """R5 on arbitrary non-negative integer weights: the first v whose inclusive prefix sum
+    exceeds (u * W) >> 32, W = sum(w)."""
+    W = sum(int(a) for a in w)
+    thr = (int(u) * W) >> 32
+    run = 0
+    for v, a in enumerate(w):
+        run += int(a)
+        if run > thr:
+            return v
+    raise AssertionError("threshold beyond total mass")
+
+
+def verify_sample(target_logits, draft_logits, drafts, t_target: float, t_draft: float,
+                  seed: int):
+    """Lossless stochastic verification of one draft per sequence (SpecDiff-2 notes, section 4:
+    the verifier applies a lossless acceptance rule left to right; section 5.1: its accept rate
+    alpha_SD = sum_x min(P, Q)).  The rule is the speculative-sampling rule (Leviathan et al.,
+    2023), on the integer weights of ``dnc``:
+
+    for j = 0 .. D-1: P_j from target row j at t_target, Q_j from draft row j at t_draft; accept
+    x_j with probability min(1, P_j(x_j)/Q_j(x_j)) (draw (n, 0, j)).  At the first rejection the
+    replacement token is drawn (draw (n, 1, j)) from norm(max(0, P_j - Q_j)), or from P_j when
+    that is zero everywhere; the drafts before it and the replacement are committed.  If every
+    position is accepted and a target row D exists, a bonus token is drawn from P_D (draw
+    (n, 1, D)); with only D rows there is no bonus (-1).  Draws are R4 with K = 2 streams over
+    D + 1 positions.
+
+    target_logits [N, R, V] fp32 (R = D or D+1); draft_logits [N, D, V] fp32 (the drafter's
+    logits the drafts were sampled from); drafts [N, D] int.
+    Returns (n_acc [N], bonus [N], committed [N, D+1] padded with -1)."""
+    target_logits = np.asarray(target_logits, dtype=np.float32)
+    draft_logits = np.asarray(draft_logits, dtype=np.float32)
+    drafts = np.asarray(drafts)
+    N, R, V = target_logits.shape
+    D = drafts.shape[1]
+    assert R in (D, D + 1) and draft_logits.shape == (N, D, V)
+    inv_p = dnc.inv_temperature(t_target)
+    inv_q = dnc.inv_temperature(t_draft)
+    n_acc = np.zeros(N, np.int32)
+    bonus = np.full(N, -1, np.int32)
+    committed = np.full((N, D + 1), -1, np.int32)
+    for n in range(N):
+        a, b = D, -1
+        for j in range(D):
+            qP, ZP = dnc.row_weights(target_logits[n, j], inv_p)
+            qQ, ZQ = dnc.row_weights(draft_logits[n, j], inv_q)
+            x = int(drafts[n, j])
+            u = dnc.draw_u32(seed, n, 0, j, 2, D + 1)
+            if spec_accept_token(qP, ZP, qQ, ZQ, x, u):
+                continue
+            w = residual_weights(qP, ZP, qQ, ZQ)
+            if sum(w) == 0:
+                w = [int(c) for c in qP]
+            a, b = j, sample_from_weights(w, dnc.draw_u32(seed, n, 1, j, 2, D + 1))
+            break
+        else:
+            if R > D:
+                qP, ZP = dnc.row_weights(target_logits[n, D], inv_p)
+                b = sample_from_weights([int(c) for c in qP], dnc.draw_u32(seed, n, 1, D, 2, D + 1))
+        n_acc[n], bonus[n] = a, b
+        committed[n, :a] = drafts[n, :a]
+        if b >= 0:
+            committed[n, a] = b
+    return n_acc, bonus, committed
 
 
 # ---- helpers for the self-checks (SpecDiff-2 notes, section 5.1) ----

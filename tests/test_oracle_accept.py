@@ -193,3 +193,149 @@ def test_select_streak_planted_streaks():
         assert n_acc[n] == a[n, sel[n]]
         if n_acc[n] == G:
             assert bonus[n] == -1          # only G rows: no bonus after a full accept
+
+
+# ---- lossless stochastic verification (verify_sample) ----
+
+def _broadcast(row, N):
+    return np.broadcast_to(np.asarray(row, np.float32), (N,) + np.asarray(row).shape).copy()
+
+
+def _spec_case(seed, V=8, t_p=1.0, t_q=1.0):
+    rng = np.random.default_rng(seed)
+    lp = (rng.normal(size=V) * 1.5).astype(np.float32)
+    lq = (rng.normal(size=V) * 1.5).astype(np.float32)
+    return lp, lq
+
+
+def test_verify_sample_identical_P_and_Q_accept_everything():
+    """P = Q: the ratio is 1 at every drafted token, so every position is accepted whatever the
+    draw, and the bonus comes from row D."""
+    rng = np.random.default_rng(3)
+    N, D, V = 64, 5, 12
+    dl = (rng.normal(size=(N, D, V)) * 2).astype(np.float32)
+    tl = np.concatenate([dl, rng.normal(size=(N, 1, V)).astype(np.float32)], axis=1)
+    drafts = dnc.sample_drafts(dl, 1, 1.0, seed=11)[:, 0]
+    n_acc, bonus, committed = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=5)
+    assert (n_acc == D).all()
+    assert ((bonus >= 0) & (bonus < V)).all()
+    assert (committed[:, :D] == drafts).all() and (committed[:, D] == bonus).all()
+    # without a row D there is no bonus
+    n_acc, bonus, committed = accept.verify_sample(dl, dl, drafts, 1.0, 1.0, seed=5)
+    assert (n_acc == D).all() and (bonus == -1).all() and (committed[:, D] == -1).all()
+
+
+def test_verify_sample_accept_rate_is_sum_min_monte_carlo():
+    """Drafts x ~ Q (the DNC sampler), accepted with min(1, P/Q): the accept rate of one position
+    is sum_x min(P(x), Q(x)) (SpecDiff-2 notes, section 5.1), checked against the fp64 softmax
+    within 4 sigma."""
+    N, V = 20_000, 8
+    lp, lq = _spec_case(1, V)
+    tl, dl = _broadcast(lp, N)[:, None], _broadcast(lq, N)[:, None]
+    drafts = dnc.sample_drafts(dl, 1, 1.0, seed=21)[:, 0]
+    n_acc, bonus, _ = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=22)
+    a = accept.alpha_min(accept.softmax64(lp), accept.softmax64(lq))
+    rate = float(np.mean(n_acc == 1))
+    assert abs(rate - a) < 4 * np.sqrt(a * (1 - a) / N), (rate, a)
+
+
+@pytest.mark.parametrize("t_p,t_q", [(1.0, 1.0), (1.0, 1.5), (0.7, 1.0)])
+def test_verify_sample_output_is_distributed_as_P(t_p, t_q):
+    """Losslessness: the committed token of a one-position block (the accepted draft or the
+    replacement) is distributed as the target's P, whatever Q is: chi-square against the fp64
+    softmax of the target row at its temperature."""
+    from scipy import stats
+    N, V = 20_000, 8
+    lp, lq = _spec_case(2, V)
+    tl, dl = _broadcast(lp, N)[:, None], _broadcast(lq, N)[:, None]
+    drafts = dnc.sample_drafts(dl, 1, t_q, seed=31)[:, 0]
+    _, _, committed = accept.verify_sample(tl, dl, drafts, t_p, t_q, seed=32)
+    tok = committed[:, 0]
+    assert (tok >= 0).all()
+    P = accept.softmax64(lp, t_p)
+    counts = np.bincount(tok, minlength=V)
+    chi2 = float(((counts - N * P) ** 2 / (N * P)).sum())
+    assert chi2 < stats.chi2.ppf(1 - 1e-4, V - 1), chi2
+
+
+def test_verify_sample_second_position_and_bonus_are_distributed_as_P():
+    """Two positions and a bonus row, all target rows independent of the prefix: whenever
+    position 1 is committed it is distributed as P_1, and a bonus after a full accept as P_2."""
+    from scipy import stats
+    N, V = 30_000, 6
+    rng = np.random.default_rng(4)
+    lp = (rng.normal(size=(3, V)) * 1.2).astype(np.float32)
+    lq = (rng.normal(size=(2, V)) * 1.2).astype(np.float32)
+    tl, dl = _broadcast(lp, N), _broadcast(lq, N)
+    drafts = dnc.sample_drafts(dl, 1, 1.0, seed=41)[:, 0]
+    n_acc, bonus, committed = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=42)
+    for pos, row in ((1, 1), (2, 2)):
+        sel = n_acc >= pos
+        tok = committed[sel, pos]
+        P = accept.softmax64(lp[row])
+        counts = np.bincount(tok, minlength=V)
+        n = int(sel.sum())
+        chi2 = float(((counts - n * P) ** 2 / (n * P)).sum())
+        assert chi2 < stats.chi2.ppf(1 - 1e-4, V - 1), (pos, chi2)
+
+
+def test_verify_sample_residual_mass_is_total_variation_exactly():
+    """In integers, sum_v (qP_v ZQ - qQ_v ZP) = 0, so the residual mass W / (ZP ZQ) equals
+    1 - sum_v min(P_v, Q_v) = (1/2) sum_v |P_v - Q_v| exactly (rational arithmetic)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        V = int(rng.integers(2, 40))
+        qP, ZP = dnc.row_weights((rng.normal(size=V) * 3).astype(np.float32))
+        qQ, ZQ = dnc.row_weights((rng.normal(size=V) * 3).astype(np.float32), dnc.inv_temperature(1.5))
+        diff = [int(a) * ZQ - int(b) * ZP for a, b in zip(qP, qQ)]
+        assert sum(diff) == 0
+        W = sum(accept.residual_weights(qP, ZP, qQ, ZQ))
+        smin = sum(min(Fraction(int(a), ZP), Fraction(int(b), ZQ)) for a, b in zip(qP, qQ))
+        tv = sum(abs(Fraction(int(a), ZP) - Fraction(int(b), ZQ)) for a, b in zip(qP, qQ)) / 2
+        assert Fraction(W, ZP * ZQ) == 1 - smin == tv
+
+
+def test_verify_sample_disjoint_supports_always_reject_and_resample_P():
+    """Q's mass only on tokens where P is zero: every draft is rejected at position 0 and the
+    replacement comes from P's support."""
+    N, V = 500, 4
+    lp = np.array([0.0, 0.3, -1e4, -1e4], np.float32)
+    lq = np.array([-1e4, -1e4, 0.0, -0.2], np.float32)
+    tl, dl = _broadcast(lp, N)[:, None], _broadcast(lq, N)[:, None]
+    drafts = dnc.sample_drafts(dl, 1, 1.0, seed=51)[:, 0]
+    assert set(drafts[:, 0].tolist()) <= {2, 3}
+    n_acc, bonus, committed = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=52)
+    assert (n_acc == 0).all()
+    assert set(bonus.tolist()) == {0, 1}
+    assert (committed[:, 0] == bonus).all() and (committed[:, 1] == -1).all()
+
+
+def test_verify_sample_accept_test_by_hand():
+    """u * qQ[x] * ZP < qP[x] * ZQ * 2^32 at its boundary, and out-of-vocabulary tokens."""
+    qP, ZP = [1, 3], 4                      # P = (1/4, 3/4)
+    qQ, ZQ = [1, 1], 2                      # Q = (1/2, 1/2): P(0)/Q(0) = 1/2
+    half = 1 << 31
+    assert accept.spec_accept_token(qP, ZP, qQ, ZQ, 0, half - 1)
+    assert not accept.spec_accept_token(qP, ZP, qQ, ZQ, 0, half)
+    assert accept.spec_accept_token(qP, ZP, qQ, ZQ, 1, (1 << 32) - 1)     # ratio 3/2 > 1
+    assert not accept.spec_accept_token(qP, ZP, qQ, ZQ, 2, 0)
+    assert not accept.spec_accept_token(qP, ZP, qQ, ZQ, -1, 0)
+    # residual of P - Q = (-1/4, 1/4) is all on token 1
+    assert accept.residual_weights(qP, ZP, qQ, ZQ) == [0, 2]      # 2 / (ZP ZQ) = 1/4
+    assert accept.sample_from_weights([0, 4], 0) == 1
+    assert accept.sample_from_weights([1, 1, 2], (1 << 32) - 1) == 2
+    assert accept.sample_from_weights([1, 1, 2], 1 << 30) == 1      # thr = 1
+
+
+def test_verify_sample_is_a_function_of_inputs_and_seed():
+    rng = np.random.default_rng(7)
+    N, D, V = 16, 4, 10
+    tl = rng.normal(size=(N, D + 1, V)).astype(np.float32)
+    dl = rng.normal(size=(N, D, V)).astype(np.float32)
+    drafts = dnc.sample_drafts(dl, 1, 1.0, seed=3)[:, 0]
+    a = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=9)
+    b = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=9)
+    c = accept.verify_sample(tl, dl, drafts, 1.0, 1.0, seed=10)
+    assert all((x == y).all() for x, y in zip(a, b))
+    assert any((x != y).any() for x, y in zip(a, c))
