@@ -307,6 +307,38 @@ def main():
                      "ctxkv_TFLOPs": round(2 * T_cold * 2 * sh.kv_dim * sh.hidden * sh.n_layers
                                            / (tc["gemm_ctxkv"][0] * 1e-3) / 1e12, 1)}
 
+    # lossless stochastic verification (not part of the step): the step's target rows against
+    # draft logits near them, drafts sampled from the draft logits by the library's sampler
+    vsample = None
+    if not args.profile_steps_only:
+        g = torch.Generator(device=dev).manual_seed(2)
+        dlog = (tlogits[:, :D] + 0.5 * torch.randn(tlogits[:, :D].shape, generator=g,
+                                                   device=dev)).contiguous()
+        sws = torch.empty(max(dbd.sample_workspace_bytes(N, D, V), 256), dtype=torch.uint8,
+                          device=dev)
+        sdr = torch.empty((N, 1, D), dtype=torch.int32, device=dev)
+        dbd.sample_from_logits(dlog, 1, 1.0, 5, sdr, sws)
+        sdr = sdr[:, 0].contiguous()
+        vws = torch.empty(dbd.verify_sample_workspace_bytes(N, D, wl.verify_rows, V),
+                          dtype=torch.uint8, device=dev)
+        run = lambda i: dbd.verify_sample(tlogits, dlog, sdr, 1.0, 1.0, i, n_acc, bonus,
+                                          committed, vws)
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        v0.record()
+        for i in range(args.steps):
+            run(i)
+        v1.record()
+        torch.cuda.synchronize()
+        vms = v0.elapsed_time(v1) / args.steps
+        vb = (N * wl.verify_rows + N * D) * V * 4
+        vsample = {"ms": round(vms, 4), "logit_bytes": vb,
+                   "GBps": round(vb / (vms * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(vb / (vms * 1e-3) / HBM_PEAK, 4),
+                   "mean_accepted": round(float(n_acc.float().mean().item()), 3)}
+
     # dominant kernel by time, and its roofline
     roofline = None
     if stages:
@@ -356,6 +388,7 @@ def main():
         "roofline": roofline,
         "stages": stages,
         "cold_ingest": cold_info,
+        "verify_sample": vsample,
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),
     }

@@ -68,6 +68,10 @@ def lib():
             "dbd_verify_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
             "verify_greedy": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                      _vp, _sz, _vp]),
+            "dbd_verify_sample_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32,
+                                                         _c.POINTER(_sz)]),
+            "verify_sample": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32,
+                                     _u64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
             "dbd_select_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _c.POINTER(_sz)]),
             "select_streak": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]),
@@ -194,6 +198,25 @@ def verify_greedy(target_logits, draft_tokens, n_accepted, bonus, committed, wor
     _check(lib().verify_greedy(
         _ptr(target_logits), _ptr(draft_tokens), draft_tokens.stride(0), N, D, R, V,
         _ptr(n_accepted), _ptr(bonus), _ptr(committed), _ptr(row_flags), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, target_logits)))
+
+
+def verify_sample_workspace_bytes(batch, n_draft, n_rows, vocab) -> int:
+    out = _sz(0)
+    _check(lib().dbd_verify_sample_workspace_bytes(batch, n_draft, n_rows, vocab, _c.byref(out)))
+    return out.value
+
+
+def verify_sample(target_logits, draft_logits, draft_tokens, t_target, t_draft, seed,
+                  n_accepted, bonus, committed, workspace, row_flags=None, stream=None):
+    """target_logits [N, R, V] fp32; draft_logits [N, D, V] fp32; draft_tokens [N, D] int32 (row
+    stride taken from the tensor)."""
+    N, R, V = target_logits.shape
+    D = draft_tokens.shape[-1]
+    _check(lib().verify_sample(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), draft_tokens.stride(0), N,
+        D, R, V, float(t_target), float(t_draft), int(seed) & ((1 << 64) - 1), _ptr(n_accepted),
+        _ptr(bonus), _ptr(committed), _ptr(row_flags), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, target_logits)))
 
 

@@ -181,6 +181,16 @@ hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int3
                                   int nch, const int32_t* drafts, int draft_stride, int batch,
                                   int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,
                                   int32_t* committed, int32_t* row_flags, hipStream_t s);
+// Lossless stochastic verification after the argmax partials (pf_*) and integer weight sums
+// (zp_*, rm_*) of the target rows [batch * R] and draft rows [batch * D]; spec: [batch * 4]
+// int64 scratch, wpart: [batch * chunks] 16-byte (128-bit) scratch.
+hipError_t launch_verify_sample(const float* tl, const float* dl, const int32_t* drafts,
+                                int stride, int batch, int D, int R, int V, int chunk,
+                                const uint64_t* zp_t, const float* rm_t, const uint64_t* zp_d,
+                                const float* rm_d, const int32_t* pf_t, const int32_t* pf_d,
+                                float inv_p, float inv_q, uint64_t seed, int64_t* spec,
+                                void* wpart, int32_t* n_acc, int32_t* bonus,
+                                int32_t* committed, int32_t* row_flags, hipStream_t s);
 hipError_t launch_select_finalize(const float* x, int vocab, int chunk, const uint64_t* zpart,
                                   const float* row_max, const int32_t* row_arg,
                                   const int32_t* pflag, const int32_t* drafts, int batch,

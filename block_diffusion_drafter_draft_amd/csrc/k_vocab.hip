@@ -56,6 +56,10 @@ __device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
   return z ^ (z >> 31);
 }
 
+// Logits per thread in the pick kernels' chunk scans (256 threads per chunk): chunks are at most
+// 256 * PICK_SEG wide.
+constexpr int PICK_SEG = 16;
+
 // ------------------------------------------------------------------ block reductions
 template <int NT>
 __device__ __forceinline__ void block_argmax(float& v, int& i, float* sv, int* si) {
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   int bi = 0x7fffffff;
   int bad = 0;
   const float* xr = x + rbase;
-  if (((rbase & 3) == 0) && ((v0 & 3) == 0)) {
+  if (((uintptr_t)(xr + v0) & 15) == 0) {
     const int nv = (v1 - v0) >> 2;
     for (int k = threadIdx.x; k < nv; k += 256) {
       const float4 q = *reinterpret_cast<const float4*>(xr + v0 + 4 * k);
@@ -215,7 +219,29 @@ __global__ __launch_bounds__(256) void zsum_partial_kernel(
   const float* xr = x + (int64_t)row * V;
   const int v0 = c * chunk, v1 = min(V, v0 + chunk);
   uint64_t acc = 0;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += weight_q(xr[v], M, inv_t);
+  if (((uintptr_t)(xr + v0) & 15) == 0) {
+    // four float4 loads in flight per thread before their weights are computed
+    const int nv = (v1 - v0) >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(xr + v0);
+    int k = threadIdx.x;
+    for (; k + 3 * 256 < nv; k += 4 * 256) {
+      float4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = x4[k + u * 256];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc += weight_q(q[u].x, M, inv_t) + weight_q(q[u].y, M, inv_t) +
+               weight_q(q[u].z, M, inv_t) + weight_q(q[u].w, M, inv_t);
+    }
+    for (; k < nv; k += 256) {
+      const float4 q = x4[k];
+      acc += weight_q(q.x, M, inv_t) + weight_q(q.y, M, inv_t) + weight_q(q.z, M, inv_t) +
+             weight_q(q.w, M, inv_t);
+    }
+    for (int v = v0 + 4 * nv + threadIdx.x; v < v1; v += 256) acc += weight_q(xr[v], M, inv_t);
+  } else {
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += weight_q(xr[v], M, inv_t);
+  }
   acc = wave_sum_u64(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
@@ -274,10 +300,15 @@ __global__ __launch_bounds__(256) void sample_pick_kernel(
   const float M = row_max[row];
   const float* xr = x + (int64_t)row * V;
   const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-  const int per = (chunk + 255) / 256;         // contiguous segment per thread
+  const int per = (chunk + 255) / 256;         // contiguous segment per thread, loaded once
   const int a0 = v0 + threadIdx.x * per, a1 = min(v1, a0 + per);
+  float lx[PICK_SEG];
+#pragma unroll
+  for (int e = 0; e < PICK_SEG; ++e) lx[e] = a0 + e < a1 ? xr[a0 + e] : 0.f;
   uint64_t mine = 0;
-  for (int v = a0; v < a1; ++v) mine += weight_q(xr[v], M, inv_t);
+#pragma unroll
+  for (int e = 0; e < PICK_SEG; ++e)
+    if (a0 + e < a1) mine += weight_q(lx[e], M, inv_t);
   // exclusive scan of the 256 segment sums: wave scan then wave offsets
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t incl = mine;
@@ -293,13 +324,15 @@ __global__ __launch_bounds__(256) void sample_pick_kernel(
   for (int q = 0; q < w; ++q) excl += wsum[q];
   if (excl <= thr && thr < excl + mine) {
     uint64_t run = excl;
-    for (int v = a0; v < a1; ++v) {
-      run += weight_q(xr[v], M, inv_t);
-      if (run > thr) {
-        out[oidx] = v;
-        break;
+    int tok = -1;
+#pragma unroll
+    for (int e = 0; e < PICK_SEG; ++e) {
+      if (tok < 0 && a0 + e < a1) {
+        run += weight_q(lx[e], M, inv_t);
+        if (run > thr) tok = a0 + e;
       }
     }
+    if (tok >= 0) out[oidx] = tok;
   }
 }
 
@@ -309,6 +342,7 @@ hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
                               const int32_t* row_valid_pos, int block_len, int n_anchor,
                               int32_t* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (chunk > 256 * PICK_SEG) return hipErrorInvalidValue;
   const int nch = ceil_div(vocab, chunk);
   hipLaunchKernelGGL(sample_pick_kernel, dim3(n_drafts, rows), dim3(256), 0, s, x, vocab, chunk,
                      nch, zpart, row_max, inv_t, n_draft, n_drafts, seed, row_valid_pos,
@@ -379,6 +413,338 @@ hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int3
   hipLaunchKernelGGL(verify_finalize_kernel, dim3(batch), dim3(64 * VF_WAVES), 0, s, pv, pi,
                      pflag, nch, drafts, draft_stride, n_draft, n_rows, n_acc, bonus, committed,
                      row_flags);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ lossless stochastic verify
+// SpecDiff-2 notes, section 4 (the verifier accepts left to right with a lossless rule) and
+// section 5.1 (its per-position accept rate is sum_x min(P, Q)).  The rule is the
+// speculative-sampling rule (Leviathan et al., 2023) on the integer weights: with P(x) = qP_x/ZP
+// (target row, temperature t_target) and Q(x) = qQ_x/ZQ (draft row, t_draft), draft token x is
+// accepted iff u * qQ_x * ZP < qP_x * ZQ * 2^32 for the 32-bit draw u of (n, stream 0, j); at the
+// first rejection the replacement is drawn (stream 1) from w_v = max(0, qP_v ZQ - qQ_v ZP), or
+// from qP when every w_v is 0; after a full accept the bonus is drawn from target row D if it
+// exists.  Draws: the SplitMix64 counter with 2 streams over D + 1 positions.  The two sides of
+// the accept test reach 130 bits and are compared as (high 128, low 64) pairs; residual weights
+// are below 2^98 and their sums below 2^116.
+typedef unsigned __int128 u128;
+
+__device__ __forceinline__ uint64_t spec_draw(uint64_t seed, int n, int stream, int j, int D) {
+  const uint64_t idx = ((uint64_t)n * 2 + stream) * (uint64_t)(D + 1) + j;
+  return splitmix_mix(splitmix_mix(seed) + (idx + 1) * 0x9E3779B97F4A7C15ull) >> 32;
+}
+
+// u * qq * zp < qp * zq * 2^32, exactly
+__device__ __forceinline__ bool spec_accept(uint64_t u, uint64_t qq, uint64_t zp, uint64_t qp,
+                                            uint64_t zq) {
+  const u128 a = (u128)qq * zp, b = (u128)qp * zq;
+  const u128 pl = (u128)u * (uint64_t)a;
+  const u128 lhi = (u128)u * (uint64_t)(a >> 64) + (pl >> 64);
+  const uint64_t llo = (uint64_t)pl;
+  const u128 rhi = b >> 32;
+  const uint64_t rlo = (uint64_t)b << 32;
+  return lhi < rhi || (lhi == rhi && llo < rlo);
+}
+
+// (u * W) >> 32 for W < 2^116
+__device__ __forceinline__ u128 spec_threshold(uint64_t u, u128 W) {
+  return (((u128)u * (uint64_t)(W >> 64)) << 32) + (((u128)u * (uint64_t)W) >> 32);
+}
+
+__device__ __forceinline__ u128 shfl_xor_u128(u128 v, int o) {
+  const uint64_t lo = (uint64_t)v, hi = (uint64_t)(v >> 64);
+  const uint64_t l = ((uint64_t)__shfl_xor((uint32_t)(lo >> 32), o, 64) << 32) |
+                     __shfl_xor((uint32_t)lo, o, 64);
+  const uint64_t h = ((uint64_t)__shfl_xor((uint32_t)(hi >> 32), o, 64) << 32) |
+                     __shfl_xor((uint32_t)hi, o, 64);
+  return ((u128)h << 64) | l;
+}
+__device__ __forceinline__ u128 shfl_up_u128(u128 v, int o) {
+  const uint64_t lo = (uint64_t)v, hi = (uint64_t)(v >> 64);
+  const uint64_t l = ((uint64_t)__shfl_up((uint32_t)(lo >> 32), o, 64) << 32) |
+                     __shfl_up((uint32_t)lo, o, 64);
+  const uint64_t h = ((uint64_t)__shfl_up((uint32_t)(hi >> 32), o, 64) << 32) |
+                     __shfl_up((uint32_t)hi, o, 64);
+  return ((u128)h << 64) | l;
+}
+
+__device__ __forceinline__ u128 shfl_idx_u128(u128 v, int src) {
+  const uint64_t lo = (uint64_t)v, hi = (uint64_t)(v >> 64);
+  const uint64_t l = ((uint64_t)__shfl((uint32_t)(lo >> 32), src, 64) << 32) |
+                     __shfl((uint32_t)lo, src, 64);
+  const uint64_t h = ((uint64_t)__shfl((uint32_t)(hi >> 32), src, 64) << 32) |
+                     __shfl((uint32_t)hi, src, 64);
+  return ((u128)h << 64) | l;
+}
+
+// residual weight of token v at a rejected position (mode 1) or P's weight (otherwise)
+__device__ __forceinline__ u128 spec_weight(const float* tr, const float* dr, int v, float Mp,
+                                            float Mq, float inv_p, float inv_q, uint64_t zp,
+                                            uint64_t zq, bool resid) {
+  const uint64_t qp = weight_q(tr[v], Mp, inv_p);
+  if (!resid) return qp;
+  const u128 a = (u128)qp * zq, b = (u128)weight_q(dr[v], Mq, inv_q) * zp;
+  return a > b ? a - b : 0;
+}
+
+// One workgroup per sequence.  Wave w sums the chunk partials of positions w, w + 4, ... (lane c
+// takes chunk c), its lane 0 runs the position's accept test; the first rejection (lowest
+// rejected position) ends the accepted prefix.  spec[n] = {mode, position, ZP, ZQ}: mode 1
+// residual draw at the rejected position, 2 bonus draw from target row D, 0 no draw.
+__global__ __launch_bounds__(256) void spec_accept_kernel(
+    const float* __restrict__ tl, const float* __restrict__ dl, const int32_t* __restrict__ drafts,
+    int stride, int D, int R, int V, int nch, const uint64_t* __restrict__ zp_t,
+    const float* __restrict__ rm_t, const uint64_t* __restrict__ zp_d,
+    const float* __restrict__ rm_d, float inv_p, float inv_q, uint64_t seed,
+    int32_t* __restrict__ n_acc, int64_t* __restrict__ spec) {
+  __shared__ uint64_t s_zp[65], s_zq[65];
+  __shared__ int s_first;
+  const int n = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) s_first = D;
+  __syncthreads();
+  for (int j = wave; j <= D; j += 4) {
+    if (j == D && R == D) break;
+    const int64_t rt = (int64_t)n * R + j, rd = (int64_t)n * D + j;
+    uint64_t zp = 0, zq = 0;
+    for (int c = lane; c < nch; c += 64) {
+      zp += zp_t[rt * nch + c];
+      if (j < D) zq += zp_d[rd * nch + c];
+    }
+    zp = wave_sum_u64(zp);
+    zq = wave_sum_u64(zq);
+    if (lane == 0) {
+      s_zp[j] = zp;
+      s_zq[j] = zq;
+      if (j < D) {
+        const int x = drafts[(int64_t)n * stride + j];
+        const bool in = x >= 0 && x < V;
+        const uint64_t qp = in ? weight_q(tl[rt * V + x], rm_t[rt], inv_p) : 0;
+        const uint64_t qq = in ? weight_q(dl[rd * V + x], rm_d[rd], inv_q) : 0;
+        if (!spec_accept(spec_draw(seed, n, 0, j, D), qq, zp, qp, zq)) atomicMin(&s_first, j);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int first = s_first;
+    int64_t* sp = spec + (int64_t)n * 4;
+    n_acc[n] = first;
+    sp[0] = first < D ? 1 : (R > D ? 2 : 0);
+    sp[1] = first;
+    sp[2] = first < D || R > D ? (int64_t)s_zp[first] : 0;
+    sp[3] = first < D ? (int64_t)s_zq[first] : 0;
+  }
+}
+
+// grid (chunks, N): chunk sums of the residual weights of a rejected position (mode 1 only).
+__global__ __launch_bounds__(256) void spec_resid_partial_kernel(
+    const float* __restrict__ tl, const float* __restrict__ dl, int D, int R, int V, int chunk,
+    int nch, const float* __restrict__ rm_t, const float* __restrict__ rm_d, float inv_p,
+    float inv_q, const int64_t* __restrict__ spec, u128* __restrict__ wpart) {
+  __shared__ u128 red[4];
+  const int c = blockIdx.x, n = blockIdx.y;
+  const int64_t* sp = spec + (int64_t)n * 4;
+  if (sp[0] != 1) return;
+  const int j = (int)sp[1];
+  const uint64_t zp = (uint64_t)sp[2], zq = (uint64_t)sp[3];
+  const int64_t rt = (int64_t)n * R + j, rd = (int64_t)n * D + j;
+  const float* tr = tl + rt * V;
+  const float* dr = dl + rd * V;
+  const float Mp = rm_t[rt], Mq = rm_d[rd];
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  u128 acc = 0;
+  auto w1 = [&](float a, float b) __attribute__((always_inline)) -> u128 {
+    const u128 x = (u128)weight_q(a, Mp, inv_p) * zq, y = (u128)weight_q(b, Mq, inv_q) * zp;
+    return x > y ? x - y : 0;
+  };
+  if ((((uintptr_t)(tr + v0) | (uintptr_t)(dr + v0)) & 15) == 0) {
+    const int nv = (v1 - v0) >> 2;
+    const float4* t4 = reinterpret_cast<const float4*>(tr + v0);
+    const float4* d4 = reinterpret_cast<const float4*>(dr + v0);
+    int k = threadIdx.x;
+    for (; k + 256 < nv; k += 2 * 256) {
+      const float4 a0 = t4[k], b0 = d4[k], a1 = t4[k + 256], b1 = d4[k + 256];
+      acc += w1(a0.x, b0.x) + w1(a0.y, b0.y) + w1(a0.z, b0.z) + w1(a0.w, b0.w);
+      acc += w1(a1.x, b1.x) + w1(a1.y, b1.y) + w1(a1.z, b1.z) + w1(a1.w, b1.w);
+    }
+    for (; k < nv; k += 256) {
+      const float4 a = t4[k], b = d4[k];
+      acc += w1(a.x, b.x) + w1(a.y, b.y) + w1(a.z, b.z) + w1(a.w, b.w);
+    }
+    for (int v = v0 + 4 * nv + threadIdx.x; v < v1; v += 256) acc += w1(tr[v], dr[v]);
+  } else {
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) acc += w1(tr[v], dr[v]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += shfl_xor_u128(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) wpart[(int64_t)n * nch + c] = red[0] + red[1] + red[2] + red[3];
+}
+
+// One workgroup per sequence: the replacement / bonus token by threshold search (chunk from the
+// chunk sums, then a block-wide exclusive scan over that chunk), the committed tokens and the
+// non-finite flag of the sequence's rows.
+__global__ __launch_bounds__(256) void spec_pick_kernel(
+    const float* __restrict__ tl, const float* __restrict__ dl,
+    const int32_t* __restrict__ drafts, int stride, int D, int R, int V, int chunk, int nch,
+    const uint64_t* __restrict__ zp_t, const float* __restrict__ rm_t,
+    const float* __restrict__ rm_d, const int32_t* __restrict__ pf_t,
+    const int32_t* __restrict__ pf_d, float inv_p, float inv_q, uint64_t seed,
+    const int64_t* __restrict__ spec, const u128* __restrict__ wpart,
+    const int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus,
+    int32_t* __restrict__ committed, int32_t* __restrict__ row_flags) {
+  __shared__ u128 s_thr;
+  __shared__ int s_chunk, s_resid, s_tok, s_bad;
+  __shared__ u128 wsum[4];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int64_t* sp = spec + (int64_t)n * 4;
+  const int mode = (int)sp[0], j = (int)sp[1];
+  const uint64_t zp = (uint64_t)sp[2], zq = (uint64_t)sp[3];
+  const int64_t rt = (int64_t)n * R + j, rd = (int64_t)n * D + (j < D ? j : 0);
+  if (tid == 0) {
+    s_tok = -1;
+    s_bad = 0;
+  }
+  if (mode != 0 && tid < 64) {
+    // wave 0: chunk sums (lane c holds chunks c, c + 64, ...), total, threshold, then the first
+    // chunk whose inclusive prefix exceeds it by a wave-wide scan per 64-chunk group
+    const int lane = tid;
+    bool resid = mode == 1;
+    u128 W = 0;
+    if (resid) {
+      for (int c = lane; c < nch; c += 64) W += wpart[(int64_t)n * nch + c];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) W += shfl_xor_u128(W, o);
+      if (W == 0) resid = false;                // P <= Q everywhere: draw from P
+    }
+    if (!resid) {
+      uint64_t z = 0;
+      for (int c = lane; c < nch; c += 64) z += zp_t[rt * nch + c];
+      W = wave_sum_u64(z);
+    }
+    const u128 thr = spec_threshold(spec_draw(seed, n, 1, j, D), W);
+    u128 base = 0;
+    int found = -1;
+    u128 below = 0;
+    for (int c0 = 0; c0 < nch && found < 0; c0 += 64) {
+      const int c = c0 + lane;
+      const u128 wc = c < nch ? (resid ? wpart[(int64_t)n * nch + c] : (u128)zp_t[rt * nch + c])
+                              : (u128)0;
+      u128 incl = wc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const u128 t = shfl_up_u128(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const uint64_t hit = __ballot(c < nch && base + incl > thr);
+      if (hit) {
+        found = c0 + __ffsll((unsigned long long)hit) - 1;
+        const int src = found - c0;
+        const u128 ex = shfl_idx_u128(incl - wc, src);
+        below = base + ex;
+      } else {
+        base += shfl_idx_u128(incl, 63);
+      }
+    }
+    if (lane == 0) {
+      if (found < 0) {                           // threshold beyond the sums: last chunk
+        found = nch - 1;
+        below = base - (resid ? wpart[(int64_t)n * nch + found] : (u128)zp_t[rt * nch + found]);
+      }
+      s_chunk = found;
+      s_thr = thr - below;
+      s_resid = resid;
+    }
+  }
+  __syncthreads();
+  int bad = 0;
+  for (int q = tid; q < R * nch; q += 256) bad |= pf_t[(int64_t)n * R * nch + q];
+  for (int q = tid; q < D * nch; q += 256) bad |= pf_d[(int64_t)n * D * nch + q];
+  if (bad) atomicOr(&s_bad, 1);
+  if (mode != 0) {
+    const bool resid = s_resid;
+    const int c = s_chunk;
+    const u128 thr = s_thr;
+    const float* tr = tl + rt * V;
+    const float* dr = dl + rd * V;
+    const float Mp = rm_t[rt], Mq = resid ? rm_d[rd] : 0.f;
+    const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+    // the thread's contiguous segment of the chunk, loaded once (all loads in flight together)
+    const int per = (chunk + 255) / 256;
+    const int a0 = v0 + tid * per, a1 = min(v1, a0 + per);
+    float lt[PICK_SEG], ld[PICK_SEG];
+#pragma unroll
+    for (int e = 0; e < PICK_SEG; ++e) {
+      const int v = a0 + e;
+      lt[e] = v < a1 ? tr[v] : 0.f;
+      ld[e] = v < a1 && resid ? dr[v] : 0.f;
+    }
+    auto wgt = [&](int e) __attribute__((always_inline)) -> u128 {
+      const uint64_t qp = weight_q(lt[e], Mp, inv_p);
+      if (!resid) return qp;
+      const u128 a = (u128)qp * zq, b = (u128)weight_q(ld[e], Mq, inv_q) * zp;
+      return a > b ? a - b : 0;
+    };
+    u128 mine = 0;
+#pragma unroll
+    for (int e = 0; e < PICK_SEG; ++e)
+      if (a0 + e < a1) mine += wgt(e);
+    const int lane = tid & 63, w = tid >> 6;
+    u128 incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const u128 t = shfl_up_u128(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    u128 excl = incl - mine;
+    for (int q = 0; q < w; ++q) excl += wsum[q];
+    if (excl <= thr && thr < excl + mine) {
+      u128 run = excl;
+      int tok = -1;
+#pragma unroll
+      for (int e = 0; e < PICK_SEG; ++e) {
+        if (tok < 0 && a0 + e < a1) {
+          run += wgt(e);
+          if (run > thr) tok = a0 + e;
+        }
+      }
+      s_tok = tok;
+    }
+  }
+  __syncthreads();
+  const int a = n_acc[n], b = s_tok;
+  for (int q = tid; q <= D; q += 256)
+    committed[(int64_t)n * (D + 1) + q] =
+        q < a ? drafts[(int64_t)n * stride + q] : (q == a ? b : -1);
+  if (tid == 0) {
+    bonus[n] = b;
+    if (row_flags) row_flags[n] = s_bad ? 1 : 0;
+  }
+}
+
+hipError_t launch_verify_sample(const float* tl, const float* dl, const int32_t* drafts,
+                                int stride, int batch, int D, int R, int V, int chunk,
+                                const uint64_t* zp_t, const float* rm_t, const uint64_t* zp_d,
+                                const float* rm_d, const int32_t* pf_t, const int32_t* pf_d,
+                                float inv_p, float inv_q, uint64_t seed, int64_t* spec,
+                                void* wpart, int32_t* n_acc, int32_t* bonus,
+                                int32_t* committed, int32_t* row_flags, hipStream_t s) {
+  if (chunk > 256 * PICK_SEG) return hipErrorInvalidValue;
+  const int nch = ceil_div(V, chunk);
+  hipLaunchKernelGGL(spec_accept_kernel, dim3(batch), dim3(256), 0, s, tl, dl, drafts, stride, D,
+                     R, V, nch, zp_t, rm_t, zp_d, rm_d, inv_p, inv_q, seed, n_acc, spec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_resid_partial_kernel, dim3(nch, batch), dim3(256), 0, s, tl, dl, D, R,
+                     V, chunk, nch, rm_t, rm_d, inv_p, inv_q, spec, (u128*)wpart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_pick_kernel, dim3(batch), dim3(256), 0, s, tl, dl, drafts, stride, D, R,
+                     V, chunk, nch, zp_t, rm_t, rm_d, pf_t, pf_d, inv_p, inv_q, seed, spec,
+                     (const u128*)wpart, n_acc, bonus, committed, row_flags);
   return hipGetLastError();
 }
 

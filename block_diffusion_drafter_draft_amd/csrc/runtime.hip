@@ -665,6 +665,96 @@ int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32
   return DBD_OK;
 }
 
+// Workspace of verify_sample: argmax partials, integer weight sums, row max / argmax of the
+// target rows [batch * n_rows] and of the draft rows [batch * n_draft]; per sequence the accept
+// result and the residual chunk sums (128-bit).
+struct VsampleWs {
+  float *pv_t, *pv_d, *rm_t, *rm_d;
+  int32_t *pi_t, *pi_d, *pf_t, *pf_d, *ra_t, *ra_d;
+  uint64_t *zp_t, *zp_d;
+  int64_t* spec;
+  void* wpart;
+};
+static size_t carve_vsample(int batch, int n_draft, int n_rows, int vocab, char* base,
+                            VsampleWs* w) {
+  Carver c{base};
+  const int nch = ceil_div(vocab, vocab_chunk());
+  const int64_t rt = (int64_t)batch * n_rows, rd = (int64_t)batch * n_draft;
+  VsampleWs t;
+  t.pv_t = c.take<float>(rt * nch);
+  t.pi_t = c.take<int32_t>(rt * nch);
+  t.pf_t = c.take<int32_t>(rt * nch);
+  t.zp_t = c.take<uint64_t>(rt * nch);
+  t.rm_t = c.take<float>(rt);
+  t.ra_t = c.take<int32_t>(rt);
+  t.pv_d = c.take<float>(rd * nch);
+  t.pi_d = c.take<int32_t>(rd * nch);
+  t.pf_d = c.take<int32_t>(rd * nch);
+  t.zp_d = c.take<uint64_t>(rd * nch);
+  t.rm_d = c.take<float>(rd);
+  t.ra_d = c.take<int32_t>(rd);
+  t.spec = c.take<int64_t>((int64_t)batch * 4);
+  t.wpart = c.take<char>((int64_t)batch * nch * 16);
+  if (w) *w = t;
+  return (c.off + kAlign - 1) / kAlign * kAlign;
+}
+
+int dbd_verify_sample_workspace_bytes(int32_t batch, int32_t n_draft, int32_t n_rows,
+                                      int32_t vocab, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (batch < 1 || n_draft < 1 || n_rows < 1 || vocab < 2) return fail(DBD_ERR_ARG, "bad dimensions");
+  *bytes = carve_vsample(batch, n_draft, n_rows, vocab, nullptr, nullptr);
+  return DBD_OK;
+}
+
+int verify_sample(const float* target_logits, const float* draft_logits,
+                  const int32_t* draft_tokens, int32_t draft_stride, int32_t batch,
+                  int32_t n_draft, int32_t n_rows, int32_t vocab, float t_target, float t_draft,
+                  uint64_t seed, int32_t* n_accepted, int32_t* bonus, int32_t* committed,
+                  int32_t* row_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!target_logits || !draft_logits || !draft_tokens || !n_accepted || !bonus || !committed)
+    return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2 || vocab >= (1 << 18))
+    return fail(DBD_ERR_ARG, "bad dimensions (batch %d, n_draft %d, vocab %d)", batch, n_draft,
+                vocab);
+  if (!(t_target > 0.f) || !(t_draft > 0.f) || !std::isfinite(t_target) ||
+      !std::isfinite(t_draft))
+    return fail(DBD_ERR_ARG, "temperatures must be finite and > 0 (%g, %g)", t_target, t_draft);
+  if (n_draft > 64) return fail(DBD_ERR_UNSUPPORTED, "n_draft %d > 64", n_draft);
+  if (n_rows != n_draft && n_rows != n_draft + 1)
+    return fail(DBD_ERR_SHAPE, "n_rows %d must be n_draft or n_draft + 1", n_rows);
+  if (draft_stride < n_draft) return fail(DBD_ERR_SHAPE, "draft_stride < n_draft");
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const size_t need = carve_vsample(batch, n_draft, n_rows, vocab, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  VsampleWs w;
+  carve_vsample(batch, n_draft, n_rows, vocab, (char*)workspace, &w);
+  hipStream_t st = (hipStream_t)stream;
+  const int ch = vocab_chunk();
+  const int rt = batch * n_rows, rd = batch * n_draft;
+  const float inv_p = (float)(1.0 / (double)t_target), inv_q = (float)(1.0 / (double)t_draft);
+  HIP_STAGE(DBD_STAGE_VERIFY, st,
+            launch_argmax_partial(target_logits, rt, vocab, ch, w.pv_t, w.pi_t, w.pf_t, st));
+  HIP_STAGE(DBD_STAGE_VERIFY, st,
+            launch_argmax_partial(draft_logits, rd, vocab, ch, w.pv_d, w.pi_d, w.pf_d, st));
+  HIP_STAGE(DBD_STAGE_VERIFY, st,
+            launch_zsum_partial(target_logits, rt, vocab, ch, w.pv_t, w.pi_t, inv_p, w.zp_t,
+                                w.rm_t, w.ra_t, st));
+  HIP_STAGE(DBD_STAGE_VERIFY, st,
+            launch_zsum_partial(draft_logits, rd, vocab, ch, w.pv_d, w.pi_d, inv_q, w.zp_d,
+                                w.rm_d, w.ra_d, st));
+  HIP_STAGE(DBD_STAGE_VERIFY, st,
+            launch_verify_sample(target_logits, draft_logits, draft_tokens, draft_stride, batch,
+                                 n_draft, n_rows, vocab, ch, w.zp_t, w.rm_t, w.zp_d, w.rm_d,
+                                 w.pf_t, w.pf_d, inv_p, inv_q, seed, w.spec, w.wpart,
+                                 n_accepted, bonus, committed, row_flags, st));
+  return DBD_OK;
+}
+
 static size_t carve_select(int rows, int vocab, char* base, float** pv, int32_t** pi,
                            int32_t** pf, uint64_t** zp, float** rm, int32_t** ra) {
   Carver c{base};

@@ -189,6 +189,40 @@ int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32
                   int32_t* n_accepted, int32_t* bonus, int32_t* committed, int32_t* row_flags,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace size (host) for verify_sample. */
+int dbd_verify_sample_workspace_bytes(int32_t batch, int32_t n_draft, int32_t n_rows,
+                                      int32_t vocab, size_t* bytes /* host out */);
+
+/* verify_sample: lossless stochastic verification of one draft per sequence ([SpecDiff-2]
+ * section 4: the verifier applies a lossless acceptance rule left to right; section 5.1: its
+ * per-position accept rate is sum_x min(P, Q)).  The rule is the speculative-sampling rule
+ * (Leviathan et al., 2023) in the library's integer arithmetic: P_j = the integer weights of
+ * target row j at t_target, Q_j = those of draft row j at t_draft (as in the sampler of
+ * draft_block), each a pure function of the fp32 logits.
+ *
+ * For j = 0 .. D-1: draft token x_j is accepted iff u * q_Q(x_j) * Z_P < q_P(x_j) * Z_Q * 2^32
+ * (probability min(1, P_j(x_j) / Q_j(x_j))), u the 32-bit draw (seed, n, stream 0, j); a token
+ * outside [0, V) is rejected.  At the first rejection j the replacement token is drawn (stream 1,
+ * position j) from the weights max(0, q_P(v) Z_Q - q_Q(v) Z_P) (from q_P when those are all 0)
+ * and verification stops; after a full accept a bonus token is drawn from target row D (stream
+ * 1, position D) when n_rows = D + 1, else there is none (-1).  The committed tokens are thus
+ * distributed as the target's P.
+ *
+ * target_logits [N, n_rows, V] fp32 (device), n_rows = D or D+1.
+ * draft_logits  [N, D, V] fp32 (device): the drafter's logits the drafts were sampled from (the
+ *               logits_out of draft_block).
+ * draft_tokens  [N, D] int32 (device), row stride `draft_stride` (>= D).
+ * t_target, t_draft  temperatures (> 0, finite) of P and Q.
+ * Outputs as verify_greedy: n_accepted[n], bonus[n] (the replacement or bonus token, -1 if
+ * none), committed[n][0 .. D] (accepted drafts, then bonus, padded with -1), row_flags[n]
+ * (optional) DBD_SEQ_NONFINITE if a non-finite logit was seen in the sequence's target or draft
+ * rows (the results are then unspecified). */
+int verify_sample(const float* target_logits, const float* draft_logits,
+                  const int32_t* draft_tokens, int32_t draft_stride, int32_t batch,
+                  int32_t n_draft, int32_t n_rows, int32_t vocab, float t_target, float t_draft,
+                  uint64_t seed, int32_t* n_accepted, int32_t* bonus, int32_t* committed,
+                  int32_t* row_flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace size (host) for select_streak. */
 int dbd_select_workspace_bytes(int32_t batch, int32_t n_drafts, int32_t n_rows, int32_t vocab,
                                size_t* bytes /* host out */);

@@ -243,3 +243,25 @@ def test_gemm_override_validation():
     finally:
         dbd.gemm_override("gemm_down")
     assert dbd.draft_workspace_bytes(desc, 32, 16, 1, 64, 1, 0.0, 4096) == base
+
+
+def test_verify_sample_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    ws = dbd.verify_sample_workspace_bytes(4, 5, 6, 1000)
+    assert ws > 0
+    args = lambda **k: dict(dict(t=fake, d=fake, dr=fake, st=5, N=4, D=5, R=6, V=1000, tp=1.0,
+                                 tq=1.0, seed=1, na=fake, b=fake, c=fake, f=None, w=fake,
+                                 wb=ws), **k)
+    call = lambda a: L.verify_sample(a["t"], a["d"], a["dr"], a["st"], a["N"], a["D"], a["R"],
+                                     a["V"], a["tp"], a["tq"], a["seed"], a["na"], a["b"],
+                                     a["c"], a["f"], a["w"], a["wb"], None)
+    assert call(args(d=None)) == -1
+    assert call(args(tp=0.0)) == -1
+    assert call(args(tq=float("nan"))) == -1
+    assert call(args(R=7)) == -2
+    assert call(args(st=4)) == -2
+    assert call(args(D=65, R=65)) == -5
+    assert call(args(V=1 << 18)) == -1
+    assert call(args(wb=ws - 1)) == -4
+    assert call(args(w=fake + 16)) == -4

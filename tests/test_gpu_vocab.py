@@ -175,3 +175,107 @@ def test_sampling_depends_on_seed_and_draft_index():
     b = _sample_gpu(logits, 8, 1.0, 2)
     assert not np.array_equal(a, b)
     assert len({tuple(a[0, k]) for k in range(8)}) > 1
+
+
+# ---- lossless stochastic verification ----
+
+def _vsample_gpu(tl, dl, drafts, t_p, t_q, seed):
+    N, R, V = tl.shape
+    D = drafts.shape[1]
+    ws = torch.empty(dbd.verify_sample_workspace_bytes(N, D, R, V), dtype=torch.uint8,
+                     device=DEV)
+    n_acc = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    bonus = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    com = torch.full((N, D + 1), -7, dtype=torch.int32, device=DEV)
+    flags = torch.full((N,), -7, dtype=torch.int32, device=DEV)
+    dbd.verify_sample(tl, dl, drafts, t_p, t_q, seed, n_acc, bonus, com, ws, row_flags=flags)
+    torch.cuda.synchronize()
+    return n_acc.cpu().numpy(), bonus.cpu().numpy(), com.cpu().numpy(), flags.cpu().numpy()
+
+
+def _check_vsample(tl, dl, drafts, t_p, t_q, seed):
+    print(f"verify_sample target={tuple(tl.shape)} T=({t_p}, {t_q}) seed={seed}", flush=True)
+    got = _vsample_gpu(tl, dl, drafts, t_p, t_q, seed)
+    ref = accept.verify_sample(tl.cpu().numpy(), dl.cpu().numpy(), drafts.cpu().numpy(), t_p,
+                               t_q, seed)
+    for g, r in zip(got[:3], ref):
+        assert np.array_equal(g, r), (g, r)
+    assert np.all(got[3] == 0)
+    return got
+
+
+@pytest.mark.parametrize("N,D,R,V", [(6, 5, 6, 37), (4, 7, 8, 4099), (3, 15, 16, 10000),
+                                     (2, 64, 65, 300), (5, 1, 1, 8192), (2, 3, 3, 2)])
+@pytest.mark.parametrize("t_p,t_q", [(1.0, 1.0), (1.0, 1.5), (0.7, 1.3)])
+def test_verify_sample_bit_exact(N, D, R, V, t_p, t_q):
+    """Drafts sampled from the draft logits with the library's sampler, target logits close to
+    them (so acceptance lengths vary), over ragged vocabulary chunks; every output bit-exact."""
+    g = torch.Generator(device=DEV).manual_seed(N * 977 + V + D)
+    dl = torch.randn((N, D, V), generator=g, device=DEV) * 2.0
+    tl = torch.randn((N, R, V), generator=g, device=DEV) * 2.0
+    tl[:, :D] = dl + 0.6 * torch.randn((N, D, V), generator=g, device=DEV)
+    drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, t_q, seed=V)[:, 0]).to(DEV)
+    got = _check_vsample(tl, dl, drafts.contiguous(), t_p, t_q, seed=12345 + D)
+    if N * D >= 20:
+        assert len(set(got[0].tolist())) > 1           # acceptance lengths differ
+
+
+def test_verify_sample_workload_shape():
+    """The Qwen3-8B drafter's vocabulary and block: 15 drafted positions, 16 target rows."""
+    V, D, N = 151936, 15, 4
+    g = torch.Generator(device=DEV).manual_seed(5)
+    dl = torch.randn((N, D, V), generator=g, device=DEV) * 3.0
+    tl = torch.randn((N, D + 1, V), generator=g, device=DEV) * 3.0
+    tl[:, :D] = dl + 0.3 * torch.randn((N, D, V), generator=g, device=DEV)
+    drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, 1.0, seed=9)[:, 0]).to(DEV)
+    _check_vsample(tl, dl, drafts.contiguous(), 1.0, 1.0, seed=77)
+
+
+def test_verify_sample_identical_P_Q_accepts_all():
+    N, D, V = 8, 6, 5000
+    g = torch.Generator(device=DEV).manual_seed(8)
+    dl = torch.randn((N, D, V), generator=g, device=DEV) * 2.0
+    tl = torch.cat([dl, torch.randn((N, 1, V), generator=g, device=DEV)], 1).contiguous()
+    drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, 1.0, seed=1)[:, 0]).to(DEV)
+    got = _check_vsample(tl, dl, drafts.contiguous(), 1.0, 1.0, seed=3)
+    assert np.all(got[0] == D) and np.all(got[1] >= 0)
+
+
+def test_verify_sample_out_of_range_and_disjoint():
+    """Draft tokens outside the vocabulary are rejected; Q's mass only where P is zero rejects
+    at position 0 and resamples from P's support."""
+    N, D, V = 4, 3, 64
+    dl = torch.full((N, D, V), -1e4, device=DEV)
+    dl[:, :, 40:] = 0.0
+    tl = torch.full((N, D + 1, V), -1e4, device=DEV)
+    tl[:, :, :8] = torch.arange(8, device=DEV, dtype=torch.float32) * 0.1
+    drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, 1.0, seed=2)[:, 0]).to(DEV)
+    drafts[1, 0] = V
+    drafts[2, 0] = -3
+    got = _check_vsample(tl, dl, drafts.contiguous(), 1.0, 1.0, seed=4)
+    assert np.all(got[0] == 0) and np.all((got[1] >= 0) & (got[1] < 8))
+
+
+def test_verify_sample_flags_non_finite():
+    N, D, V = 3, 4, 300
+    g = torch.Generator(device=DEV).manual_seed(9)
+    dl = torch.randn((N, D, V), generator=g, device=DEV)
+    tl = torch.randn((N, D + 1, V), generator=g, device=DEV)
+    tl[1, 2, 17] = float("nan")
+    dl[2, 0, 5] = float("inf")
+    drafts = torch.randint(0, V, (N, D), generator=g, device=DEV, dtype=torch.int32)
+    got = _vsample_gpu(tl, dl, drafts.contiguous(), 1.0, 1.0, 5)
+    assert got[3].tolist() == [0, 1, 1]
+
+
+def test_verify_sample_unaligned_logits():
+    """Logits that start 4 bytes past a 16-byte boundary take the scalar load paths."""
+    N, D, R, V = 3, 6, 7, 5003
+    g = torch.Generator(device=DEV).manual_seed(12)
+    tb = torch.randn(N * R * V + 1, generator=g, device=DEV) * 2.0
+    db = torch.randn(N * D * V + 1, generator=g, device=DEV) * 2.0
+    tl = tb[1:].view(N, R, V)
+    dl = db[1:].view(N, D, V)
+    tl[:, :D] = dl + 0.5
+    drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, 1.0, seed=6)[:, 0]).to(DEV)
+    _check_vsample(tl, dl, drafts.contiguous(), 1.0, 1.2, seed=8)
