@@ -68,17 +68,39 @@ def rope(x, pos, theta: float) -> np.ndarray:
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
-def mix_weights(mix_logits) -> np.ndarray:
-    """Softmax over the target layers, one row per draft layer: [L_d, L_t]."""
-    return softmax_rows(f64(mix_logits))
+def mix_weights(mix_logits, raw: bool = False) -> np.ndarray:
+    """Mixing coefficients, one row per draft layer: [L_d, L_t].  Softmax over the target layers
+    (DFlare page, per-layer mixing section), or the given values as they are (raw = True: the
+    page's "without softmax" ablation)."""
+    return f64(mix_logits) if raw else softmax_rows(f64(mix_logits))
 
 
 def context_features(shape, W, layer: int, hidden) -> np.ndarray:
-    """c_l(t) = RMSNorm(sum_i w_{l,i} h_i(t)) * g_mix_l.  hidden: [T, L_t, H] -> [T, H]."""
-    w = mix_weights(W["mix_logits"])[layer]                                   # [L_t]
+    """Context features of draft layer `layer` from target hidden states [T, L_t, H] -> [T, H].
+
+    Mixing (DFlare page, per-layer mixing section): c_l(t) = RMSNorm(sum_i w_{l,i} h_i(t)) *
+    g_mix_l with w the mixing coefficients of the layer.
+    Fully connected fusion (DFlare page, comparison with DFlash; DFlash article, section on
+    conditioning every layer on target features): one shared feature for every draft layer,
+    c(t) = RMSNorm(W_fc . [h_0(t); h_1(t); ...; h_{L_t-1}(t)]) * g_fc, the target layers
+    concatenated in order; the RMSNorm after the fusion is a reading (the pages name only the
+    fully connected layer), matching the normalisation of the mixing path."""
     h = f64(hidden)
+    if getattr(shape, "ctx_fusion", "mix") == "fc":
+        T = h.shape[0]
+        m = h.reshape(T, -1) @ f64(W["fc_w"]).T
+        return rmsnorm(m, f64(W["fc_norm_w"]), shape.rms_eps)
+    w = mix_weights(W["mix_logits"], getattr(shape, "mix_raw", False))[layer]     # [L_t]
     m = np.einsum("i,tih->th", w, h)
     return rmsnorm(m, f64(W["mix_norm_w"][layer]), shape.rms_eps)
+
+
+def context_projection(shape, W, layer: int):
+    """The (K, V) weights that project context features: the context's own (DFlare page, section
+    on splitting the K/V projections by source) or, without the split, the draft block's."""
+    if getattr(shape, "ctx_shared_kv", False):
+        return W["wk_draft"][layer], W["wv_draft"][layer]
+    return W["wk_ctx"][layer], W["wv_ctx"][layer]
 
 
 def context_kv(shape, W, layer: int, hidden, pos0: int = 0):
@@ -87,8 +109,9 @@ def context_kv(shape, W, layer: int, hidden, pos0: int = 0):
     c = context_features(shape, W, layer, hidden)
     T = c.shape[0]
     kvh, hd = shape.n_kv_heads, shape.head_dim
-    k = (c @ f64(W["wk_ctx"][layer]).T).reshape(T, kvh, hd)
-    v = (c @ f64(W["wv_ctx"][layer]).T).reshape(T, kvh, hd)
+    wk, wv = context_projection(shape, W, layer)
+    k = (c @ f64(wk).T).reshape(T, kvh, hd)
+    v = (c @ f64(wv).T).reshape(T, kvh, hd)
     k = rope(k, np.arange(pos0, pos0 + T), shape.rope_theta)
     return k.transpose(1, 0, 2), v.transpose(1, 0, 2)
 

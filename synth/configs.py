@@ -22,6 +22,12 @@ class DrafterShape:
     dtype: str                 # "f32" or "bf16"
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
+    # context-feature path: "mix" = per-draft-layer mixing of the target layers then RMSNorm;
+    # "fc" = one fully connected fusion of the concatenated target layers then RMSNorm, shared
+    # by every draft layer
+    ctx_fusion: str = "mix"
+    mix_raw: bool = False          # mixing coefficients used as given (no softmax)
+    ctx_shared_kv: bool = False    # context K/V projected with the draft block's K/V weights
 
     @property
     def mask_token_id(self) -> int:
@@ -74,6 +80,11 @@ QWEN3_8B = DrafterShape(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, f
                         n_layers=7, n_target_layers=9, vocab=151936, dtype="bf16")
 GPT_OSS_20B = DrafterShape(hidden=2880, n_q_heads=64, n_kv_heads=8, head_dim=64, ffn=11520,
                            n_layers=8, n_target_layers=7, vocab=201088, dtype="bf16")
+# DFlash-style context path (fully connected fusion, one K/V projection for context and block)
+# and the mixing ablations, on the tiny and Qwen3-8B shapes
+TINY_FC = replace(TINY, ctx_fusion="fc", ctx_shared_kv=True)
+TINY_ABL = replace(TINY, mix_raw=True, ctx_shared_kv=True)
+QWEN3_8B_FC = replace(QWEN3_8B, ctx_fusion="fc", ctx_shared_kv=True)
 SPECDIFF2_7B = DrafterShape(hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128, ffn=18944,
                             n_layers=28, n_target_layers=0, vocab=152064, dtype="bf16")
 
@@ -86,6 +97,21 @@ WORKLOADS = {
         temperature=0.0, ctx_lo=56, ctx_hi=56, ctx_source="hidden", verify="greedy",
         verify_rows=8, planted_alpha=0.7, fixed_new=8,
         notes="context 64 = 56 cached + 8 ingested; fp32 path"),
+    "tiny-dflash-fp32": Workload(
+        name="tiny-dflash-fp32", shape=TINY_FC, batch=1, block_len=8, n_anchor=1, n_drafts=1,
+        temperature=0.0, ctx_lo=56, ctx_hi=56, ctx_source="hidden", verify="greedy",
+        verify_rows=8, planted_alpha=0.7, fixed_new=8,
+        notes="fully connected context fusion, shared K/V projection; fp32 path"),
+    "tiny-ablate-fp32": Workload(
+        name="tiny-ablate-fp32", shape=TINY_ABL, batch=1, block_len=8, n_anchor=1, n_drafts=1,
+        temperature=0.0, ctx_lo=56, ctx_hi=56, ctx_source="hidden", verify="greedy",
+        verify_rows=8, planted_alpha=0.7, fixed_new=8,
+        notes="mixing without softmax, shared K/V projection; fp32 path"),
+    "qwen3-8b-dflash": Workload(
+        name="qwen3-8b-dflash", shape=QWEN3_8B_FC, batch=32, block_len=16, n_anchor=1,
+        n_drafts=1, temperature=0.0, ctx_lo=256, ctx_hi=3072, ctx_source="hidden",
+        verify="greedy", verify_rows=16, planted_alpha=0.8818,
+        notes="the bench workload with the DFlash-style context path"),
     "qwen3-4b": Workload(
         name="qwen3-4b", shape=QWEN3_4B, batch=1, block_len=16, n_anchor=1, n_drafts=1,
         temperature=0.0, ctx_lo=1024, ctx_hi=1024, ctx_source="hidden", verify="greedy",

@@ -55,10 +55,15 @@ def make_weights(shape: DrafterShape, seed: int = 0, device="cpu") -> dict:
         w[name] = _randn(s, device, seed, name, std=0.02, mean=1.0, dtype=dt)
 
     if shape.n_target_layers > 0:
-        w["mix_logits"] = _randn((L, shape.n_target_layers), device, seed, "mix_logits")
-        gain("mix_norm_w", L, H)
-        lin("wk_ctx", L, kd, H)
-        lin("wv_ctx", L, kd, H)
+        if shape.ctx_fusion == "fc":
+            lin("fc_w", H, shape.n_target_layers * H)
+            gain("fc_norm_w", H)
+        else:
+            w["mix_logits"] = _randn((L, shape.n_target_layers), device, seed, "mix_logits")
+            gain("mix_norm_w", L, H)
+        if not shape.ctx_shared_kv:
+            lin("wk_ctx", L, kd, H)
+            lin("wv_ctx", L, kd, H)
     gain("attn_norm_w", L, H)
     gain("mlp_norm_w", L, H)
     lin("wq", L, qd, H)

@@ -272,3 +272,85 @@ def test_workloads_follow_page_constants():
     wl = synth.workload("specdiff2-7b")
     a = wl.planted_alpha
     assert abs(1 + sum(a ** m for m in range(1, 33)) - g["specdiff2_avg_streak"]["value"]) < 0.01
+
+
+# ---- context-path variants: fully connected fusion, raw mixing, shared K/V ---------------------
+
+TINY_FC = synth.workload("tiny-dflash-fp32").shape
+TINY_ABL = synth.workload("tiny-ablate-fp32").shape
+
+
+def test_fc_fusion_with_block_scalar_weights_equals_mixing(tiny_w):
+    """W_fc = [w_0 I | w_1 I | ...] with w the softmax mixing coefficients of a layer, and the same
+    gain, makes the fully connected fusion the same weighted sum as that layer's mixing."""
+    H, Lt = TINY.hidden, TINY.n_target_layers
+    h = _hidden(9)
+    for l in range(TINY.n_layers):
+        w = od.mix_weights(tiny_w["mix_logits"])[l]
+        Wfc = {"fc_w": np.concatenate([w[i] * np.eye(H) for i in range(Lt)], axis=1),
+               "fc_norm_w": tiny_w["mix_norm_w"][l]}
+        a = od.context_features(TINY_FC, Wfc, l, h)
+        b = od.context_features(TINY, tiny_w, l, h)
+        assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_fc_fusion_concatenates_target_layers_in_order():
+    """A fully connected layer that reads only target layer i's block of the concatenation
+    (identity there, zero elsewhere) gives RMSNorm(h_i) * g for every draft layer."""
+    H, Lt = TINY.hidden, TINY.n_target_layers
+    h = _hidden(7)
+    g = 1.0 + 0.1 * np.arange(H) / H
+    for i in range(Lt):
+        fc = np.zeros((H, Lt * H))
+        fc[:, i * H:(i + 1) * H] = np.eye(H)
+        c = od.context_features(TINY_FC, {"fc_w": fc, "fc_norm_w": g}, 1, h)
+        ref = h[:, i, :] / np.sqrt(np.mean(h[:, i, :].astype(np.float64) ** 2, 1, keepdims=True)
+                                   + TINY.rms_eps) * g
+        assert np.max(np.abs(c - ref)) < 1e-12
+
+
+def test_raw_mixing_with_log_coefficients_equals_softmax_mixing(tiny_w):
+    """Without softmax the coefficients are used as given: coefficients w that sum to 1 give the
+    same features as softmax mixing over logits log(w)."""
+    h = _hidden(6)
+    rng = np.random.default_rng(3)
+    w = rng.dirichlet(np.ones(TINY.n_target_layers), size=TINY.n_layers)
+    Wraw = dict(tiny_w, mix_logits=w)
+    Wsm = dict(tiny_w, mix_logits=np.log(w))
+    for l in range(TINY.n_layers):
+        a = od.context_features(TINY_ABL, Wraw, l, h)
+        b = od.context_features(TINY, Wsm, l, h)
+        assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_raw_mixing_is_linear_in_the_coefficients(tiny_w):
+    """Raw coefficients a and 3a give the same features up to RMSNorm's epsilon (the norm removes
+    the scale), while softmax(a) and softmax(3a) differ."""
+    h = _hidden(5)
+    W1 = dict(tiny_w)
+    W3 = dict(tiny_w, mix_logits=3.0 * tiny_w["mix_logits"])
+    a = od.context_features(TINY_ABL, W1, 0, h)
+    b = od.context_features(TINY_ABL, W3, 0, h)
+    assert np.max(np.abs(a - b)) < 1e-5
+    assert np.max(np.abs(od.context_features(TINY, W1, 0, h) -
+                         od.context_features(TINY, W3, 0, h))) > 1e-2
+
+
+def test_shared_kv_switch_uses_the_draft_projection(tiny_w):
+    """Context K/V without the split equal the split path with W_kc := W_kd, W_vc := W_vd."""
+    h = _hidden(10)
+    W = dict(tiny_w)
+    W["wk_ctx"], W["wv_ctx"] = W["wk_draft"], W["wv_draft"]
+    shared = TINY.__class__(**{**TINY.__dict__, "ctx_shared_kv": True})
+    for l in range(TINY.n_layers):
+        k1, v1 = od.context_kv(shared, tiny_w, l, h, pos0=3)
+        k2, v2 = od.context_kv(TINY, W, l, h, pos0=3)
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_generated_weights_follow_the_context_path():
+    fc = synth.make_weights(TINY_FC, seed=0)
+    abl = synth.make_weights(TINY_ABL, seed=0)
+    H, Lt = TINY.hidden, TINY.n_target_layers
+    assert tuple(fc["fc_w"].shape) == (H, Lt * H) and "mix_logits" not in fc
+    assert "wk_ctx" not in fc and "wk_ctx" not in abl and "mix_logits" in abl
