@@ -178,7 +178,12 @@ def algorithmic_costs(wl, ctx, new):
     T = int(np.sum(new))
     keys = ctx + new + B                              # keys attended per sequence
     c = {}
-    c["mix"] = (T * Lt * H * es + Ld * T * H * es, 0)
+    if getattr(sh, "ctx_fusion", "mix") == "fc":
+        # fully connected fusion: fusion weights and the concatenated target rows once, the
+        # shared feature written once
+        c["mix"] = (H * Lt * H * es + T * Lt * H * es + T * H * es, 2 * T * H * Lt * H)
+    else:
+        c["mix"] = (T * Lt * H * es + Ld * T * H * es, 0)
     c["gemm_ctxkv"] = (Ld * (2 * kd * H * es + T * H * es + T * 2 * kd * es),
                        2 * T * 2 * kd * H * Ld)
     c["gemm_qkv"] = (Ld * ((qd + 2 * kd) * H * es + M * H * es + M * (qd + 2 * kd) * es),

@@ -29,12 +29,13 @@ class ModelDesc(_c.Structure):
     _fields_ = [("hidden", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
                 ("ffn", _i32), ("n_layers", _i32), ("n_target_layers", _i32), ("vocab", _i32),
                 ("mask_token_id", _i32), ("dtype", _i32), ("rms_eps", _f32),
-                ("act_pairs", _i32), ("rope_theta", _c.c_double)]
+                ("act_pairs", _i32), ("rope_theta", _c.c_double), ("ctx_fusion", _i32),
+                ("mix_raw", _i32), ("ctx_shared_kv", _i32)]
 
 
 WEIGHT_FIELDS = ["mix_logits", "mix_norm_w", "wk_ctx", "wv_ctx", "attn_norm_w", "wq", "wk_draft",
                  "wv_draft", "wo", "mlp_norm_w", "w_gate", "w_up", "w_down", "final_norm_w",
-                 "embed", "lm_head"]
+                 "embed", "lm_head", "fc_w", "fc_norm_w"]
 
 
 class Weights(_c.Structure):
@@ -125,7 +126,10 @@ def model_desc(shape, dtype=None, act_pairs=0) -> ModelDesc:
                      shape.n_layers, shape.n_target_layers, shape.vocab,
                      shape.vocab - 1 if not hasattr(shape, "mask_token_id")
                      else shape.mask_token_id, code, float(shape.rms_eps), int(act_pairs),
-                     float(shape.rope_theta))
+                     float(shape.rope_theta),
+                     1 if getattr(shape, "ctx_fusion", "mix") == "fc" else 0,
+                     int(bool(getattr(shape, "mix_raw", False))),
+                     int(bool(getattr(shape, "ctx_shared_kv", False))))
 
 
 def kv_cache_shapes(shape, batch, ctx_capacity):

@@ -137,9 +137,10 @@ struct AttnArgs {
 hipError_t launch_prep(const int32_t* ctx_len, const int32_t* new_offsets, int batch,
                        int block_len, int n_new_total, int cap, int hd, const double* inv_freq,
                        RowMeta meta, int32_t* seq_status, hipStream_t s);
+// raw: the mixing coefficients are used as given (no softmax over the target layers)
 hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls, int n_tok,
-                              int H, int Lt, int Ld, const float* mix_logits, const void* g,
-                              void* out, void* out_lo, float eps, hipStream_t s);
+                              int H, int Lt, int Ld, const float* mix_logits, int raw,
+                              const void* g, void* out, void* out_lo, float eps, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H,
                         int V, float* x, hipStream_t s);

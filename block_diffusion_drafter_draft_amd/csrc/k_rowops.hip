@@ -111,7 +111,7 @@ template <> struct Vec16<float> { static constexpr int n = 4; };
 template <typename T, int CPT>
 __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
     const T* __restrict__ hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt, int Ld,
-    const float* __restrict__ mix_logits, const T* __restrict__ g, T* __restrict__ out,
+    const float* __restrict__ mix_logits, int raw, const T* __restrict__ g, T* __restrict__ out,
     T* __restrict__ out_lo, float eps) {
   constexpr int VEC = Vec16<T>::n;
   __shared__ float w[kMaxLd * kMaxLt];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
     for (int i = 0; i < Lt; ++i) m = fmaxf(m, lg[i]);
     float sum = 0.f;
     for (int i = 0; i < Lt; ++i) sum += expf(lg[i] - m);
-    for (int i = 0; i < Lt; ++i) w[tid * Lt + i] = expf(lg[i] - m) / sum;
+    for (int i = 0; i < Lt; ++i) w[tid * Lt + i] = raw ? lg[i] : expf(lg[i] - m) / sum;
   }
   __syncthreads();
   const int nch = H / VEC;
@@ -197,32 +197,32 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
 
 template <typename T>
 static hipError_t mix_dispatch(const void* hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt,
-                               int Ld, const float* ml, const void* g, void* out, void* out_lo,
-                               float eps, hipStream_t s) {
+                               int Ld, const float* ml, int raw, const void* g, void* out,
+                               void* out_lo, float eps, hipStream_t s) {
   constexpr int VEC = Vec16<T>::n;
   const int cpt = ceil_div(H / VEC, 256);
   const T* h = (const T*)hid;
   if (n_tok == 0) return hipSuccess;
   if (cpt <= 1)
     hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 1>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, (const T*)g, (T*)out, (T*)out_lo, eps);
+                       H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps);
   else if (cpt <= 2)
     hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 2>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, (const T*)g, (T*)out, (T*)out_lo, eps);
+                       H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps);
   else if (cpt <= 4)
     hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 4>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, (const T*)g, (T*)out, (T*)out_lo, eps);
+                       H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls, int n_tok,
-                              int H, int Lt, int Ld, const float* mix_logits, const void* g,
-                              void* out, void* out_lo, float eps, hipStream_t s) {
-  return dtype == 1 ? mix_dispatch<bf16>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out,
+                              int H, int Lt, int Ld, const float* mix_logits, int raw,
+                              const void* g, void* out, void* out_lo, float eps, hipStream_t s) {
+  return dtype == 1 ? mix_dispatch<bf16>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, raw, g, out,
                                          out_lo, eps, s)
-                    : mix_dispatch<float>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, g, out,
+                    : mix_dispatch<float>(hid, ts, ls, n_tok, H, Lt, Ld, mix_logits, raw, g, out,
                                           nullptr, eps, s);
 }
 

@@ -94,6 +94,7 @@ static bool bad_split(int32_t split) { return split < 0 || split > kMaxGemmSplit
 struct DraftBufs {
   RowMeta meta;
   void* ctxfeat;
+  float* fcout;         // fully connected fusion output before its RMSNorm [T, H] fp32
   float* x;
   void* xn;
   void* q;
@@ -138,10 +139,14 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.meta.rope_blk = c.take<float2>(M * half);
   t.meta.rope_ctx = c.take<float2>((int64_t)Tn * half);
   // context features; bf16 keeps the (high, low) pair so the K/V projection sees ~16 bits
+  // (one shared feature with the fully connected fusion, one per draft layer with mixing)
   const int nparts = d.dtype == DBD_BF16 ? 2 : 1;
+  const int nfeat = d.ctx_fusion ? 1 : d.n_layers;
   t.ctxfeat = d.n_target_layers > 0
-                  ? (void*)c.take<char>((int64_t)nparts * d.n_layers * Tn * d.hidden * es)
+                  ? (void*)c.take<char>((int64_t)nparts * nfeat * Tn * d.hidden * es)
                   : nullptr;
+  t.fcout = d.n_target_layers > 0 && d.ctx_fusion ? c.take<float>((int64_t)Tn * d.hidden)
+                                                  : nullptr;
   t.x = c.take<float>(M * d.hidden);
   t.xn = c.take<char>(M * d.hidden * es);
   t.q = c.take<char>(M * qd * es);
@@ -160,7 +165,7 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   {
     const bool pr = d.dtype == DBD_BF16 && d.act_pairs;
     const int kd = d.n_kv_heads * d.head_dim;
-    GemmPlan pl[6];
+    GemmPlan pl[7];
     int np = 0;
     pl[np++] = plan_gemm(d.dtype, EPI_QKV, g_ov_cfg[DBD_STAGE_GEMM_QKV], (int)M, qd + 2 * kd,
                          d.hidden, 1, 0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_QKV]);
@@ -177,6 +182,9 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
       pl[np++] = plan_gemm(d.dtype, EPI_CTXKV, g_ov_cfg[DBD_STAGE_GEMM_CTXKV], T, 2 * kd,
                            d.hidden, d.n_layers, 0, 0, d.dtype == DBD_BF16, true,
                            g_ov_split[DBD_STAGE_GEMM_CTXKV]);
+    if (d.n_target_layers > 0 && T > 0 && d.ctx_fusion)
+      pl[np++] = plan_gemm(d.dtype, EPI_STORE_F32, -1, T, d.hidden, d.n_target_layers * d.hidden,
+                           1, 0, 0, false, true);
     size_t part = 0;
     for (int i = 0; i < np; ++i)
       if (pl[i].split > 1) part = part > pl[i].part_bytes ? part : pl[i].part_bytes;
@@ -230,7 +238,12 @@ int check_desc(const dbd_model_desc* d) {
   }
   if (d->n_target_layers > 16)
     return fail(DBD_ERR_UNSUPPORTED, "n_target_layers %d > 16", d->n_target_layers);
-  if (d->n_target_layers > 0 && d->n_layers > 8)
+  if ((d->ctx_fusion != 0 && d->ctx_fusion != 1) || (d->mix_raw != 0 && d->mix_raw != 1) ||
+      (d->ctx_shared_kv != 0 && d->ctx_shared_kv != 1))
+    return fail(DBD_ERR_ARG, "ctx_fusion, mix_raw and ctx_shared_kv must be 0 or 1");
+  if (d->ctx_fusion && d->mix_raw)
+    return fail(DBD_ERR_ARG, "mix_raw applies to the mixing path only (ctx_fusion == 0)");
+  if (d->n_target_layers > 0 && !d->ctx_fusion && d->n_layers > 8)
     return fail(DBD_ERR_UNSUPPORTED, "target mixing supports at most 8 draft layers (got %d)",
                 d->n_layers);
   if (d->act_pairs != 0 && d->act_pairs != 1)
@@ -352,8 +365,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   const int es = elem_size(d.dtype);
   const int vec = 16 / es;
   if (d.n_target_layers > 0) {
-    if (!w->mix_logits || !w->mix_norm_w || !w->wk_ctx || !w->wv_ctx)
-      return fail(DBD_ERR_ARG, "mixing weights are NULL but n_target_layers > 0");
+    if (d.ctx_fusion ? (!w->fc_w || !w->fc_norm_w) : (!w->mix_logits || !w->mix_norm_w))
+      return fail(DBD_ERR_ARG, "context fusion weights are NULL but n_target_layers > 0");
+    if (!d.ctx_shared_kv && (!w->wk_ctx || !w->wv_ctx))
+      return fail(DBD_ERR_ARG, "context K/V weights are NULL but n_target_layers > 0");
     if (n_new_total > 0) {
       if (!target_hidden_new) return fail(DBD_ERR_ARG, "target_hidden_new is NULL");
       if (!aligned16(target_hidden_new) || hid_token_stride % vec || hid_layer_stride % vec)
@@ -361,6 +376,11 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
                     "that are multiples of %d elements", vec);
       if (hid_token_stride <= 0 || hid_layer_stride <= 0)
         return fail(DBD_ERR_ARG, "hidden strides must be positive");
+      if (d.ctx_fusion && (hid_layer_stride != d.hidden ||
+                           hid_token_stride < (int64_t)d.n_target_layers * d.hidden))
+        return fail(DBD_ERR_SHAPE, "fully connected fusion reads each token's target layers as "
+                    "one concatenated row: hid_layer_stride must be H and hid_token_stride >= "
+                    "L_t * H");
     }
   }
   if (!workspace || ((uintptr_t)workspace % kAlign))
@@ -388,23 +408,46 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
 
   // 1. ingest: mix + RMSNorm, then context K/V for every draft layer (batched over layers)
   if (d.n_target_layers > 0 && T > 0) {
+    const int nfeat = d.ctx_fusion ? 1 : d.n_layers;
     void* ctx_lo = d.dtype == DBD_BF16
-                       ? (void*)((char*)b.ctxfeat + (int64_t)d.n_layers * T * H * es)
+                       ? (void*)((char*)b.ctxfeat + (int64_t)nfeat * T * H * es)
                        : nullptr;
-    HIP_STAGE(DBD_STAGE_MIX, st, launch_mix_rmsnorm(d.dtype, target_hidden_new,
-                                                    hid_token_stride, hid_layer_stride, T, H,
-                                                    d.n_target_layers, d.n_layers,
-                                                    w->mix_logits, w->mix_norm_w, b.ctxfeat,
-                                                    ctx_lo, d.rms_eps, st));
+    if (d.ctx_fusion) {
+      // c = RMSNorm(fc_w . [h_0; ...; h_{L_t-1}]) * fc_norm_w, one feature for every layer
+      GemmArgs f{};
+      f.part = b.gemm_part;
+      f.part_cap = b.gemm_part_bytes;
+      f.A = target_hidden_new;
+      f.lda = hid_token_stride;
+      f.seg[0] = BSeg{w->fc_w, 0, H};
+      f.nseg = 1;
+      f.ldb = (int64_t)d.n_target_layers * H;
+      f.M = T;
+      f.N = H;
+      f.K = d.n_target_layers * H;
+      EpiArgs fe{};
+      fe.kind = EPI_STORE_F32;
+      fe.C = b.fcout;
+      fe.ldc = H;
+      HIP_STAGE(DBD_STAGE_MIX, st, launch_gemm(d.dtype, f, fe, 1, st));
+      HIP_STAGE(DBD_STAGE_MIX, st, launch_rmsnorm(d.dtype, b.fcout, w->fc_norm_w, b.ctxfeat,
+                                                  ctx_lo, T, H, d.rms_eps, 0, 0, st));
+    } else {
+      HIP_STAGE(DBD_STAGE_MIX, st, launch_mix_rmsnorm(d.dtype, target_hidden_new,
+                                                      hid_token_stride, hid_layer_stride, T, H,
+                                                      d.n_target_layers, d.n_layers,
+                                                      w->mix_logits, d.mix_raw, w->mix_norm_w,
+                                                      b.ctxfeat, ctx_lo, d.rms_eps, st));
+    }
     GemmArgs g{};
     g.part = b.gemm_part;
     g.part_cap = b.gemm_part_bytes;
     g.A = b.ctxfeat;
     g.A2 = ctx_lo;
     g.lda = H;
-    g.a_bs = (int64_t)T * H;
-    g.seg[0] = BSeg{w->wk_ctx, 0, kd};
-    g.seg[1] = BSeg{w->wv_ctx, kd, 2 * kd};
+    g.a_bs = d.ctx_fusion ? 0 : (int64_t)T * H;
+    g.seg[0] = BSeg{d.ctx_shared_kv ? w->wk_draft : w->wk_ctx, 0, kd};
+    g.seg[1] = BSeg{d.ctx_shared_kv ? w->wv_draft : w->wv_ctx, kd, 2 * kd};
     g.nseg = 2;
     g.ldb = H;
     g.b_bs = (int64_t)kd * H;
@@ -882,6 +925,7 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
                 vec);
   HIP_TRY(launch_mix_rmsnorm(desc->dtype, hidden, hid_token_stride, hid_layer_stride, n_tokens,
                              desc->hidden, desc->n_target_layers, desc->n_layers, mix_logits,
+                             desc->mix_raw,
                              mix_norm_w, out, nullptr, desc->rms_eps, (hipStream_t)stream));
   return DBD_OK;
 }

@@ -84,6 +84,17 @@ typedef struct {
                                 work; 0 = plain bf16 activations.  The mixed context features
                                 always use the pair. */
   double rope_theta;         /* e.g. 1e6 */
+  /* Context-feature path ([DFlare] sections on per-layer mixing and on splitting K/V by source;
+   * its ablations; [DFlash] fusion of the target features).  All 0 = the mixing drafter. */
+  int32_t ctx_fusion;        /* 0: per-draft-layer softmax mixing of the L_t target layers, then
+                                RMSNorm * mix_norm_w[l]; 1: one fully connected fusion of the
+                                concatenated target layers, RMSNorm(fc_w . [h_0; ...; h_{L_t-1}])
+                                * fc_norm_w, shared by every draft layer (needs
+                                hid_layer_stride == H) */
+  int32_t mix_raw;           /* ctx_fusion 0 only: 1 = mixing coefficients used as given, no
+                                softmax */
+  int32_t ctx_shared_kv;     /* 1 = the context K/V are projected with the draft block's
+                                wk_draft / wv_draft (no K/V split; wk_ctx / wv_ctx unused) */
 } dbd_model_desc;
 
 /* Drafter weights (device pointers, element type desc.dtype unless noted).  Per-layer tensors
@@ -105,6 +116,8 @@ typedef struct {
   const void* final_norm_w;  /* [H] */
   const void* embed;         /* [V, H] shared token embedding */
   const void* lm_head;       /* [V, H] shared LM head (may alias embed) */
+  const void* fc_w;          /* [H, L_t*H] fully connected context fusion (ctx_fusion == 1) */
+  const void* fc_norm_w;     /* [H] RMSNorm gain after the fusion (ctx_fusion == 1) */
 } dbd_weights;
 
 /* KV-cache layout (device, element type desc.dtype, caller-owned, persistent across calls):

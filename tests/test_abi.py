@@ -48,15 +48,35 @@ def test_library_exports_every_declared_function():
     assert not missing, missing
 
 
-def test_struct_layouts_match_header():
-    # dbd_model_desc: 10 int32 + 2 float + 1 double = 56 bytes; dbd_weights: 16 pointers
-    assert ctypes.sizeof(dbd.ModelDesc) == 56
-    assert ctypes.sizeof(dbd.Weights) == 16 * 8
+def test_struct_layouts_match_header(tmp_path):
+    """Every field offset and the size of dbd_model_desc and dbd_weights, as the C compiler lays
+    them out from include/dbd.h, equal the ctypes mirrors of the binding."""
+    import shutil
+    import subprocess
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     body = src[: src.index("} dbd_weights;")]
     body = body[body.rindex("typedef struct {"):]
     names = re.findall(r"\*\s*(\w+);", body)
     assert names == dbd.WEIGHT_FIELDS
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    probe = tmp_path / "probe.c"
+    lines = ['#include <stddef.h>', '#include <stdio.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for st, cls in (("dbd_model_desc", dbd.ModelDesc), ("dbd_weights", dbd.Weights)):
+        lines.append(f'  printf("{st} size %zu\\n", sizeof({st}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    lines.append("  return 0;\n}")
+    probe.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run([cc, str(probe), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for st, cls in (("dbd_model_desc", dbd.ModelDesc), ("dbd_weights", dbd.Weights)):
+        assert got[(st, "size")] == ctypes.sizeof(cls), st
+        for f, _ in cls._fields_:
+            assert got[(st, f)] == getattr(cls, f).offset, (st, f)
 
 
 def _desc(name="qwen3-8b", **kw):
@@ -265,3 +285,18 @@ def test_verify_sample_validation():
     assert call(args(V=1 << 18)) == -1
     assert call(args(wb=ws - 1)) == -4
     assert call(args(w=fake + 16)) == -4
+
+
+def test_context_path_switch_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    for kw, code in ((dict(ctx_fusion=2), -1), (dict(mix_raw=3), -1),
+                     (dict(ctx_shared_kv=-1), -1), (dict(ctx_fusion=1, mix_raw=1), -1)):
+        d = _desc(**kw)
+        out = ctypes.c_size_t(0)
+        assert L.dbd_draft_workspace_bytes(ctypes.byref(d), 32, 16, 1, 64, 1, 0.0, 4096,
+                                           ctypes.byref(out)) == code, kw
+    # the fusion workspace holds one shared feature instead of one per draft layer
+    mix = dbd.draft_workspace_bytes(_desc(), 32, 16, 1, 256, 1, 0.0, 4096)
+    fc = dbd.draft_workspace_bytes(_desc("qwen3-8b-dflash"), 32, 16, 1, 256, 1, 0.0, 4096)
+    assert fc < mix

@@ -173,3 +173,33 @@ def test_gpt_oss_20b_sampled_sequence_matches_oracle():
 @pytest.mark.timeout(900)
 def test_specdiff2_7b_sampled_sequence_matches_oracle():
     _run("specdiff2-7b", seqs=[2])
+
+
+@pytest.mark.parametrize("name", ["tiny-dflash-fp32", "tiny-ablate-fp32"])
+def test_context_path_variants_fp32_match_oracle(name):
+    """Fully connected fusion with the shared K/V projection, and mixing without softmax with the
+    shared projection: cache K/V and logits within 1e-4 of the oracle, argmax drafts equal."""
+    case, drafts, logits = _run(name)
+    toks, hid, kv = case.oracle_inputs(0)
+    ref = od.drafter_forward(case.shape, case.cpu_weights(), toks, 1, hidden=hid)
+    assert np.array_equal(drafts[0, 0].cpu().numpy(), ref["logits"].argmax(-1))
+
+
+def test_tiny_dflash_cold_ingest_equals_incremental():
+    wl = synth.workload("tiny-dflash-fp32")
+    case = Case(wl, dev=DEV)
+    case.fill_cache()
+    d1, l1, _ = case.step()
+    case2 = Case(wl, dev=DEV, ctx=np.zeros(1, np.int64), new=case.ctx + case.new)
+    d2, l2, _ = case2.step()
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(d1, d2)
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_dflash_sampled_sequence_matches_oracle():
+    """The bench workload with the fully connected context fusion, bf16; the shortest sequence
+    keeps the oracle's fusion GEMM (36,864 inputs per position) quick."""
+    wl = synth.workload("qwen3-8b-dflash")
+    ctx, _ = synth.make_lengths(wl, 0)
+    _run("qwen3-8b-dflash", seqs=[int(np.argmin(ctx))])
