@@ -39,6 +39,8 @@ def parse():
                     help="skip the instrumented pass and the cold-ingest timing")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-traffic", metavar="DIR")
+    ap.add_argument("--sweep-block", action="store_true",
+                    help="draft_block latency against block length (SpecDiff-2-shaped drafter)")
     return ap.parse_args()
 
 
@@ -206,6 +208,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.sweep_block:
+        sweep_block(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -398,6 +403,95 @@ def main():
         "setup_s": round(t_setup, 1),
     }
     print(json.dumps(out), flush=True)
+
+
+def sweep_block(args, gammas=(8, 16, 32, 64), ctx_len=256):
+    """draft_block latency against the block length gamma for the SpecDiff-2-shaped drafter (28
+    layers, hidden 3584, 8 joint drafts at T = 1.5, batch 4) over a cached context of 256
+    positions: the forward over gamma masks plus drafting.  The SpecDiff-2 notes (latency
+    analysis) find the diffusion drafter's latency nearly flat in gamma until the GPU saturates;
+    this measures the same shape of curve with synthetic weights."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import block_diffusion_drafter_draft_amd as dbd
+    import synth
+    dev = "cuda"
+    base = synth.workload("specdiff2-7b")
+    sh = base.shape
+    N, K, T = base.batch, base.n_drafts, base.temperature
+    W = synth.make_weights(sh, 0, dev)
+    desc, wst = dbd.model_desc(sh, act_pairs=base.act_pairs), dbd.weights_struct(W)
+    Kc, Vc = synth.make_cache_kv(sh, N, ctx_len, 0, dev)
+    points = []
+    for g in gammas:
+        cap = ((ctx_len + g + 63) // 64) * 64
+        ks, vs = dbd.kv_cache_shapes(sh, N, cap)
+        kv_k = torch.zeros(ks, dtype=Kc.dtype, device=dev)
+        kv_v = torch.zeros(vs, dtype=Vc.dtype, device=dev)
+        kv_k[:, :, :, :ctx_len] = Kc
+        kv_v[:, :, :, : ctx_len // 8] = dbd.pack_values(Vc)
+        tokens = torch.full((N, g), sh.mask_token_id, dtype=torch.int32, device=dev)
+        off = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+        ctx = torch.full((N,), ctx_len, dtype=torch.int32, device=dev)
+        drafts = torch.empty((N, K, g), dtype=torch.int32, device=dev)
+        ws = torch.empty(dbd.draft_workspace_bytes(desc, N, g, 0, 0, K, T, cap),
+                         dtype=torch.uint8, device=dev)
+        run = lambda: dbd.draft_block(desc, wst, tokens, None, off, ctx, kv_k, kv_v, drafts, ws,
+                                      0, n_drafts=K, temperature=T, seed=7, n_anchor=0)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        # the same call captured once in a HIP graph and replayed: the ~10 launches per layer
+        # are short at these sizes, so launch gaps are a visible part of the eager time.  Every
+        # replay is checked against the eager drafts (same seed), with eager work in between.
+        ref = drafts.clone()
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            run()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            run()
+        for _ in range(3):
+            drafts.fill_(-1)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(drafts, ref), "graph replay differs from the eager call"
+            run()
+            torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / args.steps
+        dbd.timing_reset()
+        dbd.timing_enable(True)
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        tm = dbd.timing_read()
+        dbd.timing_enable(False)
+        dbd.timing_reset()
+        stages = {k: round(v[0] / args.steps, 3) for k, v in tm.items() if v[1]}
+        points.append({"gamma": g, "ms": round(ms, 3), "graph_ms": round(gms, 3),
+                       "drafted_tok_per_s": round(N * K * g / (gms * 1e-3), 1),
+                       "stage_ms": stages})
+        print(f"gamma {g}: {ms:.3f} ms eager, {gms:.3f} ms graph", file=sys.stderr, flush=True)
+        del graph, kv_k, kv_v, ws
+    print(json.dumps({"sweep": "block_len", "workload": f"specdiff2-7b-shaped drafter, batch {N}, "
+                      f"{K} drafts at T={T}, cached context {ctx_len}",
+                      "unit": "ms per draft_block (eager; graph = one HIP graph replay)",
+                      "points": points}), flush=True)
 
 
 def cpu_baseline(wl, W, tokens, hidden, ctx, new, tlogits, v_drafts, min_s=10.0, max_seqs=8):

@@ -9,6 +9,8 @@
 // 16x16x32 bf16, so that its lanes hold 8 consecutive keys of one query (keys are permuted inside
 // the MFMA tiles), runs the online softmax in fp32 (exp2 domain) and feeds P^T straight from
 // registers into O^T += V^T.P^T.  Splits of one (n, g) are merged by attn_combine_kernel.
+#include <algorithm>
+
 #include "dbd_internal.h"
 
 namespace dbd {
@@ -37,7 +39,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   constexpr int VI = (VT + NT - 1) / NT;        // V chunks staged per thread
   __shared__ __attribute__((aligned(16))) bf16 Ks[KCH * HD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[HD * KCH];
-  const int s = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+  // grid.y = kv head + kvh * row block: a group of more than 16 * NW query rows is spread over
+  // several workgroups that read the same keys
+  const int s = blockIdx.x, g = blockIdx.y % a.kvh, rb = blockIdx.y / a.kvh, n = blockIdx.z;
   const int L = a.seq_keys[n];
   const int k_begin = s * a.split;
   if (L <= 0 || k_begin >= L) return;
@@ -45,15 +49,16 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   const int nsplit = (L + a.split - 1) / a.split;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.block_len * a.grp;
+  const int r0 = rb * 16 * NW;
 
   const bf16* Kg = (const bf16*)a.kv_k + ((int64_t)n * a.kvh + g) * a.cap * HD;
   // V cache of (n, g): blocks of 8 positions, [cap/8][HD][8]
   const bf16* Vg = (const bf16*)a.kv_v + ((int64_t)n * a.kvh + g) * HD * a.cap;
 
   // this lane's query row (column of S^T / O^T)
-  const int r = wave * 16 + (lane & 15);
+  const int r = r0 + wave * 16 + (lane & 15);
   const bool rvalid = r < R;
-  const bool wactive = wave * 16 < R;           // wave owns at least one query row
+  const bool wactive = r0 + wave * 16 < R;      // wave owns at least one query row
   const int b = rvalid ? r % a.block_len : 0, h = rvalid ? r / a.block_len : 0;
   const int64_t qrow = (int64_t)n * a.block_len + b;
   const int qcol = (g * a.grp + h) * HD;
@@ -333,7 +338,8 @@ hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s)
   const int R = a.block_len * a.grp;
   dim3 cgrid(ceil_div(R, 4), a.kvh, a.batch);
   if (dtype == 1) {
-    const int nw = ceil_div(R, 16);
+    const int nw = std::min(16, ceil_div(R, 16));
+    grid.y = a.kvh * ceil_div(R, 16 * nw);
     if (hd == 128) launch_bf16<128>(a, grid, nw, s);
     else launch_bf16<64>(a, grid, nw, s);
     hipError_t err = hipGetLastError();

@@ -260,9 +260,6 @@ int check_draft_shape(const dbd_model_desc* d, int N, int B, int n_anchor, int T
   if (N < 1) return fail(DBD_ERR_ARG, "batch %d < 1", N);
   if (n_anchor != 0 && n_anchor != 1) return fail(DBD_ERR_ARG, "n_anchor must be 0 or 1");
   if (B < 1 + n_anchor || B > 64) return fail(DBD_ERR_SHAPE, "block_len %d out of range", B);
-  const int grp = d->n_q_heads / d->n_kv_heads;
-  if (d->dtype == DBD_BF16 && B * grp > 256)
-    return fail(DBD_ERR_UNSUPPORTED, "block_len * (q_heads / kv_heads) = %d > 256", B * grp);
   if (T < 0) return fail(DBD_ERR_ARG, "n_new_total %d < 0", T);
   if (d->n_target_layers == 0 && T > 0)
     return fail(DBD_ERR_ARG, "n_new_total must be 0 for a drafter without target mixing");

@@ -203,3 +203,21 @@ def test_qwen3_8b_dflash_sampled_sequence_matches_oracle():
     wl = synth.workload("qwen3-8b-dflash")
     ctx, _ = synth.make_lengths(wl, 0)
     _run("qwen3-8b-dflash", seqs=[int(np.argmin(ctx))])
+
+
+def test_query_groups_beyond_one_workgroup_match_oracle():
+    """8 query heads per kv head and a 40-position block: 320 query rows per kv head, more than
+    one attention workgroup holds, so two row blocks read the same keys (bf16 path)."""
+    sh = synth.DrafterShape(hidden=512, n_q_heads=16, n_kv_heads=2, head_dim=64, ffn=1024,
+                            n_layers=2, n_target_layers=2, vocab=2048, dtype="bf16")
+    wl = synth.Workload(name="wide-group", shape=sh, batch=2, block_len=40, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=90, ctx_hi=130, ctx_source="hidden",
+                        verify="greedy", verify_rows=40, planted_alpha=0.8, fixed_new=8)
+    print("draft_block workload=wide-group", flush=True)
+    case = Case(wl, dev=DEV)
+    case.fill_cache()
+    drafts, logits, status = case.step()
+    torch.cuda.synchronize()
+    assert torch.all(status == 0)
+    _check_drafts_property(case, drafts, logits)
+    _compare(case, logits, range(wl.batch), [])
