@@ -21,6 +21,10 @@ hardware, probabilities are built from integers:
       idx = (n*K + k)*D + j, all modulo 2^64.
   R5  sampling: thr = (u * Z) >> 32; token = the smallest v with q_0 + ... + q_v > thr.
   R6  selection probability of token x: double(q_x) / double(Z), each rounded to nearest.
+  Top-p (a reading; the pages name no nucleus rule): the nucleus is the shortest run of tokens,
+      in order of decreasing weight with ties by increasing index, whose mass reaches
+      ceil(p * Z) for p the float32 value (a dyadic rational, so the ceiling is exact); the draw
+      is R5 on the weights restricted to it.
 """
 import math
 
@@ -107,10 +111,37 @@ def sample_token(q, Z: int, u: int) -> int:
     return v
 
 
-def sample_drafts(logits, n_drafts: int, temperature: float, seed: int) -> np.ndarray:
+def top_p_threshold(Z: int, top_p: float) -> int:
+    """ceil(p * Z) for p the float32 value of top_p, exactly (p is a dyadic rational)."""
+    from fractions import Fraction
+    return math.ceil(Fraction(float(np.float32(top_p))) * int(Z))
+
+
+def nucleus_weights(q, Z: int, top_p: float):
+    """Top-p filter on integer weights: the tokens ordered by weight (descending), ties by index
+    (ascending); the nucleus is the shortest prefix of that order whose mass reaches
+    ceil(p * Z); weights outside it become 0.  p >= 1 keeps every token."""
+    q = [int(a) for a in q]
+    if float(np.float32(top_p)) >= 1.0:
+        return q
+    need = top_p_threshold(Z, top_p)
+    order = sorted(range(len(q)), key=lambda v: (-q[v], v))
+    keep, mass = set(), 0
+    for v in order:
+        if mass >= need:
+            break
+        keep.add(v)
+        mass += q[v]
+    return [a if v in keep else 0 for v, a in enumerate(q)]
+
+
+def sample_drafts(logits, n_drafts: int, temperature: float, seed: int,
+                  top_p: float = 1.0) -> np.ndarray:
     """K joint drafts per sequence from single-step marginals (SpecDiff-2 notes, section 5.2).
 
-    logits: [N, D, V] fp32.  temperature <= 0 gives the argmax draft (K must be 1).
+    logits: [N, D, V] fp32.  temperature <= 0 gives the argmax draft (K must be 1).  top_p < 1
+    restricts each position's draw to its nucleus (``nucleus_weights``); the draw is R5 on the
+    restricted weights, in token order.
     Returns [N, K, D] int32."""
     logits = np.asarray(logits, dtype=np.float32)
     N, D, V = logits.shape
@@ -125,6 +156,9 @@ def sample_drafts(logits, n_drafts: int, temperature: float, seed: int) -> np.nd
     for n in range(N):
         for j in range(D):
             q, Z = row_weights(logits[n, j], inv_t)
+            if float(np.float32(top_p)) < 1.0:
+                w = nucleus_weights(q, Z, top_p)
+                q, Z = np.array(w, dtype=np.uint64), sum(w)
             for k in range(n_drafts):
                 out[n, k, j] = sample_token(q, Z, draw_u32(seed, n, k, j, n_drafts, D))
     return out

@@ -1,5 +1,6 @@
 """Pins of the integer-exact numerics contract (oracle/dnc.py) against published definitions,
 error bounds, statistics and brute force.  CPU only."""
+import itertools
 import math
 import os
 
@@ -153,3 +154,74 @@ def test_sample_drafts_argmax_mode_and_shapes():
     s = dnc.sample_drafts(lg, 4, 1.5, 123)
     assert s.shape == (2, 4, 3) and s.min() >= 0 and s.max() < 17
     assert np.array_equal(s, dnc.sample_drafts(lg, 4, 1.5, 123))   # pure function of the seed
+
+
+# ---- top-p nucleus filter ----
+
+def test_top_p_nucleus_is_a_smallest_heaviest_set_brute_force():
+    """Against every subset of a tiny vocabulary: the nucleus reaches ceil(p Z), no smaller subset
+    does, every token outside it weighs no more than every token inside, and among equal
+    weights the lower indices are inside."""
+    rng = np.random.default_rng(4)
+    for _ in range(60):
+        V = int(rng.integers(2, 9))
+        logits = rng.integers(-4, 3, V).astype(np.float32) * np.float32(0.5)   # planted ties
+        q, Z = dnc.row_weights(logits)
+        p = float(np.float32(rng.uniform(0.05, 0.999)))
+        need = dnc.top_p_threshold(Z, p)
+        w = dnc.nucleus_weights(q, Z, p)
+        inside = [v for v in range(V) if w[v] > 0]
+        assert sum(int(q[v]) for v in inside) >= need
+        best = min(len(S) for r in range(1, V + 1) for S in itertools.combinations(range(V), r)
+                   if sum(int(q[v]) for v in S) >= need)
+        assert len(inside) == best
+        outside = [v for v in range(V) if w[v] == 0]
+        if outside and inside:
+            assert max(int(q[v]) for v in outside) <= min(int(q[v]) for v in inside)
+        for a in inside:
+            for b in outside:
+                if int(q[a]) == int(q[b]):
+                    assert a < b
+
+
+def test_top_p_threshold_is_the_exact_ceiling():
+    from fractions import Fraction
+    for Z in (1, 7, 1 << 40, (1 << 57) + 12345):
+        for p in (0.5, 0.9, 0.25, 1e-7, 0.3):
+            pf = Fraction(float(np.float32(p)))
+            t = dnc.top_p_threshold(Z, p)
+            assert t - 1 < pf * Z <= t
+
+
+def test_top_p_one_is_plain_sampling_and_tiny_p_is_argmax():
+    rng = np.random.default_rng(5)
+    logits = (rng.normal(size=(3, 4, 50)) * 2).astype(np.float32)
+    a = dnc.sample_drafts(logits, 4, 1.3, seed=8)
+    b = dnc.sample_drafts(logits, 4, 1.3, seed=8, top_p=1.0)
+    assert np.array_equal(a, b)
+    c = dnc.sample_drafts(logits, 4, 1.3, seed=8, top_p=1e-6)
+    assert np.array_equal(c, np.broadcast_to(logits.argmax(-1)[:, None, :], c.shape))
+
+
+@pytest.mark.parametrize("p", [0.6, 0.9])
+def test_top_p_sampler_chi_square(p):
+    """Draws restricted to the nucleus follow the fp64 softmax renormalised over it (the nucleus
+    boundary is away from p here, so fp64 and the integer weights select the same set)."""
+    from scipy import stats
+    V, n = 16, 20_000
+    logits = np.linspace(2.0, -2.0, V).astype(np.float32)
+    P = np.exp(logits.astype(np.float64) - logits.max())
+    P /= P.sum()
+    cum = np.cumsum(np.sort(P)[::-1])
+    k = int(np.searchsorted(cum, p) + 1)
+    assert min(abs(cum - p)) > 1e-3
+    keep = np.argsort(-P, kind="stable")[:k]
+    Pn = np.zeros(V)
+    Pn[keep] = P[keep] / P[keep].sum()
+    rows = np.broadcast_to(logits, (n, 1, V)).copy()
+    toks = dnc.sample_drafts(rows, 1, 1.0, seed=3, top_p=p)[:, 0, 0]
+    counts = np.bincount(toks, minlength=V)
+    assert counts[Pn == 0].sum() == 0
+    sel = Pn > 0
+    chi2 = float(((counts[sel] - n * Pn[sel]) ** 2 / (n * Pn[sel])).sum())
+    assert chi2 < stats.chi2.ppf(1 - 1e-4, int(sel.sum()) - 1), chi2
