@@ -319,7 +319,7 @@ def main():
 
     # lossless stochastic verification (not part of the step): the step's target rows against
     # draft logits near them, drafts sampled from the draft logits by the library's sampler
-    vsample = None
+    vsample = top_p = None
     if not args.profile_steps_only:
         g = torch.Generator(device=dev).manual_seed(2)
         dlog = (tlogits[:, :D] + 0.5 * torch.randn(tlogits[:, :D].shape, generator=g,
@@ -344,6 +344,23 @@ def main():
         torch.cuda.synchronize()
         vms = v0.elapsed_time(v1) / args.steps
         vb = (N * wl.verify_rows + N * D) * V * 4
+        # top-p nucleus drafting on the same draft logits (8 draws per position, p = 0.9)
+        tws = torch.empty(dbd.sample_top_p_workspace_bytes(N, D, V), dtype=torch.uint8,
+                          device=dev)
+        tout = torch.empty((N, 8, D), dtype=torch.int32, device=dev)
+        for i in range(3):
+            dbd.sample_top_p(dlog, 8, 1.0, 0.9, i, tout, tws)
+        torch.cuda.synchronize()
+        v0.record()
+        for i in range(args.steps):
+            dbd.sample_top_p(dlog, 8, 1.0, 0.9, i, tout, tws)
+        v1.record()
+        torch.cuda.synchronize()
+        tms = v0.elapsed_time(v1) / args.steps
+        tb = N * D * V * 4
+        top_p = {"ms": round(tms, 4), "logit_bytes": tb, "draws_per_position": 8, "p": 0.9,
+                 "GBps": round(tb / (tms * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(tb / (tms * 1e-3) / HBM_PEAK, 4)}
         vsample = {"ms": round(vms, 4), "logit_bytes": vb,
                    "GBps": round(vb / (vms * 1e-3) / 1e9, 1),
                    "hbm_frac": round(vb / (vms * 1e-3) / HBM_PEAK, 4),
@@ -399,6 +416,7 @@ def main():
         "stages": stages,
         "cold_ingest": cold_info,
         "verify_sample": vsample,
+        "top_p_sampling": top_p,
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),
     }

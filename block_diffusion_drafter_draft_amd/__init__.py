@@ -77,6 +77,9 @@ def lib():
             "select_streak": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]),
             "dbd_sample_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
+            "dbd_sample_top_p_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
+            "dbd_sample_top_p": (_i32, [_vp, _i32, _i32, _i32, _i32, _f32, _f32, _u64, _vp,
+                                        _vp, _sz, _vp]),
             "dbd_sample_from_logits": (_i32, [_vp, _i32, _i32, _i32, _i32, _f32, _u64, _vp, _vp,
                                               _sz, _vp]),
             "dbd_mix_rmsnorm": (_i32, [_c.POINTER(ModelDesc), _vp, _vp, _vp, _i64, _i64, _i32,
@@ -253,6 +256,21 @@ def sample_from_logits(logits, n_drafts, temperature, seed, out, workspace, stre
     _check(lib().dbd_sample_from_logits(
         _ptr(logits), N, D, V, n_drafts, float(temperature), int(seed) & (2**64 - 1), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, logits)))
+
+
+def sample_top_p_workspace_bytes(batch, n_draft, vocab) -> int:
+    out = _sz(0)
+    _check(lib().dbd_sample_top_p_workspace_bytes(batch, n_draft, vocab, _c.byref(out)))
+    return out.value
+
+
+def sample_top_p(logits, n_drafts, temperature, top_p, seed, out, workspace, stream=None):
+    """logits [N, D, V] fp32 -> out [N, K, D] int32, each draw restricted to its top-p nucleus."""
+    N, D, V = logits.shape
+    _check(lib().dbd_sample_top_p(
+        _ptr(logits), N, D, V, n_drafts, float(temperature), float(top_p),
+        int(seed) & (2**64 - 1), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, logits)))
 
 
 def mix_rmsnorm(desc, mix_logits, mix_norm_w, hidden, out, stream=None):

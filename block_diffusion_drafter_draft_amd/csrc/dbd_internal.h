@@ -173,11 +173,19 @@ hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int rows, int
 hipError_t launch_zsum_partial(const float* x, int rows, int vocab, int chunk, const float* pv,
                                const int32_t* pi, float inv_t, uint64_t* zpart, float* row_max,
                                int32_t* row_arg, hipStream_t s);
+// topp: optional per-row nucleus state of launch_top_p ({q*, -, v_cut, -}); zpart then holds
+// the nucleus chunk sums (rz of launch_top_p)
 hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
                               const uint64_t* zpart, const float* row_max, float inv_t,
                               int n_draft, int n_drafts, uint64_t seed,
                               const int32_t* row_valid_pos, int block_len, int n_anchor,
-                              int32_t* out, hipStream_t s);
+                              const int64_t* topp, int32_t* out, hipStream_t s);
+// Top-p nucleus of each row after launch_zsum_partial (zpart, row_max): p = mp / 2^sp exactly.
+// st [rows * 4] int64, hist [rows * chunks * 256] uint64, cnt [rows * chunks] int32,
+// rz [rows * chunks] uint64 (the nucleus chunk sums).
+hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const uint64_t* zpart,
+                        const float* row_max, float inv_t, uint64_t mp, int sp, int64_t* st,
+                        uint64_t* hist, int32_t* cnt, uint64_t* rz, hipStream_t s);
 hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int32_t* pflag,
                                   int nch, const int32_t* drafts, int draft_stride, int batch,
                                   int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,

@@ -60,6 +60,8 @@ __device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
 // 256 * PICK_SEG wide.
 constexpr int PICK_SEG = 16;
 
+typedef unsigned __int128 u128;
+
 // ------------------------------------------------------------------ block reductions
 template <int NT>
 __device__ __forceinline__ void block_argmax(float& v, int& i, float* sv, int* si) {
@@ -265,7 +267,8 @@ hipError_t launch_zsum_partial(const float* x, int rows, int vocab, int chunk, c
 __global__ __launch_bounds__(256) void sample_pick_kernel(
     const float* __restrict__ x, int V, int chunk, int nch, const uint64_t* __restrict__ zpart,
     const float* __restrict__ row_max, float inv_t, int n_draft, int n_drafts, uint64_t seed,
-    const int32_t* __restrict__ blk_pos, int block_len, int n_anchor, int32_t* __restrict__ out) {
+    const int32_t* __restrict__ blk_pos, int block_len, int n_anchor,
+    const int64_t* __restrict__ topp, int32_t* __restrict__ out) {
   __shared__ uint64_t s_thr;
   __shared__ int s_chunk;
   __shared__ uint64_t wsum[4];
@@ -302,13 +305,20 @@ __global__ __launch_bounds__(256) void sample_pick_kernel(
   const int v0 = c * chunk, v1 = min(V, v0 + chunk);
   const int per = (chunk + 255) / 256;         // contiguous segment per thread, loaded once
   const int a0 = v0 + threadIdx.x * per, a1 = min(v1, a0 + per);
+  // top-p: only the nucleus (weight above q*, or equal to it up to index v_cut) keeps its weight
+  const uint64_t qs = topp ? (uint64_t)topp[(int64_t)row * 4] : 0;
+  const int vcut = topp ? (int)topp[(int64_t)row * 4 + 2] : 0;
+  auto wq = [&](float l, int v) __attribute__((always_inline)) -> uint64_t {
+    const uint64_t q = weight_q(l, M, inv_t);
+    return (!topp || q > qs || (q == qs && v <= vcut)) ? q : 0;
+  };
   float lx[PICK_SEG];
 #pragma unroll
   for (int e = 0; e < PICK_SEG; ++e) lx[e] = a0 + e < a1 ? xr[a0 + e] : 0.f;
   uint64_t mine = 0;
 #pragma unroll
   for (int e = 0; e < PICK_SEG; ++e)
-    if (a0 + e < a1) mine += weight_q(lx[e], M, inv_t);
+    if (a0 + e < a1) mine += wq(lx[e], a0 + e);
   // exclusive scan of the 256 segment sums: wave scan then wave offsets
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t incl = mine;
@@ -328,7 +338,7 @@ __global__ __launch_bounds__(256) void sample_pick_kernel(
 #pragma unroll
     for (int e = 0; e < PICK_SEG; ++e) {
       if (tok < 0 && a0 + e < a1) {
-        run += weight_q(lx[e], M, inv_t);
+        run += wq(lx[e], a0 + e);
         if (run > thr) tok = a0 + e;
       }
     }
@@ -340,13 +350,229 @@ hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
                               const uint64_t* zpart, const float* row_max, float inv_t,
                               int n_draft, int n_drafts, uint64_t seed,
                               const int32_t* row_valid_pos, int block_len, int n_anchor,
-                              int32_t* out, hipStream_t s) {
+                              const int64_t* topp, int32_t* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (chunk > 256 * PICK_SEG) return hipErrorInvalidValue;
   const int nch = ceil_div(vocab, chunk);
   hipLaunchKernelGGL(sample_pick_kernel, dim3(n_drafts, rows), dim3(256), 0, s, x, vocab, chunk,
                      nch, zpart, row_max, inv_t, n_draft, n_drafts, seed, row_valid_pos,
-                     block_len, n_anchor, out);
+                     block_len, n_anchor, topp, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ top-p nucleus
+// The nucleus of a row is the shortest run of tokens, in order of decreasing integer weight
+// with ties by increasing index, whose mass reaches Tp = ceil(p * Z) (p = mp / 2^sp exactly).
+// Its boundary weight q* is found by a radix select on the 41-bit weights, most significant
+// digit first, weighted by mass: per digit, every chunk histograms the mass of the tokens whose
+// higher digits equal the prefix found so far (topp_hist_kernel), then topp_select_kernel picks
+// the digit where the mass above reaches the remaining target.  The tokens of weight q* enter in
+// index order until the target is met: topp_tie_kernel counts them per chunk, topp_cut_kernel
+// finds the index of the last one needed.  State per row: {q*, remaining target, v_cut, -}.
+constexpr int TOPP_DIGITS = 6;
+__constant__ int kToppShift[TOPP_DIGITS] = {33, 25, 17, 9, 1, 0};
+__constant__ int kToppWidth[TOPP_DIGITS] = {8, 8, 8, 8, 8, 1};
+
+__global__ __launch_bounds__(64) void topp_init_kernel(const uint64_t* __restrict__ zpart,
+                                                       int nch, uint64_t mp, int sp,
+                                                       int64_t* __restrict__ st) {
+  const int row = blockIdx.x;
+  uint64_t z = 0;
+  for (int c = threadIdx.x; c < nch; c += 64) z += zpart[(int64_t)row * nch + c];
+  z = wave_sum_u64(z);
+  if (threadIdx.x == 0) {
+    // Tp = ceil(mp * Z / 2^sp); mp < 2^24 and Z < 2^58, so mp * Z < 2^82
+    const u128 prod = (u128)mp * z;
+    const uint64_t tp = sp >= 82 ? (prod ? 1 : 0)
+                                 : (uint64_t)((prod + (((u128)1 << sp) - 1)) >> sp);
+    st[(int64_t)row * 4] = 0;
+    st[(int64_t)row * 4 + 1] = (int64_t)tp;
+  }
+}
+
+// grid (chunks, rows): mass histogram of digit `d` over the chunk's tokens that match the prefix
+__global__ __launch_bounds__(256) void topp_hist_kernel(
+    const float* __restrict__ x, int V, int chunk, int nch, const float* __restrict__ row_max,
+    float inv_t, int d, const int64_t* __restrict__ st, uint64_t* __restrict__ hist) {
+  __shared__ unsigned long long lh[256];
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int shift = kToppShift[d], width = kToppWidth[d];
+  const uint64_t pre = (uint64_t)st[(int64_t)row * 4] >> (shift + width);
+  lh[threadIdx.x] = 0;
+  __syncthreads();
+  const float M = row_max[row];
+  const float* xr = x + (int64_t)row * V;
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  const uint32_t mask = (1u << width) - 1;
+  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+    const uint64_t q = weight_q(xr[v], M, inv_t);
+    if ((q >> (shift + width)) == pre && q)
+      atomicAdd(&lh[(q >> shift) & mask], (unsigned long long)q);
+  }
+  __syncthreads();
+  hist[((int64_t)row * nch + c) * 256 + threadIdx.x] = lh[threadIdx.x];
+}
+
+// one workgroup per row: bucket masses (thread b sums bucket b over the chunks), the suffix sums
+// from the top bucket, and the bucket b with above(b) < R <= above(b) + mass(b)
+__global__ __launch_bounds__(256) void topp_select_kernel(const uint64_t* __restrict__ hist,
+                                                          int nch, int d,
+                                                          int64_t* __restrict__ st) {
+  __shared__ uint64_t wtot[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int shift = kToppShift[d], width = kToppWidth[d];
+  uint64_t m = 0;
+  for (int c = 0; c < nch; ++c) m += hist[((int64_t)row * nch + c) * 256 + tid];
+  // inclusive suffix sum over buckets: thread tid gets sum_{b >= tid} mass(b)
+  const int lane = tid & 63, w = tid >> 6;
+  uint64_t incl = m;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_down((uint32_t)incl, o, 64);
+    const uint32_t hi = __shfl_down((uint32_t)(incl >> 32), o, 64);
+    if (lane + o < 64) incl += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane == 0) wtot[w] = incl;
+  __syncthreads();
+  for (int q = w + 1; q < 4; ++q) incl += wtot[q];
+  const uint64_t above = incl - m;
+  const uint64_t R = (uint64_t)st[(int64_t)row * 4 + 1];
+  if (tid < (1 << width) && m && above < R && R <= above + m) {
+    st[(int64_t)row * 4] = (int64_t)((uint64_t)st[(int64_t)row * 4] | ((uint64_t)tid << shift));
+    st[(int64_t)row * 4 + 1] = (int64_t)(R - above);
+  }
+}
+
+// grid (chunks, rows): tokens of weight q* per chunk
+__global__ __launch_bounds__(256) void topp_tie_kernel(const float* __restrict__ x, int V,
+                                                       int chunk, int nch,
+                                                       const float* __restrict__ row_max,
+                                                       float inv_t,
+                                                       const int64_t* __restrict__ st,
+                                                       int32_t* __restrict__ cnt) {
+  __shared__ int red[4];
+  const int c = blockIdx.x, row = blockIdx.y;
+  const uint64_t qs = (uint64_t)st[(int64_t)row * 4];
+  const float M = row_max[row];
+  const float* xr = x + (int64_t)row * V;
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  int k = 0;
+  for (int v = v0 + threadIdx.x; v < v1; v += 256) k += weight_q(xr[v], M, inv_t) == qs;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) k += __shfl_xor(k, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[(int64_t)row * nch + c] = red[0] + red[1] + red[2] + red[3];
+}
+
+// one workgroup per row: n_tie = ceil(R / q*) tokens of weight q* are needed; the chunk holding
+// the n_tie-th one (from the chunk counts), then its index (block scan over that chunk).
+__global__ __launch_bounds__(256) void topp_cut_kernel(const float* __restrict__ x, int V,
+                                                       int chunk, int nch,
+                                                       const float* __restrict__ row_max,
+                                                       float inv_t, const int32_t* __restrict__ cnt,
+                                                       int64_t* __restrict__ st) {
+  __shared__ int s_chunk, s_rel, s_cut;
+  __shared__ int wsum[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const uint64_t qs = (uint64_t)st[(int64_t)row * 4];
+  const uint64_t R = (uint64_t)st[(int64_t)row * 4 + 1];
+  if (tid == 0) {
+    s_cut = -1;
+    const int64_t need = qs ? (int64_t)((R + qs - 1) / qs) : 0;
+    int64_t cum = 0;
+    int cc = 0;
+    for (; cc < nch; ++cc) {
+      const int k = cnt[(int64_t)row * nch + cc];
+      if (cum + k >= need) break;
+      cum += k;
+    }
+    s_chunk = cc < nch ? cc : -1;
+    s_rel = (int)(need - cum);                 // 1-based rank of the last needed tie in it
+  }
+  __syncthreads();
+  const int c = s_chunk;
+  if (c >= 0) {
+    const float M = row_max[row];
+    const float* xr = x + (int64_t)row * V;
+    const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+    const int per = (chunk + 255) / 256;
+    const int a0 = v0 + tid * per, a1 = min(v1, a0 + per);
+    float lx[PICK_SEG];
+#pragma unroll
+    for (int e = 0; e < PICK_SEG; ++e) lx[e] = a0 + e < a1 ? xr[a0 + e] : 0.f;
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < PICK_SEG; ++e) mine += a0 + e < a1 && weight_q(lx[e], M, inv_t) == qs;
+    const int lane = tid & 63, w = tid >> 6;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int excl = incl - mine;
+    for (int q = 0; q < w; ++q) excl += wsum[q];
+    const int rel = s_rel;
+    if (excl < rel && rel <= excl + mine) {
+      int k = excl;
+#pragma unroll
+      for (int e = 0; e < PICK_SEG; ++e) {
+        if (a0 + e < a1 && weight_q(lx[e], M, inv_t) == qs) {
+          if (++k == rel) s_cut = a0 + e;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) st[(int64_t)row * 4 + 2] = s_cut;
+}
+
+// grid (chunks, rows): chunk sums of the nucleus weights
+__global__ __launch_bounds__(256) void topp_rsum_kernel(const float* __restrict__ x, int V,
+                                                        int chunk, int nch,
+                                                        const float* __restrict__ row_max,
+                                                        float inv_t,
+                                                        const int64_t* __restrict__ st,
+                                                        uint64_t* __restrict__ rz) {
+  __shared__ uint64_t red[4];
+  const int c = blockIdx.x, row = blockIdx.y;
+  const uint64_t qs = (uint64_t)st[(int64_t)row * 4];
+  const int vcut = (int)st[(int64_t)row * 4 + 2];
+  const float M = row_max[row];
+  const float* xr = x + (int64_t)row * V;
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  uint64_t acc = 0;
+  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+    const uint64_t q = weight_q(xr[v], M, inv_t);
+    if (q > qs || (q == qs && v <= vcut)) acc += q;
+  }
+  acc = wave_sum_u64(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) rz[(int64_t)row * nch + c] = red[0] + red[1] + red[2] + red[3];
+}
+
+hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const uint64_t* zpart,
+                        const float* row_max, float inv_t, uint64_t mp, int sp, int64_t* st,
+                        uint64_t* hist, int32_t* cnt, uint64_t* rz, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (chunk > 256 * PICK_SEG) return hipErrorInvalidValue;
+  const int nch = ceil_div(vocab, chunk);
+  hipLaunchKernelGGL(topp_init_kernel, dim3(rows), dim3(64), 0, s, zpart, nch, mp, sp, st);
+  for (int d = 0; d < TOPP_DIGITS; ++d) {
+    hipLaunchKernelGGL(topp_hist_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
+                       row_max, inv_t, d, st, hist);
+    hipLaunchKernelGGL(topp_select_kernel, dim3(rows), dim3(256), 0, s, hist, nch, d, st);
+  }
+  hipLaunchKernelGGL(topp_tie_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
+                     row_max, inv_t, st, cnt);
+  hipLaunchKernelGGL(topp_cut_kernel, dim3(rows), dim3(256), 0, s, x, vocab, chunk, nch, row_max,
+                     inv_t, cnt, st);
+  hipLaunchKernelGGL(topp_rsum_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
+                     row_max, inv_t, st, rz);
   return hipGetLastError();
 }
 
@@ -427,7 +653,6 @@ hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int3
 // exists.  Draws: the SplitMix64 counter with 2 streams over D + 1 positions.  The two sides of
 // the accept test reach 130 bits and are compared as (high 128, low 64) pairs; residual weights
 // are below 2^98 and their sums below 2^116.
-typedef unsigned __int128 u128;
 
 __device__ __forceinline__ uint64_t spec_draw(uint64_t seed, int n, int stream, int j, int D) {
   const uint64_t idx = ((uint64_t)n * 2 + stream) * (uint64_t)(D + 1) + j;

@@ -647,7 +647,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     HIP_STAGE(DBD_STAGE_DRAFT, st, launch_zsum_partial(logits, Md, V, ch, b.vpv, b.vpi, inv_t, b.zpart, b.row_max,
                                 b.row_arg, st));
     HIP_STAGE(DBD_STAGE_DRAFT, st, launch_sample_pick(logits, Md, V, ch, b.zpart, b.row_max, inv_t, D, n_drafts, seed,
-                               b.meta.blk_pos, B, n_anchor, draft_tokens, st));
+                               b.meta.blk_pos, B, n_anchor, nullptr, draft_tokens, st));
   }
   return DBD_OK;
 }
@@ -903,7 +903,77 @@ int dbd_sample_from_logits(const float* logits, int32_t batch, int32_t n_draft, 
   const float inv_t = (float)(1.0 / (double)temperature);
   HIP_TRY(launch_zsum_partial(logits, rows, vocab, ch, pv, pi, inv_t, zp, rm, ra, st));
   HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, zp, rm, inv_t, n_draft, n_drafts, seed,
-                             nullptr, 0, 0, out, st));
+                             nullptr, 0, 0, nullptr, out, st));
+  return DBD_OK;
+}
+
+// Top-p sampling workspace: the sampler's buffers, then the nucleus state, per-chunk digit
+// histograms, tie counts and nucleus chunk sums.
+static size_t carve_top_p(int rows, int vocab, char* base, int64_t** stt, uint64_t** hist,
+                          int32_t** cnt, uint64_t** rz) {
+  const size_t s0 = carve_sample(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, nullptr);
+  Carver c{base ? base + s0 : nullptr};
+  const int64_t nch = ceil_div(vocab, vocab_chunk());
+  int64_t* a = c.take<int64_t>((int64_t)rows * 4);
+  uint64_t* h = c.take<uint64_t>((int64_t)rows * nch * 256);
+  int32_t* k = c.take<int32_t>((int64_t)rows * nch);
+  uint64_t* r = c.take<uint64_t>((int64_t)rows * nch);
+  if (stt) { *stt = a; *hist = h; *cnt = k; *rz = r; }
+  return s0 + (c.off + kAlign - 1) / kAlign * kAlign;
+}
+
+int dbd_sample_top_p_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab,
+                                     size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2) return fail(DBD_ERR_ARG, "bad dimensions");
+  *bytes = carve_top_p(batch * n_draft, vocab, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return DBD_OK;
+}
+
+int dbd_sample_top_p(const float* logits, int32_t batch, int32_t n_draft, int32_t vocab,
+                     int32_t n_drafts, float temperature, float top_p, uint64_t seed,
+                     int32_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!logits || !out) return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2 || vocab >= (1 << 18))
+    return fail(DBD_ERR_ARG, "bad dimensions");
+  if (n_drafts < 1 || n_drafts > 64) return fail(DBD_ERR_ARG, "n_drafts out of [1, 64]");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DBD_ERR_ARG, "top-p sampling needs a finite temperature > 0");
+  if (!(top_p > 0.f) || !std::isfinite(top_p))
+    return fail(DBD_ERR_ARG, "top_p must be finite and > 0");
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const int rows = batch * n_draft;
+  const size_t need = carve_top_p(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  float *pv, *rm;
+  int32_t *pi, *pf, *ra, *cnt;
+  uint64_t *zp, *hist, *rz;
+  int64_t* stt;
+  carve_sample(rows, vocab, (char*)workspace, &pv, &pi, &pf, &zp, &rm, &ra);
+  carve_top_p(rows, vocab, (char*)workspace, &stt, &hist, &cnt, &rz);
+  hipStream_t st = (hipStream_t)stream;
+  const int ch = vocab_chunk();
+  const float inv_t = (float)(1.0 / (double)temperature);
+  HIP_TRY(launch_argmax_partial(logits, rows, vocab, ch, pv, pi, pf, st));
+  HIP_TRY(launch_zsum_partial(logits, rows, vocab, ch, pv, pi, inv_t, zp, rm, ra, st));
+  if (top_p >= 1.f) {
+    HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, zp, rm, inv_t, n_draft, n_drafts, seed,
+                               nullptr, 0, 0, nullptr, out, st));
+    return DBD_OK;
+  }
+  // p = mp / 2^sp exactly: the float's 24-bit significand and its binary exponent
+  int e = 0;
+  const float m = std::frexp(top_p, &e);              // top_p = m * 2^e, m in [0.5, 1)
+  const uint64_t mp = (uint64_t)std::ldexp((double)m, 24);
+  const int sp = 24 - e;
+  HIP_TRY(launch_top_p(logits, rows, vocab, ch, zp, rm, inv_t, mp, sp, stt, hist, cnt, rz, st));
+  HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, rz, rm, inv_t, n_draft, n_drafts, seed,
+                             nullptr, 0, 0, stt, out, st));
   return DBD_OK;
 }
 

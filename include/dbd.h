@@ -267,6 +267,22 @@ int dbd_sample_from_logits(const float* logits, int32_t batch, int32_t n_draft, 
                            int32_t n_drafts, float temperature, uint64_t seed, int32_t* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace size (host) for dbd_sample_top_p. */
+int dbd_sample_top_p_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab,
+                                     size_t* bytes /* host out */);
+
+/* Top-p (nucleus) drafting from fp32 logits [N, D, V] (device): the drafting stage of
+ * draft_block with each position's draw restricted to its nucleus.  The pages name no nucleus
+ * rule; in the library's integer arithmetic: with the weights q_v of the row at `temperature`
+ * and Z = sum q_v, the nucleus is the shortest run of tokens, in order of decreasing weight with
+ * ties by increasing index, whose mass reaches ceil(p * Z), p the float value of top_p (a dyadic
+ * rational, so the ceiling is exact); the n_drafts draws are the sampler's (same counter draws)
+ * on the weights restricted to it.  top_p >= 1 is plain sampling.  out [N, n_drafts, D] int32.
+ * temperature must be finite and > 0, top_p finite and > 0. */
+int dbd_sample_top_p(const float* logits, int32_t batch, int32_t n_draft, int32_t vocab,
+                     int32_t n_drafts, float temperature, float top_p, uint64_t seed,
+                     int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The ingest mixing stage of draft_block ([DFlare] section on per-draft-layer mixing):
  * out[l, t, :] = RMSNorm(sum_i softmax(mix_logits[l])_i * hidden[t, i, :]) * mix_norm_w[l],
  * out [L_d, n_tokens, H] in desc.dtype. */

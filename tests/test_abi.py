@@ -300,3 +300,17 @@ def test_context_path_switch_validation():
     mix = dbd.draft_workspace_bytes(_desc(), 32, 16, 1, 256, 1, 0.0, 4096)
     fc = dbd.draft_workspace_bytes(_desc("qwen3-8b-dflash"), 32, 16, 1, 256, 1, 0.0, 4096)
     assert fc < mix
+
+
+def test_sample_top_p_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    ws = dbd.sample_top_p_workspace_bytes(2, 3, 1000)
+    assert ws > dbd.sample_workspace_bytes(2, 3, 1000)
+    call = lambda T, p, wb=ws, w=fake: L.dbd_sample_top_p(fake, 2, 3, 1000, 4, T, p, 1, fake, w,
+                                                          wb, None)
+    assert call(0.0, 0.9) == -1
+    assert call(1.0, 0.0) == -1
+    assert call(1.0, float("nan")) == -1
+    assert call(1.0, 0.9, wb=ws - 1) == -4
+    assert call(1.0, 0.9, w=fake + 8) == -4

@@ -279,3 +279,54 @@ def test_verify_sample_unaligned_logits():
     tl[:, :D] = dl + 0.5
     drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, 1.0, seed=6)[:, 0]).to(DEV)
     _check_vsample(tl, dl, drafts.contiguous(), 1.0, 1.2, seed=8)
+
+
+# ---- top-p nucleus drafting ----
+
+def _top_p_gpu(logits, K, T, p, seed):
+    N, D, V = logits.shape
+    ws = torch.empty(dbd.sample_top_p_workspace_bytes(N, D, V), dtype=torch.uint8, device=DEV)
+    out = torch.full((N, K, D), -7, dtype=torch.int32, device=DEV)
+    dbd.sample_top_p(logits, K, T, p, seed, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,D,V,K,T,p", [(2, 5, 37, 4, 1.0, 0.9), (3, 7, 4099, 8, 1.5, 0.5),
+                                         (2, 4, 10000, 3, 0.7, 0.95), (1, 3, 8192, 2, 1.0, 0.3),
+                                         (2, 32, 1000, 8, 1.5, 0.99), (4, 2, 300, 1, 2.0, 0.05)])
+def test_top_p_sampling_bit_exact(N, D, V, K, T, p):
+    print(f"top-p N={N} D={D} V={V} K={K} T={T} p={p}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(N * 31 + V + D)
+    logits = torch.randn((N, D, V), generator=g, device=DEV) * 3.0
+    got = _top_p_gpu(logits, K, T, p, seed=99)
+    ref = dnc.sample_drafts(logits.cpu().numpy(), K, T, 99, top_p=p)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("p", [0.2, 0.5, 0.8])
+def test_top_p_boundary_inside_tie_groups(p):
+    """Small integer logits: many tokens share each weight, so the nucleus boundary falls inside
+    a tie group and the lowest indices of it are taken."""
+    N, D, V, K = 3, 6, 5000, 6
+    g = torch.Generator(device=DEV).manual_seed(int(p * 100))
+    logits = torch.randint(-4, 3, (N, D, V), generator=g, device=DEV).float()
+    got = _top_p_gpu(logits, K, 1.0, p, seed=5)
+    ref = dnc.sample_drafts(logits.cpu().numpy(), K, 1.0, 5, top_p=p)
+    assert np.array_equal(got, ref)
+
+
+def test_top_p_workload_vocabulary_and_limits():
+    N, D, V, K = 2, 4, 151936, 8
+    g = torch.Generator(device=DEV).manual_seed(17)
+    logits = torch.randn((N, D, V), generator=g, device=DEV) * 2.5
+    lc = logits.cpu().numpy()
+    assert np.array_equal(_top_p_gpu(logits, K, 1.5, 0.9, 4), dnc.sample_drafts(lc, K, 1.5, 4, top_p=0.9))
+    # p = 1: plain sampling; tiny p: the argmax
+    ws = torch.empty(dbd.sample_workspace_bytes(N, D, V), dtype=torch.uint8, device=DEV)
+    plain = torch.empty((N, K, D), dtype=torch.int32, device=DEV)
+    dbd.sample_from_logits(logits, K, 1.5, 4, plain, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_top_p_gpu(logits, K, 1.5, 1.0, 4), plain.cpu().numpy())
+    tiny = _top_p_gpu(logits, K, 1.5, 1e-7, 4)
+    assert np.array_equal(tiny, np.broadcast_to(lc.argmax(-1)[:, None, :], tiny.shape))
