@@ -283,32 +283,55 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int HD) {
   const int64_t base = ((int64_t)n * a.kvh + g) * a.s_max;
   constexpr int SU = 8;
   float m = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += SU) {
-    float2 ml[SU];
-#pragma unroll
-    for (int q = 0; q < SU; ++q)
-      ml[q] = s0 + q < nsplit ? a.part_ml[(base + s0 + q) * R + r] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int q = 0; q < SU; ++q) m = fmaxf(m, ml[q].x);
-  }
   float l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit; s0 += SU) {
+  if (nsplit <= SU) {
+    // every split's (max, sum) and partial output in one round of loads
     float2 ml[SU];
     f32x4 po[SU];
 #pragma unroll
     for (int q = 0; q < SU; ++q) {
-      const bool ok = s0 + q < nsplit;
-      const int64_t pr = (base + s0 + q) * R + r;
+      const bool ok = q < nsplit;
+      const int64_t pr = (base + q) * R + r;
       ml[q] = ok ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
       po[q] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + pr * HD + 4 * d4)
                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
+    for (int q = 0; q < SU; ++q) m = fmaxf(m, ml[q].x);
+#pragma unroll
     for (int q = 0; q < SU; ++q) {
       const float w = exp2f(ml[q].x - m);
       l += w * ml[q].y;
       o += w * po[q];
+    }
+  } else {
+    for (int s0 = 0; s0 < nsplit; s0 += SU) {
+      float2 ml[SU];
+#pragma unroll
+      for (int q = 0; q < SU; ++q)
+        ml[q] = s0 + q < nsplit ? a.part_ml[(base + s0 + q) * R + r]
+                                : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int q = 0; q < SU; ++q) m = fmaxf(m, ml[q].x);
+    }
+    for (int s0 = 0; s0 < nsplit; s0 += SU) {
+      float2 ml[SU];
+      f32x4 po[SU];
+#pragma unroll
+      for (int q = 0; q < SU; ++q) {
+        const bool ok = s0 + q < nsplit;
+        const int64_t pr = (base + s0 + q) * R + r;
+        ml[q] = ok ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
+        po[q] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + pr * HD + 4 * d4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int q = 0; q < SU; ++q) {
+        const float w = exp2f(ml[q].x - m);
+        l += w * ml[q].y;
+        o += w * po[q];
+      }
     }
   }
   const float inv = 1.f / l;

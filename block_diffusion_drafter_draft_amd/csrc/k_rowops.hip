@@ -134,7 +134,19 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
 #pragma unroll
     for (int e = 0; e < CPT * VEC; ++e) acc[l][e] = 0.f;
   const T* base = hid + (int64_t)t * ts;
+  // target layer i + 1 is loaded while layer i is mixed, so the L_t loads of a thread do not
+  // wait for each other
+  u32x4 cur[CPT], nxt[CPT];
+  auto load = [&](u32x4* r, int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 256;
+      if (ch < nch) r[c] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * ls + ch * VEC);
+    }
+  };
+  load(cur, 0);
   for (int i = 0; i < Lt; ++i) {
+    if (i + 1 < Lt) load(nxt, i + 1);
     float wl[kMaxLd];
 #pragma unroll
     for (int l = 0; l < kMaxLd; ++l) wl[l] = l < Ld ? w[l * Lt + i] : 0.f;
@@ -143,8 +155,7 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
       const int ch = tid + c * 256;
       if (ch < nch) {
         T v[VEC];
-        *reinterpret_cast<u32x4*>(v) =
-            *reinterpret_cast<const u32x4*>(base + (int64_t)i * ls + ch * VEC);
+        *reinterpret_cast<u32x4*>(v) = cur[c];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           const float x = to_f(v[e]);
@@ -153,6 +164,8 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
         }
       }
     }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) cur[c] = nxt[c];
   }
   float ss[kMaxLd];
 #pragma unroll
