@@ -221,3 +221,20 @@ def test_query_groups_beyond_one_workgroup_match_oracle():
     assert torch.all(status == 0)
     _check_drafts_property(case, drafts, logits)
     _compare(case, logits, range(wl.batch), [])
+
+
+def test_sixty_four_mask_block_without_anchor():
+    """block_len 64 (the interface's maximum), all masks, context from a given cache, 7 query
+    heads per kv head: 448 query rows per kv head over two attention row blocks."""
+    sh = synth.DrafterShape(hidden=896, n_q_heads=7, n_kv_heads=1, head_dim=128, ffn=1536,
+                            n_layers=2, n_target_layers=0, vocab=3000, dtype="bf16")
+    wl = synth.Workload(name="block64", shape=sh, batch=2, block_len=64, n_anchor=0, n_drafts=4,
+                        temperature=1.5, ctx_lo=70, ctx_hi=70, ctx_source="cache",
+                        verify="streak", verify_rows=64, planted_alpha=0.8, fixed_new=0)
+    print("draft_block workload=block64", flush=True)
+    case = Case(wl, dev=DEV)
+    drafts, logits, status = case.step()
+    torch.cuda.synchronize()
+    assert torch.all(status == 0)
+    _check_drafts_property(case, drafts, logits)
+    _compare(case, logits, range(wl.batch), [])

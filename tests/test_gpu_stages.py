@@ -118,3 +118,22 @@ def test_mix_rmsnorm_strided_layer_major_input():
     ref = od.context_features(sh, {k: W[k].cpu() for k in ("mix_logits", "mix_norm_w")}, 1,
                               hid.cpu())
     assert rel_l2(out[1].cpu().numpy(), ref) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mix_rmsnorm_sixteen_target_layers_eight_draft_layers(dtype):
+    """The mixing kernel at its limits: 16 target layers mixed into 8 draft layers."""
+    sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
+                            n_layers=8, n_target_layers=16, vocab=512, dtype=dtype)
+    W = synth.make_weights(sh, 3, DEV)
+    T = 37
+    hid = synth.make_hidden(sh, T, 3, 0, DEV)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty((sh.n_layers, T, sh.hidden), dtype=dt, device=DEV)
+    dbd.mix_rmsnorm(dbd.model_desc(sh), W["mix_logits"], W["mix_norm_w"], hid, out)
+    torch.cuda.synchronize()
+    Wc = {k: W[k].cpu() for k in ("mix_logits", "mix_norm_w")}
+    tol = 5e-3 if dtype == "bf16" else 1e-5
+    for l in range(sh.n_layers):
+        ref = od.context_features(sh, Wc, l, hid.cpu())
+        assert rel_l2(out[l].float().cpu().numpy(), ref) < tol

@@ -330,3 +330,33 @@ def test_top_p_workload_vocabulary_and_limits():
     assert np.array_equal(_top_p_gpu(logits, K, 1.5, 1.0, 4), plain.cpu().numpy())
     tiny = _top_p_gpu(logits, K, 1.5, 1e-7, 4)
     assert np.array_equal(tiny, np.broadcast_to(lc.argmax(-1)[:, None, :], tiny.shape))
+
+
+# ---- limits of the interface ----
+
+def test_largest_vocabulary_verify_sample_and_top_p():
+    """V = 2^18 - 1, the largest vocabulary the integer weights allow (Z < 2^58): greedy and
+    stochastic verification, sampling and top-p, all bit-exact."""
+    V, N, D = (1 << 18) - 1, 2, 3
+    g = torch.Generator(device=DEV).manual_seed(21)
+    dl = torch.randn((N, D, V), generator=g, device=DEV) * 2.0
+    tl = torch.cat([dl + 0.4 * torch.randn((N, D, V), generator=g, device=DEV),
+                    torch.randn((N, 1, V), generator=g, device=DEV)], 1).contiguous()
+    drafts = torch.from_numpy(dnc.sample_drafts(dl.cpu().numpy(), 1, 1.0, seed=2)[:, 0]).to(DEV)
+    drafts = drafts.contiguous()
+    _check_verify(tl, drafts)
+    _check_vsample(tl, dl, drafts, 1.0, 1.0, seed=6)
+    ref = dnc.sample_drafts(dl.cpu().numpy(), 4, 1.3, 11, top_p=0.8)
+    assert np.array_equal(_top_p_gpu(dl, 4, 1.3, 0.8, 11), ref)
+
+
+def test_sixty_four_drafts_per_position():
+    N, D, V, K = 2, 5, 3000, 64
+    g = torch.Generator(device=DEV).manual_seed(22)
+    logits = torch.randn((N, D, V), generator=g, device=DEV) * 2.0
+    ws = torch.empty(dbd.sample_workspace_bytes(N, D, V), dtype=torch.uint8, device=DEV)
+    out = torch.empty((N, K, D), dtype=torch.int32, device=DEV)
+    dbd.sample_from_logits(logits, K, 1.5, 123, out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(),
+                          dnc.sample_drafts(logits.cpu().numpy(), K, 1.5, 123))
