@@ -180,12 +180,17 @@ hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
                               int n_draft, int n_drafts, uint64_t seed,
                               const int32_t* row_valid_pos, int block_len, int n_anchor,
                               const int64_t* topp, int32_t* out, hipStream_t s);
-// Top-p nucleus of each row after launch_zsum_partial (zpart, row_max): p = mp / 2^sp exactly.
-// st [rows * 4] int64, hist [rows * chunks * 256] uint64, cnt [rows * chunks] int32,
-// rz [rows * chunks] uint64 (the nucleus chunk sums).
-hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const uint64_t* zpart,
-                        const float* row_max, float inv_t, uint64_t mp, int sp, int64_t* st,
-                        uint64_t* hist, int32_t* cnt, uint64_t* rz, hipStream_t s);
+// Top-p nucleus of each row after launch_argmax_partial (pv, pi): p = mp / 2^sp exactly.  Writes
+// row_max [rows]; st [rows * 4] int64; hist [rows * top_p_spans * top_p_bins] uint64;
+// above, rz [rows * chunks] uint64 (rz: the nucleus chunk sums); cnt [rows * chunks] int32;
+// keys [rows * chunks * top_p_cap] uint64.  chunks <= 64.
+int top_p_spans(int vocab, int chunk);
+int top_p_bins();
+int top_p_cap();
+hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const float* pv,
+                        const int32_t* pi, float inv_t, uint64_t mp, int sp, float* row_max,
+                        int64_t* st, uint64_t* hist, uint64_t* above, int32_t* cnt,
+                        uint64_t* keys, uint64_t* rz, hipStream_t s);
 hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int32_t* pflag,
                                   int nch, const int32_t* drafts, int draft_stride, int batch,
                                   int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,

@@ -279,23 +279,34 @@ __global__ __launch_bounds__(256) void sample_pick_kernel(
     if (threadIdx.x == 0) out[oidx] = -1;
     return;
   }
-  if (threadIdx.x == 0) {
-    uint64_t Z = 0;
-    for (int c = 0; c < nch; ++c) Z += zpart[(int64_t)row * nch + c];
+  if (threadIdx.x < 64) {
+    // chunk sums in one wave (nch <= 64): inclusive scan, Z, the first chunk whose inclusive
+    // sum exceeds the threshold
+    const int lane = threadIdx.x;
+    const uint64_t zc = lane < nch ? zpart[(int64_t)row * nch + lane] : 0;
+    uint64_t incl = zc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t lo = __shfl_up((uint32_t)incl, o, 64);
+      const uint32_t hi = __shfl_up((uint32_t)(incl >> 32), o, 64);
+      if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+    }
+    const uint64_t Z = ((uint64_t)__shfl((uint32_t)(incl >> 32), 63, 64) << 32) |
+                       __shfl((uint32_t)incl, 63, 64);
     const uint64_t idx = ((uint64_t)n * n_drafts + k) * n_draft + j;
     const uint64_t u = splitmix_mix(splitmix_mix(seed) + (idx + 1) * 0x9E3779B97F4A7C15ull) >> 32;
     // (u * Z) >> 32 with the full 128-bit product
     const uint64_t lo = u * Z, hi = __umul64hi(u, Z);
-    uint64_t thr = (hi << 32) | (lo >> 32);
-    int cc = 0;
-    uint64_t cum = 0;
-    for (; cc < nch; ++cc) {
-      const uint64_t zc = zpart[(int64_t)row * nch + cc];
-      if (cum + zc > thr) break;
-      cum += zc;
+    const uint64_t thr = (hi << 32) | (lo >> 32);
+    const uint64_t past = __ballot(lane < nch && incl > thr);
+    const int cc = past ? __ffsll((unsigned long long)past) - 1 : nch - 1;
+    const uint64_t ex = incl - zc;
+    const uint64_t cum = ((uint64_t)__shfl((uint32_t)(ex >> 32), cc, 64) << 32) |
+                         __shfl((uint32_t)ex, cc, 64);
+    if (lane == 0) {
+      s_chunk = cc;
+      s_thr = past ? thr - cum : 0;            // relative to the chunk start
     }
-    s_chunk = cc < nch ? cc : nch - 1;
-    s_thr = thr - cum;                       // threshold relative to the chunk start
   }
   __syncthreads();
   const int c = s_chunk;
@@ -352,7 +363,7 @@ hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
                               const int32_t* row_valid_pos, int block_len, int n_anchor,
                               const int64_t* topp, int32_t* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (chunk > 256 * PICK_SEG) return hipErrorInvalidValue;
+  if (chunk > 256 * PICK_SEG || ceil_div(vocab, chunk) > 64) return hipErrorInvalidValue;
   const int nch = ceil_div(vocab, chunk);
   hipLaunchKernelGGL(sample_pick_kernel, dim3(n_drafts, rows), dim3(256), 0, s, x, vocab, chunk,
                      nch, zpart, row_max, inv_t, n_draft, n_drafts, seed, row_valid_pos,
@@ -363,69 +374,117 @@ hipError_t launch_sample_pick(const float* x, int rows, int vocab, int chunk,
 // ------------------------------------------------------------------ top-p nucleus
 // The nucleus of a row is the shortest run of tokens, in order of decreasing integer weight
 // with ties by increasing index, whose mass reaches Tp = ceil(p * Z) (p = mp / 2^sp exactly).
-// Its boundary weight q* is found by a radix select on the 41-bit weights, most significant
-// digit first, weighted by mass: per digit, every chunk histograms the mass of the tokens whose
-// higher digits equal the prefix found so far (topp_hist_kernel), then topp_select_kernel picks
-// the digit where the mass above reaches the remaining target.  The tokens of weight q* enter in
-// index order until the target is met: topp_tie_kernel counts them per chunk, topp_cut_kernel
-// finds the index of the last one needed.  State per row: {q*, remaining target, v_cut, -}.
-constexpr int TOPP_DIGITS = 6;
-__constant__ int kToppShift[TOPP_DIGITS] = {33, 25, 17, 9, 1, 0};
-__constant__ int kToppWidth[TOPP_DIGITS] = {8, 8, 8, 8, 8, 1};
+// Tokens are ordered by the 59-bit key (q << 18) | (2^18 - 1 - v), unique per token, so the
+// nucleus is every token whose key is at least the boundary key K*.
+//  1. topp_hist_kernel: per span of the row, the mass of the weights in logarithmic bins
+//     (octave of q, then its next 5 bits: monotone in q, at most 3.2 % wide).
+//  2. topp_bin_kernel: Z, Tp and the bin b* that holds the boundary (mass above < Tp <= mass
+//     above + its own), with R = Tp - mass above.
+//  3. topp_collect_kernel: per chunk, the mass of the bins above b* and the keys of the tokens
+//     in b* (at most TOPP_CAP per chunk are stored; the count is exact).
+//  4. topp_resolve_kernel: one workgroup per row finds K* by a mass-weighted radix select over
+//     the keys in b* (from LDS, or by rescanning the row when the stored keys overflow) and
+//     writes the nucleus chunk sums and {q*, -, v_cut, b*} for the sampler.
+constexpr int TOPP_SUB = 5;                       // bits below the octave in a bin
+constexpr int TOPP_BINS = 41 << TOPP_SUB;         // q <= 2^40
+constexpr int TOPP_SPAN = 8;                      // chunks per histogram workgroup
+constexpr int TOPP_CAP = 256;                     // keys stored per chunk
+constexpr int TOPP_LDS_CAP = 6144;                // keys resolved from LDS
+constexpr uint64_t TOPP_VMASK = (1u << 18) - 1;
+static_assert(TOPP_BINS <= 6 * 256, "bins per thread in topp_bin_kernel");
 
-__global__ __launch_bounds__(64) void topp_init_kernel(const uint64_t* __restrict__ zpart,
-                                                       int nch, uint64_t mp, int sp,
-                                                       int64_t* __restrict__ st) {
-  const int row = blockIdx.x;
-  uint64_t z = 0;
-  for (int c = threadIdx.x; c < nch; c += 64) z += zpart[(int64_t)row * nch + c];
-  z = wave_sum_u64(z);
-  if (threadIdx.x == 0) {
-    // Tp = ceil(mp * Z / 2^sp); mp < 2^24 and Z < 2^58, so mp * Z < 2^82
-    const u128 prod = (u128)mp * z;
-    const uint64_t tp = sp >= 82 ? (prod ? 1 : 0)
-                                 : (uint64_t)((prod + (((u128)1 << sp) - 1)) >> sp);
-    st[(int64_t)row * 4] = 0;
-    st[(int64_t)row * 4 + 1] = (int64_t)tp;
-  }
+__device__ __forceinline__ int topp_bin(uint64_t q) {     // q > 0
+  const int msb = 63 - __clzll((long long)q);
+  const uint32_t sub = msb >= TOPP_SUB ? (uint32_t)(q >> (msb - TOPP_SUB))
+                                       : (uint32_t)q << (TOPP_SUB - msb);
+  return (msb << TOPP_SUB) | (int)(sub & ((1u << TOPP_SUB) - 1));
 }
 
-// grid (chunks, rows): mass histogram of digit `d` over the chunk's tokens that match the prefix
+// f(logit, index) over [v0, v1) of a row, NT threads: unaligned head, then float4 loads four in
+// flight per thread, then the tail.
+template <int NT, typename F>
+__device__ __forceinline__ void for_logits(const float* __restrict__ xr, int v0, int v1, F&& f) {
+  const int head = min(v1 - v0, (int)((4 - (((uintptr_t)(xr + v0) >> 2) & 3)) & 3));
+  if ((int)threadIdx.x < head) f(xr[v0 + threadIdx.x], v0 + (int)threadIdx.x);
+  const int a0 = v0 + head;
+  const int nv = (v1 - a0) >> 2;
+  const float4* x4 = reinterpret_cast<const float4*>(xr + a0);
+  int k = threadIdx.x;
+  for (; k + 3 * NT < nv; k += 4 * NT) {
+    float4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = x4[k + u * NT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = a0 + 4 * (k + u * NT);
+      f(q[u].x, b);
+      f(q[u].y, b + 1);
+      f(q[u].z, b + 2);
+      f(q[u].w, b + 3);
+    }
+  }
+  for (; k < nv; k += NT) {
+    const float4 q = x4[k];
+    const int b = a0 + 4 * k;
+    f(q.x, b);
+    f(q.y, b + 1);
+    f(q.z, b + 2);
+    f(q.w, b + 3);
+  }
+  for (int v = a0 + 4 * nv + threadIdx.x; v < v1; v += NT) f(xr[v], v);
+}
+
+// grid (spans, rows): M from the argmax partials (span 0 stores it), then the bin masses of the
+// span's weights.
 __global__ __launch_bounds__(256) void topp_hist_kernel(
-    const float* __restrict__ x, int V, int chunk, int nch, const float* __restrict__ row_max,
-    float inv_t, int d, const int64_t* __restrict__ st, uint64_t* __restrict__ hist) {
-  __shared__ unsigned long long lh[256];
-  const int c = blockIdx.x, row = blockIdx.y;
-  const int shift = kToppShift[d], width = kToppWidth[d];
-  const uint64_t pre = (uint64_t)st[(int64_t)row * 4] >> (shift + width);
-  lh[threadIdx.x] = 0;
-  __syncthreads();
-  const float M = row_max[row];
-  const float* xr = x + (int64_t)row * V;
-  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-  const uint32_t mask = (1u << width) - 1;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
-    const uint64_t q = weight_q(xr[v], M, inv_t);
-    if ((q >> (shift + width)) == pre && q)
-      atomicAdd(&lh[(q >> shift) & mask], (unsigned long long)q);
+    const float* __restrict__ x, int V, int chunk, int nch, int nsp,
+    const float* __restrict__ pv, const int32_t* __restrict__ pi, float inv_t,
+    float* __restrict__ row_max, uint64_t* __restrict__ hist) {
+  __shared__ unsigned long long lh[TOPP_BINS];
+  __shared__ float sM;
+  const int s = blockIdx.x, row = blockIdx.y;
+  for (int b = threadIdx.x; b < TOPP_BINS; b += 256) lh[b] = 0;
+  if (threadIdx.x < 64) {
+    float bv;
+    int bi;
+    reduce_partials(pv, pi, row, nch, bv, bi);
+    if (threadIdx.x == 0) {
+      sM = bv;
+      if (s == 0) row_max[row] = bv;
+    }
   }
   __syncthreads();
-  hist[((int64_t)row * nch + c) * 256 + threadIdx.x] = lh[threadIdx.x];
+  const float M = sM;
+  const int v0 = s * TOPP_SPAN * chunk, v1 = min(V, v0 + TOPP_SPAN * chunk);
+  for_logits<256>(x + (int64_t)row * V, v0, v1, [&](float l, int) {
+    const uint64_t q = weight_q(l, M, inv_t);
+    if (q) atomicAdd(&lh[topp_bin(q)], (unsigned long long)q);
+  });
+  __syncthreads();
+  uint64_t* h = hist + ((int64_t)row * nsp + s) * TOPP_BINS;
+  for (int b = threadIdx.x; b < TOPP_BINS; b += 256) h[b] = lh[b];
 }
 
-// one workgroup per row: bucket masses (thread b sums bucket b over the chunks), the suffix sums
-// from the top bucket, and the bucket b with above(b) < R <= above(b) + mass(b)
-__global__ __launch_bounds__(256) void topp_select_kernel(const uint64_t* __restrict__ hist,
-                                                          int nch, int d,
-                                                          int64_t* __restrict__ st) {
+// one workgroup per row: thread t owns bins [6t, 6t + 6); suffix sums over the threads give the
+// mass above each bin, Z is the total.  st = {-, R, -, b*}; b* = -1 if no bin qualifies
+// (non-finite logits), which makes the nucleus every token of positive weight.
+__global__ __launch_bounds__(256) void topp_bin_kernel(const uint64_t* __restrict__ hist,
+                                                       int nsp, uint64_t mp, int sp,
+                                                       int64_t* __restrict__ st) {
   __shared__ uint64_t wtot[4];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int shift = kToppShift[d], width = kToppWidth[d];
-  uint64_t m = 0;
-  for (int c = 0; c < nch; ++c) m += hist[((int64_t)row * nch + c) * 256 + tid];
-  // inclusive suffix sum over buckets: thread tid gets sum_{b >= tid} mass(b)
+  uint64_t m[6], tot = 0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const int b = 6 * tid + k;
+    m[k] = 0;
+    if (b < TOPP_BINS)
+      for (int s = 0; s < nsp; ++s) m[k] += hist[((int64_t)row * nsp + s) * TOPP_BINS + b];
+    tot += m[k];
+  }
+  // inclusive suffix sum over threads
   const int lane = tid & 63, w = tid >> 6;
-  uint64_t incl = m;
+  uint64_t incl = tot;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t lo = __shfl_down((uint32_t)incl, o, 64);
@@ -433,146 +492,186 @@ __global__ __launch_bounds__(256) void topp_select_kernel(const uint64_t* __rest
     if (lane + o < 64) incl += ((uint64_t)hi << 32) | lo;
   }
   if (lane == 0) wtot[w] = incl;
+  if (tid == 0) {
+    st[(int64_t)row * 4 + 1] = 0;
+    st[(int64_t)row * 4 + 3] = -1;
+  }
   __syncthreads();
   for (int q = w + 1; q < 4; ++q) incl += wtot[q];
-  const uint64_t above = incl - m;
-  const uint64_t R = (uint64_t)st[(int64_t)row * 4 + 1];
-  if (tid < (1 << width) && m && above < R && R <= above + m) {
-    st[(int64_t)row * 4] = (int64_t)((uint64_t)st[(int64_t)row * 4] | ((uint64_t)tid << shift));
-    st[(int64_t)row * 4 + 1] = (int64_t)(R - above);
+  const uint64_t Z = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  // Tp = ceil(mp * Z / 2^sp); mp < 2^24 and Z < 2^58, so mp * Z < 2^82
+  const u128 prod = (u128)mp * Z;
+  const uint64_t tp = sp >= 82 ? (prod ? 1 : 0)
+                               : (uint64_t)((prod + (((u128)1 << sp) - 1)) >> sp);
+  uint64_t above = incl - tot;
+#pragma unroll
+  for (int k = 5; k >= 0; --k) {
+    if (m[k] && above < tp && tp <= above + m[k]) {
+      st[(int64_t)row * 4 + 1] = (int64_t)(tp - above);
+      st[(int64_t)row * 4 + 3] = 6 * tid + k;
+    }
+    above += m[k];
   }
 }
 
-// grid (chunks, rows): tokens of weight q* per chunk
-__global__ __launch_bounds__(256) void topp_tie_kernel(const float* __restrict__ x, int V,
-                                                       int chunk, int nch,
-                                                       const float* __restrict__ row_max,
-                                                       float inv_t,
-                                                       const int64_t* __restrict__ st,
-                                                       int32_t* __restrict__ cnt) {
-  __shared__ int red[4];
-  const int c = blockIdx.x, row = blockIdx.y;
-  const uint64_t qs = (uint64_t)st[(int64_t)row * 4];
-  const float M = row_max[row];
-  const float* xr = x + (int64_t)row * V;
-  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-  int k = 0;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) k += weight_q(xr[v], M, inv_t) == qs;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) k += __shfl_xor(k, o, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
-  __syncthreads();
-  if (threadIdx.x == 0) cnt[(int64_t)row * nch + c] = red[0] + red[1] + red[2] + red[3];
-}
-
-// one workgroup per row: n_tie = ceil(R / q*) tokens of weight q* are needed; the chunk holding
-// the n_tie-th one (from the chunk counts), then its index (block scan over that chunk).
-__global__ __launch_bounds__(256) void topp_cut_kernel(const float* __restrict__ x, int V,
-                                                       int chunk, int nch,
-                                                       const float* __restrict__ row_max,
-                                                       float inv_t, const int32_t* __restrict__ cnt,
-                                                       int64_t* __restrict__ st) {
-  __shared__ int s_chunk, s_rel, s_cut;
-  __shared__ int wsum[4];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const uint64_t qs = (uint64_t)st[(int64_t)row * 4];
-  const uint64_t R = (uint64_t)st[(int64_t)row * 4 + 1];
-  if (tid == 0) {
-    s_cut = -1;
-    const int64_t need = qs ? (int64_t)((R + qs - 1) / qs) : 0;
-    int64_t cum = 0;
-    int cc = 0;
-    for (; cc < nch; ++cc) {
-      const int k = cnt[(int64_t)row * nch + cc];
-      if (cum + k >= need) break;
-      cum += k;
-    }
-    s_chunk = cc < nch ? cc : -1;
-    s_rel = (int)(need - cum);                 // 1-based rank of the last needed tie in it
-  }
-  __syncthreads();
-  const int c = s_chunk;
-  if (c >= 0) {
-    const float M = row_max[row];
-    const float* xr = x + (int64_t)row * V;
-    const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-    const int per = (chunk + 255) / 256;
-    const int a0 = v0 + tid * per, a1 = min(v1, a0 + per);
-    float lx[PICK_SEG];
-#pragma unroll
-    for (int e = 0; e < PICK_SEG; ++e) lx[e] = a0 + e < a1 ? xr[a0 + e] : 0.f;
-    int mine = 0;
-#pragma unroll
-    for (int e = 0; e < PICK_SEG; ++e) mine += a0 + e < a1 && weight_q(lx[e], M, inv_t) == qs;
-    const int lane = tid & 63, w = tid >> 6;
-    int incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    int excl = incl - mine;
-    for (int q = 0; q < w; ++q) excl += wsum[q];
-    const int rel = s_rel;
-    if (excl < rel && rel <= excl + mine) {
-      int k = excl;
-#pragma unroll
-      for (int e = 0; e < PICK_SEG; ++e) {
-        if (a0 + e < a1 && weight_q(lx[e], M, inv_t) == qs) {
-          if (++k == rel) s_cut = a0 + e;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if (tid == 0) st[(int64_t)row * 4 + 2] = s_cut;
-}
-
-// grid (chunks, rows): chunk sums of the nucleus weights
-__global__ __launch_bounds__(256) void topp_rsum_kernel(const float* __restrict__ x, int V,
-                                                        int chunk, int nch,
-                                                        const float* __restrict__ row_max,
-                                                        float inv_t,
-                                                        const int64_t* __restrict__ st,
-                                                        uint64_t* __restrict__ rz) {
+// grid (chunks, rows): mass of the bins above b* and the keys of the tokens in b*.
+__global__ __launch_bounds__(256) void topp_collect_kernel(
+    const float* __restrict__ x, int V, int chunk, int nch, const float* __restrict__ row_max,
+    float inv_t, const int64_t* __restrict__ st, uint64_t* __restrict__ above,
+    int32_t* __restrict__ cnt, uint64_t* __restrict__ keys) {
   __shared__ uint64_t red[4];
+  __shared__ int s_n;
   const int c = blockIdx.x, row = blockIdx.y;
-  const uint64_t qs = (uint64_t)st[(int64_t)row * 4];
-  const int vcut = (int)st[(int64_t)row * 4 + 2];
+  const int bs = (int)st[(int64_t)row * 4 + 3];
   const float M = row_max[row];
-  const float* xr = x + (int64_t)row * V;
-  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  uint64_t* kk = keys + ((int64_t)row * nch + c) * TOPP_CAP;
   uint64_t acc = 0;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
-    const uint64_t q = weight_q(xr[v], M, inv_t);
-    if (q > qs || (q == qs && v <= vcut)) acc += q;
-  }
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  for_logits<256>(x + (int64_t)row * V, v0, v1, [&](float l, int v) {
+    const uint64_t q = weight_q(l, M, inv_t);
+    if (!q) return;
+    const int b = topp_bin(q);
+    if (b > bs) {
+      acc += q;
+    } else if (b == bs) {
+      const int slot = atomicAdd(&s_n, 1);
+      if (slot < TOPP_CAP) kk[slot] = (q << 18) | (TOPP_VMASK - (uint64_t)v);
+    }
+  });
   acc = wave_sum_u64(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) rz[(int64_t)row * nch + c] = red[0] + red[1] + red[2] + red[3];
+  if (threadIdx.x == 0) {
+    above[(int64_t)row * nch + c] = red[0] + red[1] + red[2] + red[3];
+    cnt[(int64_t)row * nch + c] = s_n;
+  }
 }
 
-hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const uint64_t* zpart,
-                        const float* row_max, float inv_t, uint64_t mp, int sp, int64_t* st,
-                        uint64_t* hist, int32_t* cnt, uint64_t* rz, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  if (chunk > 256 * PICK_SEG) return hipErrorInvalidValue;
-  const int nch = ceil_div(vocab, chunk);
-  hipLaunchKernelGGL(topp_init_kernel, dim3(rows), dim3(64), 0, s, zpart, nch, mp, sp, st);
-  for (int d = 0; d < TOPP_DIGITS; ++d) {
-    hipLaunchKernelGGL(topp_hist_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
-                       row_max, inv_t, d, st, hist);
-    hipLaunchKernelGGL(topp_select_kernel, dim3(rows), dim3(256), 0, s, hist, nch, d, st);
+// one workgroup per row (nch <= 64).  The keys of bin b* come from LDS when every chunk kept all
+// of its keys and they fit, otherwise every pass rescans the row.  Radix select from the top
+// digit: per digit, the mass of each digit value among the keys matching the prefix, and the
+// digit where the mass above reaches the remaining target.
+__global__ __launch_bounds__(256) void topp_resolve_kernel(
+    const float* __restrict__ x, int V, int chunk, int nch, const float* __restrict__ row_max,
+    float inv_t, const uint64_t* __restrict__ above, const int32_t* __restrict__ cnt,
+    const uint64_t* __restrict__ keys, int64_t* __restrict__ st, uint64_t* __restrict__ rz) {
+  __shared__ uint64_t lk[TOPP_LDS_CAP];
+  __shared__ unsigned long long lh[256];
+  __shared__ unsigned long long ts[64];
+  __shared__ int off[65];
+  __shared__ int s_fast;
+  __shared__ uint64_t s_pre, s_R, wtot[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int bs = (int)st[(int64_t)row * 4 + 3];
+  if (tid < 64) {
+    // offsets of the chunks' stored keys: one wave scan (nch <= 64)
+    const int k = tid < nch ? cnt[(int64_t)row * nch + tid] : 0;
+    const int kept = min(k, TOPP_CAP);
+    int incl = kept;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += t;
+    }
+    if (tid < nch) off[tid] = incl - kept;
+    const int total = __shfl(incl, 63, 64);
+    const bool over = __ballot(k > TOPP_CAP) != 0;
+    if (tid == 0) {
+      off[nch] = total;
+      s_fast = !over && total <= TOPP_LDS_CAP;
+      s_pre = 0;
+      s_R = (uint64_t)st[(int64_t)row * 4 + 1];
+    }
   }
-  hipLaunchKernelGGL(topp_tie_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
-                     row_max, inv_t, st, cnt);
-  hipLaunchKernelGGL(topp_cut_kernel, dim3(rows), dim3(256), 0, s, x, vocab, chunk, nch, row_max,
-                     inv_t, cnt, st);
-  hipLaunchKernelGGL(topp_rsum_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
-                     row_max, inv_t, st, rz);
+  if (tid < 64) ts[tid] = 0;
+  __syncthreads();
+  const bool fast = s_fast;
+  const int n = off[nch];
+  if (fast) {
+    const int lane = tid & 63;
+    for (int c = tid >> 6; c < nch; c += 4) {
+      const uint64_t* kk = keys + ((int64_t)row * nch + c) * TOPP_CAP;
+      for (int j = lane; j < off[c + 1] - off[c]; j += 64) lk[off[c] + j] = kk[j];
+    }
+  }
+  __syncthreads();
+  const float M = row_max[row];
+  const float* xr = x + (int64_t)row * V;
+  // g(key) over the keys of bin b*
+  auto each_key = [&](auto&& g) __attribute__((always_inline)) {
+    if (fast) {
+      for (int i = tid; i < n; i += 256) g(lk[i]);
+    } else {
+      for_logits<256>(xr, 0, V, [&](float l, int v) {
+        const uint64_t q = weight_q(l, M, inv_t);
+        if (q && topp_bin(q) == bs) g((q << 18) | (TOPP_VMASK - (uint64_t)v));
+      });
+    }
+  };
+  const int lane = tid & 63, w = tid >> 6;
+  for (int d = 0; d < 8; ++d) {
+    const int shift = d < 7 ? 51 - 8 * d : 0, width = d < 7 ? 8 : 3;
+    lh[tid] = 0;
+    __syncthreads();
+    const uint64_t hp = s_pre >> (shift + width);
+    const uint32_t mask = (1u << width) - 1;
+    each_key([&](uint64_t k) {
+      if ((k >> (shift + width)) == hp)
+        atomicAdd(&lh[(k >> shift) & mask], (unsigned long long)(k >> 18));
+    });
+    __syncthreads();
+    const uint64_t m = lh[tid];
+    uint64_t incl = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t lo = __shfl_down((uint32_t)incl, o, 64);
+      const uint32_t hi = __shfl_down((uint32_t)(incl >> 32), o, 64);
+      if (lane + o < 64) incl += ((uint64_t)hi << 32) | lo;
+    }
+    if (lane == 0) wtot[w] = incl;
+    __syncthreads();
+    for (int q = w + 1; q < 4; ++q) incl += wtot[q];
+    const uint64_t ab = incl - m, R = s_R;
+    __syncthreads();
+    if (tid <= (int)mask && m && ab < R && R <= ab + m) {
+      s_pre |= (uint64_t)tid << shift;
+      s_R = R - ab;
+    }
+    __syncthreads();
+  }
+  const uint64_t ks = s_pre;
+  each_key([&](uint64_t k) {
+    if (k >= ks) atomicAdd(&ts[(int)(TOPP_VMASK - (k & TOPP_VMASK)) / chunk],
+                           (unsigned long long)(k >> 18));
+  });
+  __syncthreads();
+  if (tid < nch) rz[(int64_t)row * nch + tid] = above[(int64_t)row * nch + tid] + ts[tid];
+  if (tid == 0) {
+    st[(int64_t)row * 4] = (int64_t)(ks >> 18);
+    st[(int64_t)row * 4 + 2] = (int64_t)(TOPP_VMASK - (ks & TOPP_VMASK));
+  }
+}
+
+int top_p_spans(int vocab, int chunk) { return ceil_div(ceil_div(vocab, chunk), TOPP_SPAN); }
+int top_p_bins() { return TOPP_BINS; }
+int top_p_cap() { return TOPP_CAP; }
+
+hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const float* pv,
+                        const int32_t* pi, float inv_t, uint64_t mp, int sp, float* row_max,
+                        int64_t* st, uint64_t* hist, uint64_t* above, int32_t* cnt,
+                        uint64_t* keys, uint64_t* rz, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int nch = ceil_div(vocab, chunk), nsp = top_p_spans(vocab, chunk);
+  if (nch > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topp_hist_kernel, dim3(nsp, rows), dim3(256), 0, s, x, vocab, chunk, nch,
+                     nsp, pv, pi, inv_t, row_max, hist);
+  hipLaunchKernelGGL(topp_bin_kernel, dim3(rows), dim3(256), 0, s, hist, nsp, mp, sp, st);
+  hipLaunchKernelGGL(topp_collect_kernel, dim3(nch, rows), dim3(256), 0, s, x, vocab, chunk, nch,
+                     row_max, inv_t, st, above, cnt, keys);
+  hipLaunchKernelGGL(topp_resolve_kernel, dim3(rows), dim3(256), 0, s, x, vocab, chunk, nch,
+                     row_max, inv_t, above, cnt, keys, st, rz);
   return hipGetLastError();
 }
 

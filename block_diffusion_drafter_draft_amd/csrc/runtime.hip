@@ -909,17 +909,26 @@ int dbd_sample_from_logits(const float* logits, int32_t batch, int32_t n_draft, 
 
 // Top-p sampling workspace: the sampler's buffers, then the nucleus state, per-chunk digit
 // histograms, tie counts and nucleus chunk sums.
-static size_t carve_top_p(int rows, int vocab, char* base, int64_t** stt, uint64_t** hist,
-                          int32_t** cnt, uint64_t** rz) {
+struct ToppWs {
+  int64_t* st;
+  uint64_t *hist, *above, *keys, *rz;
+  int32_t* cnt;
+};
+
+static size_t carve_top_p(int rows, int vocab, char* base, ToppWs* t) {
   const size_t s0 = carve_sample(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
                                  nullptr, nullptr);
   Carver c{base ? base + s0 : nullptr};
-  const int64_t nch = ceil_div(vocab, vocab_chunk());
-  int64_t* a = c.take<int64_t>((int64_t)rows * 4);
-  uint64_t* h = c.take<uint64_t>((int64_t)rows * nch * 256);
-  int32_t* k = c.take<int32_t>((int64_t)rows * nch);
-  uint64_t* r = c.take<uint64_t>((int64_t)rows * nch);
-  if (stt) { *stt = a; *hist = h; *cnt = k; *rz = r; }
+  const int ch = vocab_chunk();
+  const int64_t nch = ceil_div(vocab, ch);
+  ToppWs w;
+  w.st = c.take<int64_t>((int64_t)rows * 4);
+  w.hist = c.take<uint64_t>((int64_t)rows * top_p_spans(vocab, ch) * top_p_bins());
+  w.above = c.take<uint64_t>((int64_t)rows * nch);
+  w.rz = c.take<uint64_t>((int64_t)rows * nch);
+  w.cnt = c.take<int32_t>((int64_t)rows * nch);
+  w.keys = c.take<uint64_t>((int64_t)rows * nch * top_p_cap());
+  if (t) *t = w;
   return s0 + (c.off + kAlign - 1) / kAlign * kAlign;
 }
 
@@ -928,7 +937,7 @@ int dbd_sample_top_p_workspace_bytes(int32_t batch, int32_t n_draft, int32_t voc
   g_err.clear();
   if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
   if (batch < 1 || n_draft < 1 || vocab < 2) return fail(DBD_ERR_ARG, "bad dimensions");
-  *bytes = carve_top_p(batch * n_draft, vocab, nullptr, nullptr, nullptr, nullptr, nullptr);
+  *bytes = carve_top_p(batch * n_draft, vocab, nullptr, nullptr);
   return DBD_OK;
 }
 
@@ -947,21 +956,21 @@ int dbd_sample_top_p(const float* logits, int32_t batch, int32_t n_draft, int32_
   if (!workspace || ((uintptr_t)workspace % kAlign))
     return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
   const int rows = batch * n_draft;
-  const size_t need = carve_top_p(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const size_t need = carve_top_p(rows, vocab, nullptr, nullptr);
   if (workspace_bytes < need)
     return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
   float *pv, *rm;
-  int32_t *pi, *pf, *ra, *cnt;
-  uint64_t *zp, *hist, *rz;
-  int64_t* stt;
+  int32_t *pi, *pf, *ra;
+  uint64_t* zp;
+  ToppWs tw;
   carve_sample(rows, vocab, (char*)workspace, &pv, &pi, &pf, &zp, &rm, &ra);
-  carve_top_p(rows, vocab, (char*)workspace, &stt, &hist, &cnt, &rz);
+  carve_top_p(rows, vocab, (char*)workspace, &tw);
   hipStream_t st = (hipStream_t)stream;
   const int ch = vocab_chunk();
   const float inv_t = (float)(1.0 / (double)temperature);
   HIP_TRY(launch_argmax_partial(logits, rows, vocab, ch, pv, pi, pf, st));
-  HIP_TRY(launch_zsum_partial(logits, rows, vocab, ch, pv, pi, inv_t, zp, rm, ra, st));
   if (top_p >= 1.f) {
+    HIP_TRY(launch_zsum_partial(logits, rows, vocab, ch, pv, pi, inv_t, zp, rm, ra, st));
     HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, zp, rm, inv_t, n_draft, n_drafts, seed,
                                nullptr, 0, 0, nullptr, out, st));
     return DBD_OK;
@@ -971,9 +980,10 @@ int dbd_sample_top_p(const float* logits, int32_t batch, int32_t n_draft, int32_
   const float m = std::frexp(top_p, &e);              // top_p = m * 2^e, m in [0.5, 1)
   const uint64_t mp = (uint64_t)std::ldexp((double)m, 24);
   const int sp = 24 - e;
-  HIP_TRY(launch_top_p(logits, rows, vocab, ch, zp, rm, inv_t, mp, sp, stt, hist, cnt, rz, st));
-  HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, rz, rm, inv_t, n_draft, n_drafts, seed,
-                             nullptr, 0, 0, stt, out, st));
+  HIP_TRY(launch_top_p(logits, rows, vocab, ch, pv, pi, inv_t, mp, sp, rm, tw.st, tw.hist,
+                       tw.above, tw.cnt, tw.keys, tw.rz, st));
+  HIP_TRY(launch_sample_pick(logits, rows, vocab, ch, tw.rz, rm, inv_t, n_draft, n_drafts, seed,
+                             nullptr, 0, 0, tw.st, out, st));
   return DBD_OK;
 }
 

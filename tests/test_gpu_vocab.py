@@ -360,3 +360,48 @@ def test_sixty_four_drafts_per_position():
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(),
                           dnc.sample_drafts(logits.cpu().numpy(), K, 1.5, 123))
+
+
+def _plateau_rows(V, per_chunk_counts, rest=-20.0, seed=0):
+    """One row per entry: per_chunk_counts[c] tokens of chunk c (4096 wide) at logit 0, every
+    other token at `rest`; the nucleus boundary then lies inside the plateau's tie group."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for counts in per_chunk_counts:
+        r = np.full(V, rest, dtype=np.float32)
+        for c, k in enumerate(counts):
+            lo, hi = c * 4096, min(V, (c + 1) * 4096)
+            r[rng.choice(np.arange(lo, hi), size=k, replace=False)] = 0.0
+        rows.append(r)
+    return np.stack(rows)
+
+
+def test_top_p_bin_capacities_and_row_rescan():
+    """Rows at both sides of the stored-key capacities (256 per chunk, 6144 per row) in one call,
+    next to ordinary rows: the LDS radix select and the rescan of the row give the oracle's draws."""
+    V = 151936
+    nch = (V + 4095) // 4096
+    plate = _plateau_rows(V, [[256, 256] + [0] * (nch - 2),          # stored, LDS
+                              [256, 257] + [0] * (nch - 2),          # chunk 1 overflows
+                              [161] * nch,                           # 6118 keys: LDS
+                              [162] * nch])                          # 6156 keys: rescan
+    g = torch.Generator(device=DEV).manual_seed(23)
+    rnd = (torch.randn((2, V), generator=g, device=DEV) * 2.0).cpu().numpy()
+    logits = torch.from_numpy(np.concatenate([plate, rnd])).reshape(3, 2, V).to(DEV)
+    lc = logits.cpu().numpy()
+    for p in (0.3, 0.999):
+        print(f"top-p capacities p={p}", flush=True)
+        got = _top_p_gpu(logits, 8, 1.0, p, 31)
+        assert np.array_equal(got, dnc.sample_drafts(lc, 8, 1.0, 31, top_p=p))
+
+
+def test_top_p_uniform_rows():
+    """All weights equal: every token lies in one bin, the boundary is an index cut."""
+    N, D, V, K = 1, 3, 20000, 8
+    logits = torch.zeros((N, D, V), device=DEV)
+    logits[0, 1] = 5.0
+    for p in (0.01, 0.5, 0.9999):
+        got = _top_p_gpu(logits, K, 1.0, p, 3)
+        assert np.array_equal(got, dnc.sample_drafts(logits.cpu().numpy(), K, 1.0, 3, top_p=p))
+        n = int(np.ceil(p * V))
+        assert got.max() < n        # the nucleus is the n lowest indices
