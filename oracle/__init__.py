@@ -11,12 +11,13 @@ Modules:
              bidirectional block attention over the context, SwiGLU MLP, shared LM head);
   dnc      - integer-exact sampling and selection probabilities (argmax, exp, weights, RNG);
   accept   - greedy verification and streak-score self-selection, plus the helpers used only to
-             pin the oracle (acceptance rates, Monte Carlo, enumeration).
+             pin the oracle (acceptance rates, Monte Carlo, enumeration);
+  refine   - iterative refinement of a drafted block (Mask-Predict on the integer confidences).
 
 Pins (tests/test_oracle_*.py): every function is checked against closed forms, invariants,
 special cases, Monte Carlo or brute force.  The composed forward pass has no printed worked
 example on the pages: beyond the pins of its parts it is "parity unpinned".
 """
-from . import accept, dnc, drafter
+from . import accept, dnc, drafter, refine
 
-__all__ = ["accept", "dnc", "drafter"]
+__all__ = ["accept", "dnc", "drafter", "refine"]
