@@ -319,7 +319,7 @@ def main():
 
     # lossless stochastic verification (not part of the step): the step's target rows against
     # draft logits near them, drafts sampled from the draft logits by the library's sampler
-    vsample = top_p = None
+    vsample = top_p = refinement = None
     if not args.profile_steps_only:
         g = torch.Generator(device=dev).manual_seed(2)
         dlog = (tlogits[:, :D] + 0.5 * torch.randn(tlogits[:, :D].shape, generator=g,
@@ -361,6 +361,48 @@ def main():
         top_p = {"ms": round(tms, 4), "logit_bytes": tb, "draws_per_position": 8, "p": 0.9,
                  "GBps": round(tb / (tms * 1e-3) / 1e9, 1),
                  "hbm_frac": round(tb / (tms * 1e-3) / HBM_PEAK, 4)}
+        # block refinement (Mask-Predict, two passes): the step's forward with its LM-head logits
+        # kept, refine_block re-masking the floor(D/2) least confident drafts, the forward again
+        # on the partly filled block (no new rows), the final update, the same greedy verify
+        rlog = torch.empty((N, D, V), dtype=torch.float32, device=dev)
+        rws = torch.empty(dbd.refine_workspace_bytes(N, D, V), dtype=torch.uint8, device=dev)
+        gws = torch.empty(dbd.verify_workspace_bytes(N, wl.verify_rows, V), dtype=torch.uint8,
+                          device=dev)
+        rblk = tokens.clone()
+        conf = torch.zeros((N, D), dtype=torch.int64, device=dev)
+        ctx2 = torch.tensor((ctx + new).astype(np.int32), device=dev)
+        off0 = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+
+        def refined_step():
+            rblk.copy_(tokens)
+            conf.zero_()
+            dbd.draft_block(desc, ws_w, rblk, step_rows, off_step, ctx_t, kv_k, kv_v, drafts, ws,
+                            T_step, logits_out=rlog)
+            dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, D // 2, rws)
+            dbd.draft_block(desc, ws_w, rblk, None, off0, ctx2, kv_k, kv_v, drafts, ws, 0,
+                            logits_out=rlog)
+            dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, 0, rws)
+            dbd.verify_greedy(tlogits, rblk[:, wl.n_anchor:], n_acc, bonus, committed, gws)
+
+        for _ in range(2):
+            refined_step()
+        torch.cuda.synchronize()
+        v0.record()
+        for _ in range(args.steps):
+            refined_step()
+        v1.record()
+        torch.cuda.synchronize()
+        rms = v0.elapsed_time(v1) / args.steps
+        v0.record()
+        for _ in range(args.steps):
+            dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, D // 2, rws)
+        v1.record()
+        torch.cuda.synchronize()
+        ums = v0.elapsed_time(v1) / args.steps
+        refinement = {"rule": "mask-predict", "passes": 2, "remasked": D // 2,
+                      "ms_per_step": round(rms, 4), "blocks_per_s": round(N / (rms * 1e-3), 1),
+                      "refine_block_ms": round(ums, 4),
+                      "refine_block_GBps": round(tb / (ums * 1e-3) / 1e9, 1)}
         vsample = {"ms": round(vms, 4), "logit_bytes": vb,
                    "GBps": round(vb / (vms * 1e-3) / 1e9, 1),
                    "hbm_frac": round(vb / (vms * 1e-3) / HBM_PEAK, 4),
@@ -417,6 +459,7 @@ def main():
         "cold_ingest": cold_info,
         "verify_sample": vsample,
         "top_p_sampling": top_p,
+        "refinement": refinement,
         "cpu_baseline": cpu,
         "setup_s": round(t_setup, 1),
     }

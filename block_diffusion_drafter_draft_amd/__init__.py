@@ -7,6 +7,7 @@ tensors provide device memory and the current HIP stream.  The library must be b
 Entry points (same names as the C ABI in include/dbd.h):
   draft_block, verify_greedy, select_streak
   draft_workspace_bytes, verify_workspace_bytes, select_workspace_bytes
+  refine_block, refine_workspace_bytes (Mask-Predict update between draft_block passes)
 Stage hooks used by the parity tests: sample_from_logits, mix_rmsnorm, gemm_nt.
 """
 import ctypes
@@ -78,6 +79,9 @@ def lib():
                                      _vp, _vp, _vp, _sz, _vp]),
             "dbd_sample_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
             "dbd_sample_top_p_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
+            "dbd_refine_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
+            "refine_block": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                    _vp]),
             "dbd_sample_top_p": (_i32, [_vp, _i32, _i32, _i32, _i32, _f32, _f32, _u64, _vp,
                                         _vp, _sz, _vp]),
             "dbd_sample_from_logits": (_i32, [_vp, _i32, _i32, _i32, _i32, _f32, _u64, _vp, _vp,
@@ -270,6 +274,23 @@ def sample_top_p(logits, n_drafts, temperature, top_p, seed, out, workspace, str
     _check(lib().dbd_sample_top_p(
         _ptr(logits), N, D, V, n_drafts, float(temperature), float(top_p),
         int(seed) & (2**64 - 1), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, logits)))
+
+
+def refine_workspace_bytes(batch, n_draft, vocab) -> int:
+    out = _sz(0)
+    _check(lib().dbd_refine_workspace_bytes(batch, n_draft, vocab, _c.byref(out)))
+    return out.value
+
+
+def refine_block(logits, block_tokens, conf, n_anchor, mask_id, n_remask, workspace,
+                 stream=None):
+    """One refinement update: logits [N, D, V] fp32 of the forward that read block_tokens [N, B]
+    int32; block_tokens and conf [N, D] uint64 (stored as int64) are updated in place."""
+    N, D, V = logits.shape
+    _check(lib().refine_block(
+        _ptr(logits), N, block_tokens.shape[1], n_anchor, V, mask_id, n_remask,
+        _ptr(block_tokens), _ptr(conf), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, logits)))
 
 

@@ -191,6 +191,11 @@ hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const fl
                         const int32_t* pi, float inv_t, uint64_t mp, int sp, float* row_max,
                         int64_t* st, uint64_t* hist, uint64_t* above, int32_t* cnt,
                         uint64_t* keys, uint64_t* rz, hipStream_t s);
+// One Mask-Predict update per sequence from row_arg / zpart of launch_zsum_partial at
+// temperature 1 over the N * D rows: tokens [N, B] and conf [N, D] in/out.
+hipError_t launch_refine(const int32_t* row_arg, const uint64_t* zpart, int batch, int vocab,
+                         int chunk, int D, int B, int n_anchor, int mask_id, int n_remask,
+                         int32_t* tokens, uint64_t* conf, hipStream_t s);
 hipError_t launch_verify_finalize(const float* pv, const int32_t* pi, const int32_t* pflag,
                                   int nch, const int32_t* drafts, int draft_stride, int batch,
                                   int n_draft, int n_rows, int32_t* n_acc, int32_t* bonus,

@@ -1,6 +1,9 @@
 // Vocabulary-wide kernels: row argmax, integer-exact sampling weights, drafting by sampling,
 // greedy verification and streak-score self-selection.
 //
+// Block refinement: the DFlash summary page's paragraph on block diffusion (a block drafted in one
+// forward pass, refined when needed), read as Mask-Predict (Ghazvininejad et al., EMNLP 2019).
+//
 // Greedy verification: DFlare page, section on drafting in parallel and accepting with the target
 // (keep the prefix up to the first mismatch, append the target's token).  Sampling K joint
 // drafts from the single-step marginals and choosing the one with the largest expected streak:
@@ -672,6 +675,52 @@ hipError_t launch_top_p(const float* x, int rows, int vocab, int chunk, const fl
                      row_max, inv_t, st, above, cnt, keys);
   hipLaunchKernelGGL(topp_resolve_kernel, dim3(rows), dim3(256), 0, s, x, vocab, chunk, nch,
                      row_max, inv_t, above, cnt, keys, st, rz);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ block refinement
+// One wave per sequence (D <= 64), after the argmax and weight sums of the D rows at temperature
+// 1.  A position masked in the forward that produced the logits (conf 0) takes its row's argmax
+// and Z; the argmax weight is 2^40, so its probability 2^40 / Z orders like 1 / Z.  Then the
+// n_remask positions of largest Z, the lower index first on ties, are masked again (block token
+// mask_id, conf 0) for the next forward.
+__global__ __launch_bounds__(64) void refine_kernel(const int32_t* __restrict__ row_arg,
+                                                    const uint64_t* __restrict__ zpart, int nch,
+                                                    int D, int B, int n_anchor, int mask_id,
+                                                    int n_remask, int32_t* __restrict__ tokens,
+                                                    uint64_t* __restrict__ conf) {
+  const int n = blockIdx.x, j = threadIdx.x;
+  uint64_t z = 0;
+  int tok = 0;
+  if (j < D) {
+    const int64_t row = (int64_t)n * D + j;
+    z = conf[row];
+    tok = tokens[(int64_t)n * B + n_anchor + j];
+    if (z == 0) {
+      for (int c = 0; c < nch; ++c) z += zpart[row * nch + c];
+      tok = row_arg[row];
+    }
+  }
+  int rank = 0;                                // positions less confident than this one
+  for (int k = 0; k < D; ++k) {
+    const uint64_t zk = ((uint64_t)__shfl((uint32_t)(z >> 32), k, 64) << 32) |
+                        __shfl((uint32_t)z, k, 64);
+    rank += zk > z || (zk == z && k < j);
+  }
+  if (j < D) {
+    const bool re = rank < n_remask;
+    tokens[(int64_t)n * B + n_anchor + j] = re ? mask_id : tok;
+    conf[(int64_t)n * D + j] = re ? 0 : z;
+  }
+}
+
+hipError_t launch_refine(const int32_t* row_arg, const uint64_t* zpart, int batch, int vocab,
+                         int chunk, int D, int B, int n_anchor, int mask_id, int n_remask,
+                         int32_t* tokens, uint64_t* conf, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  if (D > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(refine_kernel, dim3(batch), dim3(64), 0, s, row_arg, zpart,
+                     ceil_div(vocab, chunk), D, B, n_anchor, mask_id, n_remask, tokens, conf);
   return hipGetLastError();
 }
 

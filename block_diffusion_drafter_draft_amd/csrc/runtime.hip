@@ -987,6 +987,49 @@ int dbd_sample_top_p(const float* logits, int32_t batch, int32_t n_draft, int32_
   return DBD_OK;
 }
 
+int dbd_refine_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(DBD_ERR_ARG, "bytes is NULL");
+  if (batch < 1 || n_draft < 1 || vocab < 2) return fail(DBD_ERR_ARG, "bad dimensions");
+  *bytes = carve_sample(batch * n_draft, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, nullptr);
+  return DBD_OK;
+}
+
+int refine_block(const float* logits, int32_t batch, int32_t block_len, int32_t n_anchor,
+                 int32_t vocab, int32_t mask_id, int32_t n_remask, int32_t* block_tokens,
+                 uint64_t* conf, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!logits || !block_tokens || !conf)
+    return fail(DBD_ERR_ARG, "a required device pointer is NULL");
+  if (n_anchor != 0 && n_anchor != 1) return fail(DBD_ERR_ARG, "n_anchor must be 0 or 1");
+  if (batch < 1 || block_len < 1 + n_anchor || block_len > 64)
+    return fail(DBD_ERR_SHAPE, "batch %d / block_len %d out of range", batch, block_len);
+  if (vocab < 2 || vocab >= (1 << 18)) return fail(DBD_ERR_SHAPE, "vocab %d out of range", vocab);
+  const int D = block_len - n_anchor;
+  if (mask_id < 0 || mask_id >= vocab) return fail(DBD_ERR_ARG, "mask_id %d not in the vocabulary", mask_id);
+  if (n_remask < 0 || n_remask > D)
+    return fail(DBD_ERR_ARG, "n_remask %d out of [0, %d]", n_remask, D);
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const int rows = batch * D;
+  const size_t need = carve_sample(rows, vocab, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  float *pv, *rm;
+  int32_t *pi, *pf, *ra;
+  uint64_t* zp;
+  carve_sample(rows, vocab, (char*)workspace, &pv, &pi, &pf, &zp, &rm, &ra);
+  hipStream_t st = (hipStream_t)stream;
+  const int ch = vocab_chunk();
+  HIP_TRY(launch_argmax_partial(logits, rows, vocab, ch, pv, pi, pf, st));
+  HIP_TRY(launch_zsum_partial(logits, rows, vocab, ch, pv, pi, 1.0f, zp, rm, ra, st));
+  HIP_TRY(launch_refine(ra, zp, batch, vocab, ch, D, block_len, n_anchor, mask_id, n_remask,
+                        block_tokens, conf, st));
+  return DBD_OK;
+}
+
 int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const void* mix_norm_w,
                     const void* hidden, int64_t hid_token_stride, int64_t hid_layer_stride,
                     int32_t n_tokens, void* out, void* stream) {

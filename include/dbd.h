@@ -256,6 +256,31 @@ int select_streak(const float* verifier_logits, const int32_t* drafts, int32_t b
                   int32_t* committed, int32_t* row_flags, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Workspace size (host) for refine_block. */
+int dbd_refine_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab,
+                               size_t* bytes /* host out */);
+
+/* refine_block: one update of iterative block refinement between two draft_block passes.  The
+ * DFlash summary page (paragraph on block diffusion) says a block drafted in one forward pass is
+ * refined when needed and gives no rule; the library reads it as Mask-Predict (Ghazvininejad,
+ * Levy, Liu and Zettlemoyer, EMNLP 2019): T passes, the first drafts every position, before pass
+ * t the floor(D (T - t) / T) least confident positions are masked again and re-drafted.
+ *
+ * logits       [N, D, V] fp32 (device): the D drafted rows of the forward that read block_tokens
+ *              (draft_block's logits_out).
+ * block_tokens [N, B] int32 (device, in/out): the block of that forward -> the block of the next.
+ * conf         [N, D] uint64 (device, in/out): 0 marks a position masked in that forward; other
+ *              values are confidences kept from earlier passes.  Start with all zeros.
+ * For every position with conf 0: token = the row's argmax (lowest index on ties), conf = Z of
+ * the row's integer weights at temperature 1 (its argmax probability is 2^40 / Z).  Then the
+ * n_remask positions with the largest conf (lower index first on ties) get mask_id and conf 0;
+ * n_remask = 0 after the last pass leaves the final tokens in block_tokens.
+ * Anchors (n_anchor = 1: column 0) are never touched.  Results for rows with non-finite logits
+ * are unspecified. */
+int refine_block(const float* logits, int32_t batch, int32_t block_len, int32_t n_anchor,
+                 int32_t vocab, int32_t mask_id, int32_t n_remask, int32_t* block_tokens,
+                 uint64_t* conf, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Test hooks: exported for parity tests of single stages; not part of the drafting API ---- */
 
 /* Workspace size (host) for dbd_sample_from_logits. */

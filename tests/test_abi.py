@@ -314,3 +314,22 @@ def test_sample_top_p_validation():
     assert call(1.0, float("nan")) == -1
     assert call(1.0, 0.9, wb=ws - 1) == -4
     assert call(1.0, 0.9, w=fake + 8) == -4
+
+
+def test_refine_block_validation():
+    L = dbd.lib()
+    fake = 1 << 20
+    ws = dbd.refine_workspace_bytes(2, 15, 1000)
+    assert ws == dbd.sample_workspace_bytes(2, 15, 1000)
+
+    def call(B=16, anchor=1, V=1000, mask=999, n=3, wb=ws, w=fake, lg=fake):
+        return L.refine_block(lg, 2, B, anchor, V, mask, n, fake, fake, w, wb, None)
+
+    assert call(lg=None) == -1
+    assert call(anchor=2) == -1
+    assert call(B=1) == -2 and call(B=65) == -2
+    assert call(V=1 << 18, mask=5) == -2
+    assert call(mask=1000) == -1 and call(mask=-1) == -1
+    assert call(n=16) == -1 and call(n=-1) == -1
+    assert call(wb=ws - 1) == -4
+    assert call(w=fake + 8) == -4
