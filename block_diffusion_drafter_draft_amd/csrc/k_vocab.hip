@@ -33,8 +33,9 @@ __device__ __forceinline__ float exp_i(float x) {
   const float c7 = 1.0f / 5040.0f, c6 = 1.0f / 720.0f, c5 = 1.0f / 120.0f, c4 = 1.0f / 24.0f,
               c3 = 1.0f / 6.0f, c2 = 0.5f;
   const float t = __fmul_rn(x, EXPI_LOG2E);
-  if (t < -64.0f) return 0.0f;
-  const float k = rintf(t);
+  // Branch-free: inputs with t < -64 are computed too and replaced by 0 at the end.  The clamp
+  // leaves every t >= -64 unchanged and keeps k's conversion to int in range for the others.
+  const float k = rintf(fmaxf(t, -65.0f));
   float r = __fsub_rn(x, __fmul_rn(k, EXPI_LN2_HI));
   r = __fsub_rn(r, __fmul_rn(k, EXPI_LN2_LO));
   float p = c7;
@@ -45,12 +46,18 @@ __device__ __forceinline__ float exp_i(float x) {
   p = __fadd_rn(__fmul_rn(p, r), c2);
   p = __fadd_rn(__fmul_rn(p, r), 1.0f);
   p = __fadd_rn(__fmul_rn(p, r), 1.0f);
-  return ldexpf(p, (int)k);
+  const float v = ldexpf(p, (int)k);
+  return t < -64.0f ? 0.0f : v;
 }
 
+// q = floor(e * 2^40) for e in [0, 1]: f = e * 2^40 < 2^41 is exact, hi = floor(f / 2^32) and
+// lo = f - hi * 2^32 in [0, 2^32) are exact, and converting lo truncates, which is its floor.
 __device__ __forceinline__ uint64_t weight_q(float l, float M, float inv_t) {
   const float e = exp_i(__fmul_rn(__fsub_rn(l, M), inv_t));
-  return (uint64_t)floorf(ldexpf(e, 40));
+  const float f = ldexpf(e, 40);
+  const float hi = floorf(__fmul_rn(f, 0x1p-32f));
+  const float lo = fmaf(hi, -0x1p32f, f);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
 __device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
