@@ -370,6 +370,9 @@ def main():
                           device=dev)
         rblk = tokens.clone()
         conf = torch.zeros((N, D), dtype=torch.int64, device=dev)
+        r_acc = torch.empty(N, dtype=torch.int32, device=dev)
+        r_bonus = torch.empty(N, dtype=torch.int32, device=dev)
+        r_com = torch.empty((N, D + 1), dtype=torch.int32, device=dev)
         ctx2 = torch.tensor((ctx + new).astype(np.int32), device=dev)
         off0 = torch.zeros(N + 1, dtype=torch.int32, device=dev)
 
@@ -382,7 +385,7 @@ def main():
             dbd.draft_block(desc, ws_w, rblk, None, off0, ctx2, kv_k, kv_v, drafts, ws, 0,
                             logits_out=rlog)
             dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, 0, rws)
-            dbd.verify_greedy(tlogits, rblk[:, wl.n_anchor:], n_acc, bonus, committed, gws)
+            dbd.verify_greedy(tlogits, rblk[:, wl.n_anchor:], r_acc, r_bonus, r_com, gws)
 
         for _ in range(2):
             refined_step()
