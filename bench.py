@@ -100,15 +100,16 @@ def summarize_traffic(d):
     ff, fw = copy_factor("copy_fetch", "FETCH_SIZE"), copy_factor("copy_write", "WRITE_SIZE")
     fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
     out = {"commands": [
+               "REPO=<repository root>; OUT=<output directory>",
                "cd /tmp && export TMPDIR=/tmp",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/m/traffic/fetch"
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic/fetch"
                " -o run -- python3 $REPO/bench.py --steps 3 --warmup 1 --profile-steps-only"
                " --no-cpu-baseline",
-               "(the same with --pmc WRITE_SIZE into .../traffic/write)",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/m/traffic/copy_fetch"
+               "(the same with --pmc WRITE_SIZE into $OUT/traffic/write)",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic/copy_fetch"
                " -o run -- python3 $REPO/bench.py --calibrate-copy",
-               "(the same with --pmc WRITE_SIZE into .../traffic/copy_write)",
-               "python3 bench.py --summarize-traffic gpurun_out/m/traffic"],
+               "(the same with --pmc WRITE_SIZE into $OUT/traffic/copy_write)",
+               "python3 $REPO/bench.py --summarize-traffic $OUT/traffic"],
            "source_hash": kernel_source_hash(), "copy_factor_fetch": round(ff, 4),
            "copy_factor_write": round(fw, 4), "kernels": {}}
     for k in fetch:
