@@ -238,3 +238,63 @@ def test_sixty_four_mask_block_without_anchor():
     assert torch.all(status == 0)
     _check_drafts_property(case, drafts, logits)
     _compare(case, logits, range(wl.batch), [])
+
+
+def test_step_replays_from_a_hip_graph():
+    """A sampling draft_block (ingest + block forward + 4 joint drafts) and verify_greedy, captured
+    once in a HIP graph: every replay, with eager library calls and torch work between replays,
+    gives the eager call's drafts, logits, status and acceptance bit for bit."""
+    sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
+                            n_layers=2, n_target_layers=2, vocab=2048, dtype="bf16")
+    wl = synth.Workload(name="graph", shape=sh, batch=3, block_len=16, n_anchor=1, n_drafts=4,
+                        temperature=1.2, ctx_lo=70, ctx_hi=130, ctx_source="hidden",
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=5)
+    print("draft_block + verify_greedy under graph capture", flush=True)
+    case = Case(wl, dev=DEV)
+    case.fill_cache()
+    N, D, V, K = wl.batch, case.D, sh.vocab, wl.n_drafts
+    hid = case._hidden_rows(case.ctx, case.ctx + case.new)
+    off, tot = case._offsets(case.new)
+    ctx = torch.tensor(case.ctx.astype(np.int32), device=DEV)
+    ws = case.workspace(tot, K, wl.temperature)
+    drafts = torch.empty((N, K, D), dtype=torch.int32, device=DEV)
+    logits = torch.empty((N, D, V), dtype=torch.float32, device=DEV)
+    status = torch.empty((N,), dtype=torch.int32, device=DEV)
+    tl, _ = synth.make_planted_verify_logits(synth.make_drafts(N, 1, D, V, seed=3, device=DEV)[:, 0]
+                                             .contiguous(), wl.verify_rows, V, 0.8, seed=3,
+                                             device=DEV)
+    vws = torch.empty(dbd.verify_workspace_bytes(N, wl.verify_rows, V), dtype=torch.uint8,
+                      device=DEV)
+    n_acc = torch.empty((N,), dtype=torch.int32, device=DEV)
+    bonus = torch.empty((N,), dtype=torch.int32, device=DEV)
+    com = torch.empty((N, D + 1), dtype=torch.int32, device=DEV)
+    outs = (drafts, logits, status, n_acc, bonus, com)
+
+    def run():
+        dbd.draft_block(case.desc, case.wstruct, case.tokens, hid, off, ctx, case.kv_k,
+                        case.kv_v, drafts, ws, tot, n_drafts=K, temperature=wl.temperature,
+                        seed=99, n_anchor=wl.n_anchor, logits_out=logits, seq_status=status)
+        dbd.verify_greedy(tl, drafts[:, 0], n_acc, bonus, com, vws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(-3)
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(outs, ref):
+            assert torch.equal(t, r), f"replay {rep} differs"
+        run()                                     # eager work between replays
+        torch.cuda.synchronize()
+    assert torch.all(status == 0)
