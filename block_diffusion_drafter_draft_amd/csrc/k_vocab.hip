@@ -1,8 +1,8 @@
 // Vocabulary-wide kernels: row argmax, integer-exact sampling weights, drafting by sampling,
 // greedy verification and streak-score self-selection.
 //
-// Block refinement: the DFlash summary page's paragraph on block diffusion (a block drafted in one
-// forward pass, refined when needed), read as Mask-Predict (Ghazvininejad et al., EMNLP 2019).
+// Block refinement: the DFlash article's section on writing a whole block in one forward pass (the
+// block is refined when needed), read as Mask-Predict (Ghazvininejad et al., EMNLP 2019).
 //
 // Greedy verification: DFlare page, section on drafting in parallel and accepting with the target
 // (keep the prefix up to the first mismatch, append the target's token).  Sampling K joint

@@ -261,7 +261,7 @@ int dbd_refine_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab,
                                size_t* bytes /* host out */);
 
 /* refine_block: one update of iterative block refinement between two draft_block passes.  The
- * DFlash summary page (paragraph on block diffusion) says a block drafted in one forward pass is
+ * DFlash article (section on writing a whole block in one forward pass) says the block is
  * refined when needed and gives no rule; the library reads it as Mask-Predict (Ghazvininejad,
  * Levy, Liu and Zettlemoyer, EMNLP 2019): T passes, the first drafts every position, before pass
  * t the floor(D (T - t) / T) least confident positions are masked again and re-drafted.

@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE: part of the CPU oracle (see the package docstring); only the tests, the
 smoke check and the bench's CPU-baseline leg may import it.
 
-The DFlash summary page (its paragraph on block diffusion, in Japanese) says the drafter emits a
-whole block in one forward pass and refines it when needed; no page states how.  Reading:
+The DFlash article (its section on writing a whole block in one forward pass) says the drafter
+emits the block in one forward pass and refines it when needed; no page states how.  Reading:
 Mask-Predict (Ghazvininejad, Levy, Liu and Zettlemoyer, EMNLP 2019), the published rule for
 refining parallel masked predictions.  A block of D drafted positions gets T forward passes; the
 first drafts every position; before pass t (1 <= t < T) the n_t = floor(D (T - t) / T) least
