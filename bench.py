@@ -49,13 +49,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3-8b_bs32.json")
 COPY_BYTES = 1 << 30
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources: traffic counters are only valid for the build they came from."""
-    d = os.path.join(ROOT, "block_diffusion_drafter_draft_amd", "csrc")
+def strip_comments(src: str) -> str:
+    """C/C++ source without comments and blank-space differences (the code the compiler sees)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+
+
+def kernel_source_hash(d=None):
+    """Hash of the HIP sources' code (comments and spacing ignored): traffic counters are only
+    valid for the build they came from."""
+    d = d or os.path.join(ROOT, "block_diffusion_drafter_draft_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(strip_comments(open(os.path.join(d, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
