@@ -107,15 +107,25 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   const float* xr = x + rbase;
   if (((uintptr_t)(xr + v0) & 15) == 0) {
     const int nv = (v1 - v0) >> 2;
-    for (int k = threadIdx.x; k < nv; k += 256) {
-      const float4 q = *reinterpret_cast<const float4*>(xr + v0 + 4 * k);
-      const int b = v0 + 4 * k;
+    const float4* x4 = reinterpret_cast<const float4*>(xr + v0);
+    auto take = [&](const float4& q, int b) __attribute__((always_inline)) {
       bad |= !isfinite(q.x) | !isfinite(q.y) | !isfinite(q.z) | !isfinite(q.w);
       argmax_combine(bv, bi, q.x, b);
       argmax_combine(bv, bi, q.y, b + 1);
       argmax_combine(bv, bi, q.z, b + 2);
       argmax_combine(bv, bi, q.w, b + 3);
+    };
+    // four float4 loads in flight per thread before any is combined (a 4096-wide chunk is
+    // exactly one such round); the combine is order-independent (max, lowest index on ties)
+    int k = threadIdx.x;
+    for (; k + 3 * 256 < nv; k += 4 * 256) {
+      float4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = x4[k + u * 256];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) take(q[u], v0 + 4 * (k + u * 256));
     }
+    for (; k < nv; k += 256) take(x4[k], v0 + 4 * k);
     for (int v = v0 + 4 * nv + threadIdx.x; v < v1; v += 256) {
       const float q = xr[v];
       bad |= !isfinite(q);
