@@ -249,7 +249,20 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);       // out-of-range ids are clamped
   const T* e = E + (int64_t)id * H;
   float* o = x + (int64_t)r * H;
-  for (int i = threadIdx.x; i < H; i += 256) o[i] = to_f(e[i]);
+  constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte load
+  if (H % VEC == 0 && (((uintptr_t)e | (uintptr_t)o) & 15) == 0) {
+    // 16-byte loads, two in flight per thread for H = 4096 bf16
+    for (int i = threadIdx.x * VEC; i < H; i += 256 * VEC) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(e + i);
+      const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int q = 0; q < VEC; q += 4)
+        *reinterpret_cast<f32x4*>(o + i + q) =
+            f32x4{to_f(v[q]), to_f(v[q + 1]), to_f(v[q + 2]), to_f(v[q + 3])};
+    }
+  } else {
+    for (int i = threadIdx.x; i < H; i += 256) o[i] = to_f(e[i]);
+  }
 }
 
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H, int V,

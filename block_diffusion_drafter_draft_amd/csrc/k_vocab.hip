@@ -162,8 +162,21 @@ __device__ __forceinline__ void reduce_partials(const float* pv, const int32_t* 
                                                 int nch, float& bv, int& bi) {
   bv = -INFINITY;
   bi = 0x7fffffff;
-  for (int c = threadIdx.x & 63; c < nch; c += 64)
-    argmax_combine(bv, bi, pv[row * nch + c], pi[row * nch + c]);
+  const int lane = threadIdx.x & 63;
+  // eight partials per lane loaded before any is combined (the combine is order-independent)
+  int c = lane;
+  for (; c + 7 * 64 < nch; c += 8 * 64) {
+    float v[8];
+    int ix[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = pv[row * nch + c + 64 * u];
+      ix[u] = pi[row * nch + c + 64 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) argmax_combine(bv, bi, v[u], ix[u]);
+  }
+  for (; c < nch; c += 64) argmax_combine(bv, bi, pv[row * nch + c], pi[row * nch + c]);
   wave_argmax(bv, bi);
 }
 
