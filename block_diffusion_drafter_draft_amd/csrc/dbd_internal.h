@@ -160,7 +160,7 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
                    int F, bool pair, bool split_ok, int split_req = 0);
-constexpr int kMaxGemmCfg = 16;
+constexpr int kMaxGemmCfg = 18;
 constexpr int kMaxGemmSplit = 16;
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
 hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,

@@ -242,9 +242,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, EpiArgs e) {
 // optional split-K (k_gemm_deep.hip; 8-10 four waves, 11-13 eight waves).
 constexpr int kNumCfg = kMaxGemmCfg + 1;
 static const int kCfgBM[kNumCfg] = {256, 256, 128, 64, 128, 64, 256, 128, 256, 128, 128,
-                                    256, 256, 256, 256, 256, 256};
+                                    256, 256, 256, 256, 256, 256, 64, 32};
 static const int kCfgBN[kNumCfg] = {256, 128, 128, 128, 128, 128, 128, 256, 128, 256, 128,
-                                    256, 192, 128, 256, 192, 128};
+                                    256, 192, 128, 256, 192, 128, 128, 128};
+// 17, 18: the skinny tiles (64 or 32 rows, every weight read once) for M <= 64
+static bool is_skinny(int cfg) { return cfg == 17 || cfg == 18; }
 static bool is_deep(int cfg) { return cfg >= 8; }
 
 template <int BM, int BN, int ST, int KIND, bool SPLITA>
@@ -282,6 +284,7 @@ static void launch_cfg(int cfg, const GemmArgs& a, const EpiArgs& e, int batch, 
 // The configuration a bf16-pair launch of `cfg` really uses (the pair doubles the A operand's
 // LDS and registers, so only the smaller tiles take it).
 static int pair_cfg(int cfg) {
+  if (is_skinny(cfg)) return cfg;                 // the skinny tiles take the pair themselves
   if (is_deep(cfg)) return 10;
   if (cfg == 3 || cfg == 5) return 5;
   return 4;
@@ -327,6 +330,12 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
     const int n = gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N;
     return ceil_div(M, kCfgBM[c]) * ceil_div(n, kCfgBN[c]) * batch;
   };
+  // M <= 64 rows: the skinny tiles, which read every weight element once, where they measured
+  // faster on the SpecDiff-2-shaped drafter (M = 32 and 64 rows): gate/up and the LM head, and
+  // the residual projections at M <= 32; Q/K/V keeps the deep tile with split-K
+  if (M <= 64 && (kind == EPI_SWIGLU || kind == EPI_ARGMAX || kind == EPI_STORE_F32 ||
+                  (kind == EPI_RESID && M <= 32)))
+    return M <= 32 ? 18 : 17;
   if (M >= 64 && (pair || kind == EPI_QKV || kind == EPI_CTXKV)) return 10;
   if (!pair && kind != EPI_QKV && kind != EPI_CTXKV && M >= 128) {
     // the register-staged forms of the 256 x 256 and 256 x 192 tiles (14, 15)
@@ -391,6 +400,15 @@ struct TileChoice {
 static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gateup, int F,
                               bool pair) {
   const int base = choose_cfg(kind, M, N, K, batch, gateup, F, pair);
+  if (is_skinny(base)) {
+    // split K (powers of two, each unit keeping at least two 64-wide k stages) until there are
+    // about 512 units: weight streaming wants every CU busy with several workgroups
+    const int nv = gateup ? ceil_div(F, 64) * 128 : N;
+    const int tiles = ceil_div(nv, 128) * batch;
+    int S = 1;
+    while (S < 16 && tiles * S < 512 && K / 64 / (2 * S) >= 2) S *= 2;
+    return {base, S};
+  }
   if (gateup || (base != 3 && base != 10)) return {base, 1};
   TileChoice best{base, 1};
   double best_t = model_us(kind, base, M, N, K, batch, 1, pair);

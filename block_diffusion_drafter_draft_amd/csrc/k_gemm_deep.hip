@@ -559,6 +559,182 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
   store_tile([&](int i, int j) { return acc[i][j]; });
 }
 
+// ------------------------------------------------------------------ skinny: M <= 64 rows
+// For a handful of rows (a small block, few sequences) the projections stream their weights:
+// one row tile covers all M rows (MT = 32 or 64), so every weight element is read exactly once.
+// Block tile MT x 128, four waves in a 1 x 4 grid, each wave all MT rows and 32 columns.  No two
+// waves share a B fragment, so B goes straight from memory into VGPRs (the MFMA fragment layout,
+// 8 consecutive k of one column per lane), two 64-wide k stages ahead in three register sets;
+// A (and its low bf16 part with SPLITA) is staged global -> VGPRs -> a two-slot LDS ring.
+// Split-K gives every CU work: units = column tiles x S.
+template <int MT, bool SPLITA>
+struct SkinnyCfg {
+  static constexpr int BM = MT, BN = 128, KS = 64, NT = 256, NW = 4, ROWB = 128;
+  static constexpr int NA = SPLITA ? 2 : 1;
+  static constexpr int ABYTES = BM * ROWB;                  // one A part of a stage
+  static constexpr int STAGE = NA * ABYTES;
+  static constexpr int CH = (ABYTES + 16 * NT - 1) / (16 * NT);   // A chunks per thread
+  static constexpr int WTN = BN / NW, MI = BM / 16, NI = WTN / 16;
+  static constexpr int TM = MT > 32 ? 32 : MT;              // epilogue rows per pass
+  static constexpr int CBYTES = TM * (BN + 4) * 4;
+  static constexpr int SMEM = 2 * STAGE > CBYTES ? 2 * STAGE : CBYTES;
+  static_assert(MI >= 1 && NI == 2, "tile shape");
+};
+
+template <int MT, int KIND, bool SPLITA>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e) {
+  using C = SkinnyCfg<MT, SPLITA>;
+  constexpr int BM = C::BM, BN = C::BN, KS = C::KS, MI = C::MI, NI = C::NI;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int z = blockIdx.z;
+  const int M = a.M, N = a.N, K = a.K;
+  const int S = a.split > 1 ? a.split : 1;
+  const int tiles_m = (M + BM - 1) / BM;                    // 1 for M <= MT
+  int tm, tn, sp;
+  unit_of(blockIdx.x, gridDim.x, tiles_m, S, &tm, &tn, &sp);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk_all = K / KS;
+  const int kb = (int)((int64_t)nk_all * sp / S), nk = (int)((int64_t)nk_all * (sp + 1) / S) - kb;
+
+  // A: chunk c = tid + 256 q of a part is row c / 8, 16-byte chunk c % 8 (slot (c % 8) ^ swz(row))
+  const bf16* asrc[C::CH];
+  const bf16* a2src[C::CH];
+  uint32_t adst[C::CH];
+  bool aok[C::CH];
+#pragma unroll
+  for (int q = 0; q < C::CH; ++q) {
+    const int c = tid + C::NT * q, row = c >> 3, ch = c & 7;
+    aok[q] = row < BM;
+    const int64_t off = (int64_t)z * a.a_bs + (int64_t)min(m0 + min(row, BM - 1), M - 1) * a.lda +
+                        (int64_t)kb * KS + ch * 8;
+    asrc[q] = (const bf16*)a.A + off;
+    a2src[q] = SPLITA ? (const bf16*)a.A2 + off : asrc[q];
+    adst[q] = (uint32_t)(min(row, BM - 1) * C::ROWB + ((ch ^ swz(row)) * 16));
+  }
+  // B: lane (fr, fk) of column tile j holds column n0 + 32 wave + 16 j + fr, k = 32 s + 8 fk
+  const int fr = lane & 15, fk = lane >> 4;
+  const BMap bm = make_bmap(a);
+  const bf16* bsrc[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    bsrc[j] = brow_ptr<bf16, BN>(bm, min(n0 + wave * C::WTN + 16 * j + fr, N - 1), z) +
+              (int64_t)kb * KS + 8 * fk;
+
+  u32x4 sa0[C::CH][2], sa1[C::CH][2], sa2[C::CH][2];
+  u32x4 b0[NI][2], b1[NI][2], b2[NI][2];
+  auto load = [&](u32x4 (*sa)[2], u32x4 (*bq)[2], int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) bq[j][s2] = load_global16(bsrc[j] + kt * KS + 32 * s2);
+#pragma unroll
+    for (int q = 0; q < C::CH; ++q) {
+      if (!aok[q]) continue;
+      sa[q][0] = load_global16(asrc[q] + kt * KS);
+      if constexpr (SPLITA) sa[q][1] = load_global16(a2src[q] + kt * KS);
+    }
+  };
+  auto store = [&](u32x4 (*sa)[2], int slot) __attribute__((always_inline)) {
+    char* base = smem + slot * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < C::CH; ++q) {
+      if (!aok[q]) continue;
+      *reinterpret_cast<u32x4*>(base + adst[q]) = sa[q][0];
+      if constexpr (SPLITA) *reinterpret_cast<u32x4*>(base + C::ABYTES + adst[q]) = sa[q][1];
+    }
+  };
+  int rd[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) rd[s2] = fr * C::ROWB + (((4 * s2 + fk) ^ swz(fr)) * 16);
+
+  f32x4 acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot, u32x4 (*bq)[2]) __attribute__((always_inline)) {
+    const char* st = smem + slot * C::STAGE;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const bf16x8 fa = *reinterpret_cast<const bf16x8*>(st + rd[s2] + i * 16 * C::ROWB);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              fa, *reinterpret_cast<const bf16x8*>(&bq[j][s2]), acc[i][j], 0, 0, 0);
+        if constexpr (SPLITA) {
+          const bf16x8 fa2 =
+              *reinterpret_cast<const bf16x8*>(st + C::ABYTES + rd[s2] + i * 16 * C::ROWB);
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                fa2, *reinterpret_cast<const bf16x8*>(&bq[j][s2]), acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // Stage kt: LDS slot kt & 1 holds A of stage kt; register set `cur` B of stage kt, `nx1` A and
+  // B of stage kt + 1, `nx2` free: stage kt + 2 is loaded into it, stage kt computed, A of stage
+  // kt + 1 stored into the other slot (last read in stage kt - 1, before the barrier ending it).
+  // Loads past the last stage reload the last one.
+  auto step = [&](int kt, u32x4 (*bcur)[2], u32x4 (*anx1)[2], u32x4 (*anx2)[2],
+                  u32x4 (*bnx2)[2]) __attribute__((always_inline)) {
+    load(anx2, bnx2, min(kt + 2, nk - 1));
+    compute(kt & 1, bcur);
+    store(anx1, (kt + 1) & 1);
+    __syncthreads();
+  };
+
+  load(sa0, b0, 0);
+  store(sa0, 0);
+  load(sa1, b1, min(1, nk - 1));
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 3) {
+    step(kt, b0, sa1, sa2, b2);
+    step(kt + 1, b1, sa2, sa0, b0);
+    step(kt + 2, b2, sa0, sa1, b1);
+  }
+  if (kt < nk) {
+    step(kt, b0, sa1, sa2, b2);
+    if (kt + 1 < nk) step(kt + 1, b1, sa2, sa0, b0);
+  }
+
+  if (S > 1) {
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tile = (z * tiles_n + tn) * tiles_m + tm;
+    constexpr int FR = MI * NI * 64;
+    f32x4* mine = reinterpret_cast<f32x4*>(a.part) +
+                  (((int64_t)tile * S + sp) * C::NW + wave) * FR + lane;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) mine[(i * NI + j) * 64] = acc[i][j];
+    return;
+  }
+  float* Cs = (float*)smem;
+  constexpr int CS_LD = BN + 4;
+#pragma unroll
+  for (int h = 0; h < BM / C::TM; ++h) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (i * 16 / C::TM != h) continue;
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Cs[(i * 16 - h * C::TM + fk * 4 + r) * CS_LD + wave * C::WTN + j * 16 + fr] =
+              acc[i][j][r];
+    }
+    __syncthreads();
+    run_epilogue<bf16, C::TM, BN, KIND, C::NT>(e, Cs, m0 + h * C::TM, n0, tn, z, M, N);
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ split-K reduction
 // Second kernel of a split-K GEMM (the units of the first only publish their partials): each
 // workgroup adds, in split order, the S partials of TM rows x BN columns of one output tile and
@@ -637,6 +813,16 @@ static void launch_w8r(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   if (S > 1) launch_reduce<256, BN, 2, 4, KIND>(a, e, batch, s);
 }
 
+template <int MT, int KIND, bool SPLITA>
+static void launch_skinny(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
+  if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, 64) * 128;
+  const int S = a.split > 1 ? a.split : 1;
+  const int units = ceil_div(a.M, MT) * ceil_div(a.N, 128) * S;
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, KIND, SPLITA>), dim3(units, 1, batch), dim3(256), 0,
+                     s, a, e);
+  if (S > 1) launch_reduce<MT, 128, 1, 4, KIND>(a, e, batch, s);
+}
+
 template <int BN, int NS, int KS, int KIND>
 static void launch_w8(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, BN / 2) * BN;
@@ -659,12 +845,18 @@ static void launch_deep(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) 
 
 // 8: 256 x 128 (3 stages), 9: 128 x 256 (3), 10: 128 x 128 (4): four waves, 32-wide k stages;
 // 11: 256 x 256 (2), 12: 256 x 192 (2), 13: 256 x 128 (3): eight waves, 64-wide k stages;
-// 14: 256 x 256, 15: 256 x 192, 16: 256 x 128: eight waves, register-staged two-slot ring.  The bf16-pair A operand doubles the A part
+// 14: 256 x 256, 15: 256 x 192, 16: 256 x 128: eight waves, register-staged two-slot ring;
+// 17: 64 x 128, 18: 32 x 128: the skinny tile for M <= 64 (B straight into registers, bf16 pairs
+// too).  The bf16-pair A operand doubles the A part
 // of a stage and the A fragments: pairs always take the four-wave 128 x 128 tile with 6 stages.
 // The value-cache epilogues (QKV, context K/V) need 128-column tiles.
 template <int KIND, bool SPLITA>
 void launch_deep_cfg(int cfg, GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
-  if constexpr (SPLITA) {
+  if (cfg == 17) {
+    launch_skinny<64, KIND, SPLITA>(a, e, batch, s);
+  } else if (cfg == 18) {
+    launch_skinny<32, KIND, SPLITA>(a, e, batch, s);
+  } else if constexpr (SPLITA) {
     launch_deep<128, 128, 6, KIND, true>(a, e, batch, s);
   } else if constexpr (KIND == EPI_QKV || KIND == EPI_CTXKV) {
     switch (cfg) {

@@ -210,7 +210,7 @@ def test_gemm_validation():
     assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 48, 48, 48, 4, -1, 0, None, 0, None) == -2
     assert L.dbd_gemm_nt(0, fake, fake, fake, 4, 4, 8, 4, 8, 4, -1, 0, None, 0, None) == -2
     assert L.dbd_gemm_nt(3, fake, fake, fake, 4, 4, 8, 8, 8, 4, -1, 0, None, 0, None) == -1
-    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 17, 0, None, 0, None) == -1
+    assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 19, 0, None, 0, None) == -1
     for bad in (17, -1):
         assert L.dbd_gemm_nt(1, fake, fake, fake, 4, 4, 64, 64, 64, 4, 8, bad, None, 0, None) == -1
         with pytest.raises(dbd.DbdError):
@@ -240,7 +240,7 @@ def test_gemm_split_plan_fits_workspace():
     """Split-K partials are sized by the same plan the launch uses: for every deep tile the
     workspace holds one fp32 tile per (output tile, split)."""
     for M, N, K in [(512, 4096, 4096), (512, 4096, 12288), (128, 2048, 4096), (16, 6144, 4096)]:
-        for cfg in range(8, 17):
+        for cfg in range(8, 19):
             b = dbd.gemm_workspace_bytes(dbd.DBD_BF16, M, N, K, cfg)
             assert b % 4 == 0
             if b:
@@ -250,7 +250,7 @@ def test_gemm_split_plan_fits_workspace():
 def test_gemm_override_validation():
     L = dbd.lib()
     assert L.dbd_gemm_override(5, -1, 0) == -1          # attention is not a GEMM stage
-    assert L.dbd_gemm_override(4, 17, 0) == -1
+    assert L.dbd_gemm_override(4, 19, 0) == -1
     assert L.dbd_gemm_override(4, 10, 17) == -1
     # an override changes the planned split partials, and -1 / 0 restore the default
     sh = synth.workload("qwen3-8b").shape

@@ -29,7 +29,7 @@ def test_gemm_nt(dtype, M, N, K):
     assert rel_l2(C.cpu().numpy(), ref) < 1e-5
 
 
-@pytest.mark.parametrize("cfg", list(range(17)))
+@pytest.mark.parametrize("cfg", list(range(19)))
 @pytest.mark.parametrize("M,N,K", [(200, 300, 192), (512, 640, 4096), (235, 1000, 2560),
                                    (16, 384, 4096)])
 def test_gemm_nt_tile_configs(cfg, M, N, K):
@@ -52,7 +52,7 @@ def test_gemm_nt_tile_configs(cfg, M, N, K):
     assert torch.equal(C1, C2)
 
 
-@pytest.mark.parametrize("cfg", list(range(8, 17)))
+@pytest.mark.parametrize("cfg", list(range(8, 19)))
 @pytest.mark.parametrize("split", [2, 3, 5, 16])
 @pytest.mark.parametrize("M,N,K", [(235, 1000, 2560), (512, 640, 4096)])
 def test_gemm_nt_requested_split(cfg, split, M, N, K):
