@@ -330,12 +330,11 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
     const int n = gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N;
     return ceil_div(M, kCfgBM[c]) * ceil_div(n, kCfgBN[c]) * batch;
   };
-  // M <= 64 rows: the skinny tiles, which read every weight element once, where they measured
-  // faster on the SpecDiff-2-shaped drafter (M = 32 and 64 rows): gate/up and the LM head, and
-  // the residual projections at M <= 32; Q/K/V keeps the deep tile with split-K
-  if (M <= 64 && (kind == EPI_SWIGLU || kind == EPI_ARGMAX || kind == EPI_STORE_F32 ||
-                  (kind == EPI_RESID && M <= 32)))
-    return M <= 32 ? 18 : 17;
+  // M <= 64 rows: the skinny tiles, which read every weight element once (measured on the
+  // SpecDiff-2-shaped drafter at 32 and 64 rows, faster than every other tile for each
+  // projection); 32-row tiles for Q/K/V even at 64 rows
+  if (M <= 32 || (M <= 64 && (kind == EPI_QKV || kind == EPI_CTXKV))) return 18;
+  if (M <= 64) return 17;
   if (M >= 64 && (pair || kind == EPI_QKV || kind == EPI_CTXKV)) return 10;
   if (!pair && kind != EPI_QKV && kind != EPI_CTXKV && M >= 128) {
     // the register-staged forms of the 256 x 256 and 256 x 192 tiles (14, 15)
@@ -401,12 +400,13 @@ static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gate
                               bool pair) {
   const int base = choose_cfg(kind, M, N, K, batch, gateup, F, pair);
   if (is_skinny(base)) {
-    // split K (powers of two, each unit keeping at least two 64-wide k stages) until there are
-    // about 512 units: weight streaming wants every CU busy with several workgroups
+    // split K in powers of two while there are fewer than 1024 units and each unit keeps at
+    // least 7 k stages of 64 (measured at 32 and 64 rows: Q/K/V and O best at 8, down at 16,
+    // gate/up at 4)
     const int nv = gateup ? ceil_div(F, 64) * 128 : N;
-    const int tiles = ceil_div(nv, 128) * batch;
+    const int tiles = ceil_div(M, kCfgBM[base]) * ceil_div(nv, 128) * batch;
     int S = 1;
-    while (S < 16 && tiles * S < 512 && K / 64 / (2 * S) >= 2) S *= 2;
+    while (S < 16 && tiles * S < 1024 && K / 64 / (2 * S) >= 7) S *= 2;
     return {base, S};
   }
   if (gateup || (base != 3 && base != 10)) return {base, 1};

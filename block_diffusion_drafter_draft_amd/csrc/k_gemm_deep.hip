@@ -562,17 +562,20 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
 // ------------------------------------------------------------------ skinny: M <= 64 rows
 // For a handful of rows (a small block, few sequences) the projections stream their weights:
 // one row tile covers all M rows (MT = 32 or 64), so every weight element is read exactly once.
-// Block tile MT x 128, four waves in a 1 x 4 grid, each wave all MT rows and 32 columns.  No two
-// waves share a B fragment, so B goes straight from memory into VGPRs (the MFMA fragment layout,
-// 8 consecutive k of one column per lane), two 64-wide k stages ahead in three register sets;
-// A (and its low bf16 part with SPLITA) is staged global -> VGPRs -> a two-slot LDS ring.
-// Split-K gives every CU work: units = column tiles x S.
+// Block tile MT x 128, four waves in a 1 x 4 grid, each wave all MT rows and 32 columns.  Each
+// wave loads its own 32 weight rows as whole 128-byte lines (eight lanes a line) into registers,
+// two 64-wide k stages ahead in three register sets, and stages them through its own region of
+// the two-slot LDS ring, from which it reads its MFMA fragments; A (and its low bf16 part with
+// SPLITA) shares the ring.  Loading B fragments straight into registers instead (each load
+// instruction then touches 16 half lines) streamed 8 % slower at 32 rows.  Split-K gives every
+// CU work: units = column tiles x S.
 template <int MT, bool SPLITA>
 struct SkinnyCfg {
   static constexpr int BM = MT, BN = 128, KS = 64, NT = 256, NW = 4, ROWB = 128;
   static constexpr int NA = SPLITA ? 2 : 1;
   static constexpr int ABYTES = BM * ROWB;                  // one A part of a stage
-  static constexpr int STAGE = NA * ABYTES;
+  static constexpr int BBYTES = BN * ROWB;                  // 4 waves x 32 rows of B
+  static constexpr int STAGE = NA * ABYTES + BBYTES;
   static constexpr int CH = (ABYTES + 16 * NT - 1) / (16 * NT);   // A chunks per thread
   static constexpr int WTN = BN / NW, MI = BM / 16, NI = WTN / 16;
   static constexpr int TM = MT > 32 ? 32 : MT;              // epilogue rows per pass
@@ -612,22 +615,26 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e)
     a2src[q] = SPLITA ? (const bf16*)a.A2 + off : asrc[q];
     adst[q] = (uint32_t)(min(row, BM - 1) * C::ROWB + ((ch ^ swz(row)) * 16));
   }
-  // B: lane (fr, fk) of column tile j holds column n0 + 32 wave + 16 j + fr, k = 32 s + 8 fk
+  // B: each wave's 32 weight rows (columns of C) as whole 128-byte lines, eight lanes a line: lane
+  // l of load q is row 32 wave + 8 q + l / 8, chunk l % 8, stored in the wave's LDS region at
+  // slot (l % 8) ^ swz(row); the fragments are read back like A's
   const int fr = lane & 15, fk = lane >> 4;
   const BMap bm = make_bmap(a);
-  const bf16* bsrc[NI];
+  const bf16* bsrc[4];
+  uint32_t bdst[4];
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
-    bsrc[j] = brow_ptr<bf16, BN>(bm, min(n0 + wave * C::WTN + 16 * j + fr, N - 1), z) +
-              (int64_t)kb * KS + 8 * fk;
-
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * q + (lane >> 3), ch = lane & 7;
+    bsrc[q] = brow_ptr<bf16, BN>(bm, min(n0 + wave * C::WTN + row, N - 1), z) +
+              (int64_t)kb * KS + ch * 8;
+    bdst[q] = (uint32_t)(C::NA * C::ABYTES + wave * C::WTN * C::ROWB + row * C::ROWB +
+                         ((ch ^ swz(row)) * 16));
+  }
   u32x4 sa0[C::CH][2], sa1[C::CH][2], sa2[C::CH][2];
   u32x4 b0[NI][2], b1[NI][2], b2[NI][2];
   auto load = [&](u32x4 (*sa)[2], u32x4 (*bq)[2], int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) bq[j][s2] = load_global16(bsrc[j] + kt * KS + 32 * s2);
+    for (int q = 0; q < 4; ++q) bq[q / 2][q % 2] = load_global16(bsrc[q] + kt * KS);
 #pragma unroll
     for (int q = 0; q < C::CH; ++q) {
       if (!aok[q]) continue;
@@ -635,8 +642,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e)
       if constexpr (SPLITA) sa[q][1] = load_global16(a2src[q] + kt * KS);
     }
   };
-  auto store = [&](u32x4 (*sa)[2], int slot) __attribute__((always_inline)) {
+  auto store = [&](u32x4 (*sa)[2], u32x4 (*bq)[2], int slot) __attribute__((always_inline)) {
     char* base = smem + slot * C::STAGE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(base + bdst[q]) = bq[q / 2][q % 2];
 #pragma unroll
     for (int q = 0; q < C::CH; ++q) {
       if (!aok[q]) continue;
@@ -654,24 +663,29 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e)
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int slot, u32x4 (*bq)[2]) __attribute__((always_inline)) {
+  auto compute = [&](int slot) __attribute__((always_inline)) {
     const char* st = smem + slot * C::STAGE;
+    const char* sb = st + C::NA * C::ABYTES + wave * C::WTN * C::ROWB;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 bq[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        bq[j] = *reinterpret_cast<const bf16x8*>(sb + rd[s2] + j * 16 * C::ROWB);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const bf16x8 fa = *reinterpret_cast<const bf16x8*>(st + rd[s2] + i * 16 * C::ROWB);
 #pragma unroll
         for (int j = 0; j < NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              fa, *reinterpret_cast<const bf16x8*>(&bq[j][s2]), acc[i][j], 0, 0, 0);
+              fa, bq[j], acc[i][j], 0, 0, 0);
         if constexpr (SPLITA) {
           const bf16x8 fa2 =
               *reinterpret_cast<const bf16x8*>(st + C::ABYTES + rd[s2] + i * 16 * C::ROWB);
 #pragma unroll
           for (int j = 0; j < NI; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                fa2, *reinterpret_cast<const bf16x8*>(&bq[j][s2]), acc[i][j], 0, 0, 0);
+                fa2, bq[j], acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -680,27 +694,27 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e)
   // B of stage kt + 1, `nx2` free: stage kt + 2 is loaded into it, stage kt computed, A of stage
   // kt + 1 stored into the other slot (last read in stage kt - 1, before the barrier ending it).
   // Loads past the last stage reload the last one.
-  auto step = [&](int kt, u32x4 (*bcur)[2], u32x4 (*anx1)[2], u32x4 (*anx2)[2],
+  auto step = [&](int kt, u32x4 (*anx1)[2], u32x4 (*bnx1)[2], u32x4 (*anx2)[2],
                   u32x4 (*bnx2)[2]) __attribute__((always_inline)) {
     load(anx2, bnx2, min(kt + 2, nk - 1));
-    compute(kt & 1, bcur);
-    store(anx1, (kt + 1) & 1);
+    compute(kt & 1);
+    store(anx1, bnx1, (kt + 1) & 1);
     __syncthreads();
   };
 
   load(sa0, b0, 0);
-  store(sa0, 0);
+  store(sa0, b0, 0);
   load(sa1, b1, min(1, nk - 1));
   __syncthreads();
   int kt = 0;
   for (; kt + 2 < nk; kt += 3) {
-    step(kt, b0, sa1, sa2, b2);
-    step(kt + 1, b1, sa2, sa0, b0);
-    step(kt + 2, b2, sa0, sa1, b1);
+    step(kt, sa1, b1, sa2, b2);
+    step(kt + 1, sa2, b2, sa0, b0);
+    step(kt + 2, sa0, b0, sa1, b1);
   }
   if (kt < nk) {
-    step(kt, b0, sa1, sa2, b2);
-    if (kt + 1 < nk) step(kt + 1, b1, sa2, sa0, b0);
+    step(kt, sa1, b1, sa2, b2);
+    if (kt + 1 < nk) step(kt + 1, sa2, b2, sa0, b0);
   }
 
   if (S > 1) {

@@ -329,7 +329,7 @@ int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int
  * 13: 256x128/3) which splits K over several workgroups when `workspace` is given (NULL: no
  * split); 14-16 the 8-wave tiles 256x256, 256x192, 256x128 staged through registers instead of
  * global->LDS DMA; 17, 18 the skinny tiles 64x128, 32x128 for M <= 64 (every weight element
- * read once, B straight into registers) (14-18: same split rule; Q/K/V and context K/V take
+ * read once) (14-18: same split rule; Q/K/V and context K/V take
  * 256x128 for 14-16); -1: the library's choice.  split (deep-ring tiles with a
  * workspace only; in [0, 16]): 0 the library's choice, 1 no split, S > 1 K split over S
  * workgroups per output tile whose fp32 partials a second kernel adds, in split order, with
