@@ -81,20 +81,26 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   const int kr0 = 8 * (i16 >> 2) + (i16 & 3);
   const int kr1 = kr0 + 4;
 
+  // A 64-key chunk of K ([cap][HD]) and of V ([cap/8][HD][8]) is one contiguous run of
+  // KCH * HD * 2 bytes starting c0 * HD * 2 bytes into the (n, g) region, and chunk starts are
+  // multiples of 64 inside a capacity that is a multiple of 64: 16-byte piece idx of a chunk
+  // sits idx * 16 bytes in.  Buffer loads take that as one per-thread offset plus a uniform
+  // one, so staging needs no per-load 64-bit addresses.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(Kg), (short)0, a.cap * HD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(Vg), (short)0, a.cap * HD * 2, 0x00020000);
   u32x4 kreg[KI], vreg[VI];
   auto load_chunk = [&](int c0) {
+    const int base = c0 * HD * 2;
 #pragma unroll
-    for (int j = 0; j < KI; ++j) {
-      const int idx = tid + j * NT, row = idx / KC, c = idx % KC;
-      if (KT % NT == 0 || idx < KT)
-        kreg[j] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)(c0 + row) * HD + c * 8);
-    }
+    for (int j = 0; j < KI; ++j)
+      if (KT % NT == 0 || tid + j * NT < KT)
+        kreg[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, base + j * NT * 16, 0);
 #pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const int idx = tid + j * NT, c = idx / HD, d = idx % HD;    // lanes: consecutive d
-      if (VT % NT == 0 || idx < VT)
-        vreg[j] = *reinterpret_cast<const u32x4*>(Vg + ((int64_t)(c0 / 8 + c) * HD + d) * 8);
-    }
+    for (int j = 0; j < VI; ++j)
+      if (VT % NT == 0 || tid + j * NT < VT)
+        vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, base + j * NT * 16, 0);
   };
   auto store_chunk = [&](int c0) {
 #pragma unroll
