@@ -1,5 +1,6 @@
 // C ABI of libdbd.so: argument validation (host, before any launch), workspace carving and the
 // launch sequence of draft_block, verify_greedy and select_streak.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -83,7 +84,25 @@ struct Carver {
 
 int elem_size(int dtype) { return dtype == DBD_BF16 ? 2 : 4; }
 
-int attn_split(int dtype) { return dtype == DBD_BF16 ? 512 : 256; }
+// Keys per attention split: the largest of 512 (256 for the fp32 kernel, which gives each key
+// of a split its own thread), 256, 128 and 64 that still gives the launch at least 512
+// workgroups over the capacity.  Short contexts and small batches are then spread over many
+// workgroups instead of a few that walk every chunk of their keys in turn.
+int attn_split(int dtype, int cap, int kvh, int batch) {
+  int s = dtype == DBD_BF16 ? 512 : 256;
+  while (s > 64 && (int64_t)ceil_div(cap, s) * kvh * batch < 512) s /= 2;
+  return s;
+}
+
+// (sequence, split) pairs of attention partials to reserve for up to `batch` sequences.  The
+// split shrinks with the batch, so the largest batch does not always need the most pairs; the
+// maximum over 1 .. batch keeps a workspace sized for a batch enough for every smaller one.
+static int64_t attn_partial_pairs(int dtype, int cap, int kvh, int batch) {
+  int64_t m = 0;
+  for (int n = 1; n <= batch; ++n)
+    m = std::max(m, (int64_t)n * ceil_div(cap, attn_split(dtype, cap, kvh, n)));
+  return m;
+}
 
 // Per-stage GEMM tile / split overrides (dbd_gemm_override), indexed by DBD_STAGE_*: -1 / 0 =
 // the library's choice.
@@ -121,8 +140,56 @@ struct DraftBufs {
   size_t gemm_part_bytes;
 };
 
+// Split-K partial bytes of one step's GEMMs with n sequences of block length B (the block
+// projections and the LM head) and t ingested rows (the context K/V projection and the fully
+// connected fusion; t = 0: none), kept apart because they depend on different sizes.  *lm_bn is
+// the LM head tile's width.
+static void step_gemm_parts(const dbd_model_desc& d, int n, int B, int n_anchor, int t,
+                            float temperature, size_t* block_part, size_t* ingest_part,
+                            int* lm_bn) {
+  const bool pr = d.dtype == DBD_BF16 && d.act_pairs;
+  const int kd = d.n_kv_heads * d.head_dim, qd = d.n_q_heads * d.head_dim;
+  const int M = n * B, Md = n * (B - n_anchor);
+  auto need = [](const GemmPlan& p) { return p.split > 1 ? p.part_bytes : (size_t)0; };
+  size_t bp = 0, ip = 0;
+  if (n > 0) {
+    const GemmPlan pl[5] = {
+        plan_gemm(d.dtype, EPI_QKV, g_ov_cfg[DBD_STAGE_GEMM_QKV], M, qd + 2 * kd, d.hidden, 1,
+                  0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_QKV]),
+        plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_O], M, d.hidden, qd, 1, 0, 0, pr,
+                  true, g_ov_split[DBD_STAGE_GEMM_O]),
+        plan_gemm(d.dtype, EPI_SWIGLU, g_ov_cfg[DBD_STAGE_GEMM_GATEUP], M, 2 * d.ffn, d.hidden,
+                  1, 1, d.ffn, pr, true, g_ov_split[DBD_STAGE_GEMM_GATEUP]),
+        plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_DOWN], M, d.hidden, d.ffn, 1, 0, 0,
+                  pr, true, g_ov_split[DBD_STAGE_GEMM_DOWN]),
+        plan_gemm(d.dtype, temperature > 0.f ? EPI_STORE_F32 : EPI_ARGMAX,
+                  g_ov_cfg[DBD_STAGE_GEMM_LMHEAD], Md, d.vocab, d.hidden, 1, 0, 0, pr, true,
+                  g_ov_split[DBD_STAGE_GEMM_LMHEAD])};
+    for (const GemmPlan& p : pl) bp = std::max(bp, need(p));
+    if (lm_bn) *lm_bn = pl[4].bn;
+  }
+  if (d.n_target_layers > 0 && t > 0) {
+    ip = need(plan_gemm(d.dtype, EPI_CTXKV, g_ov_cfg[DBD_STAGE_GEMM_CTXKV], t, 2 * kd, d.hidden,
+                        d.n_layers, 0, 0, d.dtype == DBD_BF16, true,
+                        g_ov_split[DBD_STAGE_GEMM_CTXKV]));
+    if (d.ctx_fusion)
+      ip = std::max(ip, need(plan_gemm(d.dtype, EPI_STORE_F32, -1, t, d.hidden,
+                                       d.n_target_layers * d.hidden, 1, 0, 0, false, true)));
+  }
+  *block_part = bp;
+  *ingest_part = ip;
+}
+
+// Rows of ingest up to which the workspace query takes the split-K need at every row count (the
+// planner splits K only while a problem has too few tiles to fill the chip, far below this).
+constexpr int kExactIngestRows = 4096;
+
+// Workspace layout of one draft_block call; returns its size.  With at_most, the split-partial
+// regions (attention and split-K) take their largest size over every batch 1 .. N and every
+// ingest 1 .. T (exactly up to kExactIngestRows rows, and at T): both depend on the sizes
+// through the tile and split choices and are not monotone, while every other buffer is.
 size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, int K,
-                   float temperature, int cap, char* base, DraftBufs* b) {
+                   float temperature, int cap, char* base, DraftBufs* b, bool at_most) {
   Carver c{base};
   DraftBufs t{};
   const int es = elem_size(d.dtype);
@@ -157,40 +224,33 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
     t.attn_lo = c.take<char>(M * qd * es);
     t.act_lo = c.take<char>(M * d.ffn * es);
   }
-  t.split = attn_split(d.dtype);
+  t.split = attn_split(d.dtype, cap, d.n_kv_heads, N);
   t.s_max = ceil_div(cap, t.split);
-  t.part_o = c.take<float>((int64_t)N * d.n_kv_heads * t.s_max * R * d.head_dim);
-  t.part_ml = c.take<float2>((int64_t)N * d.n_kv_heads * t.s_max * R);
+  const int64_t pairs = at_most ? attn_partial_pairs(d.dtype, cap, d.n_kv_heads, N)
+                                : (int64_t)N * t.s_max;
+  t.part_o = c.take<float>(pairs * d.n_kv_heads * R * d.head_dim);
+  t.part_ml = c.take<float2>(pairs * d.n_kv_heads * R);
   // split-K partials: the largest need over the step's GEMMs
   {
-    const bool pr = d.dtype == DBD_BF16 && d.act_pairs;
-    const int kd = d.n_kv_heads * d.head_dim;
-    GemmPlan pl[7];
-    int np = 0;
-    pl[np++] = plan_gemm(d.dtype, EPI_QKV, g_ov_cfg[DBD_STAGE_GEMM_QKV], (int)M, qd + 2 * kd,
-                         d.hidden, 1, 0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_QKV]);
-    pl[np++] = plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_O], (int)M, d.hidden, qd, 1,
-                         0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_O]);
-    pl[np++] = plan_gemm(d.dtype, EPI_SWIGLU, g_ov_cfg[DBD_STAGE_GEMM_GATEUP], (int)M, 2 * d.ffn,
-                         d.hidden, 1, 1, d.ffn, pr, true, g_ov_split[DBD_STAGE_GEMM_GATEUP]);
-    pl[np++] = plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_DOWN], (int)M, d.hidden, d.ffn,
-                         1, 0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_DOWN]);
-    pl[np++] = plan_gemm(d.dtype, temperature > 0.f ? EPI_STORE_F32 : EPI_ARGMAX,
-                         g_ov_cfg[DBD_STAGE_GEMM_LMHEAD], (int)Md, d.vocab, d.hidden, 1, 0, 0,
-                         pr, true, g_ov_split[DBD_STAGE_GEMM_LMHEAD]);
-    if (d.n_target_layers > 0 && T > 0)
-      pl[np++] = plan_gemm(d.dtype, EPI_CTXKV, g_ov_cfg[DBD_STAGE_GEMM_CTXKV], T, 2 * kd,
-                           d.hidden, d.n_layers, 0, 0, d.dtype == DBD_BF16, true,
-                           g_ov_split[DBD_STAGE_GEMM_CTXKV]);
-    if (d.n_target_layers > 0 && T > 0 && d.ctx_fusion)
-      pl[np++] = plan_gemm(d.dtype, EPI_STORE_F32, -1, T, d.hidden, d.n_target_layers * d.hidden,
-                           1, 0, 0, false, true);
-    size_t part = 0;
-    for (int i = 0; i < np; ++i)
-      if (pl[i].split > 1) part = part > pl[i].part_bytes ? part : pl[i].part_bytes;
+    size_t bp = 0, ip = 0;
+    int lm_bn = 128;
+    step_gemm_parts(d, N, B, n_anchor, T, temperature, &bp, &ip, &lm_bn);
+    t.ntiles = ceil_div(d.vocab, lm_bn);
+    if (at_most) {
+      for (int n = 1; n < N; ++n) {
+        size_t x, y;
+        step_gemm_parts(d, n, B, n_anchor, 0, temperature, &x, &y, nullptr);
+        bp = std::max(bp, x);
+      }
+      for (int r = 1; r < T && r <= kExactIngestRows; ++r) {
+        size_t x, y;
+        step_gemm_parts(d, 0, B, n_anchor, r, temperature, &x, &y, nullptr);
+        ip = std::max(ip, y);
+      }
+    }
+    const size_t part = std::max(bp, ip);
     t.gemm_part = part ? (float*)c.take<char>((int64_t)part) : nullptr;
     t.gemm_part_bytes = part;
-    t.ntiles = ceil_div(d.vocab, pl[4].bn);
   }
   const int64_t max_tiles = ceil_div(d.vocab, 128);          // any configuration fits
   t.lm_pv = c.take<float>(Md * max_tiles);
@@ -336,7 +396,7 @@ int dbd_draft_workspace_bytes(const dbd_model_desc* desc, int32_t max_batch, int
                              temperature, ctx_capacity);
   if (rc) return rc;
   *bytes = carve_draft(*desc, max_batch, block_len, n_anchor, max_new_tokens, n_drafts,
-                       temperature, ctx_capacity, nullptr, nullptr);
+                       temperature, ctx_capacity, nullptr, nullptr, true);
   return DBD_OK;
 }
 
@@ -383,12 +443,12 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   if (!workspace || ((uintptr_t)workspace % kAlign))
     return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
   const size_t need = carve_draft(d, batch, block_len, n_anchor, n_new_total, n_drafts,
-                                  temperature, ctx_capacity, nullptr, nullptr);
+                                  temperature, ctx_capacity, nullptr, nullptr, false);
   if (workspace_bytes < need)
     return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
   DraftBufs b;
   carve_draft(d, batch, block_len, n_anchor, n_new_total, n_drafts, temperature, ctx_capacity,
-              (char*)workspace, &b);
+              (char*)workspace, &b, false);
   hipStream_t st = (hipStream_t)stream;
 
   const int N = batch, B = block_len, T = n_new_total;

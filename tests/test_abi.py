@@ -102,6 +102,27 @@ def test_workspace_query_is_positive_and_monotone():
     assert a % 256 == 0
 
 
+@pytest.mark.parametrize("name,cap,new", [("qwen3-8b", 3136, 256), ("qwen3-8b", 1024, 64),
+                                          ("specdiff2-7b", 320, 0), ("tiny-fp32", 448, 40)])
+def test_workspace_for_a_batch_covers_every_smaller_batch(name, cap, new):
+    """The query sizes a workspace for at most `max_batch` sequences: the split-K tiles and
+    splits and the attention split change with the number of rows, so a smaller batch can need
+    more split partials (3 or 4 sequences of 16 rows take the skinny split-K tiles); the query
+    for a batch must still cover every smaller one."""
+    d = _desc(name)
+    sizes = [_ws(d, batch=b, ctx_capacity=cap, block_len=16, n_anchor=1, max_new_tokens=new)
+             for b in range(1, 41)]
+    assert all(x <= y for x, y in zip(sizes, sizes[1:])), sizes
+
+
+def test_workspace_for_an_ingest_covers_every_smaller_one():
+    """Likewise for at most `max_new_tokens` ingested rows (the context K/V projection takes
+    split-K tiles at a few dozen rows)."""
+    d = _desc("qwen3-8b")
+    sizes = [_ws(d, batch=2, max_new_tokens=t) for t in range(1, 300)]
+    assert all(x <= y for x, y in zip(sizes, sizes[1:]))
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, -2),            # only 64 / 128
     ("n_kv_heads", 5, -2),           # 32 % 5 != 0
