@@ -116,6 +116,13 @@ struct EpiArgs {
   int32_t* part_idx;
   int ntiles;
   float* logits;        // optional [M, N] fp32
+  // EPI_RESID: the RMSNorm of the updated residual rows, norm_out = T(x / rms(x) * norm_g) (and
+  // the low part of the bf16 pair); done in the split-K reduction of the skinny tiles, else
+  // left to the caller (launch_gemm reports which).  norm_g null: no norm.
+  const void* norm_g;
+  void* norm_out;
+  void* norm_out_lo;
+  float norm_eps;
 };
 
 // Attention over the cache: every block row of sequence n, head h, attends to cache positions
@@ -147,8 +154,9 @@ hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int row
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, void* out_lo,
                           int rows, int H, float eps, int block_len, int n_anchor, hipStream_t s);
 // cfg: bf16 block-tile configuration index (see dbd_gemm_nt in dbd.h), -1 = pick for the shape
+// *norm_done (optional) tells whether an EPI_RESID launch with e.norm_g also wrote the norm.
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
-                       hipStream_t s, int cfg = -1, int split = 0);
+                       hipStream_t s, int cfg = -1, int split = 0, bool* norm_done = nullptr);
 // What launch_gemm does for a problem: the tile configuration (-1 on the fp32 path), its column
 // tile width, the split-K factor (1 unless split_ok: a partial buffer and counters are given),
 // the output tiles over the batch and the partial-buffer bytes.  pair = the A operand comes as a

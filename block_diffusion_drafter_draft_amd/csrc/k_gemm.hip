@@ -466,15 +466,22 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
 
 template <int KIND>
 static void launch_kind(int dtype, int cfg, int split, GemmArgs a, const EpiArgs& e, int batch,
-                        hipStream_t s) {
+                        hipStream_t s, bool* norm_done) {
+  if (norm_done) *norm_done = false;
   if (dtype == 1) {
     const int F = a.seg[0].n1 - a.seg[0].n0;
     GemmPlan p = plan_gemm(dtype, KIND, cfg, a.M, a.N, a.K, batch, a.gateup, F,
                            a.A2 != nullptr, a.part != nullptr, split);
     if (p.split > 1 && p.part_bytes > a.part_cap) p.split = 1;
     a.split = p.split;
-    if (a.A2) launch_cfg<KIND, true>(p.cfg, a, e, batch, s);
-    else launch_cfg<KIND, false>(p.cfg, a, e, batch, s);
+    // the residual's norm rides on the skinny tiles' split-K reduction, which sees whole rows
+    const bool fuse = KIND == EPI_RESID && e.norm_g && is_skinny(p.cfg) && p.split > 1 &&
+                      batch == 1 && e.ldc == a.N;
+    EpiArgs ee = e;
+    if (!fuse) ee.norm_g = nullptr;
+    if (a.A2) launch_cfg<KIND, true>(p.cfg, a, ee, batch, s);
+    else launch_cfg<KIND, false>(p.cfg, a, ee, batch, s);
+    if (norm_done) *norm_done = fuse;
   } else {
     if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, FN / 2) * FN;
     dim3 grid(ceil_div(a.N, FN), ceil_div(a.M, FM), batch);
@@ -483,15 +490,17 @@ static void launch_kind(int dtype, int cfg, int split, GemmArgs a, const EpiArgs
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& a, const EpiArgs& e, int batch,
-                       hipStream_t s, int cfg, int split) {
+                       hipStream_t s, int cfg, int split, bool* norm_done) {
+  if (norm_done) *norm_done = false;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  bool* nd = norm_done;
   switch (e.kind) {
-    case EPI_STORE_F32: launch_kind<EPI_STORE_F32>(dtype, cfg, split, a, e, batch, s); break;
-    case EPI_RESID: launch_kind<EPI_RESID>(dtype, cfg, split, a, e, batch, s); break;
-    case EPI_QKV: launch_kind<EPI_QKV>(dtype, cfg, split, a, e, batch, s); break;
-    case EPI_CTXKV: launch_kind<EPI_CTXKV>(dtype, cfg, split, a, e, batch, s); break;
-    case EPI_SWIGLU: launch_kind<EPI_SWIGLU>(dtype, cfg, split, a, e, batch, s); break;
-    case EPI_ARGMAX: launch_kind<EPI_ARGMAX>(dtype, cfg, split, a, e, batch, s); break;
+    case EPI_STORE_F32: launch_kind<EPI_STORE_F32>(dtype, cfg, split, a, e, batch, s, nd); break;
+    case EPI_RESID: launch_kind<EPI_RESID>(dtype, cfg, split, a, e, batch, s, nd); break;
+    case EPI_QKV: launch_kind<EPI_QKV>(dtype, cfg, split, a, e, batch, s, nd); break;
+    case EPI_CTXKV: launch_kind<EPI_CTXKV>(dtype, cfg, split, a, e, batch, s, nd); break;
+    case EPI_SWIGLU: launch_kind<EPI_SWIGLU>(dtype, cfg, split, a, e, batch, s, nd); break;
+    case EPI_ARGMAX: launch_kind<EPI_ARGMAX>(dtype, cfg, split, a, e, batch, s, nd); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -718,6 +718,24 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e)
   }
 
   if (S > 1) {
+    if constexpr (KIND == EPI_RESID) {
+      if (e.norm_g) {
+        // row-major partials [S][M][N] for resid_norm_kernel, which reduces whole rows
+        float* pr = reinterpret_cast<float*>(a.part) + (int64_t)sp * M * N;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int col = n0 + wave * C::WTN + j * 16 + fr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = m0 + i * 16 + fk * 4 + r;
+              if (row < M && col < N) pr[(int64_t)row * N + col] = acc[i][j][r];
+            }
+          }
+        return;
+      }
+    }
     const int tiles_n = (N + BN - 1) / BN;
     const int tile = (z * tiles_n + tn) * tiles_m + tm;
     constexpr int FR = MI * NI * 64;
@@ -811,6 +829,78 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
   run_epilogue<bf16, TM, BN, KIND, R::NT>(e, Cs, m0 + r0, n0, tn, z, M, N);
 }
 
+// Split-K reduction of a skinny residual projection fused with the RMSNorm that follows it: one
+// workgroup per row (a skinny launch has at most 64) adds the row's S row-major partials in
+// split order, adds the sum to the residual as the residual epilogue does, writes the residual
+// and the normalised row T(x / sqrt(mean(x^2) + eps) * g), with the low part of the bf16 pair
+// when norm_out_lo is set.  The loads of RB splits are in flight together.
+template <typename T>
+__global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e) {
+  constexpr int NT = 1024, MAXG = 2, RB = 8;          // rows of up to 8192 columns
+  __shared__ float red[NT / 64];
+  const int row = blockIdx.x, tid = threadIdx.x, N = a.N, S = a.split;
+  const float* part = reinterpret_cast<const float*>(a.part) + (int64_t)row * N;
+  const int64_t ps = (int64_t)a.M * N;                  // one split's partials
+  float* xr = reinterpret_cast<float*>(e.C) + (int64_t)row * N;
+  f32x4 acc[MAXG], xv[MAXG];
+#pragma unroll
+  for (int q = 0; q < MAXG; ++q) {
+    const int i = (tid + q * NT) * 4;
+    if (i < N) {
+      xv[q] = *reinterpret_cast<const f32x4*>(xr + i);
+      acc[q] = *reinterpret_cast<const f32x4*>(part + i);
+    }
+  }
+  for (int s0 = 1; s0 < S; s0 += RB) {
+    f32x4 w[RB][MAXG];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int q = 0; q < MAXG; ++q) {
+        const int i = (tid + q * NT) * 4;
+        if (s0 + b < S && i < N)
+          w[b][q] = *reinterpret_cast<const f32x4*>(part + (s0 + b) * ps + i);
+      }
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int q = 0; q < MAXG; ++q)
+        if (s0 + b < S) acc[q] += w[b][q];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < MAXG; ++q) {
+    const int i = (tid + q * NT) * 4;
+    if (i < N) {
+      xv[q] += acc[q];
+      *reinterpret_cast<f32x4*>(xr + i) = xv[q];
+      ss += xv[q][0] * xv[q][0] + xv[q][1] * xv[q][1] + xv[q][2] * xv[q][2] + xv[q][3] * xv[q][3];
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) tot += red[w];
+  const float inv = rsqrtf(tot / (float)N + e.norm_eps);
+  const T* g = reinterpret_cast<const T*>(e.norm_g);
+  T* o = reinterpret_cast<T*>(e.norm_out) + (int64_t)row * N;
+  T* ol = e.norm_out_lo ? reinterpret_cast<T*>(e.norm_out_lo) + (int64_t)row * N : nullptr;
+#pragma unroll
+  for (int q = 0; q < MAXG; ++q) {
+    const int i = (tid + q * NT) * 4;
+    if (i >= N) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float y = xv[q][c] * inv * to_f(g[i + c]);
+      const T hi = from_f<T>(y);
+      o[i + c] = hi;
+      if (ol) ol[i + c] = from_f<T>(y - to_f(hi));
+    }
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int KIND>
 static void launch_reduce(const GemmArgs& a, const EpiArgs& e, int batch, hipStream_t s) {
   const int grid = ceil_div(a.M, BM) * ceil_div(a.N, BN) * (BM / ReduceCfg<BN>::TM);
@@ -834,7 +924,10 @@ static void launch_skinny(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s
   const int units = ceil_div(a.M, MT) * ceil_div(a.N, 128) * S;
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, KIND, SPLITA>), dim3(units, 1, batch), dim3(256), 0,
                      s, a, e);
-  if (S > 1) launch_reduce<MT, 128, 1, 4, KIND>(a, e, batch, s);
+  if (S > 1 && KIND == EPI_RESID && e.norm_g)
+    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(a.M), dim3(1024), 0, s, a, e);
+  else if (S > 1)
+    launch_reduce<MT, 128, 1, 4, KIND>(a, e, batch, s);
 }
 
 template <int BN, int NS, int KS, int KIND>

@@ -140,6 +140,14 @@ struct DraftBufs {
   size_t gemm_part_bytes;
 };
 
+// Asks a residual projection for the RMSNorm of its updated rows (see EpiArgs).
+static void set_norm(EpiArgs* e, const void* g, void* out, void* out_lo, float eps) {
+  e->norm_g = g;
+  e->norm_out = out;
+  e->norm_out_lo = out_lo;
+  e->norm_eps = eps;
+}
+
 // Split-K partial bytes of one step's GEMMs with n sequences of block length B (the block
 // projections and the LM head) and t ingested rows (the context K/V projection and the fully
 // connected fusion; t = 0: none), kept apart because they depend on different sizes.  *lm_bn is
@@ -533,12 +541,15 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   // 2. block forward
   HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_embed(d.dtype, block_tokens, w->embed, M, H, V, b.x, st));
   const char* cw = nullptr;
+  bool normed = false;        // the previous down projection already wrote this layer's norm
   for (int l = 0; l < d.n_layers; ++l) {
     auto lw = [&](const void* p, int64_t per_layer) {
       return (const void*)((const char*)p + (int64_t)l * per_layer * es);
     };
-    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->attn_norm_w, H), b.xn, b.xn_lo, M, H,
-                                                     d.rms_eps, B, 0, st));
+    if (!normed)
+      HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->attn_norm_w, H), b.xn,
+                                                       b.xn_lo, M, H, d.rms_eps, B, 0, st));
+    normed = false;
     {
       GemmArgs g{};
       g.part = b.gemm_part;
@@ -610,11 +621,14 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.kind = EPI_RESID;
       e.C = b.x;
       e.ldc = H;
+      set_norm(&e, lw(w->mlp_norm_w, H), b.xn, b.xn_lo, d.rms_eps);
       HIP_STAGE(DBD_STAGE_GEMM_O, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_O],
-                                                  g_ov_split[DBD_STAGE_GEMM_O]));
+                                                  g_ov_split[DBD_STAGE_GEMM_O], &normed));
     }
-    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->mlp_norm_w, H), b.xn, b.xn_lo, M, H,
-                                                     d.rms_eps, B, 0, st));
+    if (!normed)
+      HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, lw(w->mlp_norm_w, H), b.xn,
+                                                       b.xn_lo, M, H, d.rms_eps, B, 0, st));
+    normed = false;
     {
       GemmArgs g{};
       g.part = b.gemm_part;
@@ -655,8 +669,13 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.kind = EPI_RESID;
       e.C = b.x;
       e.ldc = H;
+      // the next layer's attention norm (the final norm after the last layer takes only the
+      // mask rows and stays separate)
+      if (l + 1 < d.n_layers)
+        set_norm(&e, (const char*)w->attn_norm_w + (int64_t)(l + 1) * H * es, b.xn, b.xn_lo,
+                 d.rms_eps);
       HIP_STAGE(DBD_STAGE_GEMM_DOWN, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_DOWN],
-                                                  g_ov_split[DBD_STAGE_GEMM_DOWN]));
+                                                  g_ov_split[DBD_STAGE_GEMM_DOWN], &normed));
     }
   }
   (void)cw;

@@ -223,6 +223,41 @@ def test_query_groups_beyond_one_workgroup_match_oracle():
     _compare(case, logits, range(wl.batch), [])
 
 
+@pytest.mark.parametrize("pairs", [0, 1])
+def test_small_block_fused_residual_norm_matches_oracle(pairs):
+    """32 block rows with K large enough that the O and down projections take the skinny tiles
+    with a split K (O split 2, down split 4): their split reduction also writes the next RMSNorm
+    (the MLP norm, the next layer's attention norm) and no separate norm runs; the last layer's
+    down projection leaves the final norm to its own kernel.  With bf16 activation pairs the
+    fused reduction writes the low parts too."""
+    sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
+                            n_layers=3, n_target_layers=2, vocab=2048, dtype="bf16")
+    wl = synth.Workload(name="fused-norm", shape=sh, batch=2, block_len=16, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=60, ctx_hi=140, ctx_source="hidden",
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=8,
+                        act_pairs=pairs)
+    print(f"draft_block workload=fused-norm pairs={pairs}", flush=True)
+    case = Case(wl, dev=DEV)
+    case.fill_cache()
+    drafts, logits, status = case.step()
+    torch.cuda.synchronize()
+    assert torch.all(status == 0)
+    _check_drafts_property(case, drafts, logits)
+    _compare(case, logits, range(wl.batch), [])
+    # the row-norm stage keeps the embedding, the first layer's attention norm and the final norm
+    dbd.timing_reset()
+    dbd.timing_enable(True)
+    try:
+        _, logits2, _ = case.step()
+        torch.cuda.synchronize()
+        launches = dbd.timing_read()["rownorm"][1]
+    finally:
+        dbd.timing_enable(False)
+        dbd.timing_reset()
+    assert launches == 3, launches
+    assert torch.equal(logits, logits2)
+
+
 def test_sixty_four_mask_block_without_anchor():
     """block_len 64 (the interface's maximum), all masks, context from a given cache, 7 query
     heads per kv head: 448 query rows per kv head over two attention row blocks."""
