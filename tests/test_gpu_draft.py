@@ -258,6 +258,24 @@ def test_small_block_fused_residual_norm_matches_oracle(pairs):
     assert torch.equal(logits, logits2)
 
 
+def test_long_context_single_sequence_many_splits():
+    """One sequence over a 716-position cache: the launch is small, so attention takes 64-key
+    splits (12 of them) and the combine kernel merges more than eight splits per row (its
+    second, looped path)."""
+    sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1024,
+                            n_layers=2, n_target_layers=0, vocab=2048, dtype="bf16")
+    wl = synth.Workload(name="long-ctx", shape=sh, batch=1, block_len=16, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=700, ctx_hi=700, ctx_source="cache",
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=0)
+    print("draft_block workload=long-ctx", flush=True)
+    case = Case(wl, dev=DEV)
+    drafts, logits, status = case.step()
+    torch.cuda.synchronize()
+    assert torch.all(status == 0)
+    _check_drafts_property(case, drafts, logits)
+    _compare(case, logits, range(wl.batch), [])
+
+
 def test_sixty_four_mask_block_without_anchor():
     """block_len 64 (the interface's maximum), all masks, context from a given cache, 7 query
     heads per kv head: 448 query rows per kv head over two attention row blocks."""
