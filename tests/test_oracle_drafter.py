@@ -107,6 +107,47 @@ def test_rope_relative_position_property():
         assert abs(np.linalg.norm(od.rope(q, [p1], 1e6)) - np.linalg.norm(q)) < 1e-12
 
 
+def _rope_by_hand(x, p, inv_freq):
+    """Rotate-half written out element by element: dimension i (i < hd/2) is paired with
+    i + hd/2, and the pair turns by the angle p * inv_freq[i]."""
+    hd = len(x)
+    half = hd // 2
+    y = [0.0] * hd
+    for i in range(half):
+        a = p * inv_freq[i]
+        y[i] = x[i] * math.cos(a) - x[i + half] * math.sin(a)
+        y[i + half] = x[i + half] * math.cos(a) + x[i] * math.sin(a)
+    return np.array(y)
+
+
+def test_rope_frequency_schedule_and_pairing_by_hand():
+    """Theta = 1e6: with head_dim 4 the two pair frequencies are 1 and 1e6^(-1/2) = 1e-3; with
+    head_dim 8 they are 1, 10^-1.5, 10^-3 and 10^-4.5 (theta^(-2i/hd) for i = 0..hd/2-1).  These
+    values are written out here as literals, so a schedule without the factor 2 (theta^(-i/hd))
+    or pairs (2i, 2i+1) instead of (i, i+hd/2) fail."""
+    rng = np.random.default_rng(11)
+    schedules = {4: [1.0, 1e-3], 8: [1.0, 10 ** -1.5, 1e-3, 10 ** -4.5]}
+    for hd, inv_freq in schedules.items():
+        x = rng.standard_normal((3, 2, hd))
+        pos = [1, 7, 3000]
+        y = od.rope(x, pos, 1e6)
+        for t, p in enumerate(pos):
+            for h in range(2):
+                ref = _rope_by_hand(list(x[t, h]), p, inv_freq)
+                assert np.max(np.abs(y[t, h] - ref)) < 1e-12, (hd, p)
+
+
+def test_rope_first_pair_at_position_one_turns_by_one_radian():
+    """Frequency 1 for the first pair means position 1 turns (x_0, x_{hd/2}) by exactly one
+    radian; the second half of a unit vector e_{hd/2} goes to (-sin 1, cos 1)."""
+    hd = 8
+    e = np.zeros((1, 1, hd))
+    e[0, 0, hd // 2] = 1.0
+    y = od.rope(e, [1], 1e6)[0, 0]
+    assert abs(y[0] + math.sin(1.0)) < 1e-15 and abs(y[hd // 2] - math.cos(1.0)) < 1e-15
+    assert np.count_nonzero(np.abs(y) > 1e-15) == 2
+
+
 # ---- attention ----------------------------------------------------------------------------------
 
 def test_attention_single_key_returns_its_value():
@@ -240,6 +281,67 @@ def test_silu_closed_form():
 def test_logits_cover_mask_rows_only(tiny_w):
     lg = _fwd(tiny_w, [5] + [TINY.mask_token_id] * 7, _hidden(64))["logits"]
     assert lg.shape == (7, TINY.vocab)
+
+
+def _planted_final_gain():
+    """A final-norm gain far from 1 and different in every element."""
+    return 0.25 + 1.5 * np.arange(TINY.hidden, dtype=np.float64) / TINY.hidden
+
+
+def test_lm_head_with_silent_layers_is_the_normed_embedding_by_hand(tiny_w):
+    """With W_o = W_down = 0 every layer adds zero, so the final residual is the block's
+    embedding.  Logits row j must then be RMSNorm(E[block token n_anchor + j]) * g_fin times the
+    LM head, written here as explicit sums over the hidden dimension for a few vocab entries.
+    The anchor's embedding differs from the mask's, so taking rows 0..D-1 instead of the mask rows
+    fails, and so does a dropped or uniform gain."""
+    W = dict(tiny_w)
+    W["wo"] = np.zeros_like(W["wo"])
+    W["w_down"] = np.zeros_like(W["w_down"])
+    g = _planted_final_gain()
+    W["final_norm_w"] = g
+    toks = [5] + [TINY.mask_token_id] * 7
+    lg = _fwd(W, toks, _hidden(16))["logits"]
+    H, eps = TINY.hidden, TINY.rms_eps
+    E, Wlm = W["embed"], W["lm_head"]
+    for j in range(len(toks) - 1):
+        e = [float(v) for v in E[toks[1 + j]]]
+        r = 1.0 / math.sqrt(sum(v * v for v in e) / H + eps)
+        for vtok in (0, 1, 77, TINY.vocab - 2, TINY.vocab - 1):
+            ref = sum(e[h] * r * g[h] * float(Wlm[vtok, h]) for h in range(H))
+            assert abs(lg[j, vtok] - ref) < 1e-12 * max(1.0, abs(ref)), (j, vtok)
+    # the anchor row's value is different, so the rows really are the mask rows
+    e0 = E[toks[0]].astype(np.float64)
+    a0 = (e0 / np.sqrt(np.mean(e0 * e0) + eps) * g) @ Wlm.T.astype(np.float64)
+    assert np.max(np.abs(a0 - lg[0])) > 1e-3
+
+
+def test_lm_head_rows_are_the_final_mask_residuals(tiny_w):
+    """Identity LM head (V = H) and a planted gain: logits row j equals RMSNorm(final residual
+    row n_anchor + j) * g_fin element by element (the residual from the forward's own per-layer
+    record), and differs from the anchor row's normed residual."""
+    sh = TINY.__class__(**{**TINY.__dict__, "vocab": TINY.hidden})
+    W = dict(tiny_w)
+    W["embed"] = tiny_w["embed"][:TINY.hidden]
+    W["lm_head"] = np.eye(TINY.hidden)
+    g = _planted_final_gain()
+    W["final_norm_w"] = g
+    toks = [5] + [sh.vocab - 1] * 7
+    out = od.drafter_forward(sh, W, toks, 1, hidden=_hidden(20), keep=True)
+    x = out["resid"][-1]
+    H, eps = sh.hidden, sh.rms_eps
+    for j in range(len(toks) - 1):
+        row = x[1 + j]
+        r = 1.0 / math.sqrt(sum(float(v) * float(v) for v in row) / H + eps)
+        ref = np.array([row[h] * r * g[h] for h in range(H)])
+        assert np.max(np.abs(out["logits"][j] - ref)) < 1e-12
+    a = x[0] / math.sqrt(float(np.mean(x[0] * x[0])) + eps) * g
+    assert np.max(np.abs(out["logits"][0] - a)) > 1e-3
+    # with no anchor every row is a mask row: D = B
+    out0 = od.drafter_forward(sh, W, toks, 0, hidden=_hidden(20), keep=True)
+    assert out0["logits"].shape == (8, H)
+    x0 = out0["resid"][-1]
+    assert np.max(np.abs(out0["logits"][0] - x0[0] / math.sqrt(float(np.mean(x0[0] ** 2)) + eps)
+                         * g)) < 1e-12
 
 
 # ---- the workload shapes follow the pages' stated structure -------------------------------------
