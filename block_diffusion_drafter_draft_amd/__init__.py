@@ -8,7 +8,8 @@ Entry points (same names as the C ABI in include/dbd.h):
   draft_block, verify_greedy, select_streak
   draft_workspace_bytes, verify_workspace_bytes, select_workspace_bytes
   refine_block, refine_workspace_bytes (Mask-Predict update between draft_block passes)
-Stage hooks used by the parity tests: sample_from_logits, mix_rmsnorm, gemm_nt.
+Stage hooks used by the parity tests: sample_from_logits, mix_rmsnorm, gemm_nt,
+draft_residual_offset.
 """
 import ctypes
 import os
@@ -88,6 +89,8 @@ def lib():
                                               _sz, _vp]),
             "dbd_mix_rmsnorm": (_i32, [_c.POINTER(ModelDesc), _vp, _vp, _vp, _i64, _i64, _i32,
                                        _vp, _vp]),
+            "dbd_draft_residual_offset": (_i32, [_c.POINTER(ModelDesc), _i32, _i32, _i32, _i32,
+                                                 _i32, _f32, _i32, _c.POINTER(_sz)]),
             "dbd_gemm_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                 _c.POINTER(_sz)]),
             "dbd_gemm_nt": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
@@ -192,6 +195,17 @@ def draft_block(desc, weights, block_tokens, target_hidden_new, new_offsets, ctx
         _ptr(kv_k), _ptr(kv_v), cap, n_drafts, float(temperature), int(seed) & (2**64 - 1),
         _ptr(draft_tokens), _ptr(logits_out), _ptr(seq_status), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, block_tokens)))
+
+
+def draft_residual_offset(desc, batch, block_len, n_anchor, n_new_total, n_drafts, temperature,
+                          ctx_capacity) -> int:
+    """Byte offset of the fp32 residual [batch * block_len, H] in the workspace of a draft_block
+    call with these arguments (test hook for per-layer parity)."""
+    out = _sz(0)
+    _check(lib().dbd_draft_residual_offset(_c.byref(desc), batch, block_len, n_anchor,
+                                           int(n_new_total), n_drafts, float(temperature),
+                                           ctx_capacity, _c.byref(out)))
+    return out.value
 
 
 def verify_workspace_bytes(batch, n_rows, vocab) -> int:

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "host_rules.h"
+
 namespace dbd {
 
 typedef __bf16 bf16;

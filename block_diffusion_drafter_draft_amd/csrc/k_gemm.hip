@@ -476,7 +476,7 @@ static void launch_kind(int dtype, int cfg, int split, GemmArgs a, const EpiArgs
     a.split = p.split;
     // the residual's norm rides on the skinny tiles' split-K reduction, which sees whole rows
     const bool fuse = KIND == EPI_RESID && e.norm_g && is_skinny(p.cfg) && p.split > 1 &&
-                      batch == 1 && e.ldc == a.N;
+                      batch == 1 && resid_norm_fits(a.N, e.ldc);
     EpiArgs ee = e;
     if (!fuse) ee.norm_g = nullptr;
     if (a.A2) launch_cfg<KIND, true>(p.cfg, a, ee, batch, s);

@@ -836,7 +836,8 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
 // when norm_out_lo is set.  The loads of RB splits are in flight together.
 template <typename T>
 __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e) {
-  constexpr int NT = 1024, MAXG = 2, RB = 8;          // rows of up to 8192 columns
+  constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread, RB = 8;
+  static_assert(NT * MAXG * 4 == kResidNormMaxCols, "row coverage of resid_norm_fits");
   __shared__ float red[NT / 64];
   const int row = blockIdx.x, tid = threadIdx.x, N = a.N, S = a.split;
   const float* part = reinterpret_cast<const float*>(a.part) + (int64_t)row * N;
@@ -925,7 +926,7 @@ static void launch_skinny(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, KIND, SPLITA>), dim3(units, 1, batch), dim3(256), 0,
                      s, a, e);
   if (S > 1 && KIND == EPI_RESID && e.norm_g)
-    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(a.M), dim3(1024), 0, s, a, e);
+    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
   else if (S > 1)
     launch_reduce<MT, 128, 1, 4, KIND>(a, e, batch, s);
 }

@@ -73,11 +73,13 @@ constexpr size_t kAlign = 256;
 struct Carver {
   char* base;
   size_t off = 0;
+  size_t last = 0;            // offset of the most recent take
   template <typename T>
   T* take(size_t count) {
     off = (off + kAlign - 1) / kAlign * kAlign;
+    last = off;
     T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
-    off += count * sizeof(T) + (count == 0 ? 0 : 0);
+    off += count * sizeof(T);
     return p;
   }
 };
@@ -115,6 +117,7 @@ struct DraftBufs {
   void* ctxfeat;
   float* fcout;         // fully connected fusion output before its RMSNorm [T, H] fp32
   float* x;
+  size_t x_off;         // byte offset of x in the workspace
   void* xn;
   void* q;
   void* attn;
@@ -223,6 +226,7 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.fcout = d.n_target_layers > 0 && d.ctx_fusion ? c.take<float>((int64_t)Tn * d.hidden)
                                                   : nullptr;
   t.x = c.take<float>(M * d.hidden);
+  t.x_off = c.last;
   t.xn = c.take<char>(M * d.hidden * es);
   t.q = c.take<char>(M * qd * es);
   t.attn = c.take<char>(M * qd * es);
@@ -405,6 +409,21 @@ int dbd_draft_workspace_bytes(const dbd_model_desc* desc, int32_t max_batch, int
   if (rc) return rc;
   *bytes = carve_draft(*desc, max_batch, block_len, n_anchor, max_new_tokens, n_drafts,
                        temperature, ctx_capacity, nullptr, nullptr, true);
+  return DBD_OK;
+}
+
+int dbd_draft_residual_offset(const dbd_model_desc* desc, int32_t batch, int32_t block_len,
+                              int32_t n_anchor, int32_t n_new_total, int32_t n_drafts,
+                              float temperature, int32_t ctx_capacity, size_t* offset) {
+  g_err.clear();
+  if (!offset) return fail(DBD_ERR_ARG, "offset is NULL");
+  int rc = check_draft_shape(desc, batch, block_len, n_anchor, n_new_total, n_drafts,
+                             temperature, ctx_capacity);
+  if (rc) return rc;
+  DraftBufs b;
+  carve_draft(*desc, batch, block_len, n_anchor, n_new_total, n_drafts, temperature,
+              ctx_capacity, nullptr, &b, false);
+  *offset = b.x_off;
   return DBD_OK;
 }
 

@@ -315,6 +315,17 @@ int dbd_mix_rmsnorm(const dbd_model_desc* desc, const float* mix_logits, const v
                     const void* hidden, int64_t hid_token_stride, int64_t hid_layer_stride,
                     int32_t n_tokens, void* out, void* stream);
 
+/* Byte offset (host out) inside the workspace of a draft_block call with these arguments of
+ * the block's fp32 residual stream x [batch * block_len, H] (row n * block_len + b is block
+ * position b of sequence n).  After the call it holds the residual after the last draft layer,
+ * before the final RMSNorm.  Called with a desc whose n_layers is truncated to l + 1 (the
+ * stacked per-layer weights, the mixing rows and the cache layers 0 .. l are prefixes of the
+ * full drafter's) it exposes the residual after layer l, for per-layer parity tests. */
+int dbd_draft_residual_offset(const dbd_model_desc* desc, int32_t batch, int32_t block_len,
+                              int32_t n_anchor, int32_t n_new_total, int32_t n_drafts,
+                              float temperature, int32_t ctx_capacity,
+                              size_t* offset /* host out */);
+
 /* Workspace size (host) for dbd_gemm_nt with the same dtype, shape, tile_cfg and split: the
  * split-K partials of the configuration (0 when it does not split K). */
 int dbd_gemm_workspace_bytes(int32_t dtype, int32_t M, int32_t N, int32_t K, int32_t tile_cfg,

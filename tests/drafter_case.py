@@ -1,5 +1,7 @@
 """Build one synthetic workload on the GPU, run the library on it, and prepare the oracle's view
 of the same inputs.  Shared by the GPU parity tests (not collected itself)."""
+from dataclasses import replace
+
 import numpy as np
 import torch
 
@@ -19,6 +21,8 @@ class Case:
 
     def __init__(self, wl, seed=0, dev="cuda", ctx=None, new=None, seqs_hidden=None):
         self.wl, self.dev, self.seed = wl, dev, seed
+        self._oracle_w = None
+        self.last_ws = None
         sh = wl.shape
         self.shape = sh
         self.desc = dbd.model_desc(sh, act_pairs=wl.act_pairs)
@@ -60,24 +64,26 @@ class Case:
         rows = [self.hidden[i][int(lo[i]):int(hi[i])] for i in range(self.wl.batch)]
         return torch.cat(rows, 0).contiguous()
 
-    def workspace(self, n_new_total, n_drafts, temperature):
-        nb = dbd.draft_workspace_bytes(self.desc, self.wl.batch, self.wl.block_len,
+    def workspace(self, n_new_total, n_drafts, temperature, desc=None):
+        nb = dbd.draft_workspace_bytes(desc or self.desc, self.wl.batch, self.wl.block_len,
                                        self.wl.n_anchor, n_new_total, n_drafts, temperature,
                                        self.cap)
         return torch.empty(nb, dtype=torch.uint8, device=self.dev)
 
     def call(self, ctx_len, counts, hidden, n_drafts=None, temperature=None, seed=1234,
-             logits=True):
+             logits=True, desc=None):
         wl = self.wl
+        desc = desc or self.desc
         K = n_drafts if n_drafts is not None else wl.n_drafts
         T = temperature if temperature is not None else wl.temperature
         off, tot = self._offsets(counts)
-        ws = self.workspace(tot, K, T)
+        ws = self.workspace(tot, K, T, desc)
+        self.last_ws = ws
         out = torch.full((wl.batch, K, self.D), -7, dtype=torch.int32, device=self.dev)
         lg = (torch.empty((wl.batch, self.D, self.shape.vocab), dtype=torch.float32,
                           device=self.dev) if logits else None)
         st = torch.full((wl.batch,), -7, dtype=torch.int32, device=self.dev)
-        dbd.draft_block(self.desc, self.wstruct, self.tokens, hidden, off,
+        dbd.draft_block(desc, self.wstruct, self.tokens, hidden, off,
                         torch.tensor(np.asarray(ctx_len, np.int32), device=self.dev), self.kv_k,
                         self.kv_v, out, ws, tot, n_drafts=K, temperature=T, seed=seed,
                         n_anchor=wl.n_anchor, logits_out=lg, seq_status=st)
@@ -98,9 +104,43 @@ class Case:
             return self.call(self.ctx, self.new, h if h.numel() else None, **kw)
         return self.call(self.ctx, np.zeros(self.wl.batch, np.int64), None, **kw)
 
+    def residuals(self):
+        """The block's fp32 residual stream after every draft layer, [L][N, B, H] numpy, from
+        calls of the measured step with the drafter truncated to l + 1 layers (the stacked
+        weights and cache layers of the first l + 1 layers are prefixes of the full ones, so
+        the call recomputes exactly the full step's first l + 1 layers)."""
+        sh, wl = self.shape, self.wl
+        out = []
+        for l in range(sh.n_layers):
+            desc = dbd.model_desc(replace(sh, n_layers=l + 1), act_pairs=wl.act_pairs)
+            if self.wl.ctx_source == "hidden":
+                h = self._hidden_rows(self.ctx, self.ctx + self.new)
+                counts, hid = self.new, (h if h.numel() else None)
+            else:
+                counts, hid = np.zeros(wl.batch, np.int64), None
+            _, tot = self._offsets(counts)
+            self.call(self.ctx, counts, hid, logits=False, desc=desc)
+            off = dbd.draft_residual_offset(desc, wl.batch, wl.block_len, wl.n_anchor, tot,
+                                            wl.n_drafts, wl.temperature, self.cap)
+            n = wl.batch * wl.block_len * sh.hidden
+            torch.cuda.synchronize()
+            x = self.last_ws[off:off + 4 * n].view(torch.float32)
+            out.append(x.reshape(wl.batch, wl.block_len, sh.hidden).cpu().numpy())
+        return out
+
     # ------------------------------------------------------------------ the oracle's view
     def cpu_weights(self):
         return {k: v.detach().to("cpu") for k, v in self.W.items()}
+
+    def oracle_weights(self):
+        """The weights as numpy arrays for the oracle, converted once: fp64 when that takes at
+        most 20 GB of host memory, else fp32 (both exact for bf16 and fp32 values; the oracle
+        upcasts fp32 to fp64 where it uses them)."""
+        if self._oracle_w is None:
+            n = sum(v.numel() for v in self.W.values())
+            dt = torch.float64 if n * 8 <= 20e9 else torch.float32
+            self._oracle_w = {k: v.detach().to(dt).cpu().numpy() for k, v in self.W.items()}
+        return self._oracle_w
 
     def oracle_inputs(self, i):
         """(block tokens, hidden [C+n, L_t, H] or None, ctx_kv or None) of sequence i on CPU."""
