@@ -1,12 +1,16 @@
 """Benchmark of the block-diffusion drafting hot path on one MI355X.
 
 A step is one draft_block call (ingest of the newly committed positions, the block forward, the
-LM head and argmax drafting) followed by verify_greedy on the target's logits, for the
-Qwen3-8B-shaped drafter at batch 32 (block 16, 7 draft layers mixing 9 target layers, cached
-context lengths uniform in [256, 3072]).  Inputs are synthetic and resident in HBM before timing.
+LM head and argmax or sampled drafting) followed by verify_greedy on the target's logits, or by
+select_streak over K sampled drafts.  The headline workload is the Qwen3-8B-shaped drafter at
+batch 32 (block 16, 7 draft layers mixing 9 target layers, cached context lengths uniform in
+[256, 3072], argmax drafts, greedy verify).  Inputs are synthetic and resident in HBM before
+timing.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-Prints one JSON line.
+    one JSON line for the headline workload
+python bench.py --workload NAME | --all-workloads [--cpu-baseline-all]
+    one JSON line per workload (qwen3-4b, qwen3-8b, gpt-oss-20b, specdiff2-7b)
 
 Auxiliary modes for the HBM-traffic figure of the dominant kernel (rocprofv3 counter passes):
   python bench.py --calibrate-copy           plain 1 GiB device copies (counter scale factor)
@@ -26,6 +30,8 @@ import numpy as np
 HBM_PEAK = 8.0e12          # bytes/s, MI355X datasheet
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s, MI355X datasheet
 WORKLOAD = "qwen3-8b"
+WORKLOADS_ALL = ["qwen3-4b", "qwen3-8b", "gpt-oss-20b", "specdiff2-7b"]
+METRIC = "drafted 16-tok blocks/s (draft fwd+verify) Qwen3-8B-shape bs=32; % roofline"
 
 
 def parse():
@@ -34,6 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="one JSON line per bf16 workload (Qwen3-4B, Qwen3-8B, GPT-OSS-20B and "
+                         "SpecDiff-2 shapes)")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="time the oracle on every workload, not only the headline one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps-only", action="store_true",
                     help="skip the instrumented pass and the cold-ingest timing")
@@ -189,14 +200,15 @@ def algorithmic_costs(wl, ctx, new):
     T = int(np.sum(new))
     keys = ctx + new + B                              # keys attended per sequence
     c = {}
-    if getattr(sh, "ctx_fusion", "mix") == "fc":
-        # fully connected fusion: fusion weights and the concatenated target rows once, the
-        # shared feature written once
-        c["mix"] = (H * Lt * H * es + T * Lt * H * es + T * H * es, 2 * T * H * Lt * H)
-    else:
-        c["mix"] = (T * Lt * H * es + Ld * T * H * es, 0)
-    c["gemm_ctxkv"] = (Ld * (2 * kd * H * es + T * H * es + T * 2 * kd * es),
-                       2 * T * 2 * kd * H * Ld)
+    if Lt > 0 and T > 0:
+        if getattr(sh, "ctx_fusion", "mix") == "fc":
+            # fully connected fusion: fusion weights and the concatenated target rows once, the
+            # shared feature written once
+            c["mix"] = (H * Lt * H * es + T * Lt * H * es + T * H * es, 2 * T * H * Lt * H)
+        else:
+            c["mix"] = (T * Lt * H * es + Ld * T * H * es, 0)
+        c["gemm_ctxkv"] = (Ld * (2 * kd * H * es + T * H * es + T * 2 * kd * es),
+                           2 * T * 2 * kd * H * Ld)
     c["gemm_qkv"] = (Ld * ((qd + 2 * kd) * H * es + M * H * es + M * (qd + 2 * kd) * es),
                      2 * M * (qd + 2 * kd) * H * Ld)
     c["attn"] = (Ld * (int(np.sum(keys)) * kvh * hd * 2 * es + 2 * M * qd * es),
@@ -204,10 +216,199 @@ def algorithmic_costs(wl, ctx, new):
     c["gemm_o"] = (Ld * (H * qd * es + M * qd * es + 2 * M * H * 4), 2 * M * H * qd * Ld)
     c["gemm_gateup"] = (Ld * (2 * F * H * es + M * H * es + M * F * es), 2 * M * 2 * F * H * Ld)
     c["gemm_down"] = (Ld * (H * F * es + M * F * es + 2 * M * H * 4), 2 * M * H * F * Ld)
-    c["gemm_lmhead"] = (V * H * es + Md * H * es, 2 * Md * V * H)
+    sampling = wl.temperature > 0
+    # sampling keeps the fp32 logits, which the drafting stage then reads once
+    c["gemm_lmhead"] = (V * H * es + Md * H * es + (Md * V * 4 if sampling else 0),
+                        2 * Md * V * H)
+    if sampling:
+        c["draft"] = (Md * V * 4 + N * wl.n_drafts * D * 4, 0)
     c["rownorm"] = ((2 * Ld + 1) * M * H * (4 + es) + M * H * (es + 4), 0)
-    c["verify"] = (N * wl.verify_rows * V * 4, 0)
+    if wl.verify == "streak":
+        c["select"] = (N * wl.n_drafts * wl.verify_rows * V * 4, 0)
+    else:
+        c["verify"] = (N * wl.verify_rows * V * 4, 0)
     return c
+
+
+class StepSetup:
+    """Inputs of one workload resident on the GPU and the timed step: one draft_block call
+    (ingest of the newly committed positions for drafters that mix target layers, the block
+    forward, the LM head, argmax or sampled drafting), then verify_greedy on the first draft
+    (greedy workloads) or select_streak over the K drafts (streak workloads)."""
+
+    def __init__(self, wl, dbd, synth, torch, dev="cuda"):
+        self.wl = wl
+        sh = self.sh = wl.shape
+        N, B, D, V, K = wl.batch, wl.block_len, wl.n_draft, sh.vocab, wl.n_drafts
+        self.N, self.B, self.D, self.V, self.K = N, B, D, V, K
+        ctx, new = synth.make_lengths(wl, 0)
+        self.ctx, self.new = ctx, new
+        cap = synth.capacity_for(wl, ctx, new)
+        self.W = W = synth.make_weights(sh, 0, dev)
+        self.desc = desc = dbd.model_desc(sh, act_pairs=wl.act_pairs)
+        self.wst = wst = dbd.weights_struct(W)
+        self.tokens = tokens = synth.make_block_tokens(wl, 0, dev)
+        dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
+        ks, vs = dbd.kv_cache_shapes(sh, N, cap)
+        self.kv_k = kv_k = torch.zeros(ks, dtype=dt, device=dev)
+        self.kv_v = kv_v = torch.zeros(vs, dtype=dt, device=dev)
+        self.hidden = None
+        T_cold = 0
+        if wl.ctx_source == "hidden":
+            self.hidden = [synth.make_hidden(sh, int(ctx[i] + new[i]), 0, i, dev)
+                           for i in range(N)]
+            self.cold_rows = torch.cat([self.hidden[i][: int(ctx[i])] for i in range(N)],
+                                       0).contiguous()
+            self.step_rows = torch.cat([self.hidden[i][int(ctx[i]):] for i in range(N)],
+                                       0).contiguous()
+            T_cold, self.T_step = self.cold_rows.shape[0], self.step_rows.shape[0]
+        else:
+            # the drafter takes its context K/V from the cache: synthetic rotated K/V, no ingest
+            Kc, Vc = synth.make_cache_kv(sh, N, int(ctx.max()), 0, dev)
+            for i in range(N):
+                C = int(ctx[i])
+                C8 = (C + 7) // 8 * 8
+                kv_k[:, i, :, :C] = Kc[:, i, :, :C]
+                vpad = torch.zeros((sh.n_layers, sh.n_kv_heads, C8, sh.head_dim), dtype=dt,
+                                   device=dev)
+                vpad[:, :, :C] = Vc[:, i, :, :C]
+                kv_v[:, i, :, : C8 // 8] = dbd.pack_values(vpad)
+            del Kc, Vc
+            self.step_rows, self.T_step = None, 0
+            new = self.new = np.zeros(N, np.int64)
+        self.T_cold = T_cold
+        self.ws = torch.empty(dbd.draft_workspace_bytes(desc, N, B, wl.n_anchor,
+                                                        max(T_cold, self.T_step), K,
+                                                        wl.temperature, cap),
+                              dtype=torch.uint8, device=dev)
+        self.off_cold = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32),
+                                     device=dev)
+        self.off_step = torch.tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32),
+                                     device=dev)
+        self.zeros = torch.zeros(N, dtype=torch.int32, device=dev)
+        self.ctx_t = torch.tensor(ctx.astype(np.int32), device=dev)
+        self.drafts = torch.empty((N, K, D), dtype=torch.int32, device=dev)
+        self.n_acc = torch.empty(N, dtype=torch.int32, device=dev)
+        self.bonus = torch.empty(N, dtype=torch.int32, device=dev)
+        self.committed = torch.empty((N, D + 1), dtype=torch.int32, device=dev)
+        R = wl.verify_rows
+        if wl.verify == "streak":
+            # verifier logits [N, K, R, V] planted per (sequence, draft) around fixed drafts
+            self.v_drafts = synth.make_drafts(N, K, D, V, seed=1, device=dev)
+            self.vlogits, _ = synth.make_planted_streak_logits(self.v_drafts, R, V,
+                                                               wl.planted_alpha, seed=1,
+                                                               device=dev)
+            self.vws = torch.empty(dbd.select_workspace_bytes(N, K, R, V), dtype=torch.uint8,
+                                   device=dev)
+            self.selected = torch.empty(N, dtype=torch.int32, device=dev)
+        else:
+            self.v_drafts = synth.make_drafts(N, 1, D, V, seed=1, device=dev)[:, 0].contiguous()
+            self.vlogits, _ = synth.make_planted_verify_logits(self.v_drafts, R, V,
+                                                               wl.planted_alpha, seed=1,
+                                                               device=dev)
+            self.vws = torch.empty(dbd.verify_workspace_bytes(N, R, V), dtype=torch.uint8,
+                                   device=dev)
+        self.dbd = dbd
+
+    def cold(self):
+        """Fill the cache: cold ingest of every cached position (mixing drafters only)."""
+        if self.wl.ctx_source != "hidden":
+            return
+        self.dbd.draft_block(self.desc, self.wst, self.tokens, self.cold_rows, self.off_cold,
+                             self.zeros, self.kv_k, self.kv_v, self.drafts, self.ws, self.T_cold,
+                             n_drafts=self.K, temperature=self.wl.temperature,
+                             n_anchor=self.wl.n_anchor)
+
+    def step(self, seed=7):
+        wl, dbd = self.wl, self.dbd
+        dbd.draft_block(self.desc, self.wst, self.tokens, self.step_rows, self.off_step,
+                        self.ctx_t, self.kv_k, self.kv_v, self.drafts, self.ws, self.T_step,
+                        n_drafts=self.K, temperature=wl.temperature, seed=seed,
+                        n_anchor=wl.n_anchor)
+        if wl.verify == "streak":
+            # the verifier scored the drafts sampled here; its logits are fixed synthetic rows
+            dbd.select_streak(self.vlogits, self.drafts, self.selected, self.n_acc, self.bonus,
+                              self.committed, self.vws)
+        else:
+            dbd.verify_greedy(self.vlogits, self.drafts[:, 0], self.n_acc, self.bonus,
+                              self.committed, self.vws)
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def stage_table(dbd, torch, fn, steps, costs):
+    """Per-stage kernel time from HIP event pairs the library records around each launch on its
+    stream, with the stage's algorithmic GB/s and TFLOP/s."""
+    dbd.timing_reset()
+    dbd.timing_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    tm = dbd.timing_read()
+    dbd.timing_enable(False)
+    dbd.timing_reset()
+    stages = {}
+    for name, (tot, n) in tm.items():
+        if n == 0:
+            continue
+        b, f = costs.get(name, (0, 0))
+        t = tot / steps * 1e-3
+        stages[name] = {"ms_per_step": round(tot / steps, 4),
+                        "launches_per_step": n // steps,
+                        "GBps": round(b / t / 1e9, 1) if b else None,
+                        "TFLOPs": round(f / t / 1e12, 1) if f else None,
+                        "roof_us": round(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6, 2)}
+    return stages
+
+
+def dominant_roofline(stages, costs, measured=True):
+    """The roofline object of the stage that takes the most time."""
+    dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
+    b, f = costs[dom]
+    n = stages[dom]["launches_per_step"]
+    avg_s = stages[dom]["ms_per_step"] / n * 1e-3
+    if f and f / b > MFMA_BF16_PEAK / HBM_PEAK:
+        ach = f / n / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(ach * 1e12 / MFMA_BF16_PEAK, 4)}
+    else:
+        ach = b / n / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(ach * 1e9 / HBM_PEAK, 4)}
+    tr = measured_traffic(dom) if measured else None
+    roof.update({"kernel": dom, "launches_per_step": n,
+                 "avg_launch_us": round(avg_s * 1e6, 2),
+                 "algorithmic_bytes_per_launch": round(b / n),
+                 "algorithmic_flops_per_launch": round(f / n),
+                 "traffic": None if tr is None else tr["bytes"],
+                 "traffic_kernel": None if tr is None else tr["kernel"],
+                 "traffic_source": None if tr is None else os.path.relpath(TRAFFIC_FILE, ROOT)})
+    return roof
+
+
+def describe(wl):
+    sh = wl.shape
+    ctx = (f"cached ctx U[{wl.ctx_lo},{wl.ctx_hi}]" if wl.ctx_lo != wl.ctx_hi
+           else f"cached ctx {wl.ctx_lo}")
+    src = (f"{sh.n_layers} draft layers x {sh.n_target_layers} target layers"
+           if sh.n_target_layers else f"{sh.n_layers} layers, context K/V given in the cache")
+    draft = ("argmax drafts" if wl.temperature <= 0
+             else f"{wl.n_drafts} draft(s) sampled at T={wl.temperature:g}")
+    ver = "greedy verify" if wl.verify == "greedy" else "streak self-selection + greedy accept"
+    return (f"{wl.name}-shaped drafter: hidden {sh.hidden}, {sh.n_q_heads}q/{sh.n_kv_heads}kv x "
+            f"{sh.head_dim}, ffn {sh.ffn}, {src}, vocab {sh.vocab}, block {wl.block_len}, batch "
+            f"{wl.batch}, {ctx}, {draft}, {ver}")
 
 
 def main():
@@ -231,251 +432,152 @@ def main():
     import block_diffusion_drafter_draft_amd as dbd
     import synth
 
+    names = WORKLOADS_ALL if args.all_workloads else [args.workload]
+    for name in names:
+        out = bench_workload(args, synth.workload(name), dbd, synth, torch)
+        print(json.dumps(out), flush=True)
+        torch.cuda.empty_cache()
+
+
+def bench_workload(args, wl, dbd, synth, torch):
     dev = "cuda"
-    wl = synth.workload(args.workload)
     sh = wl.shape
-    N, B, D, V = wl.batch, wl.block_len, wl.n_draft, sh.vocab
     t_setup = time.time()
-    ctx, new = synth.make_lengths(wl, 0)
-    cap = synth.capacity_for(wl, ctx, new)
-    W = synth.make_weights(sh, 0, dev)
-    desc, ws_w = dbd.model_desc(sh, act_pairs=wl.act_pairs), dbd.weights_struct(W)
-    tokens = synth.make_block_tokens(wl, 0, dev)
-    dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
-    ks, vs = dbd.kv_cache_shapes(sh, N, cap)
-    kv_k = torch.zeros(ks, dtype=dt, device=dev)
-    kv_v = torch.zeros(vs, dtype=dt, device=dev)
-    hidden = [synth.make_hidden(sh, int(ctx[i] + new[i]), 0, i, dev) for i in range(N)]
-    cold_rows = torch.cat([hidden[i][: int(ctx[i])] for i in range(N)], 0).contiguous()
-    step_rows = torch.cat([hidden[i][int(ctx[i]):] for i in range(N)], 0).contiguous()
-    T_cold, T_step = cold_rows.shape[0], step_rows.shape[0]
-    ws = torch.empty(dbd.draft_workspace_bytes(desc, N, B, wl.n_anchor, T_cold, 1, 0.0, cap),
-                     dtype=torch.uint8, device=dev)
-    off_cold = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32), device=dev)
-    off_step = torch.tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32), device=dev)
-    zeros = torch.zeros(N, dtype=torch.int32, device=dev)
-    ctx_t = torch.tensor(ctx.astype(np.int32), device=dev)
-    drafts = torch.empty((N, 1, D), dtype=torch.int32, device=dev)
-    # target logits with a planted accepted-prefix length per sequence
-    v_drafts = synth.make_drafts(N, 1, D, V, seed=1, device=dev)[:, 0].contiguous()
-    tlogits, _ = synth.make_planted_verify_logits(v_drafts, wl.verify_rows, V,
-                                                  wl.planted_alpha, seed=1, device=dev)
-    vws = torch.empty(dbd.verify_workspace_bytes(N, wl.verify_rows, V), dtype=torch.uint8,
-                      device=dev)
-    n_acc = torch.empty(N, dtype=torch.int32, device=dev)
-    bonus = torch.empty(N, dtype=torch.int32, device=dev)
-    committed = torch.empty((N, D + 1), dtype=torch.int32, device=dev)
+    S = StepSetup(wl, dbd, synth, torch, dev)
+    N, B, D, V, K = S.N, S.B, S.D, S.V, S.K
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
-
-    # fill the cache: cold ingest of every cached position (also the mix kernel's large regime)
-    def cold():
-        dbd.draft_block(desc, ws_w, tokens, cold_rows, off_cold, zeros, kv_k, kv_v, drafts, ws,
-                        T_cold)
-    cold()
+    S.cold()
     torch.cuda.synchronize()
+    ms = time_steps(torch, S.step, args.steps, args.warmup)
 
-    def step():
-        dbd.draft_block(desc, ws_w, tokens, step_rows, off_step, ctx_t, kv_k, kv_v, drafts, ws,
-                        T_step)
-        dbd.verify_greedy(tlogits, drafts[:, 0], n_acc, bonus, committed, vws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # instrumented pass: per-stage kernel time from HIP events the library records on its stream
-    costs = algorithmic_costs(wl, ctx, new)
-    stages = {}
-    cold_info = None
+    costs = algorithmic_costs(wl, S.ctx, S.new)
+    headline = wl.name == WORKLOAD
+    stages, cold_info = {}, None
     if not args.profile_steps_only:
-        dbd.timing_reset()
-        dbd.timing_enable(True)
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        tm = dbd.timing_read()
-        dbd.timing_reset()
-        cold()
-        torch.cuda.synchronize()
-        tc = dbd.timing_read()
-        dbd.timing_enable(False)
-        dbd.timing_reset()
-        for name, (tot, n) in tm.items():
-            if n == 0:
-                continue
-            b, f = costs.get(name, (0, 0))
-            t = tot / args.steps * 1e-3
-            stages[name] = {"ms_per_step": round(tot / args.steps, 4),
-                            "launches_per_step": n // args.steps,
-                            "GBps": round(b / t / 1e9, 1) if b else None,
-                            "TFLOPs": round(f / t / 1e12, 1) if f else None,
-                            "roof_us": round(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) * 1e6, 2)}
-        mix_b = T_cold * (sh.n_target_layers + sh.n_layers) * sh.hidden * 2
-        cold_info = {"rows": T_cold,
-                     "mix_ms": round(tc["mix"][0], 3),
-                     "mix_GBps": round(mix_b / (tc["mix"][0] * 1e-3) / 1e9, 1),
-                     "ctxkv_gemm_ms": round(tc["gemm_ctxkv"][0], 3),
-                     "ctxkv_TFLOPs": round(2 * T_cold * 2 * sh.kv_dim * sh.hidden * sh.n_layers
-                                           / (tc["gemm_ctxkv"][0] * 1e-3) / 1e12, 1)}
-
-    # lossless stochastic verification (not part of the step): the step's target rows against
-    # draft logits near them, drafts sampled from the draft logits by the library's sampler
-    vsample = top_p = refinement = None
-    if not args.profile_steps_only:
-        g = torch.Generator(device=dev).manual_seed(2)
-        dlog = (tlogits[:, :D] + 0.5 * torch.randn(tlogits[:, :D].shape, generator=g,
-                                                   device=dev)).contiguous()
-        sws = torch.empty(max(dbd.sample_workspace_bytes(N, D, V), 256), dtype=torch.uint8,
-                          device=dev)
-        sdr = torch.empty((N, 1, D), dtype=torch.int32, device=dev)
-        dbd.sample_from_logits(dlog, 1, 1.0, 5, sdr, sws)
-        sdr = sdr[:, 0].contiguous()
-        vws = torch.empty(dbd.verify_sample_workspace_bytes(N, D, wl.verify_rows, V),
-                          dtype=torch.uint8, device=dev)
-        run = lambda i: dbd.verify_sample(tlogits, dlog, sdr, 1.0, 1.0, i, n_acc, bonus,
-                                          committed, vws)
-        for i in range(3):
-            run(i)
-        torch.cuda.synchronize()
-        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        v0.record()
-        for i in range(args.steps):
-            run(i)
-        v1.record()
-        torch.cuda.synchronize()
-        vms = v0.elapsed_time(v1) / args.steps
-        vb = (N * wl.verify_rows + N * D) * V * 4
-        # top-p nucleus drafting on the same draft logits (8 draws per position, p = 0.9)
-        tws = torch.empty(dbd.sample_top_p_workspace_bytes(N, D, V), dtype=torch.uint8,
-                          device=dev)
-        tout = torch.empty((N, 8, D), dtype=torch.int32, device=dev)
-        for i in range(3):
-            dbd.sample_top_p(dlog, 8, 1.0, 0.9, i, tout, tws)
-        torch.cuda.synchronize()
-        v0.record()
-        for i in range(args.steps):
-            dbd.sample_top_p(dlog, 8, 1.0, 0.9, i, tout, tws)
-        v1.record()
-        torch.cuda.synchronize()
-        tms = v0.elapsed_time(v1) / args.steps
-        tb = N * D * V * 4
-        top_p = {"ms": round(tms, 4), "logit_bytes": tb, "draws_per_position": 8, "p": 0.9,
-                 "GBps": round(tb / (tms * 1e-3) / 1e9, 1),
-                 "hbm_frac": round(tb / (tms * 1e-3) / HBM_PEAK, 4)}
-        # block refinement (Mask-Predict, two passes): the step's forward with its LM-head logits
-        # kept, refine_block re-masking the floor(D/2) least confident drafts, the forward again
-        # on the partly filled block (no new rows), the final update, the same greedy verify
-        rlog = torch.empty((N, D, V), dtype=torch.float32, device=dev)
-        rws = torch.empty(dbd.refine_workspace_bytes(N, D, V), dtype=torch.uint8, device=dev)
-        gws = torch.empty(dbd.verify_workspace_bytes(N, wl.verify_rows, V), dtype=torch.uint8,
-                          device=dev)
-        rblk = tokens.clone()
-        conf = torch.zeros((N, D), dtype=torch.int64, device=dev)
-        r_acc = torch.empty(N, dtype=torch.int32, device=dev)
-        r_bonus = torch.empty(N, dtype=torch.int32, device=dev)
-        r_com = torch.empty((N, D + 1), dtype=torch.int32, device=dev)
-        ctx2 = torch.tensor((ctx + new).astype(np.int32), device=dev)
-        off0 = torch.zeros(N + 1, dtype=torch.int32, device=dev)
-
-        def refined_step():
-            rblk.copy_(tokens)
-            conf.zero_()
-            dbd.draft_block(desc, ws_w, rblk, step_rows, off_step, ctx_t, kv_k, kv_v, drafts, ws,
-                            T_step, logits_out=rlog)
-            dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, D // 2, rws)
-            dbd.draft_block(desc, ws_w, rblk, None, off0, ctx2, kv_k, kv_v, drafts, ws, 0,
-                            logits_out=rlog)
-            dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, 0, rws)
-            dbd.verify_greedy(tlogits, rblk[:, wl.n_anchor:], r_acc, r_bonus, r_com, gws)
-
-        for _ in range(2):
-            refined_step()
-        torch.cuda.synchronize()
-        v0.record()
-        for _ in range(args.steps):
-            refined_step()
-        v1.record()
-        torch.cuda.synchronize()
-        rms = v0.elapsed_time(v1) / args.steps
-        v0.record()
-        for _ in range(args.steps):
-            dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, D // 2, rws)
-        v1.record()
-        torch.cuda.synchronize()
-        ums = v0.elapsed_time(v1) / args.steps
-        refinement = {"rule": "mask-predict", "passes": 2, "remasked": D // 2,
-                      "ms_per_step": round(rms, 4), "blocks_per_s": round(N / (rms * 1e-3), 1),
-                      "refine_block_ms": round(ums, 4),
-                      "refine_block_GBps": round(tb / (ums * 1e-3) / 1e9, 1)}
-        vsample = {"ms": round(vms, 4), "logit_bytes": vb,
-                   "GBps": round(vb / (vms * 1e-3) / 1e9, 1),
-                   "hbm_frac": round(vb / (vms * 1e-3) / HBM_PEAK, 4),
-                   "mean_accepted": round(float(n_acc.float().mean().item()), 3)}
-
-    # dominant kernel by time, and its roofline
-    roofline = None
-    if stages:
-        dom = max(stages, key=lambda k: stages[k]["ms_per_step"])
-        b, f = costs[dom]
-        n = stages[dom]["launches_per_step"]
-        avg_s = stages[dom]["ms_per_step"] / n * 1e-3
-        if f and f / b > MFMA_BF16_PEAK / HBM_PEAK:
-            ach = f / n / avg_s / 1e12
-            roofline = {"bound": "mfma", "achieved": round(ach, 1),
-                        "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
-                        "frac": round(ach * 1e12 / MFMA_BF16_PEAK, 4)}
-        else:
-            ach = b / n / avg_s / 1e9
-            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
-                        "unit": "GB/s", "frac": round(ach * 1e9 / HBM_PEAK, 4)}
-        tr = measured_traffic(dom)
-        roofline.update({"kernel": dom, "launches_per_step": n,
-                         "avg_launch_us": round(avg_s * 1e6, 2),
-                         "algorithmic_bytes_per_launch": round(b / n),
-                         "traffic": None if tr is None else tr["bytes"],
-                         "traffic_kernel": None if tr is None else tr["kernel"],
-                         "traffic_source": None if tr is None else
-                         os.path.relpath(TRAFFIC_FILE, ROOT)})
+        stages = stage_table(dbd, torch, S.step, args.steps, costs)
+        if headline:
+            dbd.timing_reset()
+            dbd.timing_enable(True)
+            S.cold()
+            torch.cuda.synchronize()
+            tc = dbd.timing_read()
+            dbd.timing_enable(False)
+            dbd.timing_reset()
+            mix_b = S.T_cold * (sh.n_target_layers + sh.n_layers) * sh.hidden * 2
+            cold_info = {"rows": S.T_cold,
+                         "mix_ms": round(tc["mix"][0], 3),
+                         "mix_GBps": round(mix_b / (tc["mix"][0] * 1e-3) / 1e9, 1),
+                         "ctxkv_gemm_ms": round(tc["gemm_ctxkv"][0], 3),
+                         "ctxkv_TFLOPs": round(2 * S.T_cold * 2 * sh.kv_dim * sh.hidden *
+                                               sh.n_layers / (tc["gemm_ctxkv"][0] * 1e-3) /
+                                               1e12, 1)}
+    extras = headline_extras(args, S, dbd, torch) if headline and not args.profile_steps_only \
+        else {}
+    roofline = dominant_roofline(stages, costs, measured=headline) if stages else None
     step_roof_s = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in costs.values())
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, W, tokens, hidden, ctx, new, tlogits, v_drafts)
+    if not args.no_cpu_baseline and (headline or args.cpu_baseline_all):
+        cpu = cpu_baseline(S)
 
     blocks_s = N / (ms * 1e-3)
+    metric = (METRIC if headline else
+              f"drafted {D}-tok blocks/s (draft fwd+{'select' if wl.verify == 'streak' else 'verify'})"
+              f" {wl.name}-shape bs={N}; % roofline")
     out = {
-        "metric": "drafted 16-tok blocks/s (draft fwd+verify) Qwen3-8B-shape bs=32; % roofline",
+        "metric": metric,
         "value": round(blocks_s, 1), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype, "data": "synthetic",
-        "config": {"workload": f"{wl.name}-shaped drafter: hidden {sh.hidden}, "
-                               f"{sh.n_q_heads}q/{sh.n_kv_heads}kv x {sh.head_dim}, ffn {sh.ffn}, "
-                               f"{sh.n_layers} draft layers x {sh.n_target_layers} target layers,"
-                               f" vocab {V}, block {B}, batch {N}, cached ctx "
-                               f"U[{wl.ctx_lo},{wl.ctx_hi}], greedy verify",
-                   "batch": N, "block_len": B, "ctx_total": int(np.sum(ctx)),
-                   "new_rows": int(T_step)},
-        "drafted_tok_per_s": round(blocks_s * D, 1),
+        "config": {"workload": describe(wl), "batch": N, "block_len": B, "n_drafts": K,
+                   "temperature": wl.temperature, "ctx_total": int(np.sum(S.ctx)),
+                   "new_rows": int(S.T_step), "act_pairs": wl.act_pairs},
+        "drafted_tok_per_s": round(blocks_s * D * K, 1),
         "step_roofline_us": round(step_roof_s * 1e6, 1),
         "step_roofline_frac": round(step_roof_s / (ms * 1e-3), 4),
         "roofline": roofline,
         "stages": stages,
-        "cold_ingest": cold_info,
-        "verify_sample": vsample,
-        "top_p_sampling": top_p,
-        "refinement": refinement,
-        "cpu_baseline": cpu,
-        "setup_s": round(t_setup, 1),
     }
-    print(json.dumps(out), flush=True)
+    if headline:
+        out["cold_ingest"] = cold_info
+        out.update(extras)
+    out["cpu_baseline"] = cpu
+    out["setup_s"] = round(t_setup, 1)
+    return out
+
+
+def headline_extras(args, S, dbd, torch):
+    """Measurements next to the headline step (not part of it): lossless stochastic
+    verification, top-p drafting and two-pass block refinement on the same workload."""
+    dev = "cuda"
+    wl, sh = S.wl, S.sh
+    N, D, V = S.N, S.D, S.V
+    tlogits = S.vlogits
+    n_acc, bonus, committed = S.n_acc, S.bonus, S.committed
+    g = torch.Generator(device=dev).manual_seed(2)
+    dlog = (tlogits[:, :D] + 0.5 * torch.randn(tlogits[:, :D].shape, generator=g,
+                                               device=dev)).contiguous()
+    sws = torch.empty(max(dbd.sample_workspace_bytes(N, D, V), 256), dtype=torch.uint8,
+                      device=dev)
+    sdr = torch.empty((N, 1, D), dtype=torch.int32, device=dev)
+    dbd.sample_from_logits(dlog, 1, 1.0, 5, sdr, sws)
+    sdr = sdr[:, 0].contiguous()
+    vws = torch.empty(dbd.verify_sample_workspace_bytes(N, D, wl.verify_rows, V),
+                      dtype=torch.uint8, device=dev)
+    it = iter(range(1 << 30))
+    vms = time_steps(torch, lambda: dbd.verify_sample(tlogits, dlog, sdr, 1.0, 1.0, next(it),
+                                                      n_acc, bonus, committed, vws),
+                     args.steps, 3)
+    vb = (N * wl.verify_rows + N * D) * V * 4
+    vsample = {"ms": round(vms, 4), "logit_bytes": vb,
+               "GBps": round(vb / (vms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(vb / (vms * 1e-3) / HBM_PEAK, 4),
+               "mean_accepted": round(float(n_acc.float().mean().item()), 3)}
+    # top-p nucleus drafting on the same draft logits (8 draws per position, p = 0.9)
+    tws = torch.empty(dbd.sample_top_p_workspace_bytes(N, D, V), dtype=torch.uint8, device=dev)
+    tout = torch.empty((N, 8, D), dtype=torch.int32, device=dev)
+    tms = time_steps(torch, lambda: dbd.sample_top_p(dlog, 8, 1.0, 0.9, next(it), tout, tws),
+                     args.steps, 3)
+    tb = N * D * V * 4
+    top_p = {"ms": round(tms, 4), "logit_bytes": tb, "draws_per_position": 8, "p": 0.9,
+             "GBps": round(tb / (tms * 1e-3) / 1e9, 1),
+             "hbm_frac": round(tb / (tms * 1e-3) / HBM_PEAK, 4)}
+    # block refinement (Mask-Predict, two passes): the step's forward with its LM-head logits
+    # kept, refine_block re-masking the floor(D/2) least confident drafts, the forward again on
+    # the partly filled block (no new rows), the final update, the same greedy verify
+    rlog = torch.empty((N, D, V), dtype=torch.float32, device=dev)
+    rws = torch.empty(dbd.refine_workspace_bytes(N, D, V), dtype=torch.uint8, device=dev)
+    gws = torch.empty(dbd.verify_workspace_bytes(N, wl.verify_rows, V), dtype=torch.uint8,
+                      device=dev)
+    rblk = S.tokens.clone()
+    conf = torch.zeros((N, D), dtype=torch.int64, device=dev)
+    r_acc = torch.empty(N, dtype=torch.int32, device=dev)
+    r_bonus = torch.empty(N, dtype=torch.int32, device=dev)
+    r_com = torch.empty((N, D + 1), dtype=torch.int32, device=dev)
+    ctx2 = torch.tensor((S.ctx + S.new).astype(np.int32), device=dev)
+    off0 = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+
+    def refined_step():
+        rblk.copy_(S.tokens)
+        conf.zero_()
+        dbd.draft_block(S.desc, S.wst, rblk, S.step_rows, S.off_step, S.ctx_t, S.kv_k, S.kv_v,
+                        S.drafts, S.ws, S.T_step, logits_out=rlog)
+        dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, D // 2, rws)
+        dbd.draft_block(S.desc, S.wst, rblk, None, off0, ctx2, S.kv_k, S.kv_v, S.drafts, S.ws,
+                        0, logits_out=rlog)
+        dbd.refine_block(rlog, rblk, conf, wl.n_anchor, sh.mask_token_id, 0, rws)
+        dbd.verify_greedy(tlogits, rblk[:, wl.n_anchor:], r_acc, r_bonus, r_com, gws)
+
+    rms = time_steps(torch, refined_step, args.steps, 2)
+    ums = time_steps(torch, lambda: dbd.refine_block(rlog, rblk, conf, wl.n_anchor,
+                                                     sh.mask_token_id, D // 2, rws),
+                     args.steps, 0)
+    refinement = {"rule": "mask-predict", "passes": 2, "remasked": D // 2,
+                  "ms_per_step": round(rms, 4), "blocks_per_s": round(N / (rms * 1e-3), 1),
+                  "refine_block_ms": round(ums, 4),
+                  "refine_block_GBps": round(tb / (ums * 1e-3) / 1e9, 1)}
+    return {"verify_sample": vsample, "top_p_sampling": top_p, "refinement": refinement}
 
 
 def sweep_block(args, gammas=(8, 16, 32, 64), ctx_len=256):
@@ -567,36 +669,74 @@ def sweep_block(args, gammas=(8, 16, 32, 64), ctx_len=256):
                       "points": points}), flush=True)
 
 
-def cpu_baseline(wl, W, tokens, hidden, ctx, new, tlogits, v_drafts, min_s=10.0, max_seqs=8):
-    """The oracle as it stands, on a bounded sample of the same workload: for sequences 0, 1, ...
-    (until min_s seconds of CPU work or max_seqs sequences) its drafter step from the cached
-    context (context K/V precomputed by the oracle, untimed) plus greedy verification of that
-    sequence's target rows."""
+def host_info():
+    """The host's CPU model and thread counts (the machine the oracle baseline runs on)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu": model, "host_threads": os.cpu_count(), "threads_allowed": aff}
+
+
+def cpu_baseline(S, min_s=10.0, max_seqs=8):
+    """The oracle as it stands, on a bounded sample of the same workload.  For sequences 0, 1, ...
+    (until min_s seconds of CPU work or max_seqs sequences) it runs the step the GPU runs for
+    that sequence: the context K/V of the newly committed positions (drafters that mix target
+    layers; the K/V of the cached positions are computed beforehand, untimed, as the GPU keeps
+    them in its cache), the drafter forward, drafting from the fp32-rounded logits (argmax or
+    the integer-exact sampler) and greedy verification or streak selection."""
+    import torch
     from threadpoolctl import threadpool_info
-    from oracle import accept, drafter as od
-    sh = wl.shape
-    Wc = {k: v.detach().to("cpu") for k, v in W.items()}
+    from oracle import accept, dnc, drafter as od
+    wl, sh = S.wl, S.sh
+    Wc = {k: v.detach().to("cpu") for k, v in S.W.items()}
+    vl = S.vlogits
     t, seqs, lens = 0.0, 0, []
     while seqs < min(max_seqs, wl.batch) and t < min_s:
         i = seqs
-        h = hidden[i].to("cpu")
-        C = int(ctx[i] + new[i])
-        kv = [od.context_kv(sh, Wc, l, h[:C]) for l in range(sh.n_layers)]
-        toks = tokens[i].to("cpu").numpy()
-        tl = tlogits[i: i + 1].to("cpu").numpy()
-        vd = v_drafts[i: i + 1].to("cpu").numpy()
+        C, n = int(S.ctx[i]), int(S.new[i])
+        toks = S.tokens[i].to("cpu").numpy()
+        if wl.ctx_source == "hidden":
+            h = S.hidden[i].to("cpu")
+            cached = [od.context_kv(sh, Wc, l, h[:C]) for l in range(sh.n_layers)]
+        else:
+            import block_diffusion_drafter_draft_amd as dbd
+            cached = [(S.kv_k[l, i, :, :C].to("cpu"),
+                       dbd.unpack_values(S.kv_v[l, i]).to("cpu")[:, :C]) for l in
+                      range(sh.n_layers)]
+        vrow = vl[i: i + 1].to("cpu").numpy()
         t0 = time.perf_counter()
+        if wl.ctx_source == "hidden" and n > 0:
+            kv = []
+            for l in range(sh.n_layers):
+                k1, v1 = od.context_kv(sh, Wc, l, h[C:C + n], pos0=C)
+                kv.append((np.concatenate([cached[l][0], k1], 1),
+                           np.concatenate([cached[l][1], v1], 1)))
+        else:
+            kv = cached
         out = od.drafter_forward(sh, Wc, toks, wl.n_anchor, ctx_kv=kv)
-        accept.verify_greedy(tl, vd)
+        d = dnc.sample_drafts(out["logits"].astype(np.float32)[None], wl.n_drafts,
+                              wl.temperature, 7)
+        if wl.verify == "streak":
+            accept.select_streak(vrow, d)
+        else:
+            accept.verify_greedy(vrow, d[:, 0])
         t += time.perf_counter() - t0
-        assert out["logits"].shape[0] == wl.n_draft
         seqs += 1
-        lens.append(C)
+        lens.append(C + n)
+        del kv, cached
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(seqs / t, 4), "unit": "blocks/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{seqs} of {wl.batch} sequences (ctx {lens}): fp64 drafter step from the "
-                      f"cached context + greedy verify, {t:.1f} s"}
+            "kind": "oracle", **host_info(),
+            "sample": f"{seqs} of {wl.batch} sequences (context {lens}): the oracle's ingest of "
+                      f"the new positions, fp64 drafter forward from the cached context, "
+                      f"drafting and {wl.verify} verification, {t:.1f} s; cores = the BLAS "
+                      f"threads the oracle ran with"}
 
 
 if __name__ == "__main__":

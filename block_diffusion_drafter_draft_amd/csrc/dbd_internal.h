@@ -101,6 +101,7 @@ struct EpiArgs {
   int64_t ldc, c_bs;
   // attention projections
   void* q_out;          // [M, qd] element T
+  void* q_out_lo;       // optional [M, qd] low part of the bf16 pair of the rotated queries
   void* kv_k;           // cache (element T)
   void* kv_v;
   int64_t layer_off_k;  // element offset of this layer's block in the cache (QKV epilogue)
@@ -131,6 +132,7 @@ struct EpiArgs {
 // 0 .. seq_keys[n]-1 of kv head h / grp.
 struct AttnArgs {
   const void* q;        // [N*B, qd]
+  const void* q_lo;     // optional [N*B, qd]: low part of the bf16 pair of q (bf16 kernel)
   const void* kv_k;     // layer base: [N, kvh, cap, hd]
   const void* kv_v;     // layer base: [N, kvh, hd, cap]
   const int32_t* seq_keys;

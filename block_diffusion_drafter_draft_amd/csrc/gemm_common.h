@@ -226,6 +226,11 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
             rope8(crow, c, e.hd, cs + h8, v);
             if (isq) {
               store8<T>((T*)e.q_out + (int64_t)m * e.qd + n0 + c, v);
+              if (e.q_out_lo) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] -= to_f(from_f<T>(v[q]));
+                store8<T>((T*)e.q_out_lo + (int64_t)m * e.qd + n0 + c, v);
+              }
             } else {
               const int col = n0 - kbeg + c, g = col / e.hd, d = col % e.hd;
               store8<T>((T*)e.kv_k + lay + (((int64_t)n * e.kvh + g) * e.cap + pos) * e.hd + d,

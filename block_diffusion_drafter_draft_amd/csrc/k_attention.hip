@@ -29,8 +29,10 @@ __device__ __forceinline__ int vswz(int row, int c) { return c ^ ((row >> 1) & 7
 
 // NW waves (a power of two, >= the 16-row query tiles of the group); every thread stages
 // 2 * KCH * HD * 2 / (64 * NW) bytes of the next chunk in registers while the current chunk is
-// consumed from LDS.
-template <int HD, int NW>
+// consumed from LDS.  QPAIR: the queries come as a bf16 (high, low) pair and every score is the
+// sum of two MFMAs, K.Q_hi + K.Q_lo, so the scores see ~16 significant bits of the rotated
+// query instead of 8 (the keys stay bf16 as stored in the cache).
+template <int HD, int NW, bool QPAIR>
 __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KC = HD / 8;                    // 16-byte chunks per K row
   constexpr int NT = 64 * NW;
@@ -62,13 +64,19 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   const int b = rvalid ? r % a.block_len : 0, h = rvalid ? r / a.block_len : 0;
   const int64_t qrow = (int64_t)n * a.block_len + b;
   const int qcol = (g * a.grp + h) * HD;
-  bf16x8 qf[HD / 32];
+  bf16x8 qf[HD / 32], qlf[QPAIR ? HD / 32 : 1];
   {
-    const bf16* qp = (const bf16*)a.q + qrow * a.qd + qcol + (lane >> 4) * 8;
+    const int64_t qo = qrow * a.qd + qcol + (lane >> 4) * 8;
+    const bf16* qp = (const bf16*)a.q + qo;
+    const bf16* qlp = QPAIR ? (const bf16*)a.q_lo + qo : nullptr;
 #pragma unroll
     for (int ks = 0; ks < HD / 32; ++ks) {
       if (rvalid) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
       else for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.f;
+      if constexpr (QPAIR) {
+        if (rvalid) qlf[ks] = *reinterpret_cast<const bf16x8*>(qlp + ks * 32);
+        else for (int e = 0; e < 8; ++e) qlf[ks][e] = (bf16)0.f;
+      }
     }
   }
   f32x4 acc[HD / 16];
@@ -145,6 +153,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
                 *reinterpret_cast<const bf16x8*>(Ks + row1 * HD + kswz<HD>(row1, c) * 8);
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks], s1, 0, 0, 0);
+            if constexpr (QPAIR) {
+              s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qlf[ks], s0, 0, 0, 0);
+              s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qlf[ks], s1, 0, 0, 0);
+            }
           }
           // lane holds S^T[key0 + 8*(lane/16) + e][query], e = 0..7
           float sv[8];
@@ -354,12 +366,17 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int HD) {
   }
 }
 
+template <int HD, bool QP>
+static void launch_bf16_q(const AttnArgs& a, dim3 grid, int nw, hipStream_t s) {
+  if (nw <= 2) hipLaunchKernelGGL((attn_bf16_kernel<HD, 2, QP>), grid, dim3(128), 0, s, a);
+  else if (nw <= 4) hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, QP>), grid, dim3(256), 0, s, a);
+  else if (nw <= 8) hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, QP>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((attn_bf16_kernel<HD, 16, QP>), grid, dim3(1024), 0, s, a);
+}
 template <int HD>
 static void launch_bf16(const AttnArgs& a, dim3 grid, int nw, hipStream_t s) {
-  if (nw <= 2) hipLaunchKernelGGL((attn_bf16_kernel<HD, 2>), grid, dim3(128), 0, s, a);
-  else if (nw <= 4) hipLaunchKernelGGL((attn_bf16_kernel<HD, 4>), grid, dim3(256), 0, s, a);
-  else if (nw <= 8) hipLaunchKernelGGL((attn_bf16_kernel<HD, 8>), grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((attn_bf16_kernel<HD, 16>), grid, dim3(1024), 0, s, a);
+  if (a.q_lo) launch_bf16_q<HD, true>(a, grid, nw, s);
+  else launch_bf16_q<HD, false>(a, grid, nw, s);
 }
 
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s) {

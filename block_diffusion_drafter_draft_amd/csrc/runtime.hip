@@ -120,6 +120,7 @@ struct DraftBufs {
   size_t x_off;         // byte offset of x in the workspace
   void* xn;
   void* q;
+  void* q_lo;           // low part of the rotated queries' bf16 pair (bf16 drafters)
   void* attn;
   void* act;
   void* xn_lo;          // low parts of the bf16 pairs (act_pairs only, else null)
@@ -229,6 +230,7 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
   t.x_off = c.last;
   t.xn = c.take<char>(M * d.hidden * es);
   t.q = c.take<char>(M * qd * es);
+  t.q_lo = d.dtype == DBD_BF16 ? (void*)c.take<char>(M * qd * es) : nullptr;
   t.attn = c.take<char>(M * qd * es);
   t.act = c.take<char>(M * d.ffn * es);
   if (d.dtype == DBD_BF16 && d.act_pairs) {
@@ -587,6 +589,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       EpiArgs e{};
       e.kind = EPI_QKV;
       e.q_out = b.q;
+      e.q_out_lo = b.q_lo;
       e.kv_k = kv_k;
       e.kv_v = kv_v;
       e.layer_off_k = (int64_t)l * layer_elems;
@@ -605,6 +608,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
     {
       AttnArgs a{};
       a.q = b.q;
+      a.q_lo = b.q_lo;
       a.kv_k = (const char*)kv_k + (int64_t)l * layer_elems * es;
       a.kv_v = (const char*)kv_v + (int64_t)l * layer_elems * es;
       a.seq_keys = b.meta.seq_keys;
