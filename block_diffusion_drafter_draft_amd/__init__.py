@@ -71,6 +71,8 @@ def lib():
             "dbd_verify_workspace_bytes": (_i32, [_i32, _i32, _i32, _c.POINTER(_sz)]),
             "verify_greedy": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                      _vp, _sz, _vp]),
+            "verify_greedy_noalloc": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                             _vp, _vp, _vp]),
             "dbd_verify_sample_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32,
                                                          _c.POINTER(_sz)]),
             "verify_sample": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32,
@@ -224,6 +226,21 @@ def verify_greedy(target_logits, draft_tokens, n_accepted, bonus, committed, wor
         _ptr(target_logits), _ptr(draft_tokens), draft_tokens.stride(0), N, D, R, V,
         _ptr(n_accepted), _ptr(bonus), _ptr(committed), _ptr(row_flags), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, target_logits)))
+
+
+STATIC_SCRATCH_BYTES = 4 << 20      # DBD_STATIC_SCRATCH_BYTES
+
+
+def verify_greedy_noalloc(target_logits, draft_tokens, n_accepted, bonus, committed,
+                          row_flags=None, stream=None):
+    """verify_greedy without a workspace: the library's static device scratch holds the
+    partials (calls that overlap on one GPU race)."""
+    N, R, V = target_logits.shape
+    D = draft_tokens.shape[-1]
+    _check(lib().verify_greedy_noalloc(
+        _ptr(target_logits), _ptr(draft_tokens), draft_tokens.stride(0), N, D, R, V,
+        _ptr(n_accepted), _ptr(bonus), _ptr(committed), _ptr(row_flags),
+        _stream(stream, target_logits)))
 
 
 def verify_sample_workspace_bytes(batch, n_draft, n_rows, vocab) -> int:

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -774,11 +775,10 @@ int dbd_verify_workspace_bytes(int32_t batch, int32_t n_rows, int32_t vocab, siz
   return DBD_OK;
 }
 
-int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32_t draft_stride,
-                  int32_t batch, int32_t n_draft, int32_t n_rows, int32_t vocab,
-                  int32_t* n_accepted, int32_t* bonus, int32_t* committed, int32_t* row_flags,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+static int check_verify_args(const float* target_logits, const int32_t* draft_tokens,
+                             int32_t draft_stride, int32_t batch, int32_t n_draft,
+                             int32_t n_rows, int32_t vocab, const int32_t* n_accepted,
+                             const int32_t* bonus, const int32_t* committed) {
   if (!target_logits || !draft_tokens || !n_accepted || !bonus || !committed)
     return fail(DBD_ERR_ARG, "a required device pointer is NULL");
   if (batch < 1 || n_draft < 1 || vocab < 2 || vocab >= (1 << 18))
@@ -788,16 +788,21 @@ int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32
   if (n_rows != n_draft && n_rows != n_draft + 1)
     return fail(DBD_ERR_SHAPE, "n_rows %d must be n_draft or n_draft + 1", n_rows);
   if (draft_stride < n_draft) return fail(DBD_ERR_SHAPE, "draft_stride < n_draft");
-  if (!workspace || ((uintptr_t)workspace % kAlign))
-    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  return DBD_OK;
+}
+
+// The launches of verify_greedy on a scratch region of at least carve_verify() bytes.  Every
+// partial the finalize kernel reads is written first by the argmax kernel of the same call, so
+// the region needs no clearing.
+static int run_verify_greedy(const float* target_logits, const int32_t* draft_tokens,
+                             int32_t draft_stride, int32_t batch, int32_t n_draft,
+                             int32_t n_rows, int32_t vocab, int32_t* n_accepted, int32_t* bonus,
+                             int32_t* committed, int32_t* row_flags, void* scratch_mem,
+                             hipStream_t st) {
   const int rows = batch * n_rows;
-  const size_t need = carve_verify(rows, vocab, nullptr, nullptr, nullptr, nullptr);
-  if (workspace_bytes < need)
-    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
   float* pv;
   int32_t *pi, *pf;
-  carve_verify(rows, vocab, (char*)workspace, &pv, &pi, &pf);
-  hipStream_t st = (hipStream_t)stream;
+  carve_verify(rows, vocab, (char*)scratch_mem, &pv, &pi, &pf);
   const int ch = vocab_chunk();
   HIP_STAGE(DBD_STAGE_VERIFY, st, launch_argmax_partial(target_logits, rows, vocab, ch, pv, pi,
                                                         pf, st));
@@ -805,6 +810,24 @@ int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32
                                  batch, n_draft, n_rows, n_accepted, bonus, committed, row_flags,
                                  st));
   return DBD_OK;
+}
+
+int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32_t draft_stride,
+                  int32_t batch, int32_t n_draft, int32_t n_rows, int32_t vocab,
+                  int32_t* n_accepted, int32_t* bonus, int32_t* committed, int32_t* row_flags,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_verify_args(target_logits, draft_tokens, draft_stride, batch, n_draft, n_rows,
+                             vocab, n_accepted, bonus, committed);
+  if (rc) return rc;
+  if (!workspace || ((uintptr_t)workspace % kAlign))
+    return fail(DBD_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+  const size_t need = carve_verify(batch * n_rows, vocab, nullptr, nullptr, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  return run_verify_greedy(target_logits, draft_tokens, draft_stride, batch, n_draft, n_rows,
+                           vocab, n_accepted, bonus, committed, row_flags, workspace,
+                           (hipStream_t)stream);
 }
 
 // Workspace of verify_sample: argmax partials, integer weight sums, row max / argmax of the
@@ -1211,6 +1234,71 @@ int dbd_gemm_nt(int32_t dtype, const void* A, const void* Bm, float* C, int32_t 
   }
   HIP_TRY(launch_gemm(dtype, g, e, 1, st, tile_cfg, split));
   return DBD_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ verify without a workspace
+// verify_greedy_noalloc keeps its argmax partials in this file-scope device array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: kernels get the address
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kStaticScratchBytes = DBD_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];      // per device: the array's device address
+
+// The current device's scratch address; `stream` must belong to the current device.
+int static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(DBD_ERR_UNSUPPORTED, "device %d: static scratch tracks devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    HIP_TRY(hipStreamGetDevice(stream, &sdev));
+    if (sdev != dev)
+      return fail(DBD_ERR_ARG, "stream belongs to device %d but device %d is current", sdev,
+                  dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || ((uintptr_t)p % kAlign))
+      return fail(DBD_ERR_HIP, "static scratch address %p is not 256-byte aligned", p);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DBD_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int verify_greedy_noalloc(const float* target_logits, const int32_t* draft_tokens,
+                          int32_t draft_stride, int32_t batch, int32_t n_draft, int32_t n_rows,
+                          int32_t vocab, int32_t* n_accepted, int32_t* bonus, int32_t* committed,
+                          int32_t* row_flags, void* stream) {
+  g_err.clear();
+  int rc = check_verify_args(target_logits, draft_tokens, draft_stride, batch, n_draft, n_rows,
+                             vocab, n_accepted, bonus, committed);
+  if (rc) return rc;
+  const size_t need = carve_verify(batch * n_rows, vocab, nullptr, nullptr, nullptr, nullptr);
+  if (need > kStaticScratchBytes)
+    return fail(DBD_ERR_WORKSPACE, "verify_greedy_noalloc: %d rows over vocab %d need %zu bytes "
+                "of scratch, above the static limit of %zu bytes (use verify_greedy with a "
+                "workspace)", batch * n_rows, vocab, need, kStaticScratchBytes);
+  void* mem = nullptr;
+  rc = static_scratch((hipStream_t)stream, &mem);
+  if (rc) return rc;
+  return run_verify_greedy(target_logits, draft_tokens, draft_stride, batch, n_draft, n_rows,
+                           vocab, n_accepted, bonus, committed, row_flags, mem,
+                           (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -202,6 +202,26 @@ int verify_greedy(const float* target_logits, const int32_t* draft_tokens, int32
                   int32_t* n_accepted, int32_t* bonus, int32_t* committed, int32_t* row_flags,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the library's static device scratch (see verify_greedy_noalloc). */
+#define DBD_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/* verify_greedy_noalloc: verify_greedy with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and validation as verify_greedy; the argmax
+ * partials live in a static device array of DBD_STATIC_SCRATCH_BYTES that each GPU holds from
+ * the library's first use on it until the process ends.  The call allocates nothing.
+ *
+ * Limit: batch * n_rows * ceil(vocab / 4096) row-chunk partials of 12 bytes (each of the three
+ * arrays rounded up to 256 bytes) must fit the array, e.g. 512 rows over a 151,936-token vocab
+ * (233 KB); larger calls return DBD_ERR_WORKSPACE.  The stream must belong to the current device
+ * (DBD_ERR_ARG otherwise).  Every call on one GPU uses the same array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must be serialised by the caller.  No
+ * part of the array needs to start cleared: a call writes every partial it reads. */
+int verify_greedy_noalloc(const float* target_logits, const int32_t* draft_tokens,
+                          int32_t draft_stride, int32_t batch, int32_t n_draft, int32_t n_rows,
+                          int32_t vocab, int32_t* n_accepted, int32_t* bonus, int32_t* committed,
+                          int32_t* row_flags, void* stream);
+
 /* Workspace size (host) for verify_sample. */
 int dbd_verify_sample_workspace_bytes(int32_t batch, int32_t n_draft, int32_t n_rows,
                                       int32_t vocab, size_t* bytes /* host out */);

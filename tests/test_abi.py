@@ -204,6 +204,24 @@ def test_verify_validation(args, code):
     assert rc == code
 
 
+def test_verify_noalloc_validation():
+    """verify_greedy_noalloc validates like verify_greedy and rejects, before any HIP call, a call
+    whose partials exceed the static scratch (the size is checked here against the workspace
+    query first, so the rejected case really is over the limit)."""
+    L = dbd.lib()
+    fake = 1 << 20
+    N, D, R, V = 128, 64, 65, (1 << 18) - 1
+    assert dbd.verify_workspace_bytes(N, R, V) > dbd.STATIC_SCRATCH_BYTES
+    rc = L.verify_greedy_noalloc(fake, fake, D, N, D, R, V, fake, fake, fake, None, None)
+    assert rc == -4 and b"static limit" in L.dbd_last_error()
+    assert L.verify_greedy_noalloc(fake, fake, 3, 2, 3, 5, 100, fake, fake, fake, None,
+                                   None) == -2
+    assert L.verify_greedy_noalloc(None, fake, 3, 2, 3, 3, 100, fake, fake, fake, None,
+                                   None) == -1
+    assert L.verify_greedy_noalloc(fake, fake, 65, 2, 65, 66, 100, fake, fake, fake, None,
+                                   None) == -5
+
+
 def test_select_validation():
     L = dbd.lib()
     fake = 1 << 20
