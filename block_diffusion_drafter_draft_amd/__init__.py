@@ -98,6 +98,7 @@ def lib():
             "dbd_gemm_nt": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
                                    _i32, _vp, _sz, _vp]),
             "dbd_gemm_override": (_i32, [_i32, _i32, _i32]),
+            "dbd_attn_override": (_i32, [_i32, _i32]),
             "dbd_timing_enable": (_i32, [_i32]),
             "dbd_timing_reset": (_i32, []),
             "dbd_timing_read": (_i32, [_i32, _c.POINTER(_c.c_double), _c.POINTER(_i64)]),
@@ -359,6 +360,12 @@ def gemm_override(stage, tile_cfg=-1, split=0):
     """Replace the tile / split-K choice of one draft_block GEMM stage (a name of STAGES starting
     with "gemm_"); -1 / 0 restore the library's choice.  Set before sizing the workspace."""
     _check(lib().dbd_gemm_override(STAGES.index(stage), int(tile_cfg), int(split)))
+
+
+def attn_override(split=0, waves=0):
+    """Replace the attention kernel's keys per split and waves per workgroup (0, 0: the
+    library's choice).  Set before sizing the workspace."""
+    _check(lib().dbd_attn_override(int(split), int(waves)))
 
 
 # Stage order of DBD_STAGE_* in include/dbd.h.

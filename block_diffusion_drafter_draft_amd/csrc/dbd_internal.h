@@ -142,6 +142,7 @@ struct AttnArgs {
   float2* part_ml;      // [N, kvh, S_max, R] (running max in log2 units, sum)
   int batch, kvh, grp, block_len, cap, qd, s_max, split;
   float scale_log2;     // log2(e) / sqrt(hd)
+  int waves;            // bf16 kernel: waves per workgroup (16 query rows each), 0 = choose
 };
 
 // ---------------------------------------------------------------- launchers (one per TU)

@@ -384,7 +384,11 @@ hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s)
   const int R = a.block_len * a.grp;
   dim3 cgrid(ceil_div(R, 4), a.kvh, a.batch);
   if (dtype == 1) {
-    const int nw = std::min(16, ceil_div(R, 16));
+    // waves per workgroup: at most four (64 query rows) unless overridden; the kernel template
+    // takes the next power of two, and the grid's row blocks use the same count
+    const int need = ceil_div(R, 16);
+    int nw = a.waves > 0 ? std::min(a.waves, need) : std::min(4, need);
+    nw = nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : 16;
     grid.y = a.kvh * ceil_div(R, 16 * nw);
     if (hd == 128) launch_bf16<128>(a, grid, nw, s);
     else launch_bf16<64>(a, grid, nw, s);

@@ -281,10 +281,15 @@ static void launch_cfg(int cfg, const GemmArgs& a, const EpiArgs& e, int batch, 
   }
 }
 
+// The register-staged 256-row tiles (14-16) take a bf16-pair A operand as 256 rows (high part,
+// then low part) when M <= 128.
+static bool pair_rows(int cfg, int M) { return cfg >= 14 && cfg <= 16 && M <= 128; }
+
 // The configuration a bf16-pair launch of `cfg` really uses (the pair doubles the A operand's
-// LDS and registers, so only the smaller tiles take it).
-static int pair_cfg(int cfg) {
+// LDS and registers, so only the smaller tiles take it, or the 256-row tiles as pair rows).
+static int pair_cfg(int cfg, int M) {
   if (is_skinny(cfg)) return cfg;                 // the skinny tiles take the pair themselves
+  if (pair_rows(cfg, M)) return cfg;
   if (is_deep(cfg)) return 10;
   if (cfg == 3 || cfg == 5) return 5;
   return 4;
@@ -335,6 +340,10 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
   // projection); 32-row tiles for Q/K/V even at 64 rows
   if (M <= 32 || (M <= 64 && (kind == EPI_QKV || kind == EPI_CTXKV))) return 18;
   if (M <= 64) return 17;
+  // a bf16 pair on at most 128 rows: the register-staged 256 x 192 tile as pair rows for gate/up
+  // (one round of 198 units at the SpecDiff-2 shape; 2.37 against 3.76 ms per call for the
+  // 128 x 128 tile)
+  if (pair && M <= 128 && gateup) return 15;
   if (M >= 64 && (pair || kind == EPI_QKV || kind == EPI_CTXKV)) return 10;
   if (!pair && kind != EPI_QKV && kind != EPI_CTXKV && M >= 128) {
     // the register-staged forms of the 256 x 256 and 256 x 192 tiles (14, 15)
@@ -414,6 +423,9 @@ static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gate
   double best_t = model_us(kind, base, M, N, K, batch, 1, pair);
   static const int cand[6] = {1, 2, 3, 4, 6, 8};
   for (int cfg : {10, 16}) {
+    // (the 256 x 128 tile as pair rows measured slower than the 128 x 128 tile with its split
+    // on the SpecDiff-2 shape's Q/K/V, O and down projections: 0.97, 0.84, 1.79 ms per call
+    // against 0.82, 0.73, 1.66)
     if (cfg == 16 && (pair || M < 192)) continue;
     for (int S : cand) {
       if (cfg == 10 ? K / 32 / S < 4 : K / 64 / S < 2) break;
@@ -446,7 +458,7 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
   if (n128 && kCfgBN[cfg] != 128)
     cfg = cfg >= 14 ? 16 : cfg >= 11 ? 13 : is_deep(cfg) ? (kCfgBM[cfg] == 256 ? 8 : 10)
                                         : (kCfgBM[cfg] == 256 ? 1 : 4);
-  if (pair) cfg = pair_cfg(cfg);
+  if (pair) cfg = pair_cfg(cfg, M);
   auto nvirt = [&](int c) { return gateup ? ceil_div(F, kCfgBN[c] / 2) * kCfgBN[c] : N; };
   p.cfg = cfg;
   p.bn = kCfgBN[cfg];

@@ -405,25 +405,35 @@ __global__ __launch_bounds__(512) void gemm_w8_kernel(GemmArgs a, EpiArgs e) {
 // bytes per CU that the DMA path does.  Two register sets alternate: stage kt+2 is loaded while
 // stage kt is computed and stage kt+1 is written to LDS after it.  All LDS traffic is ordinary
 // compiled code, so the compiler places every wait.
-template <int BN>
+// WGM x (8 / WGM) wave grid: 2 x 4 gives each wave 128 x BN/4, 4 x 2 gives 64 x BN/2.  Every k
+// stage each wave reads its A and B fragments from LDS, (WTM + WTN) rows of 128 bytes: the
+// squarer 64 x BN/2 wave tile reads fewer bytes per MFMA (BN 128: 128 KB per stage for the
+// workgroup instead of 160 KB).
+template <int BN, int WGM = 2>
 struct W8RCfg {
   static constexpr int BM = 256, KS = 64, NT = 512, NW = 8, ROWB = 128;
+  static constexpr int WGN = NW / WGM;
   static constexpr int ABYTES = BM * ROWB, BBYTES = BN * ROWB, STAGE = ABYTES + BBYTES;
   static constexpr int CH = STAGE / 16 / NT;              // 16-byte chunks per thread per stage
-  static constexpr int WTM = 128, WTN = BN / 4, MI = 8, NI = WTN / 16;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 16, NI = WTN / 16;
   static constexpr int TM = BN == 192 ? 128 : 64;
   static constexpr int CBYTES = TM * (BN + 4) * 4;
   static constexpr int SMEM = 2 * STAGE > CBYTES ? 2 * STAGE : CBYTES;
   static_assert(STAGE % (16 * NT) == 0 && WTN % 16 == 0, "tile shape");
 };
 
-template <int BN, int KIND>
+// PR (pair rows, M <= 128 with a bf16-pair A operand): tile rows 0-127 are the rows of A's high
+// part and rows 128-255 the same rows of its low part, so the waves of the lower half of the
+// wave grid compute A_lo . B^T; the two halves are added per output row before the epilogue (and
+// in the split-K reduction).  The pair then costs what a 256-row tile costs on 128 rows, with
+// the tile's full arithmetic intensity on the weights.
+template <int BN, int KIND, int WGM, bool PR>
 __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
-  using C = W8RCfg<BN>;
+  using C = W8RCfg<BN, WGM>;
   constexpr int BM = C::BM, KS = C::KS;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int z = blockIdx.z;
   const int M = a.M, N = a.N, K = a.K;
   const int S = a.split > 1 ? a.split : 1;
@@ -445,9 +455,14 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
     const int c = tid + C::NT * q, row = c >> 3, ch = c & 7;
     const bool isA = row < BM;
     const int r = isA ? row : row - BM;
-    src[q] = (isA ? (const bf16*)a.A + (int64_t)z * a.a_bs + (int64_t)min(m0 + r, M - 1) * a.lda
-                  : brow_ptr<bf16, BN>(bm, min(n0 + r, N - 1), z)) +
-             (int64_t)kb * KS + ch * 8;
+    const bf16* arow;
+    if constexpr (PR)
+      arow = (const bf16*)(r < BM / 2 ? a.A : a.A2) + (int64_t)z * a.a_bs +
+             (int64_t)min(r % (BM / 2), M - 1) * a.lda;
+    else
+      arow = (const bf16*)a.A + (int64_t)z * a.a_bs + (int64_t)min(m0 + r, M - 1) * a.lda;
+    src[q] = (isA ? arow : brow_ptr<bf16, BN>(bm, min(n0 + r, N - 1), z)) + (int64_t)kb * KS +
+             ch * 8;
     dst[q] = (uint32_t)(row * C::ROWB + ((ch ^ swz(row)) * 16));
   }
   u32x4 stA[C::CH], stB[C::CH];
@@ -519,24 +534,32 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
   auto store_tile = [&](auto get) __attribute__((always_inline)) {
     float* Cs = (float*)smem;
     constexpr int CS_LD = BN + 4;
+    constexpr int OUT_ROWS = PR ? BM / 2 : BM;          // output rows of the tile
 #pragma unroll
-    for (int h = 0; h < BM / C::TM; ++h) {
+    for (int h = 0; h < OUT_ROWS / C::TM; ++h) {
+      // with PR the waves holding low-part rows add onto the high part's rows after a barrier
 #pragma unroll
-      for (int i = 0; i < C::MI; ++i) {
-        const int row0 = wm * C::WTM + i * 16;
-        if (row0 / C::TM != h) continue;
+      for (int part = 0; part < (PR ? 2 : 1); ++part) {
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j) {
-          const f32x4 v = get(i, j);
+        for (int i = 0; i < C::MI; ++i) {
+          const int row0 = wm * C::WTM + i * 16;
+          if (PR && (row0 >= BM / 2) != (part == 1)) continue;
+          const int orow0 = PR ? row0 % (BM / 2) : row0;
+          if (orow0 / C::TM != h) continue;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = row0 - h * C::TM + (lane >> 4) * 4 + r;
-            const int col = wn * C::WTN + j * 16 + (lane & 15);
-            Cs[row * CS_LD + col] = v[r];
+          for (int j = 0; j < C::NI; ++j) {
+            const f32x4 v = get(i, j);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = orow0 - h * C::TM + (lane >> 4) * 4 + r;
+              const int col = wn * C::WTN + j * 16 + (lane & 15);
+              if (part == 0) Cs[row * CS_LD + col] = v[r];
+              else Cs[row * CS_LD + col] += v[r];
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
       run_epilogue<bf16, C::TM, BN, KIND, C::NT>(e, Cs, m0 + h * C::TM, n0, tn, z, M, N);
       __syncthreads();
     }
@@ -783,7 +806,9 @@ struct ReduceCfg {
   static constexpr int TM = BN == 192 ? 64 : 32, NT = 256, CS_LD = BN + 4;
 };
 
-template <int BM, int BN, int WGM, int WGN, int KIND>
+// PR: the partials come from a pair-rows tile (gemm_w8r_kernel): output row r of the tile is the
+// sum of tile rows r and r + BM/2, added here per split.
+template <int BM, int BN, int WGM, int WGN, int KIND, bool PR = false>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 16, NI = WTN / 16;
   constexpr int NW = WGM * WGN, FR = MI * NI * 64;
@@ -800,10 +825,12 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
   const int tm = t % tiles_m, tn = t / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN, r0 = strip * TM;
   if (m0 + r0 >= M) return;
+  if (PR && r0 >= BM / 2) return;
   const int tile = (z * tiles_n + tn) * tiles_m + tm;
   const int wm = r0 / WTM, i0 = (r0 % WTM) / 16;
+  const int wl = (r0 + BM / 2) / WTM, il = ((r0 + BM / 2) % WTM) / 16;   // PR: low-part rows
   const f32x4* part = reinterpret_cast<const f32x4*>(a.part) + (int64_t)tile * S * NW * FR;
-  int off[UPT];
+  int off[UPT], offl[PR ? UPT : 1];
   f32x4 v[UPT];
 #pragma unroll
   for (int q = 0; q < UPT; ++q) {
@@ -811,11 +838,18 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
     const int j = rest % NI, wn = (rest / NI) % WGN, di = rest / (NI * WGN);
     off[q] = (wm * WGN + wn) * FR + ((i0 + di) * NI + j) * 64 + lane;
     v[q] = part[off[q]];
+    if constexpr (PR) {
+      offl[q] = (wl * WGN + wn) * FR + ((il + di) * NI + j) * 64 + lane;
+      v[q] += part[offl[q]];
+    }
   }
   for (int sp = 1; sp < S; ++sp) {
     const f32x4* ps = part + (int64_t)sp * NW * FR;
 #pragma unroll
-    for (int q = 0; q < UPT; ++q) v[q] += ps[off[q]];
+    for (int q = 0; q < UPT; ++q) {
+      v[q] += ps[off[q]];
+      if constexpr (PR) v[q] += ps[offl[q]];
+    }
   }
 #pragma unroll
   for (int q = 0; q < UPT; ++q) {
@@ -902,20 +936,21 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e)
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int KIND>
+template <int BM, int BN, int WGM, int WGN, int KIND, bool PR = false>
 static void launch_reduce(const GemmArgs& a, const EpiArgs& e, int batch, hipStream_t s) {
   const int grid = ceil_div(a.M, BM) * ceil_div(a.N, BN) * (BM / ReduceCfg<BN>::TM);
-  hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WGM, WGN, KIND>), dim3(grid, 1, batch),
+  hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WGM, WGN, KIND, PR>), dim3(grid, 1, batch),
                      dim3(ReduceCfg<BN>::NT), 0, s, a, e);
 }
 
-template <int BN, int KIND>
+template <int BN, int KIND, int WGM, bool PR = false>
 static void launch_w8r(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   if (a.gateup) a.N = ceil_div(a.seg[0].n1 - a.seg[0].n0, BN / 2) * BN;
   const int S = a.split > 1 ? a.split : 1;
   const int units = ceil_div(a.M, 256) * ceil_div(a.N, BN) * S;
-  hipLaunchKernelGGL((gemm_w8r_kernel<BN, KIND>), dim3(units, 1, batch), dim3(512), 0, s, a, e);
-  if (S > 1) launch_reduce<256, BN, 2, 4, KIND>(a, e, batch, s);
+  hipLaunchKernelGGL((gemm_w8r_kernel<BN, KIND, WGM, PR>), dim3(units, 1, batch), dim3(512),
+                     0, s, a, e);
+  if (S > 1) launch_reduce<256, BN, WGM, 8 / WGM, KIND, PR>(a, e, batch, s);
 }
 
 template <int MT, int KIND, bool SPLITA>
@@ -965,12 +1000,25 @@ void launch_deep_cfg(int cfg, GemmArgs a, const EpiArgs& e, int batch, hipStream
   } else if (cfg == 18) {
     launch_skinny<32, KIND, SPLITA>(a, e, batch, s);
   } else if constexpr (SPLITA) {
-    launch_deep<128, 128, 6, KIND, true>(a, e, batch, s);
+    // the register-staged tiles take a pair as rows (A high part, then low part) for M <= 128
+    if (cfg >= 14 && cfg <= 16 && a.M <= 128) {
+      if constexpr (KIND == EPI_QKV || KIND == EPI_CTXKV) {
+        launch_w8r<128, KIND, 4, true>(a, e, batch, s);
+      } else {
+        switch (cfg) {
+          case 14: launch_w8r<256, KIND, 2, true>(a, e, batch, s); break;
+          case 15: launch_w8r<192, KIND, 4, true>(a, e, batch, s); break;
+          default: launch_w8r<128, KIND, 4, true>(a, e, batch, s); break;
+        }
+      }
+    } else {
+      launch_deep<128, 128, 6, KIND, true>(a, e, batch, s);
+    }
   } else if constexpr (KIND == EPI_QKV || KIND == EPI_CTXKV) {
     switch (cfg) {
       case 8: launch_deep<256, 128, 3, KIND, false>(a, e, batch, s); break;
       case 11: case 12: case 13: launch_w8<128, 3, 64, KIND>(a, e, batch, s); break;
-      case 14: case 15: case 16: launch_w8r<128, KIND>(a, e, batch, s); break;
+      case 14: case 15: case 16: launch_w8r<128, KIND, 4>(a, e, batch, s); break;
       default: launch_deep<128, 128, 4, KIND, false>(a, e, batch, s); break;
     }
   } else {
@@ -980,9 +1028,9 @@ void launch_deep_cfg(int cfg, GemmArgs a, const EpiArgs& e, int batch, hipStream
       case 11: launch_w8<256, 2, 64, KIND>(a, e, batch, s); break;
       case 12: launch_w8<192, 2, 64, KIND>(a, e, batch, s); break;
       case 13: launch_w8<128, 3, 64, KIND>(a, e, batch, s); break;
-      case 14: launch_w8r<256, KIND>(a, e, batch, s); break;
-      case 15: launch_w8r<192, KIND>(a, e, batch, s); break;
-      case 16: launch_w8r<128, KIND>(a, e, batch, s); break;
+      case 14: launch_w8r<256, KIND, 2>(a, e, batch, s); break;
+      case 15: launch_w8r<192, KIND, 4>(a, e, batch, s); break;
+      case 16: launch_w8r<128, KIND, 4>(a, e, batch, s); break;
       default: launch_deep<128, 128, 4, KIND, false>(a, e, batch, s); break;
     }
   }

@@ -87,23 +87,39 @@ struct Carver {
 
 int elem_size(int dtype) { return dtype == DBD_BF16 ? 2 : 4; }
 
+// Attention tuning overrides (dbd_attn_override): keys per split and waves per workgroup of the
+// bf16 kernel, 0 = the library's choice.
+static int g_attn_split = 0, g_attn_waves = 0;
+
+// Row blocks per (sequence, kv head) of the bf16 kernel for R query rows per kv head: the
+// kernel takes at most four waves (64 rows) per workgroup, so a wide group (many query heads per
+// kv head, or a long block) is spread over several workgroups that read the same keys rather
+// than loading all its queries and writing all its split partials in one.  Measured on the
+// SpecDiff-2-shaped drafter (224 rows per kv head): attention 1.50 -> 0.83 ms per call against
+// one 16-wave workgroup per group.
+static int attn_row_blocks(int dtype, int R) {
+  return dtype == DBD_BF16 ? ceil_div(R, 64) : 1;
+}
+
 // Keys per attention split: the largest of 512 (256 for the fp32 kernel, which gives each key
 // of a split its own thread), 256, 128 and 64 that still gives the launch at least 512
 // workgroups over the capacity.  Short contexts and small batches are then spread over many
 // workgroups instead of a few that walk every chunk of their keys in turn.
-int attn_split(int dtype, int cap, int kvh, int batch) {
+int attn_split(int dtype, int cap, int kvh, int batch, int R) {
+  if (dtype == DBD_BF16 && g_attn_split > 0) return g_attn_split;
   int s = dtype == DBD_BF16 ? 512 : 256;
-  while (s > 64 && (int64_t)ceil_div(cap, s) * kvh * batch < 512) s /= 2;
+  const int64_t rb = attn_row_blocks(dtype, R);
+  while (s > 64 && (int64_t)ceil_div(cap, s) * kvh * batch * rb < 512) s /= 2;
   return s;
 }
 
 // (sequence, split) pairs of attention partials to reserve for up to `batch` sequences.  The
 // split shrinks with the batch, so the largest batch does not always need the most pairs; the
 // maximum over 1 .. batch keeps a workspace sized for a batch enough for every smaller one.
-static int64_t attn_partial_pairs(int dtype, int cap, int kvh, int batch) {
+static int64_t attn_partial_pairs(int dtype, int cap, int kvh, int batch, int R) {
   int64_t m = 0;
   for (int n = 1; n <= batch; ++n)
-    m = std::max(m, (int64_t)n * ceil_div(cap, attn_split(dtype, cap, kvh, n)));
+    m = std::max(m, (int64_t)n * ceil_div(cap, attn_split(dtype, cap, kvh, n, R)));
   return m;
 }
 
@@ -239,9 +255,9 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
     t.attn_lo = c.take<char>(M * qd * es);
     t.act_lo = c.take<char>(M * d.ffn * es);
   }
-  t.split = attn_split(d.dtype, cap, d.n_kv_heads, N);
+  t.split = attn_split(d.dtype, cap, d.n_kv_heads, N, R);
   t.s_max = ceil_div(cap, t.split);
-  const int64_t pairs = at_most ? attn_partial_pairs(d.dtype, cap, d.n_kv_heads, N)
+  const int64_t pairs = at_most ? attn_partial_pairs(d.dtype, cap, d.n_kv_heads, N, R)
                                 : (int64_t)N * t.s_max;
   t.part_o = c.take<float>(pairs * d.n_kv_heads * R * d.head_dim);
   t.part_ml = c.take<float2>(pairs * d.n_kv_heads * R);
@@ -367,6 +383,17 @@ int dbd_gemm_override(int32_t stage, int32_t tile_cfg, int32_t split) {
     return fail(DBD_ERR_ARG, "split %d out of [0, %d]", split, kMaxGemmSplit);
   g_ov_cfg[stage] = tile_cfg;
   g_ov_split[stage] = split;
+  return DBD_OK;
+}
+
+int dbd_attn_override(int32_t split, int32_t waves) {
+  g_err.clear();
+  if (split < 0 || split % 64 || split > 4096)
+    return fail(DBD_ERR_ARG, "split %d: 0 or a multiple of 64 up to 4096", split);
+  if (waves != 0 && waves != 2 && waves != 4 && waves != 8 && waves != 16)
+    return fail(DBD_ERR_ARG, "waves %d: 0, 2, 4, 8 or 16", waves);
+  g_attn_split = split;
+  g_attn_waves = waves;
   return DBD_OK;
 }
 
@@ -626,6 +653,7 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       a.s_max = b.s_max;
       a.split = b.split;
       a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      a.waves = g_attn_waves;
       HIP_STAGE(DBD_STAGE_ATTN, st, launch_attention(d.dtype, hd, a, st));
     }
     {

@@ -339,6 +339,69 @@ def test_query_groups_beyond_one_workgroup_match_oracle():
     _compare(case, logits, range(wl.batch), [])
 
 
+@pytest.mark.parametrize("split,waves", [(64, 2), (128, 16), (1024, 4), (2048, 8), (192, 4)])
+def test_attention_split_and_waves_overrides_match_oracle(split, waves):
+    """The attention kernel's split (keys per workgroup, one to many splits per sequence) and
+    waves per workgroup (one or several row blocks per kv head) chosen by the tuning override:
+    320 query rows per kv head, contexts of 90-130 positions."""
+    sh = synth.DrafterShape(hidden=512, n_q_heads=16, n_kv_heads=2, head_dim=64, ffn=1024,
+                            n_layers=2, n_target_layers=2, vocab=2048, dtype="bf16")
+    wl = synth.Workload(name="attn-override", shape=sh, batch=3, block_len=40, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=90, ctx_hi=130, ctx_source="hidden",
+                        verify="greedy", verify_rows=40, planted_alpha=0.8, fixed_new=8)
+    print(f"draft_block workload=attn-override split={split} waves={waves}", flush=True)
+    dbd.attn_override(split, waves)
+    try:
+        case = Case(wl, dev=DEV)
+        case.fill_cache()
+        drafts, logits, status = case.step()
+        torch.cuda.synchronize()
+        assert torch.all(status == 0)
+        _check_drafts_property(case, drafts, logits)
+        _compare(case, logits, range(wl.batch), [], residuals=False)
+    finally:
+        dbd.attn_override(0, 0)
+
+
+PAIR_ROW_OVERRIDES = [
+    {},
+    {"gemm_qkv": (16, 3), "gemm_o": (16, 2), "gemm_gateup": (15, 2), "gemm_down": (16, 4),
+     "gemm_lmhead": (14, 1)},
+    {"gemm_qkv": (16, 1), "gemm_o": (14, 3), "gemm_gateup": (14, 1), "gemm_down": (15, 2),
+     "gemm_lmhead": (16, 2)},
+]
+
+
+@pytest.mark.parametrize("batch", [5, 8])
+@pytest.mark.parametrize("ov", range(len(PAIR_ROW_OVERRIDES)))
+def test_pair_rows_tiles_match_oracle(batch, ov):
+    """bf16 activation pairs on 80 and 128 block rows: the register-staged 256-row tiles take
+    the pair as rows (high part, low part) and add them per output row, unsplit and with split K
+    (the reduction folds the two halves), under every projection's epilogue (rotation and cache
+    write, residual, SwiGLU, LM-head argmax)."""
+    sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1536,
+                            n_layers=2, n_target_layers=2, vocab=3000, dtype="bf16")
+    wl = synth.Workload(name="pair-rows", shape=sh, batch=batch, block_len=16, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=60, ctx_hi=140, ctx_source="hidden",
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=4,
+                        act_pairs=1)
+    print(f"draft_block workload=pair-rows batch={batch} overrides={PAIR_ROW_OVERRIDES[ov]}",
+          flush=True)
+    for st, (cfg, sp) in PAIR_ROW_OVERRIDES[ov].items():
+        dbd.gemm_override(st, cfg, sp)
+    try:
+        case = Case(wl, dev=DEV)
+        case.fill_cache()
+        drafts, logits, status = case.step()
+        torch.cuda.synchronize()
+        assert torch.all(status == 0)
+        _check_drafts_property(case, drafts, logits)
+        _compare(case, logits, range(wl.batch), [], residuals=False)
+    finally:
+        for st in PAIR_ROW_OVERRIDES[ov]:
+            dbd.gemm_override(st, -1, 0)
+
+
 @pytest.mark.parametrize("pairs", [0, 1])
 def test_small_block_fused_residual_norm_matches_oracle(pairs):
     """32 block rows with K large enough that the O and down projections take the skinny tiles
