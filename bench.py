@@ -50,6 +50,10 @@ def parse():
                     help="skip the instrumented pass and the cold-ingest timing")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-traffic", metavar="DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="MFMA-activity counter passes under DIR -> profiles/mfma_counters_*.json")
+    ap.add_argument("--summarize-kernel-stats", metavar="CSV",
+                    help="a rocprofv3 kernel_stats.csv -> a markdown table on stdout")
     ap.add_argument("--sweep-block", action="store_true",
                     help="draft_block latency against block length (SpecDiff-2-shaped drafter)")
     return ap.parse_args()
@@ -57,6 +61,8 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3-8b_bs32.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "mfma_counters_qwen3-8b_bs32.json")
+XCDS, SIMDS = 8, 1024       # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 COPY_BYTES = 1 << 30
 
 
@@ -143,6 +149,93 @@ def summarize_traffic(d):
     print(json.dumps({"copy_factor_fetch": out["copy_factor_fetch"],
                       "copy_factor_write": out["copy_factor_write"],
                       "kernels": len(out["kernels"])}))
+
+
+def _counter_rows(d):
+    """{kernel: {counter: mean value}} over the dispatches of each kernel with the grid of its
+    last dispatch (the measured steps; the cold ingest runs other grids), from every
+    *counter_collection.csv under d."""
+    import csv
+    import glob
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            rows.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(
+                (int(r["Dispatch_Id"]), r["Grid_Size"], float(r["Counter_Value"])))
+    out = {}
+    for (k, c), rs in rows.items():
+        rs.sort()
+        g = rs[-1][1]
+        v = [x for _, gs, x in rs if gs == g]
+        out.setdefault(k, {})[c] = sum(v) / len(v)
+    return out
+
+
+def summarize_counters(d):
+    """MFMA activity of each library kernel from rocprofv3 --pmc passes under d.  GRBM_GUI_ACTIVE
+    reads the sum over the 8 XCDs, so a kernel's cycles are GRBM_GUI_ACTIVE / 8 (checked against
+    the kernel-trace durations at the shader clock); SQ_VALU_MFMA_BUSY_CYCLES counts busy MFMA
+    cycles summed over the 1,024 SIMDs, so the busy fraction is BUSY / (1024 x cycles).
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 is the bf16 MFMA flops."""
+    cs = _counter_rows(d)
+    out = {"commands": [
+               "REPO=<repository root>; OUT=<output directory>",
+               "cd /tmp && export TMPDIR=/tmp",
+               "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+               "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
+               "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --output-format csv -d $OUT/counters -o run "
+               "-- python3 $REPO/bench.py --steps 3 --warmup 1 --profile-steps-only "
+               "--no-cpu-baseline",
+               "python3 $REPO/bench.py --summarize-counters $OUT/counters"],
+           "source_hash": kernel_source_hash(), "xcds": XCDS, "simds": SIMDS, "kernels": {}}
+    for k, v in cs.items():
+        if "dbd::" not in k and not k.startswith("_ZN3dbd"):
+            continue
+        g = v.get("GRBM_GUI_ACTIVE")
+        if not g:
+            continue
+        cyc = g / XCDS
+        e = {"cycles": round(cyc)}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            e["mfma_busy"] = round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc), 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in v:
+            e["mfma_bf16_flops"] = round(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512)
+        if "SQ_WAVE_CYCLES" in v and v["SQ_WAVE_CYCLES"]:
+            for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS"):
+                if c in v:
+                    e[c.lower() + "_per_wave_cycle"] = round(v[c] / v["SQ_WAVE_CYCLES"], 4)
+        if "SQ_LDS_BANK_CONFLICT" in v:
+            e["lds_bank_conflict_cycles"] = round(v["SQ_LDS_BANK_CONFLICT"])
+        out["kernels"][k] = e
+    json.dump(out, open(COUNTERS_FILE, "w"), indent=1)
+    print(json.dumps({k: e.get("mfma_busy") for k, e in out["kernels"].items()
+                      if e.get("mfma_busy")}))
+
+
+def summarize_kernel_stats(path):
+    """A rocprofv3 kernel_stats.csv as a markdown table (calls, average and total time, share)."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    print("| kernel | calls | avg us | total ms | % |")
+    print("|---|---|---|---|---|")
+    for r in rows:
+        name = r["Name"] if len(r["Name"]) <= 100 else r["Name"][:97] + "..."
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} |")
+
+
+def measured_mfma_busy(stage):
+    """The counter-measured MFMA busy fraction of the one library kernel the stage launches, from
+    the committed counter summary, or None when absent, ambiguous or on other kernel sources."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    t = json.load(open(COUNTERS_FILE))
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    ks = [k for k in stage_kernels(stage, t["kernels"]) if "mfma_busy" in t["kernels"][k]]
+    if len(ks) != 1:
+        return None
+    return {"mfma_busy": t["kernels"][ks[0]]["mfma_busy"], "kernel": ks[0]}
 
 
 # Epilogue kind (a template argument of every GEMM kernel) of each timed GEMM stage whose
@@ -387,13 +480,17 @@ def dominant_roofline(stages, costs, measured=True):
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
                 "unit": "GB/s", "frac": round(ach * 1e9 / HBM_PEAK, 4)}
     tr = measured_traffic(dom) if measured else None
+    mb = measured_mfma_busy(dom) if measured else None
     roof.update({"kernel": dom, "launches_per_step": n,
                  "avg_launch_us": round(avg_s * 1e6, 2),
                  "algorithmic_bytes_per_launch": round(b / n),
                  "algorithmic_flops_per_launch": round(f / n),
                  "traffic": None if tr is None else tr["bytes"],
                  "traffic_kernel": None if tr is None else tr["kernel"],
-                 "traffic_source": None if tr is None else os.path.relpath(TRAFFIC_FILE, ROOT)})
+                 "traffic_source": None if tr is None else os.path.relpath(TRAFFIC_FILE, ROOT),
+                 "mfma_busy_counter": None if mb is None else mb["mfma_busy"],
+                 "mfma_busy_source": None if mb is None else
+                 os.path.relpath(COUNTERS_FILE, ROOT)})
     return roof
 
 
@@ -415,6 +512,12 @@ def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.summarize_kernel_stats:
+        summarize_kernel_stats(args.summarize_kernel_stats)
         return
     if args.calibrate_copy:
         calibrate_copy()
