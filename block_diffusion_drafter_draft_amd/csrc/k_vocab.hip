@@ -1152,37 +1152,53 @@ hipError_t launch_verify_sample(const float* tl, const float* dl, const int32_t*
 }
 
 // ------------------------------------------------------------------ streak selection
-// One wave per sequence; lane k scores draft k: p_j = double(q_x) / double(Z) for the draft's
-// token x in row (n, k, j); S = sum_m prod_{j<=m} p_j in fp64, in position order.
-__global__ __launch_bounds__(64) void select_finalize_kernel(
+// One workgroup per sequence.  Its threads take the K x G (draft, position) rows in parallel:
+// Z from the row's chunk sums, the draft token's integer weight q, p = double(q) / double(Z)
+// correctly rounded, kept in LDS; then thread k scores draft k, S = sum_m prod_{j<=m} p_j in
+// fp64 in position order (the same operations in the same order as one thread per draft doing
+// everything, so the scores are unchanged).  K, G <= 64.
+constexpr int SF_THREADS = 256;
+__global__ __launch_bounds__(SF_THREADS) void select_finalize_kernel(
     const float* __restrict__ x, int V, int nch, const uint64_t* __restrict__ zpart,
     const float* __restrict__ row_max, const int32_t* __restrict__ row_arg,
     const int32_t* __restrict__ pflag, const int32_t* __restrict__ drafts, int K, int G, int R,
     int32_t* selected, double* scores, int32_t* n_acc, int32_t* bonus, int32_t* committed,
     int32_t* row_flags) {
+  __shared__ double s_p[64 * 64];
   __shared__ double s_score[64];
   __shared__ int32_t t_s[128];
-  __shared__ int s_best;
+  __shared__ int s_best, s_bad;
   const int n = blockIdx.x;
-  const int lane = threadIdx.x;
-  for (int k = lane; k < K; k += 64) {
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  for (int r = tid; r < K * G; r += SF_THREADS) {
+    const int k = r / G, j = r % G;
+    const int64_t row = ((int64_t)n * K + k) * R + j;
+    uint64_t Z = 0;
+    for (int c = 0; c < nch; ++c) Z += zpart[row * nch + c];
+    const int tok = drafts[((int64_t)n * K + k) * G + j];
+    const uint64_t q = (tok >= 0 && tok < V) ? weight_q(x[row * V + tok], row_max[row], 1.0f)
+                                             : 0;
+    s_p[r] = __ddiv_rn((double)q, (double)Z);
+  }
+  // non-finite flags of every row of the sequence (K x R rows)
+  int bad = 0;
+  const int64_t f0 = (int64_t)n * K * R * nch;
+  for (int i = tid; i < K * R * nch; i += SF_THREADS) bad |= pflag[f0 + i];
+  if (bad) atomicOr(&s_bad, 1);
+  __syncthreads();
+  for (int k = tid; k < K; k += SF_THREADS) {
     double P = 1.0, S = 0.0;
     for (int j = 0; j < G; ++j) {
-      const int64_t row = ((int64_t)n * K + k) * R + j;
-      uint64_t Z = 0;
-      for (int c = 0; c < nch; ++c) Z += zpart[row * nch + c];
-      const int tok = drafts[((int64_t)n * K + k) * G + j];
-      const uint64_t q = (tok >= 0 && tok < V) ? weight_q(x[row * V + tok], row_max[row], 1.0f)
-                                               : 0;
-      const double p = __ddiv_rn((double)q, (double)Z);
-      P = __dmul_rn(P, p);
+      P = __dmul_rn(P, s_p[k * G + j]);
       S = __dadd_rn(S, P);
     }
     s_score[k] = S;
     if (scores) scores[(int64_t)n * K + k] = S;
   }
   __syncthreads();
-  if (lane == 0) {
+  if (tid == 0) {
     int best = 0;
     for (int k = 1; k < K; ++k)
       if (s_score[k] > s_score[best]) best = k;
@@ -1191,16 +1207,12 @@ __global__ __launch_bounds__(64) void select_finalize_kernel(
   }
   __syncthreads();
   const int best = s_best;
-  for (int j = lane; j < R; j += 64) t_s[j] = row_arg[((int64_t)n * K + best) * R + j];
-  int bad = 0;
-  for (int r = 0; r < K * R; ++r)
-    for (int c = lane; c < nch; c += 64) bad |= pflag[((int64_t)n * K * R + r) * nch + c];
+  for (int j = tid; j < R; j += SF_THREADS) t_s[j] = row_arg[((int64_t)n * K + best) * R + j];
   __syncthreads();
-  greedy_accept(t_s, drafts + ((int64_t)n * K + best) * G, G, R, n_acc + n, bonus + n,
-                committed + (int64_t)n * (G + 1));
-  if (row_flags) {
-    const uint64_t m = __ballot(bad != 0);
-    if (lane == 0) row_flags[n] = m ? 1 : 0;
+  if (tid < 64) {
+    greedy_accept(t_s, drafts + ((int64_t)n * K + best) * G, G, R, n_acc + n, bonus + n,
+                  committed + (int64_t)n * (G + 1));
+    if (row_flags && tid == 0) row_flags[n] = s_bad ? 1 : 0;
   }
 }
 
@@ -1212,7 +1224,8 @@ hipError_t launch_select_finalize(const float* x, int vocab, int chunk, const ui
                                   int32_t* committed, int32_t* row_flags, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   const int nch = ceil_div(vocab, chunk);
-  hipLaunchKernelGGL(select_finalize_kernel, dim3(batch), dim3(64), 0, s, x, vocab, nch, zpart,
+  hipLaunchKernelGGL(select_finalize_kernel, dim3(batch), dim3(SF_THREADS), 0, s, x, vocab, nch,
+                     zpart,
                      row_max, row_arg, pflag, drafts, n_drafts, gamma, n_rows, selected, scores,
                      n_acc, bonus, committed, row_flags);
   return hipGetLastError();

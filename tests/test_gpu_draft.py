@@ -402,6 +402,51 @@ def test_pair_rows_tiles_match_oracle(batch, ov):
             dbd.gemm_override(st, -1, 0)
 
 
+@pytest.mark.parametrize("name", ["qwen3-4b-tiny-batch", "specdiff-tiny-batch"])
+def test_sequence_placement_in_the_batch_is_invisible(name):
+    """Every sequence's result depends on that sequence only: the same three sequences in another
+    order in the batch (same batch size and capacity, so the same tiles, splits and attention
+    splits) give bit-identical logits and cache contents for each sequence, and identical argmax
+    drafts (sampled drafts are keyed by the batch slot through the sampler's counter draws)."""
+    if name == "qwen3-4b-tiny-batch":
+        sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
+                                n_layers=2, n_target_layers=3, vocab=2048, dtype="bf16")
+        wl = synth.Workload(name=name, shape=sh, batch=3, block_len=16, n_anchor=1, n_drafts=1,
+                            temperature=0.0, ctx_lo=40, ctx_hi=300, ctx_source="hidden",
+                            verify="greedy", verify_rows=16, planted_alpha=0.8)
+    else:
+        sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1024,
+                                n_layers=2, n_target_layers=0, vocab=2048, dtype="bf16")
+        wl = synth.Workload(name=name, shape=sh, batch=3, block_len=32, n_anchor=0, n_drafts=4,
+                            temperature=1.5, ctx_lo=50, ctx_hi=400, ctx_source="cache",
+                            verify="streak", verify_rows=32, planted_alpha=0.8, fixed_new=0,
+                            act_pairs=1)
+    print(f"draft_block workload={name} placement", flush=True)
+    a = Case(wl, dev=DEV)
+    perm = [2, 0, 1]
+    b = Case(wl, dev=DEV)
+    assert b.cap == a.cap
+    b.tokens = a.tokens[perm].contiguous()
+    b.ctx, b.new = a.ctx[perm], a.new[perm]
+    if wl.ctx_source == "hidden":
+        b.hidden = [a.hidden[i] for i in perm]
+    else:
+        b.kv_k.copy_(a.kv_k[:, perm])
+        b.kv_v.copy_(a.kv_v[:, perm])
+    a.fill_cache()
+    b.fill_cache()
+    da, la, sa = a.step()
+    db_, lb, sb = b.step()
+    torch.cuda.synchronize()
+    assert torch.all(sa == 0) and torch.all(sb == 0)
+    for j, i in enumerate(perm):
+        assert torch.equal(la[i], lb[j]), (i, j)
+        if wl.temperature <= 0:
+            assert torch.equal(da[i], db_[j]), (i, j)
+        n = int(a.ctx[i] + a.new[i])
+        assert torch.equal(a.kv_k[:, i, :, :n], b.kv_k[:, j, :, :n])
+
+
 @pytest.mark.parametrize("pairs", [0, 1])
 def test_small_block_fused_residual_norm_matches_oracle(pairs):
     """32 block rows with K large enough that the O and down projections take the skinny tiles
