@@ -362,10 +362,10 @@ def gemm_override(stage, tile_cfg=-1, split=0):
     _check(lib().dbd_gemm_override(STAGES.index(stage), int(tile_cfg), int(split)))
 
 
-def attn_override(split=0, waves=0):
-    """Replace the attention kernel's keys per split and waves per workgroup (0, 0: the
+def attn_override(workgroups=0, depth=0):
+    """Replace the bf16 attention kernel's workgroup count and chunks loaded ahead (0, 0: the
     library's choice).  Set before sizing the workspace."""
-    _check(lib().dbd_attn_override(int(split), int(waves)))
+    _check(lib().dbd_attn_override(int(workgroups), int(depth)))
 
 
 # Stage order of DBD_STAGE_* in include/dbd.h.

@@ -130,6 +130,12 @@ struct EpiArgs {
 
 // Attention over the cache: every block row of sequence n, head h, attends to cache positions
 // 0 .. seq_keys[n]-1 of kv head h / grp.
+// Start of one bf16 attention workgroup's chunk range: sequence, segment of the sequence
+// (kv head * row blocks + row block), chunk inside the segment, and the sequence's keys.
+struct AttnPlan {
+  int32_t n, seg, chunk, keys;
+};
+
 struct AttnArgs {
   const void* q;        // [N*B, qd]
   const void* q_lo;     // optional [N*B, qd]: low part of the bf16 pair of q (bf16 kernel)
@@ -138,11 +144,18 @@ struct AttnArgs {
   const int32_t* seq_keys;
   void* out;            // [N*B, qd]
   void* out_lo;         // optional low part of the bf16 pair of out
-  float* part_o;        // [N, kvh, S_max, R, hd]
-  float2* part_ml;      // [N, kvh, S_max, R] (running max in log2 units, sum)
-  int batch, kvh, grp, block_len, cap, qd, s_max, split;
+  // partials: fp32 kernel [N, kvh, S_max, R, hd] and [N, kvh, S_max, R]; bf16 kernel
+  // [slots, 64, hd] and [slots, 64] with slots = workgroups + N * kvh * row blocks
+  float* part_o;
+  float2* part_ml;      // (running max in log2 units, sum)
+  int batch, kvh, grp, block_len, cap, qd, s_max, split;   // s_max, split: fp32 kernel
   float scale_log2;     // log2(e) / sqrt(hd)
-  int waves;            // bf16 kernel: waves per workgroup (16 query rows each), 0 = choose
+  // bf16 kernel: the chunk schedule written by launch_attn_plan once per step
+  const AttnPlan* plan;         // [workgroups]
+  const int32_t* plan_pref;     // [N + 1] chunks of the sequences before n
+  const int64_t* plan_total;    // [2]: chunks over every segment, workgroups with chunks
+  int workgroups;               // workgroups of the bf16 kernel
+  int depth;                    // chunks loaded ahead (1 or 2)
 };
 
 // ---------------------------------------------------------------- launchers (one per TU)
@@ -176,6 +189,11 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
 constexpr int kMaxGemmCfg = 18;
 constexpr int kMaxGemmSplit = 16;
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);
+// Chunk schedule of the bf16 attention for one step (the keys per sequence are the same in
+// every layer): plan [workgroups], pref [batch + 1], total [2].
+hipError_t launch_attn_plan(const int32_t* seq_keys, int batch, int hd, int kvh, int rows,
+                            int workgroups, AttnPlan* plan, int32_t* pref, int64_t* total,
+                            hipStream_t s);
 hipError_t launch_lm_argmax_final(const float* part_val, const int32_t* part_idx, int rows,
                                   int ntiles, const int32_t* blk_pos, int block_len,
                                   int n_anchor, int n_draft, int32_t* out, hipStream_t s);

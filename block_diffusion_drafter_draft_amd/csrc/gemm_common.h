@@ -60,6 +60,10 @@ __device__ __forceinline__ const T* brow_ptr(const BMap& m, int v, int z) {
 __device__ __forceinline__ u32x4 load_global16(const void* p) {
   return *(const __attribute__((address_space(1))) u32x4*)(p);
 }
+// the same load marked non-temporal (data read once)
+__device__ __forceinline__ u32x4 load_global16_nt(const void* p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(p));
+}
 
 // ------------------------------------------------------------------ epilogues
 // The finished tile (or a chunk of TM of its rows) sits in LDS as fp32, row stride BN + 4.  Each thread owns a contiguous

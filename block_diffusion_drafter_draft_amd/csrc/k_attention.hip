@@ -3,19 +3,20 @@
 // block attends to all cache positions 0 .. P+B-1 of its sequence (context, then the block's own
 // keys, which draft_block wrote into the cache first).
 //
-// Work item: (key split s, kv head g, sequence n); one wave per 16 query rows of the GQA group
-// (rows r = b + B*h over block positions b and the group's heads h).  Per 64-key chunk the K rows
-// and V (kept in the cache in blocks of 8 positions, [cap/8][hd][8]) are staged in LDS; each wave computes S^T = K.Q^T with the gfx950 MFMA
-// 16x16x32 bf16, so that its lanes hold 8 consecutive keys of one query (keys are permuted inside
-// the MFMA tiles), runs the online softmax in fp32 (exp2 domain) and feeds P^T straight from
-// registers into O^T += V^T.P^T.  Splits of one (n, g) are merged by attn_combine_kernel.
+// bf16: a fixed number of workgroups share the (sequence, kv head, query row block) segments'
+// key chunks equally (below); each wave holds 16 query rows of the GQA group (rows r = b + B*h
+// over block positions b and the group's heads h).  Per chunk the K rows and V (kept in the cache
+// in blocks of 8 positions, [cap/8][hd][8]) are staged in LDS; each wave computes S^T = K.Q^T
+// with the gfx950 MFMA 16x16x32 bf16, so that its lanes hold 8 consecutive keys of one query
+// (keys are permuted inside the MFMA tiles), runs the online softmax in fp32 (exp2 domain) and
+// feeds P^T straight from registers into O^T += V^T.P^T.  fp32: one workgroup per (key split,
+// kv head, sequence).  Pieces of a segment computed by several workgroups are merged by a
+// combine kernel in chunk order.
 #include <algorithm>
 
 #include "dbd_internal.h"
 
 namespace dbd {
-
-constexpr int KCH = 64;        // keys per LDS chunk
 
 // ------------------------------------------------------------------ helpers
 template <int HD>
@@ -27,46 +28,111 @@ __device__ __forceinline__ int kswz(int row, int c) {
 }
 __device__ __forceinline__ int vswz(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-// NW waves (a power of two, >= the 16-row query tiles of the group); every thread stages
-// 2 * KCH * HD * 2 / (64 * NW) bytes of the next chunk in registers while the current chunk is
-// consumed from LDS.  QPAIR: the queries come as a bf16 (high, low) pair and every score is the
-// sum of two MFMAs, K.Q_hi + K.Q_lo, so the scores see ~16 significant bits of the rotated
-// query instead of 8 (the keys stay bf16 as stored in the cache).
-template <int HD, int NW, bool QPAIR>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KC = HD / 8;                    // 16-byte chunks per K row
-  constexpr int NT = 64 * NW;
-  constexpr int KT = KCH * KC, VT = HD * (KCH / 8);   // 16-byte chunks of K and V per stage
-  constexpr int KI = (KT + NT - 1) / NT;        // K chunks staged per thread
-  constexpr int VI = (VT + NT - 1) / NT;        // V chunks staged per thread
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KCH * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[HD * KCH];
-  // grid.y = kv head + kvh * row block: a group of more than 16 * NW query rows is spread over
-  // several workgroups that read the same keys
-  const int s = blockIdx.x, g = blockIdx.y % a.kvh, rb = blockIdx.y / a.kvh, n = blockIdx.z;
-  const int L = a.seq_keys[n];
-  const int k_begin = s * a.split;
-  if (L <= 0 || k_begin >= L) return;
-  const int k_end = min(L, k_begin + a.split);
-  const int nsplit = (L + a.split - 1) / a.split;
+// Maximum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48): the gfx950 row
+// swaps exchange rows 1 <-> 0 and 3 <-> 2 (16 lanes) and the two 32-lane halves.
+__device__ __forceinline__ float group_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// ------------------------------------------------------------------ balanced bf16 attention
+// Work is counted in chunks of KCH keys.  A segment is one (sequence n, kv head g, row block rb)
+// with ceil(L_n / KCH) chunks; the segments lie end to end in (n, g, rb) order and their T
+// chunks are cut into P equal ranges, one per workgroup, whatever the context lengths, so every
+// workgroup streams the same number of bytes.  A range may begin or end inside a segment: such a
+// piece publishes its unnormalised output and (max, sum) as a partial that
+// attn_stream_combine_kernel merges; a piece holding a whole segment writes the output itself.
+//
+// Each workgroup is four waves of 16 query rows (one row block).  Chunk x of the range is
+// staged global -> registers -> LDS slot x & 1; DEPTH chunks are loaded ahead (two register
+// sets at DEPTH 2), so while chunk x is consumed from LDS the next DEPTH are in flight.  One
+// barrier per chunk: slot x & 1 is rewritten two chunks later, after the barrier of chunk x + 1.
+// QPAIR: the queries come as a bf16 (high, low) pair and every score is the sum of two MFMAs,
+// K.Q_hi + K.Q_lo, so the scores see ~16 significant bits of the rotated query instead of 8
+// (the keys stay bf16 as stored in the cache).
+// cache policy of the K/V loads: non-temporal (read once per step)
+constexpr int kNonTemporal = 2;
+
+template <int HD>
+struct AttnChunk {
+  static constexpr int KCH = 8192 / HD;             // keys per chunk: 16 KB of K, 16 KB of V
+  static constexpr int KC = HD / 8;                 // 16-byte pieces per K row
+  static constexpr int NT = 256;
+  static constexpr int KI = KCH * KC / NT;          // K pieces staged per thread
+  static constexpr int VI = HD * (KCH / 8) / NT;    // V pieces staged per thread
+  static_assert(KCH == attn_chunk_keys(HD) && KCH % 64 == 0 && KI == 4 && VI == 4, "chunk");
+};
+
+template <int HD, bool QPAIR, int DEPTH>
+__global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
+  using C = AttnChunk<HD>;
+  constexpr int KCH = C::KCH, KC = C::KC, NT = C::NT, KI = C::KI, VI = C::VI;
+  // K slot: [KCH][HD] rows; V slot: [KCH / 64][HD][64], i.e. 64-key halves with 128-byte rows
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KCH * HD];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][HD * KCH];
+  // consecutive workgroups go round-robin to the 8 XCDs: with every launched workgroup busy, give
+  // each XCD a contiguous run of ranges, so that the row blocks of one (sequence, kv head),
+  // which read the same keys, share an L2
+  const int bid = blockIdx.x;
+  const int64_t T = a.plan_total[0];
+  const int P = (int)a.plan_total[1];
+  const int j = P == (int)gridDim.x && P % 8 == 0 ? (bid % 8) * (P / 8) + bid / 8 : bid;
+  if (j >= P) return;
+  const AttnPlan p0 = a.plan[j];
+  const int64_t lo = attn_range_lo(j, T, P), hi = attn_range_lo(j + 1, T, P);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.block_len * a.grp;
-  const int r0 = rb * 16 * NW;
+  const int RB = attn_row_blocks(R);
+  const int segs = a.kvh * RB;
 
-  const bf16* Kg = (const bf16*)a.kv_k + ((int64_t)n * a.kvh + g) * a.cap * HD;
-  // V cache of (n, g): blocks of 8 positions, [cap/8][HD][8]
-  const bf16* Vg = (const bf16*)a.kv_v + ((int64_t)n * a.kvh + g) * HD * a.cap;
+  struct Cur {
+    int n, seg, chunk, cn, L;
+  };
+  auto set_seq = [&](Cur& c) __attribute__((always_inline)) {
+    c.L = __builtin_amdgcn_readfirstlane(a.seq_keys[c.n]);
+    c.cn = c.L > 0 ? (c.L + KCH - 1) / KCH : 0;
+  };
+  auto advance = [&](Cur& c) __attribute__((always_inline)) {
+    if (++c.chunk < c.cn) return;
+    c.chunk = 0;
+    if (++c.seg < segs) return;
+    c.seg = 0;
+    for (;;) {                                  // the next sequence with keys
+      if (++c.n >= a.batch) {
+        c.cn = 0;
+        return;
+      }
+      set_seq(c);
+      if (c.cn > 0) return;
+    }
+  };
+  Cur cc;
+  cc.n = __builtin_amdgcn_readfirstlane(p0.n);
+  cc.seg = __builtin_amdgcn_readfirstlane(p0.seg);
+  cc.chunk = __builtin_amdgcn_readfirstlane(p0.chunk);
+  cc.L = __builtin_amdgcn_readfirstlane(p0.keys);
+  cc.cn = (cc.L + KCH - 1) / KCH;
+  Cur lc = cc;
 
-  // this lane's query row (column of S^T / O^T)
-  const int r = r0 + wave * 16 + (lane & 15);
-  const bool rvalid = r < R;
-  const bool wactive = r0 + wave * 16 < R;      // wave owns at least one query row
-  const int b = rvalid ? r % a.block_len : 0, h = rvalid ? r / a.block_len : 0;
-  const int64_t qrow = (int64_t)n * a.block_len + b;
-  const int qcol = (g * a.grp + h) * HD;
+  // queries of the current segment's row block: this lane's query row (column of S^T / O^T)
   bf16x8 qf[HD / 32], qlf[QPAIR ? HD / 32 : 1];
-  {
-    const int64_t qo = qrow * a.qd + qcol + (lane >> 4) * 8;
+  int r = 0, b = 0, h = 0;
+  bool rvalid = false, wactive = false;
+  f32x4 acc[HD / 16];
+  float m_run = -INFINITY, l_run = 0.f;
+  auto begin = [&](const Cur& c) __attribute__((always_inline)) {
+    const int g = c.seg / RB, rb = c.seg % RB;
+    r = rb * kAttnRows + wave * 16 + (lane & 15);
+    rvalid = r < R;
+    wactive = rb * kAttnRows + wave * 16 < R;
+    b = rvalid ? r % a.block_len : 0;
+    h = rvalid ? r / a.block_len : 0;
+    const int64_t qo = ((int64_t)c.n * a.block_len + b) * a.qd + (g * a.grp + h) * HD +
+                       (lane >> 4) * 8;
     const bf16* qp = (const bf16*)a.q + qo;
     const bf16* qlp = QPAIR ? (const bf16*)a.q_lo + qo : nullptr;
 #pragma unroll
@@ -78,149 +144,387 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
         else for (int e = 0; e < 8; ++e) qlf[ks][e] = (bf16)0.f;
       }
     }
-  }
-  f32x4 acc[HD / 16];
+    // wait for the queries here, at a piece's start: otherwise every later chunk's MFMAs would
+    // wait behind the loads issued before the queries on some path, i.e. for the next chunk too
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
 #pragma unroll
-  for (int i = 0; i < HD / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < HD / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+
+  // A chunk of K ([cap][HD] per (n, g)) and of V ([cap/8][HD][8]) is one contiguous run of
+  // KCH * HD * 2 bytes starting chunk * KCH * HD * 2 bytes into the (n, g) region: 16-byte
+  // piece idx sits idx * 16 bytes in, a per-thread offset plus a uniform one.  The buffer
+  // resource spans the region, so a chunk running past the capacity reads zeros.  The loads are
+  // non-temporal: K and V are read once per step (3-6 % faster than cached loads; walking each
+  // chunk's 1 KB blocks in a per-workgroup order, against all workgroups reading the same
+  // offsets of their 16 KB-aligned chunks at once, changed nothing).
+  auto issue = [&](u32x4 (&kr)[KI], u32x4 (&vr)[VI], const Cur& c) {
+    const int64_t region = ((int64_t)c.n * a.kvh + c.seg / RB) * a.cap * HD;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>((const bf16*)a.kv_k + region), (short)0, a.cap * HD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>((const bf16*)a.kv_v + region), (short)0, a.cap * HD * 2, 0x00020000);
+    const int base = c.chunk * KCH * HD * 2;
+#pragma unroll
+    for (int q = 0; q < KI; ++q)
+      kr[q] = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, base + q * NT * 16,
+                                                    kNonTemporal);
+#pragma unroll
+    for (int q = 0; q < VI; ++q)
+      vr[q] = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, base + q * NT * 16,
+                                                    kNonTemporal);
+  };
+  // V piece idx = (8-key block c, dimension d); positions at or past the end read as 0 (their
+  // probabilities are 0, but the cache beyond the keys may hold anything)
+  auto store = [&](const u32x4 (&kr)[KI], const u32x4 (&vr)[VI], int slot, int c0, int k_end) {
+    bf16* ks = Ks[slot];
+    bf16* vs = Vs[slot];
+#pragma unroll
+    for (int q = 0; q < KI; ++q) {
+      const int idx = tid + q * NT, row = idx / KC, c = idx % KC;
+      *reinterpret_cast<u32x4*>(ks + row * HD + kswz<HD>(row, c) * 8) = kr[q];
+    }
+#pragma unroll
+    for (int q = 0; q < VI; ++q) {
+      const int idx = tid + q * NT, c = idx / HD, d = idx % HD;
+      const int k0 = c0 + c * 8;
+      u32x4 v = vr[q];
+      if (k0 + 8 > k_end) {
+        bf16* e = reinterpret_cast<bf16*>(&v);
+        for (int t = 0; t < 8; ++t)
+          if (k0 + t >= k_end) e[t] = (bf16)0.f;
+      }
+      *reinterpret_cast<u32x4*>(vs + (c >> 3) * HD * 64 + d * 64 + vswz(d, c & 7) * 8) = v;
+    }
+  };
+
   // key rows of the two S^T tiles in a 32-key group: lane group G = lane/16 ends up holding
   // keys 8G .. 8G+7
   const int i16 = lane & 15;
   const int kr0 = 8 * (i16 >> 2) + (i16 & 3);
   const int kr1 = kr0 + 4;
-
-  // A 64-key chunk of K ([cap][HD]) and of V ([cap/8][HD][8]) is one contiguous run of
-  // KCH * HD * 2 bytes starting c0 * HD * 2 bytes into the (n, g) region, and chunk starts are
-  // multiples of 64 inside a capacity that is a multiple of 64: 16-byte piece idx of a chunk
-  // sits idx * 16 bytes in.  Buffer loads take that as one per-thread offset plus a uniform
-  // one, so staging needs no per-load 64-bit addresses.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(Kg), (short)0, a.cap * HD * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(Vg), (short)0, a.cap * HD * 2, 0x00020000);
-  u32x4 kreg[KI], vreg[VI];
-  auto load_chunk = [&](int c0) {
-    const int base = c0 * HD * 2;
+  // One chunk: the scores of all its keys first (two MFMA tiles of 16 keys per 32-key group),
+  // one maximum and at most one rescale per chunk, then P^T into O^T.
+  constexpr int NS = KCH / 32;                  // 32-key groups per chunk
+  auto consume = [&](int slot, int c0, int k_end) __attribute__((always_inline)) {
+    const bf16* ks = Ks[slot];
+    const bf16* vs = Vs[slot];
+    f32x4 sc[NS][2];
 #pragma unroll
-    for (int j = 0; j < KI; ++j)
-      if (KT % NT == 0 || tid + j * NT < KT)
-        kreg[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16, base + j * NT * 16, 0);
+    for (int sub = 0; sub < NS; ++sub) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const int row0 = sub * 32 + kr0, row1 = sub * 32 + kr1;
 #pragma unroll
-    for (int j = 0; j < VI; ++j)
-      if (VT % NT == 0 || tid + j * NT < VT)
-        vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, tid * 16, base + j * NT * 16, 0);
-  };
-  auto store_chunk = [&](int c0) {
-#pragma unroll
-    for (int j = 0; j < KI; ++j) {
-      const int idx = tid + j * NT, row = idx / KC, c = idx % KC;
-      if (KT % NT == 0 || idx < KT)
-        *reinterpret_cast<u32x4*>(Ks + row * HD + kswz<HD>(row, c) * 8) = kreg[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const int idx = tid + j * NT, c = idx / HD, d = idx % HD;
-      if (!(VT % NT == 0 || idx < VT)) continue;
-      const int k0 = c0 + c * 8;
-      u32x4 v = vreg[j];
-      if (k0 + 8 > k_end) {               // positions past the end read as 0
-        bf16* e = reinterpret_cast<bf16*>(&v);
-        for (int q = 0; q < 8; ++q)
-          if (k0 + q >= k_end) e[q] = (bf16)0.f;
-      }
-      *reinterpret_cast<u32x4*>(Vs + d * KCH + vswz(d, c) * 8) = v;
-    }
-  };
-
-  load_chunk(k_begin);
-  for (int c0 = k_begin; c0 < k_end; c0 += KCH) {
-    store_chunk(c0);
-    __syncthreads();
-    if (c0 + KCH < k_end) load_chunk(c0 + KCH);     // in flight while this chunk is consumed
-    if (wactive) {
-#pragma unroll
-      for (int sub = 0; sub < KCH / 32; ++sub) {
-        const int key0 = c0 + sub * 32;
-        if (key0 < k_end) {
-          f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-          const int row0 = sub * 32 + kr0, row1 = sub * 32 + kr1;
-#pragma unroll
-          for (int ks = 0; ks < HD / 32; ++ks) {
-            const int c = ks * 4 + (lane >> 4);
-            bf16x8 k0v =
-                *reinterpret_cast<const bf16x8*>(Ks + row0 * HD + kswz<HD>(row0, c) * 8);
-            bf16x8 k1v =
-                *reinterpret_cast<const bf16x8*>(Ks + row1 * HD + kswz<HD>(row1, c) * 8);
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks], s1, 0, 0, 0);
-            if constexpr (QPAIR) {
-              s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qlf[ks], s0, 0, 0, 0);
-              s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qlf[ks], s1, 0, 0, 0);
-            }
-          }
-          // lane holds S^T[key0 + 8*(lane/16) + e][query], e = 0..7
-          float sv[8];
-          const int kb = key0 + 8 * (lane >> 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[e] = kb + e < k_end ? s0[e] * a.scale_log2 : -INFINITY;
-            sv[4 + e] = kb + 4 + e < k_end ? s1[e] * a.scale_log2 : -INFINITY;
-          }
-          float mx = sv[0];
-#pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = exp2f(m_run - m_new);
-          bf16x8 pb;
-          float ps = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = exp2f(sv[e] - m_new);
-            ps += p;
-            pb[e] = (bf16)p;
-          }
-          l_run = l_run * alpha + ps;
-          m_run = m_new;
-#pragma unroll
-          for (int dt = 0; dt < HD / 16; ++dt) {
-            acc[dt] *= alpha;
-            const int d = dt * 16 + (lane & 15);
-            const int c = sub * 4 + (lane >> 4);
-            bf16x8 vv = *reinterpret_cast<const bf16x8*>(Vs + d * KCH + vswz(d, c) * 8);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[dt], 0, 0, 0);
-          }
+      for (int ks_ = 0; ks_ < HD / 32; ++ks_) {
+        const int c = ks_ * 4 + (lane >> 4);
+        const bf16x8 k0v = *reinterpret_cast<const bf16x8*>(ks + row0 * HD + kswz<HD>(row0, c) * 8);
+        const bf16x8 k1v = *reinterpret_cast<const bf16x8*>(ks + row1 * HD + kswz<HD>(row1, c) * 8);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks_], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks_], s1, 0, 0, 0);
+        if constexpr (QPAIR) {
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qlf[ks_], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qlf[ks_], s1, 0, 0, 0);
         }
       }
+      sc[sub][0] = s0;
+      sc[sub][1] = s1;
     }
-    __syncthreads();
-  }
-  // per-lane partial sums of the 4 lane groups belong to the same query
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (!rvalid) return;
-  // acc[dt][i] = O^T[d = dt*16 + 4*(lane/16) + i][query]
-  if (nsplit == 1) {
-    const float inv = 1.f / l_run;
-    bf16* o = (bf16*)a.out + qrow * a.qd + qcol;
-    bf16* ol = a.out_lo ? (bf16*)a.out_lo + qrow * a.qd + qcol : nullptr;
+    // lane holds S^T[c0 + 32 sub + 8 (lane/16) + 4 t + e][query]; keys past the end -> -inf
+    // (their K rows are whatever the cache holds there, their V rows were zeroed)
+    if (c0 + KCH > k_end) {
 #pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt)
+      for (int sub = 0; sub < NS; ++sub) {
+        const int kb = c0 + sub * 32 + 8 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float y = acc[dt][i] * inv;
-        const bf16 hi = (bf16)y;
-        o[dt * 16 + (lane >> 4) * 4 + i] = hi;
-        if (ol) ol[dt * 16 + (lane >> 4) * 4 + i] = (bf16)(y - (float)hi);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kb + 4 * t + e >= k_end) sc[sub][t][e] = -INFINITY;
       }
-  } else {
-    const int64_t pr = (((int64_t)n * a.kvh + g) * a.s_max + s) * R + r;
-    float* po = a.part_o + pr * HD;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt)
-      *reinterpret_cast<f32x4*>(po + dt * 16 + (lane >> 4) * 4) = acc[dt];
-    if (lane < 16) a.part_ml[pr] = make_float2(m_run, l_run);
+    for (int sub = 0; sub < NS; ++sub)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[sub][t][0], sc[sub][t][1]),
+                             fmaxf(sc[sub][t][2], sc[sub][t][3])));
+    mx = group_max4(mx);
+    const float mxs = mx * a.scale_log2;
+    // The running maximum m_run (log2 units) is raised only when a score passes it, and O and l
+    // are rescaled only when some query of the wave needs it.  (A reference allowed to lag the
+    // maximum by up to 8 skips more rescales but leaves the dominant probabilities rounded to
+    // bf16 instead of exactly 1: logits rel-L2 1.69e-2 -> 1.73e-2 at the bench shape.)
+    const bool raise = mxs > m_run;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mxs : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub) {
+      bf16x8 pb;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[sub][t][e], a.scale_log2, -m_run));
+          ps += p;
+          pb[4 * t + e] = (bf16)p;
+        }
+      const bf16* vh = vs + (sub >> 1) * HD * 64;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) {
+        const int d = dt * 16 + (lane & 15);
+        const int c = (sub & 1) * 4 + (lane >> 4);
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vh + d * 64 + vswz(d, c) * 8);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pb, acc[dt], 0, 0, 0);
+      }
+    }
+    l_run += ps;
+  };
+  // end of a piece: the whole segment -> the output; part of it -> a partial slot
+  auto finish = [&](const Cur& c, bool whole) __attribute__((always_inline)) {
+    // per-lane partial sums of the 4 lane groups belong to the same query
+    float l = l_run + __shfl_xor(l_run, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!rvalid) return;
+    // acc[dt][i] = O^T[d = dt*16 + 4*(lane/16) + i][query]
+    if (whole) {
+      const float inv = 1.f / l;
+      const int64_t off = ((int64_t)c.n * a.block_len + b) * a.qd + (c.seg / RB * a.grp + h) * HD;
+      bf16* o = (bf16*)a.out + off;
+      bf16* ol = a.out_lo ? (bf16*)a.out_lo + off : nullptr;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float y = acc[dt][i] * inv;
+          const bf16 hi = (bf16)y;
+          o[dt * 16 + (lane >> 4) * 4 + i] = hi;
+          if (ol) ol[dt * 16 + (lane >> 4) * 4 + i] = (bf16)(y - (float)hi);
+        }
+    } else {
+      const int64_t pr = attn_partial_slot(j, (int64_t)c.n * segs + c.seg) * kAttnRows +
+                         wave * 16 + (lane & 15);
+      float* po = a.part_o + pr * HD;
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt)
+        *reinterpret_cast<f32x4*>(po + dt * 16 + (lane >> 4) * 4) = acc[dt];
+      if (lane < 16) a.part_ml[pr] = make_float2(m_run, l);
+    }
+  };
+
+  u32x4 kra[KI], vra[VI], krb[KI], vrb[VI];
+  int first = cc.chunk;                         // chunk at which the current piece began
+  // Every step issues one chunk's loads, so that the count of loads behind each register set is
+  // the same on every path and the waits before the LDS stores cover only the chunk stored (a
+  // conditional issue makes the compiler wait for every load in flight).  Past the range's last
+  // chunk the load cursor stays on it and reloads it.
+  int64_t lx = lo;                              // chunk the load cursor is on
+  auto issue_next = [&](u32x4 (&kr)[KI], u32x4 (&vr)[VI]) __attribute__((always_inline)) {
+    issue(kr, vr, lc);
+    if (lx + 1 < hi) {
+      advance(lc);
+      ++lx;
+    }
+  };
+  issue_next(kra, vra);
+  if (DEPTH == 2) issue_next(krb, vrb);
+  begin(cc);                                    // the queries load while the first chunks do
+  int64_t x = lo;
+  auto step = [&](auto par) __attribute__((always_inline)) {
+    constexpr int S = decltype(par)::value;     // LDS slot and (DEPTH 2) register set
+    auto& kr = (DEPTH == 2 && S == 1) ? krb : kra;
+    auto& vr = (DEPTH == 2 && S == 1) ? vrb : vra;
+    const int c0 = cc.chunk * KCH;
+    store(kr, vr, S, c0, cc.L);
+    issue_next(kr, vr);
+    __syncthreads();
+    if (wactive) consume(S, c0, cc.L);
+    const bool seg_end = cc.chunk == cc.cn - 1;
+    if (seg_end || x + 1 == hi) finish(cc, seg_end && first == 0);
+    advance(cc);
+    ++x;
+    if (seg_end && x < hi) {
+      begin(cc);
+      first = 0;
+    }
+  };
+  while (x + 1 < hi) {
+    step(std::integral_constant<int, 0>());
+    step(std::integral_constant<int, 1>());
+  }
+  if (x < hi) step(std::integral_constant<int, 0>());
+}
+
+// Chunk schedule, one 1,024-thread workgroup: pref[n] = chunks of the sequences before n (every
+// segment of a sequence has its chunk count), total = T over all segments, and for every
+// workgroup j the (sequence, segment, chunk) at which its range begins.
+__device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int t = s_w[w];
+      s_w[w] = run;
+      run += t;
+    }
+    s_w[16] = run;
+  }
+  __syncthreads();
+  const int ex = s_w[wave] + x - v;
+  *total = s_w[16];
+  __syncthreads();
+  return ex;
+}
+
+// Sequences whose chunk prefix the plan kernel keeps in LDS for its search; larger batches walk
+// the workgroups of each sequence instead.
+constexpr int kPlanLdsSeqs = 8192;
+
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ seq_keys,
+                                                        int batch, int kch, int segs, int P,
+                                                        AttnPlan* __restrict__ plan,
+                                                        int32_t* __restrict__ pref,
+                                                        int64_t* __restrict__ total) {
+  __shared__ int s_w[17];
+  __shared__ int s_pref[kPlanLdsSeqs + 1];
+  const int tid = threadIdx.x;
+  const bool in_lds = batch <= kPlanLdsSeqs;
+  int carry = 0;
+  for (int base = 0; base < batch; base += 1024) {
+    const int n = base + tid;
+    const int L = n < batch ? seq_keys[n] : 0;
+    const int c = L > 0 ? (L + kch - 1) / kch : 0;
+    int tot;
+    const int ex = block_excl_scan_1024(c, s_w, &tot);
+    if (n < batch) {
+      pref[n] = carry + ex;
+      if (in_lds) s_pref[n] = carry + ex;
+    }
+    carry += tot;
+  }
+  const int64_t T = (int64_t)carry * segs;
+  P = (int)attn_active_workgroups(P, T);
+  if (tid == 0) {
+    pref[batch] = carry;
+    total[0] = T;
+    total[1] = P;
+    if (in_lds) s_pref[batch] = carry;
+  }
+  if (T == 0) return;
+  if (in_lds) {
+    __syncthreads();
+    // workgroup j: its first chunk x, the first sequence whose chunks end past x, the offset
+    for (int j = tid; j < P; j += 1024) {
+      const int64_t x = attn_range_lo(j, T, P);
+      const int n = attn_seq_of_chunk(s_pref, batch, segs, x);
+      const int c = s_pref[n + 1] - s_pref[n];
+      const int64_t off = x - (int64_t)s_pref[n] * segs;
+      plan[j] = AttnPlan{n, (int)(off / c), (int)(off % c), seq_keys[n]};
+    }
+    return;
+  }
+  carry = 0;
+  for (int base = 0; base < batch; base += 1024) {
+    const int n = base + tid;
+    const int L = n < batch ? seq_keys[n] : 0;
+    const int c = L > 0 ? (L + kch - 1) / kch : 0;
+    int tot;
+    const int ex = block_excl_scan_1024(c, s_w, &tot);
+    if (c > 0) {
+      // the workgroups whose ranges begin inside this sequence's chunks
+      const int64_t S = (int64_t)(carry + ex) * segs, E = S + (int64_t)c * segs;
+      for (int64_t jj = attn_first_range_from(S, T, P); jj < attn_first_range_from(E, T, P); ++jj) {
+        const int64_t off = attn_range_lo(jj, T, P) - S;
+        plan[jj] = AttnPlan{n, (int)(off / c), (int)(off % c), L};
+      }
+    }
+    carry += tot;
+  }
+}
+
+// Merge of the partials of the segments that several workgroups share.  grid (64 / 4, kvh * row
+// blocks, N); each workgroup merges 4 query rows of one segment, thread = (row, 4 dimensions).
+// The pieces of segment s are those of the workgroups owning its first to last chunk, in chunk
+// order.
+__global__ __launch_bounds__(128) void attn_stream_combine_kernel(AttnArgs a, int HD) {
+  const int seg = blockIdx.y, n = blockIdx.z;
+  const int64_t T = a.plan_total[0];
+  const int P = (int)a.plan_total[1];
+  const int L = a.seq_keys[n];
+  if (T <= 0 || L <= 0) return;
+  const int kch = attn_chunk_keys(HD);
+  const int cn = (L + kch - 1) / kch;
+  const int R = a.block_len * a.grp;
+  const int RB = attn_row_blocks(R);
+  const int segs = a.kvh * RB;
+  const int64_t start = (int64_t)a.plan_pref[n] * segs + (int64_t)seg * cn;
+  const int64_t w0 = attn_range_owner(start, T, P), w1 = attn_range_owner(start + cn - 1, T, P);
+  if (w0 == w1) return;                         // one workgroup wrote the output
+  const int dq = HD / 4;                        // float4 groups per row
+  const int rl = blockIdx.x * 4 + threadIdx.x / dq;
+  const int d4 = threadIdx.x % dq;
+  const int r = (seg % RB) * kAttnRows + rl;
+  if (threadIdx.x >= 4 * dq || r >= R) return;
+  const int64_t sidx = (int64_t)n * segs + seg;
+  // one pass over the pieces, eight loads in flight at a time, rescaling the running sums to
+  // each batch's maximum
+  float m = -INFINITY, l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  constexpr int SU = 8;
+  for (int64_t w = w0; w <= w1; w += SU) {
+    float2 ml[SU];
+    f32x4 po[SU];
+#pragma unroll
+    for (int q = 0; q < SU; ++q) {
+      const int64_t ww = w + q;
+      const bool ok = ww <= w1;                 // every range holds a chunk: no empty pieces
+      const int64_t pr = attn_partial_slot(ok ? ww : w0, sidx) * kAttnRows + rl;
+      ml[q] = ok ? a.part_ml[pr] : make_float2(-INFINITY, 0.f);
+      po[q] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + pr * HD + 4 * d4)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mb = m;
+#pragma unroll
+    for (int q = 0; q < SU; ++q) mb = fmaxf(mb, ml[q].x);
+    const float sc = exp2f(m - mb);              // 0 while nothing is merged yet
+    l *= sc;
+    o *= sc;
+#pragma unroll
+    for (int q = 0; q < SU; ++q) {
+      const float wgt = exp2f(ml[q].x - mb);
+      l += wgt * ml[q].y;
+      o += wgt * po[q];
+    }
+    m = mb;
+  }
+  const float inv = 1.f / l;
+  const int b = r % a.block_len, h = r / a.block_len;
+  const int64_t off = ((int64_t)n * a.block_len + b) * a.qd + (seg / RB * a.grp + h) * HD + 4 * d4;
+  bf16* out = (bf16*)a.out + off;
+  bf16* out_lo = a.out_lo ? (bf16*)a.out_lo + off : nullptr;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float y = o[q] * inv;
+    const bf16 hi = (bf16)y;
+    out[q] = hi;
+    if (out_lo) out_lo[q] = (bf16)(y - (float)hi);
   }
 }
 
@@ -367,35 +671,40 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a, int HD) {
 }
 
 template <int HD, bool QP>
-static void launch_bf16_q(const AttnArgs& a, dim3 grid, int nw, hipStream_t s) {
-  if (nw <= 2) hipLaunchKernelGGL((attn_bf16_kernel<HD, 2, QP>), grid, dim3(128), 0, s, a);
-  else if (nw <= 4) hipLaunchKernelGGL((attn_bf16_kernel<HD, 4, QP>), grid, dim3(256), 0, s, a);
-  else if (nw <= 8) hipLaunchKernelGGL((attn_bf16_kernel<HD, 8, QP>), grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((attn_bf16_kernel<HD, 16, QP>), grid, dim3(1024), 0, s, a);
+static void launch_stream_q(const AttnArgs& a, hipStream_t s) {
+  if (a.depth == 1)
+    hipLaunchKernelGGL((attn_stream_kernel<HD, QP, 1>), dim3(a.workgroups), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_stream_kernel<HD, QP, 2>), dim3(a.workgroups), dim3(256), 0, s, a);
 }
 template <int HD>
-static void launch_bf16(const AttnArgs& a, dim3 grid, int nw, hipStream_t s) {
-  if (a.q_lo) launch_bf16_q<HD, true>(a, grid, nw, s);
-  else launch_bf16_q<HD, false>(a, grid, nw, s);
+static void launch_stream(const AttnArgs& a, hipStream_t s) {
+  if (a.q_lo) launch_stream_q<HD, true>(a, s);
+  else launch_stream_q<HD, false>(a, s);
+}
+
+hipError_t launch_attn_plan(const int32_t* seq_keys, int batch, int hd, int kvh, int rows,
+                            int workgroups, AttnPlan* plan, int32_t* pref, int64_t* total,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, seq_keys, batch,
+                     attn_chunk_keys(hd), kvh * attn_row_blocks(rows), workgroups, plan, pref,
+                     total);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.s_max, a.kvh, a.batch);
   const int R = a.block_len * a.grp;
-  dim3 cgrid(ceil_div(R, 4), a.kvh, a.batch);
   if (dtype == 1) {
-    // waves per workgroup: at most four (64 query rows) unless overridden; the kernel template
-    // takes the next power of two, and the grid's row blocks use the same count
-    const int need = ceil_div(R, 16);
-    int nw = a.waves > 0 ? std::min(a.waves, need) : std::min(4, need);
-    nw = nw <= 2 ? 2 : nw <= 4 ? 4 : nw <= 8 ? 8 : 16;
-    grid.y = a.kvh * ceil_div(R, 16 * nw);
-    if (hd == 128) launch_bf16<128>(a, grid, nw, s);
-    else launch_bf16<64>(a, grid, nw, s);
+    if (hd == 128) launch_stream<128>(a, s);
+    else launch_stream<64>(a, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(attn_combine_kernel<bf16>, cgrid, dim3(128), 0, s, a, hd);
+    hipLaunchKernelGGL(attn_stream_combine_kernel, dim3(kAttnRows / 4, a.kvh * attn_row_blocks(R),
+                                                        a.batch),
+                       dim3(128), 0, s, a, hd);
   } else {
+    dim3 grid(a.s_max, a.kvh, a.batch);
+    dim3 cgrid(ceil_div(R, 4), a.kvh, a.batch);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, a, hd);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

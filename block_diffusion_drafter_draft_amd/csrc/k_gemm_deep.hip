@@ -610,6 +610,10 @@ struct SkinnyCfg {
 template <int MT, int KIND, bool SPLITA>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e) {
   using C = SkinnyCfg<MT, SPLITA>;
+  // The LM head streams its weights (hundreds of MB, each element read once) non-temporally:
+  // Qwen3-4B shape, bs 1, 0.153 -> 0.141 ms per step.  The projections keep cached loads (down
+  // measured slower non-temporal, gate/up and Q/K/V unchanged).
+  constexpr bool kStreamB = KIND == EPI_ARGMAX || KIND == EPI_STORE_F32;
   constexpr int BM = C::BM, BN = C::BN, KS = C::KS, MI = C::MI, NI = C::NI;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -657,7 +661,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, EpiArgs e)
   u32x4 b0[NI][2], b1[NI][2], b2[NI][2];
   auto load = [&](u32x4 (*sa)[2], u32x4 (*bq)[2], int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bq[q / 2][q % 2] = load_global16(bsrc[q] + kt * KS);
+    for (int q = 0; q < 4; ++q)
+      bq[q / 2][q % 2] = kStreamB ? load_global16_nt(bsrc[q] + kt * KS)
+                                  : load_global16(bsrc[q] + kt * KS);
 #pragma unroll
     for (int q = 0; q < C::CH; ++q) {
       if (!aok[q]) continue;

@@ -87,40 +87,36 @@ struct Carver {
 
 int elem_size(int dtype) { return dtype == DBD_BF16 ? 2 : 4; }
 
-// Attention tuning overrides (dbd_attn_override): keys per split and waves per workgroup of the
+// Attention tuning overrides (dbd_attn_override): workgroups and chunks loaded ahead of the
 // bf16 kernel, 0 = the library's choice.
-static int g_attn_split = 0, g_attn_waves = 0;
+static int g_attn_workgroups = 0, g_attn_depth = 0;
 
-// Row blocks per (sequence, kv head) of the bf16 kernel for R query rows per kv head: the
-// kernel takes at most four waves (64 rows) per workgroup, so a wide group (many query heads per
-// kv head, or a long block) is spread over several workgroups that read the same keys rather
-// than loading all its queries and writing all its split partials in one.  Measured on the
-// SpecDiff-2-shaped drafter (224 rows per kv head): attention 1.50 -> 0.83 ms per call against
-// one 16-wave workgroup per group.
-static int attn_row_blocks(int dtype, int R) {
-  return dtype == DBD_BF16 ? ceil_div(R, 64) : 1;
-}
+// Workgroups of the bf16 attention: two per CU of the 256, which is what its registers (two
+// register sets of staged keys and values) and its two 32 KB LDS slots allow.
+static int attn_workgroups() { return g_attn_workgroups > 0 ? g_attn_workgroups : kAttnWorkgroups; }
+static int attn_depth() { return g_attn_depth > 0 ? g_attn_depth : kAttnDepth; }
 
-// Keys per attention split: the largest of 512 (256 for the fp32 kernel, which gives each key
-// of a split its own thread), 256, 128 and 64 that still gives the launch at least 512
-// workgroups over the capacity.  Short contexts and small batches are then spread over many
-// workgroups instead of a few that walk every chunk of their keys in turn.
-int attn_split(int dtype, int cap, int kvh, int batch, int R) {
-  if (dtype == DBD_BF16 && g_attn_split > 0) return g_attn_split;
-  int s = dtype == DBD_BF16 ? 512 : 256;
-  const int64_t rb = attn_row_blocks(dtype, R);
-  while (s > 64 && (int64_t)ceil_div(cap, s) * kvh * batch * rb < 512) s /= 2;
+// Keys per split of the fp32 attention (one workgroup per (split, kv head, sequence), each key
+// of a split its own thread): the largest of 256, 128 and 64 that still gives the launch at least
+// 512 workgroups over the capacity.
+static int attn_split_f32(int cap, int kvh, int batch) {
+  int s = 256;
+  while (s > 64 && (int64_t)ceil_div(cap, s) * kvh * batch < 512) s /= 2;
   return s;
 }
 
-// (sequence, split) pairs of attention partials to reserve for up to `batch` sequences.  The
-// split shrinks with the batch, so the largest batch does not always need the most pairs; the
-// maximum over 1 .. batch keeps a workspace sized for a batch enough for every smaller one.
-static int64_t attn_partial_pairs(int dtype, int cap, int kvh, int batch, int R) {
+// Attention partials (rows of hd floats) to reserve for up to `batch` sequences.  bf16: one
+// 64-row slot per (workgroup, segment) piece, at most workgroups + segments.  fp32: R rows per
+// (sequence, split, kv head); the split shrinks with the batch, so the maximum over 1 .. batch
+// keeps a workspace sized for a batch enough for every smaller one.
+static int64_t attn_partial_rows(int dtype, int cap, int kvh, int batch, int R, bool at_most) {
+  if (dtype == DBD_BF16)
+    return attn_partial_slots(attn_workgroups(), (int64_t)batch * kvh * attn_row_blocks(R)) *
+           kAttnRows;
   int64_t m = 0;
-  for (int n = 1; n <= batch; ++n)
-    m = std::max(m, (int64_t)n * ceil_div(cap, attn_split(dtype, cap, kvh, n, R)));
-  return m;
+  for (int n = at_most ? 1 : batch; n <= batch; ++n)
+    m = std::max(m, (int64_t)n * ceil_div(cap, attn_split_f32(cap, kvh, n)));
+  return m * kvh * R;
 }
 
 // Per-stage GEMM tile / split overrides (dbd_gemm_override), indexed by DBD_STAGE_*: -1 / 0 =
@@ -145,6 +141,9 @@ struct DraftBufs {
   void* act_lo;
   float* part_o;
   float2* part_ml;
+  AttnPlan* attn_plan;  // bf16 attention schedule (see launch_attn_plan)
+  int32_t* attn_pref;
+  int64_t* attn_total;
   float* lm_pv;
   int32_t* lm_pi;
   float* logits;
@@ -255,12 +254,16 @@ size_t carve_draft(const dbd_model_desc& d, int N, int B, int n_anchor, int T, i
     t.attn_lo = c.take<char>(M * qd * es);
     t.act_lo = c.take<char>(M * d.ffn * es);
   }
-  t.split = attn_split(d.dtype, cap, d.n_kv_heads, N, R);
+  t.split = attn_split_f32(cap, d.n_kv_heads, N);
   t.s_max = ceil_div(cap, t.split);
-  const int64_t pairs = at_most ? attn_partial_pairs(d.dtype, cap, d.n_kv_heads, N, R)
-                                : (int64_t)N * t.s_max;
-  t.part_o = c.take<float>(pairs * d.n_kv_heads * R * d.head_dim);
-  t.part_ml = c.take<float2>(pairs * d.n_kv_heads * R);
+  const int64_t prow = attn_partial_rows(d.dtype, cap, d.n_kv_heads, N, R, at_most);
+  t.part_o = c.take<float>(prow * d.head_dim);
+  t.part_ml = c.take<float2>(prow);
+  if (d.dtype == DBD_BF16) {
+    t.attn_plan = c.take<AttnPlan>(attn_workgroups());
+    t.attn_pref = c.take<int32_t>((int64_t)N + 1);
+    t.attn_total = c.take<int64_t>(2);
+  }
   // split-K partials: the largest need over the step's GEMMs
   {
     size_t bp = 0, ip = 0;
@@ -386,14 +389,13 @@ int dbd_gemm_override(int32_t stage, int32_t tile_cfg, int32_t split) {
   return DBD_OK;
 }
 
-int dbd_attn_override(int32_t split, int32_t waves) {
+int dbd_attn_override(int32_t workgroups, int32_t depth) {
   g_err.clear();
-  if (split < 0 || split % 64 || split > 4096)
-    return fail(DBD_ERR_ARG, "split %d: 0 or a multiple of 64 up to 4096", split);
-  if (waves != 0 && waves != 2 && waves != 4 && waves != 8 && waves != 16)
-    return fail(DBD_ERR_ARG, "waves %d: 0, 2, 4, 8 or 16", waves);
-  g_attn_split = split;
-  g_attn_waves = waves;
+  if (workgroups < 0 || workgroups > kAttnMaxWorkgroups)
+    return fail(DBD_ERR_ARG, "workgroups %d out of [0, %d]", workgroups, kAttnMaxWorkgroups);
+  if (depth < 0 || depth > 2) return fail(DBD_ERR_ARG, "depth %d out of [0, 2]", depth);
+  g_attn_workgroups = workgroups;
+  g_attn_depth = depth;
   return DBD_OK;
 }
 
@@ -519,6 +521,10 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   for (int i = 0; i < hd / 2; ++i) inv_freq[i] = std::pow(d.rope_theta, -2.0 * i / hd);
   HIP_STAGE(DBD_STAGE_PREP, st, launch_prep(ctx_len, new_offsets, N, B, T, ctx_capacity, hd, inv_freq, b.meta,
                       seq_status, st));
+  if (d.dtype == DBD_BF16)
+    HIP_STAGE(DBD_STAGE_PREP, st, launch_attn_plan(b.meta.seq_keys, N, hd, kvh, B * (d.n_q_heads / kvh),
+                                                   attn_workgroups(), b.attn_plan, b.attn_pref,
+                                                   b.attn_total, st));
 
   // 1. ingest: mix + RMSNorm, then context K/V for every draft layer (batched over layers)
   if (d.n_target_layers > 0 && T > 0) {
@@ -653,7 +659,11 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       a.s_max = b.s_max;
       a.split = b.split;
       a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
-      a.waves = g_attn_waves;
+      a.plan = b.attn_plan;
+      a.plan_pref = b.attn_pref;
+      a.plan_total = b.attn_total;
+      a.workgroups = attn_workgroups();
+      a.depth = attn_depth();
       HIP_STAGE(DBD_STAGE_ATTN, st, launch_attention(d.dtype, hd, a, st));
     }
     {

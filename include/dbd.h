@@ -403,12 +403,13 @@ int dbd_timing_read(int stage, double* total_ms /* host out */, int64_t* launche
  * stage that is not a GEMM or an out-of-range tile_cfg / split. */
 int dbd_gemm_override(int32_t stage, int32_t tile_cfg, int32_t split);
 
-/* Attention tuning: keys per split (a multiple of 64, at most 4096) and waves per workgroup
- * (2, 4, 8 or 16; each wave holds 16 query rows of a kv head's group, so a group of R rows takes
- * ceil(R / (16 * waves)) workgroups per split) of the bf16 attention kernel, process-wide; 0 and
- * 0 restore the library's choice.  dbd_draft_workspace_bytes sizes the split partials from the
- * same choice, so set it before sizing a workspace.  Not thread-safe; meant for benchmarks. */
-int dbd_attn_override(int32_t split, int32_t waves);
+/* Attention tuning of the bf16 kernel, process-wide: the number of workgroups that share the
+ * key chunks of every (sequence, kv head, 64-row query block) equally (1 .. 8192) and the chunks
+ * each loads ahead (1 or 2); 0 and 0 restore the library's choice (512 and 2).
+ * dbd_draft_workspace_bytes sizes the attention partials from the same choice, so set it before
+ * sizing a workspace.  Not thread-safe; meant for benchmarks.  Returns DBD_ERR_ARG for values
+ * out of range. */
+int dbd_attn_override(int32_t workgroups, int32_t depth);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* dbd_last_error(void);

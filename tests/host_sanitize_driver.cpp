@@ -103,8 +103,10 @@ int main() {
       EXPECT(dbd_gemm_workspace_bytes(DBD_BF16, 235, 1000, 2560, cfg, split, &gb) == DBD_OK);
     }
   EXPECT(dbd_gemm_override(DBD_STAGE_ATTN, 3, 0) == DBD_ERR_ARG);
-  EXPECT(dbd_attn_override(100, 0) == DBD_ERR_ARG);
+  EXPECT(dbd_attn_override(8193, 0) == DBD_ERR_ARG);
+  EXPECT(dbd_attn_override(-1, 0) == DBD_ERR_ARG);
   EXPECT(dbd_attn_override(0, 3) == DBD_ERR_ARG);
+  EXPECT(dbd_attn_override(0, 0) == DBD_OK);
   std::printf("host checks: %d workspace queries, %d failures\n", queries, g_fails);
   return g_fails ? 1 : 0;
 }

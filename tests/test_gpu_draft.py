@@ -339,18 +339,21 @@ def test_query_groups_beyond_one_workgroup_match_oracle():
     _compare(case, logits, range(wl.batch), [])
 
 
-@pytest.mark.parametrize("split,waves", [(64, 2), (128, 16), (1024, 4), (2048, 8), (192, 4)])
-def test_attention_split_and_waves_overrides_match_oracle(split, waves):
-    """The attention kernel's split (keys per workgroup, one to many splits per sequence) and
-    waves per workgroup (one or several row blocks per kv head) chosen by the tuning override:
-    320 query rows per kv head, contexts of 90-130 positions."""
+@pytest.mark.parametrize("workgroups,depth", [(1, 1), (3, 2), (7, 1), (64, 2), (2048, 2),
+                                               (0, 1)])
+def test_attention_workgroup_and_depth_overrides_match_oracle(workgroups, depth):
+    """The balanced attention with the workgroup count and load-ahead depth set by the tuning
+    override: one workgroup walking every segment (whole segments only, no partials), a few
+    workgroups whose ranges end inside segments (partials merged by the combine kernel), and
+    more workgroups than chunks (empty ranges, segments spread over many pieces).  320 query rows
+    per kv head (five row blocks), head size 64, contexts of 90-130 positions."""
     sh = synth.DrafterShape(hidden=512, n_q_heads=16, n_kv_heads=2, head_dim=64, ffn=1024,
                             n_layers=2, n_target_layers=2, vocab=2048, dtype="bf16")
     wl = synth.Workload(name="attn-override", shape=sh, batch=3, block_len=40, n_anchor=1,
                         n_drafts=1, temperature=0.0, ctx_lo=90, ctx_hi=130, ctx_source="hidden",
                         verify="greedy", verify_rows=40, planted_alpha=0.8, fixed_new=8)
-    print(f"draft_block workload=attn-override split={split} waves={waves}", flush=True)
-    dbd.attn_override(split, waves)
+    print(f"draft_block workload=attn-override workgroups={workgroups} depth={depth}", flush=True)
+    dbd.attn_override(workgroups, depth)
     try:
         case = Case(wl, dev=DEV)
         case.fill_cache()
@@ -403,11 +406,21 @@ def test_pair_rows_tiles_match_oracle(batch, ov):
 
 
 @pytest.mark.parametrize("name", ["qwen3-4b-tiny-batch", "specdiff-tiny-batch"])
-def test_sequence_placement_in_the_batch_is_invisible(name):
-    """Every sequence's result depends on that sequence only: the same three sequences in another
-    order in the batch (same batch size and capacity, so the same tiles, splits and attention
-    splits) give bit-identical logits and cache contents for each sequence, and identical argmax
-    drafts (sampled drafts are keyed by the batch slot through the sampler's counter draws)."""
+@pytest.mark.parametrize("workgroups", [1, 5])
+def test_sequence_placement_in_the_batch_is_invisible(name, workgroups):
+    """Every sequence's result depends on that sequence only, up to where the balanced attention
+    cuts its key chunks: the same three sequences in another order in the batch (same batch size
+    and capacity, so the same GEMM tiles and splits).  With one attention workgroup every
+    segment is computed whole, so logits, cache contents and argmax drafts are bit-identical.
+    With five workgroups the cuts depend on the lengths of the sequences before it in the batch
+    (as they do at the library's workgroup count once a batch has more chunks than workgroups),
+    so the partials merge in another grouping and the attention outputs differ in their last
+    bits.  Every single-bf16 rounding downstream (the block's keys and values in the cache, and
+    the activations without pairs) turns that into flipped roundings, each moving an element by
+    2^-8 of itself, so the two orders agree only to the bf16 path's own accuracy: one order
+    matches the oracle within its tolerance and the two match each other within the same
+    tolerance (measured 5e-3 without activation pairs and 1.1e-3 with them, against 2e-3 to 1e-2
+    from the oracle)."""
     if name == "qwen3-4b-tiny-batch":
         sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
                                 n_layers=2, n_target_layers=3, vocab=2048, dtype="bf16")
@@ -421,7 +434,15 @@ def test_sequence_placement_in_the_batch_is_invisible(name):
                             temperature=1.5, ctx_lo=50, ctx_hi=400, ctx_source="cache",
                             verify="streak", verify_rows=32, planted_alpha=0.8, fixed_new=0,
                             act_pairs=1)
-    print(f"draft_block workload={name} placement", flush=True)
+    print(f"draft_block workload={name} placement workgroups={workgroups}", flush=True)
+    dbd.attn_override(workgroups, 0)
+    try:
+        _placement(wl, workgroups == 1)
+    finally:
+        dbd.attn_override(0, 0)
+
+
+def _placement(wl, exact):
     a = Case(wl, dev=DEV)
     perm = [2, 0, 1]
     b = Case(wl, dev=DEV)
@@ -439,12 +460,25 @@ def test_sequence_placement_in_the_batch_is_invisible(name):
     db_, lb, sb = b.step()
     torch.cuda.synchronize()
     assert torch.all(sa == 0) and torch.all(sb == 0)
+    if not exact:
+        # the oracle inputs of `b` are those it was generated with, not the permuted copies of
+        # `a`'s, so only `a` is compared with the oracle
+        _check_drafts_property(a, da, la)
+        _check_drafts_property(b, db_, lb)
+        _compare(a, la, range(wl.batch), [], residuals=False)
+    bound = TOL[wl.shape.dtype]
     for j, i in enumerate(perm):
-        assert torch.equal(la[i], lb[j]), (i, j)
-        if wl.temperature <= 0:
-            assert torch.equal(da[i], db_[j]), (i, j)
         n = int(a.ctx[i] + a.new[i])
-        assert torch.equal(a.kv_k[:, i, :, :n], b.kv_k[:, j, :, :n])
+        if exact:
+            assert torch.equal(la[i], lb[j]), (i, j)
+            if wl.temperature <= 0:
+                assert torch.equal(da[i], db_[j]), (i, j)
+            assert torch.equal(a.kv_k[:, i, :, :n], b.kv_k[:, j, :, :n])
+            continue
+        x, y = la[i].double(), lb[j].double()
+        rel = float((x - y).norm() / x.norm())
+        print(f"placement seq {i}: logits rel-L2 between the two orders {rel:.3e}", flush=True)
+        assert rel < bound, (i, j, rel)
 
 
 @pytest.mark.parametrize("pairs", [0, 1])
@@ -483,9 +517,9 @@ def test_small_block_fused_residual_norm_matches_oracle(pairs):
 
 
 def test_long_context_single_sequence_many_splits():
-    """One sequence over a 716-position cache: the launch is small, so attention takes 64-key
-    splits (12 of them) and the combine kernel merges more than eight splits per row (its
-    second, looped path)."""
+    """One sequence over a 716-position cache: 12 key chunks per kv head, fewer chunks than
+    attention workgroups, so every chunk is a piece of its own and the combine kernel merges
+    twelve partials per row (more than one round of its eight loads in flight)."""
     sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1024,
                             n_layers=2, n_target_layers=0, vocab=2048, dtype="bf16")
     wl = synth.Workload(name="long-ctx", shape=sh, batch=1, block_len=16, n_anchor=1,
