@@ -26,7 +26,7 @@ constexpr bool resid_norm_fits(int n_cols, int64_t ldc) {
 constexpr int kAttnRows = 64;
 constexpr int kAttnWorkgroups = 512;
 constexpr int kAttnMaxWorkgroups = 8192;
-constexpr int kAttnDepth = 2;
+constexpr int kAttnDepth = 1;
 constexpr int attn_chunk_keys(int hd) { return 8192 / hd; }
 constexpr int attn_row_blocks(int rows) { return (rows + kAttnRows - 1) / kAttnRows; }
 

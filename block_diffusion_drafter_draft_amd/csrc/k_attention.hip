@@ -160,12 +160,14 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   // non-temporal: K and V are read once per step (3-6 % faster than cached loads; walking each
   // chunk's 1 KB blocks in a per-workgroup order, against all workgroups reading the same
   // offsets of their 16 KB-aligned chunks at once, changed nothing).
-  auto issue = [&](u32x4 (&kr)[KI], u32x4 (&vr)[VI], const Cur& c) {
+  auto issue = [&](u32x4 (&kr)[KI], u32x4 (&vr)[VI], const Cur& c, bool real)
+                   __attribute__((always_inline)) {
     const int64_t region = ((int64_t)c.n * a.kvh + c.seg / RB) * a.cap * HD;
+    const int bytes = real ? a.cap * HD * 2 : 0;   // 0: every load is out of range, reads 0
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>((const bf16*)a.kv_k + region), (short)0, a.cap * HD * 2, 0x00020000);
+        const_cast<bf16*>((const bf16*)a.kv_k + region), (short)0, bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>((const bf16*)a.kv_v + region), (short)0, a.cap * HD * 2, 0x00020000);
+        const_cast<bf16*>((const bf16*)a.kv_v + region), (short)0, bytes, 0x00020000);
     const int base = c.chunk * KCH * HD * 2;
 #pragma unroll
     for (int q = 0; q < KI; ++q)
@@ -289,56 +291,48 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
     }
     l_run += ps;
   };
-  // end of a piece: the whole segment -> the output; part of it -> a partial slot
-  auto finish = [&](const Cur& c, bool whole) __attribute__((always_inline)) {
+  // End of a piece: its unnormalised O^T and (m, l) go to the piece's partial slot, rows in
+  // order; the combine kernel merges the pieces of every segment and writes the output.
+  auto publish = [&](const f32x4 (&o)[HD / 16], float m, float lsum, int n, int seg)
+                     __attribute__((always_inline)) {
     // per-lane partial sums of the 4 lane groups belong to the same query
-    float l = l_run + __shfl_xor(l_run, 16, 64);
+    float l = lsum + __shfl_xor(lsum, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if (!rvalid) return;
-    // acc[dt][i] = O^T[d = dt*16 + 4*(lane/16) + i][query]
-    if (whole) {
-      const float inv = 1.f / l;
-      const int64_t off = ((int64_t)c.n * a.block_len + b) * a.qd + (c.seg / RB * a.grp + h) * HD;
-      bf16* o = (bf16*)a.out + off;
-      bf16* ol = a.out_lo ? (bf16*)a.out_lo + off : nullptr;
+    const int64_t slot = attn_partial_slot(j, (int64_t)n * segs + seg);
+    float* po = a.part_o + (slot * kAttnRows + wave * 16 + (lane & 15)) * HD;
+    // o[dt][i] = O^T[d = dt*16 + 4*(lane/16) + i][query]; rows past R are ignored
 #pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float y = acc[dt][i] * inv;
-          const bf16 hi = (bf16)y;
-          o[dt * 16 + (lane >> 4) * 4 + i] = hi;
-          if (ol) ol[dt * 16 + (lane >> 4) * 4 + i] = (bf16)(y - (float)hi);
-        }
-    } else {
-      const int64_t pr = attn_partial_slot(j, (int64_t)c.n * segs + c.seg) * kAttnRows +
-                         wave * 16 + (lane & 15);
-      float* po = a.part_o + pr * HD;
-#pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt)
-        *reinterpret_cast<f32x4*>(po + dt * 16 + (lane >> 4) * 4) = acc[dt];
-      if (lane < 16) a.part_ml[pr] = make_float2(m_run, l);
-    }
+    for (int dt = 0; dt < HD / 16; ++dt)
+      *reinterpret_cast<f32x4*>(po + dt * 16 + (lane >> 4) * 4) = o[dt];
+    if (lane < 16) a.part_ml[slot * kAttnRows + wave * 16 + lane] = make_float2(m, l);
   };
+  // Stores count in vmcnt like the loads on gfx9: stores issued on some paths of the loop make
+  // the compiler's waits on the following steps cover every load in flight.  So a piece that
+  // ends before the range does is kept in registers (one such piece) and published after the
+  // loop with the range's last piece; a second one in the same range is published at once and
+  // followed by a full wait, which makes the counts exact again (at the bench shape a range
+  // rarely holds more than one segment end).
+  f32x4 stash[HD / 16];
+  float stash_m = 0.f, stash_l = 0.f;
+  int stash_n = -1, stash_seg = 0;
 
   u32x4 kra[KI], vra[VI], krb[KI], vrb[VI];
-  int first = cc.chunk;                         // chunk at which the current piece began
   // Every step issues one chunk's loads, so that the count of loads behind each register set is
   // the same on every path and the waits before the LDS stores cover only the chunk stored (a
   // conditional issue makes the compiler wait for every load in flight).  Past the range's last
-  // chunk the load cursor stays on it and reloads it.
-  int64_t lx = lo;                              // chunk the load cursor is on
+  // chunk the loads go through a resource of size 0: they return zeros without a memory access
+  // (reloading the last chunk instead re-read it from HBM, the loads being non-temporal).
+  int64_t ln = lo;                              // next chunk to load, at the load cursor
   auto issue_next = [&](u32x4 (&kr)[KI], u32x4 (&vr)[VI]) __attribute__((always_inline)) {
-    issue(kr, vr, lc);
-    if (lx + 1 < hi) {
-      advance(lc);
-      ++lx;
-    }
+    const bool real = ln < hi;
+    issue(kr, vr, lc, real);
+    if (real && ++ln < hi) advance(lc);
   };
   issue_next(kra, vra);
   if (DEPTH == 2) issue_next(krb, vrb);
   begin(cc);                                    // the queries load while the first chunks do
   int64_t x = lo;
+  int last_n = cc.n, last_seg = cc.seg;         // segment of the chunk consumed last
   auto step = [&](auto par) __attribute__((always_inline)) {
     constexpr int S = decltype(par)::value;     // LDS slot and (DEPTH 2) register set
     auto& kr = (DEPTH == 2 && S == 1) ? krb : kra;
@@ -349,19 +343,32 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
     __syncthreads();
     if (wactive) consume(S, c0, cc.L);
     const bool seg_end = cc.chunk == cc.cn - 1;
-    if (seg_end || x + 1 == hi) finish(cc, seg_end && first == 0);
+    if (seg_end && x + 1 < hi) {                // a piece ending before the range does
+      if (stash_n < 0) {
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) stash[dt] = acc[dt];
+        stash_m = m_run;
+        stash_l = l_run;
+        stash_n = cc.n;
+        stash_seg = cc.seg;
+      } else {
+        publish(acc, m_run, l_run, cc.n, cc.seg);
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
+      }
+    }
+    last_n = cc.n;
+    last_seg = cc.seg;
     advance(cc);
     ++x;
-    if (seg_end && x < hi) {
-      begin(cc);
-      first = 0;
-    }
+    if (seg_end && x < hi) begin(cc);
   };
   while (x + 1 < hi) {
     step(std::integral_constant<int, 0>());
     step(std::integral_constant<int, 1>());
   }
   if (x < hi) step(std::integral_constant<int, 0>());
+  publish(acc, m_run, l_run, last_n, last_seg);
+  if (stash_n >= 0) publish(stash, stash_m, stash_l, stash_n, stash_seg);
 }
 
 // Chunk schedule, one 1,024-thread workgroup: pref[n] = chunks of the sequences before n (every
@@ -476,7 +483,6 @@ __global__ __launch_bounds__(128) void attn_stream_combine_kernel(AttnArgs a, in
   const int segs = a.kvh * RB;
   const int64_t start = (int64_t)a.plan_pref[n] * segs + (int64_t)seg * cn;
   const int64_t w0 = attn_range_owner(start, T, P), w1 = attn_range_owner(start + cn - 1, T, P);
-  if (w0 == w1) return;                         // one workgroup wrote the output
   const int dq = HD / 4;                        // float4 groups per row
   const int rl = blockIdx.x * 4 + threadIdx.x / dq;
   const int d4 = threadIdx.x % dq;
