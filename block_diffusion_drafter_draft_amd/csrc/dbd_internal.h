@@ -131,10 +131,12 @@ struct EpiArgs {
 
 // Attention over the cache: every block row of sequence n, head h, attends to cache positions
 // 0 .. seq_keys[n]-1 of kv head h / grp.
-// Start of one bf16 attention workgroup's chunk range: sequence, segment of the sequence
-// (kv head * row blocks + row block), chunk inside the segment, and the sequence's keys.
+// One launched bf16 attention workgroup's share: its range j and chunks [lo, hi) (lo == hi: no
+// work), and at lo the sequence, segment of the sequence (kv head * row blocks + row block),
+// chunk inside the segment and the sequence's keys.
 struct AttnPlan {
-  int32_t n, seg, chunk, keys;
+  int32_t n, seg, chunk, keys, j, pad;
+  int64_t lo, hi;
 };
 
 struct AttnArgs {
@@ -152,7 +154,7 @@ struct AttnArgs {
   int batch, kvh, grp, block_len, cap, qd, s_max, split;   // s_max, split: fp32 kernel
   float scale_log2;     // log2(e) / sqrt(hd)
   // bf16 kernel: the chunk schedule written by launch_attn_plan once per step
-  const AttnPlan* plan;         // [workgroups]
+  const AttnPlan* plan;         // [workgroups], indexed by blockIdx.x
   const int32_t* plan_pref;     // [N + 1] chunks of the sequences before n
   const int64_t* plan_total;    // [2]: chunks over every segment, workgroups with chunks
   int workgroups;               // workgroups of the bf16 kernel

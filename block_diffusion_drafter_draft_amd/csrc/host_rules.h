@@ -59,6 +59,20 @@ constexpr int attn_seq_of_chunk(const I* pref, int batch, int64_t segs, int64_t 
   }
   return lo;
 }
+// Workgroup j's range is computed by the launched workgroup whose blockIdx.x is
+// attn_bid_of_range(j).  Consecutive workgroups go round-robin to the 8 XCDs: when every launched
+// workgroup has a range (and their count is a multiple of 8), XCD x takes the contiguous run of
+// ranges [x P / 8, (x + 1) P / 8), so that the row blocks of one (sequence, kv head), which read
+// the same keys, share an L2; otherwise range j is blockIdx.x j.
+constexpr bool attn_xcd_order(int launched, int64_t active) {
+  return active == launched && launched % 8 == 0;
+}
+constexpr int attn_range_of_bid(int bid, int launched, int64_t active) {
+  return attn_xcd_order(launched, active) ? (bid % 8) * (launched / 8) + bid / 8 : bid;
+}
+constexpr int attn_bid_of_range(int j, int launched, int64_t active) {
+  return attn_xcd_order(launched, active) ? (j % (launched / 8)) * 8 + j / (launched / 8) : j;
+}
 // Partial slot of the piece of segment s that workgroup j computes.  Along the chunk axis every
 // new piece advances j, s or both, so distinct pieces get distinct slots, all below P + the
 // number of segments.

@@ -74,16 +74,11 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
   // K slot: [KCH][HD] rows; V slot: [KCH / 64][HD][64], i.e. 64-key halves with 128-byte rows
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][KCH * HD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][HD * KCH];
-  // consecutive workgroups go round-robin to the 8 XCDs: with every launched workgroup busy, give
-  // each XCD a contiguous run of ranges, so that the row blocks of one (sequence, kv head),
-  // which read the same keys, share an L2
-  const int bid = blockIdx.x;
-  const int64_t T = a.plan_total[0];
-  const int P = (int)a.plan_total[1];
-  const int j = P == (int)gridDim.x && P % 8 == 0 ? (bid % 8) * (P / 8) + bid / 8 : bid;
-  if (j >= P) return;
-  const AttnPlan p0 = a.plan[j];
-  const int64_t lo = attn_range_lo(j, T, P), hi = attn_range_lo(j + 1, T, P);
+  // one dependent load: this workgroup's share, written by the plan kernel
+  const AttnPlan p0 = a.plan[blockIdx.x];
+  const int64_t lo = p0.lo, hi = p0.hi;
+  if (lo >= hi) return;
+  const int j = p0.j;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.block_len * a.grp;
   const int RB = attn_row_blocks(R);
@@ -372,8 +367,9 @@ __global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
 }
 
 // Chunk schedule, one 1,024-thread workgroup: pref[n] = chunks of the sequences before n (every
-// segment of a sequence has its chunk count), total = T over all segments, and for every
-// workgroup j the (sequence, segment, chunk) at which its range begins.
+// segment of a sequence has its chunk count), total = (T over all segments, active workgroups
+// P), and for every launched workgroup its share: range j, chunks [lo, hi) and the (sequence,
+// segment, chunk) at lo.
 __device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -405,7 +401,7 @@ __device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
 constexpr int kPlanLdsSeqs = 8192;
 
 __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restrict__ seq_keys,
-                                                        int batch, int kch, int segs, int P,
+                                                        int batch, int kch, int segs, int launched,
                                                         AttnPlan* __restrict__ plan,
                                                         int32_t* __restrict__ pref,
                                                         int64_t* __restrict__ total) {
@@ -427,23 +423,29 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
     carry += tot;
   }
   const int64_t T = (int64_t)carry * segs;
-  P = (int)attn_active_workgroups(P, T);
+  const int P = (int)attn_active_workgroups(launched, T);
   if (tid == 0) {
     pref[batch] = carry;
     total[0] = T;
     total[1] = P;
     if (in_lds) s_pref[batch] = carry;
   }
+  // launched workgroups without a range (all of them when no sequence has keys) get an empty
+  // share
+  for (int bid = tid; bid < launched; bid += 1024)
+    if (attn_range_of_bid(bid, launched, P) >= P) plan[bid] = AttnPlan{0, 0, 0, 0, 0, 0, 0, 0};
   if (T == 0) return;
   if (in_lds) {
     __syncthreads();
-    // workgroup j: its first chunk x, the first sequence whose chunks end past x, the offset
+    // range j: its first chunk x, the first sequence whose chunks end past x, the offset
     for (int j = tid; j < P; j += 1024) {
       const int64_t x = attn_range_lo(j, T, P);
       const int n = attn_seq_of_chunk(s_pref, batch, segs, x);
       const int c = s_pref[n + 1] - s_pref[n];
       const int64_t off = x - (int64_t)s_pref[n] * segs;
-      plan[j] = AttnPlan{n, (int)(off / c), (int)(off % c), seq_keys[n]};
+      plan[attn_bid_of_range(j, launched, P)] =
+          AttnPlan{n, (int)(off / c), (int)(off % c), seq_keys[n], j, 0, x,
+                   attn_range_lo(j + 1, T, P)};
     }
     return;
   }
@@ -455,11 +457,13 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const int32_t* __restri
     int tot;
     const int ex = block_excl_scan_1024(c, s_w, &tot);
     if (c > 0) {
-      // the workgroups whose ranges begin inside this sequence's chunks
+      // the ranges that begin inside this sequence's chunks
       const int64_t S = (int64_t)(carry + ex) * segs, E = S + (int64_t)c * segs;
       for (int64_t jj = attn_first_range_from(S, T, P); jj < attn_first_range_from(E, T, P); ++jj) {
-        const int64_t off = attn_range_lo(jj, T, P) - S;
-        plan[jj] = AttnPlan{n, (int)(off / c), (int)(off % c), L};
+        const int64_t x = attn_range_lo(jj, T, P), off = x - S;
+        plan[attn_bid_of_range((int)jj, launched, P)] =
+            AttnPlan{n, (int)(off / c), (int)(off % c), L, (int)jj, 0, x,
+                     attn_range_lo(jj + 1, T, P)};
       }
     }
     carry += tot;

@@ -46,7 +46,7 @@ ATTN_SCHEDULE_PROBE = r'''
 // consecutive non-empty pieces; the owner of every chunk is the workgroup whose range
 // holds it; the per-sequence workgroup runs that the plan kernel walks give every workgroup
 // exactly one start, equal to its range's first chunk; the bisection finds every chunk's
-// sequence; the partial slots of all (workgroup, segment) pieces are distinct and below
+// sequence; launched workgroups and ranges map one to one; the partial slots of all (workgroup, segment) pieces are distinct and below
 // P + segments.
 static int check(const std::vector<int>& keys, int hd, int kvh, int rows, int launched) {
   const int kch = dbd::attn_chunk_keys(hd), segs = kvh * dbd::attn_row_blocks(rows);
@@ -95,6 +95,13 @@ static int check(const std::vector<int>& keys, int hd, int kvh, int rows, int la
     }
   }
   for (int j = 0; j < P; ++j) if (starts[j] != 1) return 6;
+  // launched workgroup <-> range: a bijection on [0, launched), ranges [0, P) on P workgroups
+  std::vector<int> seen(launched, 0);
+  for (int bid = 0; bid < launched; ++bid) {
+    const int j = dbd::attn_range_of_bid(bid, launched, P);
+    if (j < 0 || j >= launched || seen[j]++) return 12;
+    if (dbd::attn_bid_of_range(j, launched, P) != bid) return 13;
+  }
   std::set<int64_t> slots;
   for (int j = 0; j < P; ++j) {
     int64_t last = -1;
@@ -114,13 +121,13 @@ int main() {
   unsigned st = 12345u;
   auto rnd = [&](int m) { st = st * 1103515245u + 12345u; return (int)((st >> 8) % (unsigned)m); };
   int bad = 0, cases = 0;
-  const int Ps[] = {1, 2, 3, 7, 8, 64, 512, 1000, 4096};
+  const int Ps[] = {1, 2, 3, 7, 8, 64, 512, 1000, 4096, 24};
   for (int t = 0; t < 300; ++t) {
     const int N = 1 + rnd(40);
     std::vector<int> keys(N);
     for (auto& k : keys) k = rnd(5) == 0 ? 0 : 1 + rnd(3000);
     const int hd = rnd(2) ? 128 : 64, kvh = 1 + rnd(8), rows = 1 + rnd(300);
-    const int P = Ps[t % 9];
+    const int P = Ps[t % 10];
     const int rc = check(keys, hd, kvh, rows, P);
     ++cases;
     if (rc) { ++bad; std::printf("case %d: error %d\n", t, rc); }
