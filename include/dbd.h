@@ -405,7 +405,7 @@ int dbd_gemm_override(int32_t stage, int32_t tile_cfg, int32_t split);
 
 /* Attention tuning of the bf16 kernel, process-wide: the number of workgroups that share the
  * key chunks of every (sequence, kv head, 64-row query block) equally (1 .. 8192) and the chunks
- * each loads ahead (1 or 2); 0 and 0 restore the library's choice (512 and 2).
+ * each loads ahead (1 or 2); 0 and 0 restore the library's choice (512 and 1).
  * dbd_draft_workspace_bytes sizes the attention partials from the same choice, so set it before
  * sizing a workspace.  Not thread-safe; meant for benchmarks.  Returns DBD_ERR_ARG for values
  * out of range. */
