@@ -187,8 +187,15 @@ struct GemmPlan {
   int cfg, bn, split, tiles;
   size_t part_bytes;
 };
+// norm: a residual projection whose caller asks for the RMSNorm of the updated rows (EpiArgs
+// norm_g set, rows that resid_norm_fits); the tile choice then counts the norm's own launch
+// against the tiles whose split-K reduction can write it (gemm_fuses_norm).
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
-                   int F, bool pair, bool split_ok, int split_req = 0);
+                   int F, bool pair, bool split_ok, int split_req = 0, bool norm = false);
+// Whether a residual projection planned as p, with (pair) or without a bf16-pair A operand,
+// runs the following RMSNorm in its split-K reduction (resid_norm_kernel): the skinny tiles and
+// the register-staged 256-row tiles without pair rows, split, one batch entry.
+bool gemm_fuses_norm(const GemmPlan& p, bool pair, int batch);
 constexpr int kMaxGemmCfg = 18;
 constexpr int kMaxGemmSplit = 16;
 hipError_t launch_attention(int dtype, int hd, const AttnArgs& a, hipStream_t s);

@@ -385,7 +385,8 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
 //   3: pipelined 64 x 128, 64-wide stages: 6.7 + 0.455 per stage
 //   10: four-wave 128 x 128, 32-wide stages: 5.3 + 0.356 per stage (x 1.5 with a bf16 pair A)
 //   16: register-staged eight-wave 256 x 128, 64-wide stages: 10.4 + 0.88 per stage
-static double model_us(int kind, int cfg, int M, int Nv, int K, int batch, int S, bool pair) {
+static double model_us(int kind, int cfg, int M, int Nv, int K, int batch, int S, bool pair,
+                       bool norm) {
   const double units = (double)ceil_div(M, kCfgBM[cfg]) * ceil_div(Nv, kCfgBN[cfg]) * batch * S;
   double t;
   if (cfg == 10)
@@ -400,6 +401,9 @@ static double model_us(int kind, int cfg, int M, int Nv, int K, int batch, int S
     t += 4.2e-6 * (double)M * Nv * batch;
   else if (kind == EPI_CTXKV && is_deep(cfg))
     t += 1.3e-6 * (double)M * Nv * batch;
+  // a requested residual norm: inside the split reduction it adds the normalised rows' writes;
+  // otherwise it is a launch of its own that reads the residual back
+  if (norm) t += cfg == 16 && S > 1 && !pair ? 0.5e-6 * M * Nv : 2.0 + 1.5e-6 * M * Nv;
   return t;
 }
 
@@ -411,7 +415,7 @@ struct TileChoice {
   int cfg, split;
 };
 static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gateup, int F,
-                              bool pair) {
+                              bool pair, bool norm) {
   const int base = choose_cfg(kind, M, N, K, batch, gateup, F, pair);
   if (is_skinny(base)) {
     // split K in powers of two while there are fewer than 1024 units and each unit keeps at
@@ -425,7 +429,7 @@ static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gate
   }
   if (gateup || (base != 3 && base != 10)) return {base, 1};
   TileChoice best{base, 1};
-  double best_t = model_us(kind, base, M, N, K, batch, 1, pair);
+  double best_t = model_us(kind, base, M, N, K, batch, 1, pair, norm);
   static const int cand[6] = {1, 2, 3, 4, 6, 8};
   for (int cfg : {10, 16}) {
     // (the 256 x 128 tile as pair rows measured slower than the 128 x 128 tile with its split
@@ -434,7 +438,7 @@ static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gate
     if (cfg == 16 && (pair || M < 192)) continue;
     for (int S : cand) {
       if (cfg == 10 ? K / 32 / S < 4 : K / 64 / S < 2) break;
-      const double t = model_us(kind, cfg, M, N, K, batch, S, pair);
+      const double t = model_us(kind, cfg, M, N, K, batch, S, pair, norm);
       if (t < best_t) { best = {cfg, S}; best_t = t; }
     }
   }
@@ -442,7 +446,7 @@ static TileChoice choose_tile(int kind, int M, int N, int K, int batch, int gate
 }
 
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
-                   int F, bool pair, bool split_ok, int split_req) {
+                   int F, bool pair, bool split_ok, int split_req, bool norm) {
   GemmPlan p{};
   p.split = 1;
   if (dtype != 1) {
@@ -456,7 +460,8 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
   const bool chosen = cfg >= 0 && cfg < kNumCfg;
   int lib_split = 1;
   if (!chosen) {
-    const TileChoice c = choose_tile(kind, M, N, K, batch, gateup, F, pair);
+    const TileChoice c = choose_tile(kind, M, N, K, batch, gateup, F, pair,
+                                     norm && kind == EPI_RESID && batch == 1);
     cfg = c.cfg;
     lib_split = c.split;
   }
@@ -481,19 +486,24 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
   return p;
 }
 
+bool gemm_fuses_norm(const GemmPlan& p, bool pair, int batch) {
+  if (p.cfg < 0 || p.split <= 1 || batch != 1) return false;
+  return is_skinny(p.cfg) || (p.cfg >= 14 && p.cfg <= 16 && !pair);
+}
+
 template <int KIND>
 static void launch_kind(int dtype, int cfg, int split, GemmArgs a, const EpiArgs& e, int batch,
                         hipStream_t s, bool* norm_done) {
   if (norm_done) *norm_done = false;
   if (dtype == 1) {
     const int F = a.seg[0].n1 - a.seg[0].n0;
+    const bool want_norm = KIND == EPI_RESID && e.norm_g && resid_norm_fits(a.N, e.ldc);
     GemmPlan p = plan_gemm(dtype, KIND, cfg, a.M, a.N, a.K, batch, a.gateup, F,
-                           a.A2 != nullptr, a.part != nullptr, split);
+                           a.A2 != nullptr, a.part != nullptr, split, want_norm);
     if (p.split > 1 && p.part_bytes > a.part_cap) p.split = 1;
     a.split = p.split;
-    // the residual's norm rides on the skinny tiles' split-K reduction, which sees whole rows
-    const bool fuse = KIND == EPI_RESID && e.norm_g && is_skinny(p.cfg) && p.split > 1 &&
-                      batch == 1 && resid_norm_fits(a.N, e.ldc);
+    // the residual's norm rides on a split-K reduction that sees whole rows
+    const bool fuse = want_norm && gemm_fuses_norm(p, a.A2 != nullptr, batch);
     EpiArgs ee = e;
     if (!fuse) ee.norm_g = nullptr;
     if (a.A2) launch_cfg<KIND, true>(p.cfg, a, ee, batch, s);

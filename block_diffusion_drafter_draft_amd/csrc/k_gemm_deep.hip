@@ -566,6 +566,25 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
   };
 
   if (S > 1) {
+    if constexpr (KIND == EPI_RESID && !PR) {
+      if (e.norm_g) {
+        // row-major partials [S][M][N] for resid_norm_kernel, which reduces whole rows and
+        // writes the RMSNorm that follows the projection
+        float* pr = reinterpret_cast<float*>(a.part) + (int64_t)sp * M * N;
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j) {
+            const int col = n0 + wn * C::WTN + j * 16 + fr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = m0 + wm * C::WTM + i * 16 + fk * 4 + r;
+              if (row < M && col < N) pr[(int64_t)row * N + col] = acc[i][j][r];
+            }
+          }
+        return;
+      }
+    }
     // split-K: publish this unit's partial; gemm_reduce_kernel adds the partials and runs the
     // epilogue
     const int tiles_n = (N + BN - 1) / BN;
@@ -956,7 +975,10 @@ static void launch_w8r(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   const int units = ceil_div(a.M, 256) * ceil_div(a.N, BN) * S;
   hipLaunchKernelGGL((gemm_w8r_kernel<BN, KIND, WGM, PR>), dim3(units, 1, batch), dim3(512),
                      0, s, a, e);
-  if (S > 1) launch_reduce<256, BN, WGM, 8 / WGM, KIND, PR>(a, e, batch, s);
+  if (S > 1 && KIND == EPI_RESID && !PR && e.norm_g)
+    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+  else if (S > 1)
+    launch_reduce<256, BN, WGM, 8 / WGM, KIND, PR>(a, e, batch, s);
 }
 
 template <int MT, int KIND, bool SPLITA>

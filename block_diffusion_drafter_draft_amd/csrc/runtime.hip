@@ -181,20 +181,25 @@ static void step_gemm_parts(const dbd_model_desc& d, int n, int B, int n_anchor,
   auto need = [](const GemmPlan& p) { return p.split > 1 ? p.part_bytes : (size_t)0; };
   size_t bp = 0, ip = 0;
   if (n > 0) {
-    const GemmPlan pl[5] = {
+    // O and down ask for the following RMSNorm (down: not after the last layer), which can
+    // change their tiles
+    const bool nf = resid_norm_fits(d.hidden, d.hidden);
+    const GemmPlan pl[6] = {
         plan_gemm(d.dtype, EPI_QKV, g_ov_cfg[DBD_STAGE_GEMM_QKV], M, qd + 2 * kd, d.hidden, 1,
                   0, 0, pr, true, g_ov_split[DBD_STAGE_GEMM_QKV]),
         plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_O], M, d.hidden, qd, 1, 0, 0, pr,
-                  true, g_ov_split[DBD_STAGE_GEMM_O]),
+                  true, g_ov_split[DBD_STAGE_GEMM_O], nf),
         plan_gemm(d.dtype, EPI_SWIGLU, g_ov_cfg[DBD_STAGE_GEMM_GATEUP], M, 2 * d.ffn, d.hidden,
                   1, 1, d.ffn, pr, true, g_ov_split[DBD_STAGE_GEMM_GATEUP]),
         plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_DOWN], M, d.hidden, d.ffn, 1, 0, 0,
-                  pr, true, g_ov_split[DBD_STAGE_GEMM_DOWN]),
+                  pr, true, g_ov_split[DBD_STAGE_GEMM_DOWN], nf),
+        plan_gemm(d.dtype, EPI_RESID, g_ov_cfg[DBD_STAGE_GEMM_DOWN], M, d.hidden, d.ffn, 1, 0, 0,
+                  pr, true, g_ov_split[DBD_STAGE_GEMM_DOWN], false),
         plan_gemm(d.dtype, temperature > 0.f ? EPI_STORE_F32 : EPI_ARGMAX,
                   g_ov_cfg[DBD_STAGE_GEMM_LMHEAD], Md, d.vocab, d.hidden, 1, 0, 0, pr, true,
                   g_ov_split[DBD_STAGE_GEMM_LMHEAD])};
     for (const GemmPlan& p : pl) bp = std::max(bp, need(p));
-    if (lm_bn) *lm_bn = pl[4].bn;
+    if (lm_bn) *lm_bn = pl[5].bn;
   }
   if (d.n_target_layers > 0 && t > 0) {
     ip = need(plan_gemm(d.dtype, EPI_CTXKV, g_ov_cfg[DBD_STAGE_GEMM_CTXKV], t, 2 * kd, d.hidden,

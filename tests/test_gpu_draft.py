@@ -516,6 +516,53 @@ def test_small_block_fused_residual_norm_matches_oracle(pairs):
     assert torch.equal(logits, logits2)
 
 
+FUSED_NORM_OVERRIDES = [
+    {"gemm_o": (16, 4), "gemm_down": (16, 3)},
+    {"gemm_o": (15, 2), "gemm_down": (14, 5)},
+]
+
+
+@pytest.mark.parametrize("batch", [13, 20])
+@pytest.mark.parametrize("ov", range(len(FUSED_NORM_OVERRIDES)))
+def test_register_staged_fused_residual_norm_matches_oracle(batch, ov):
+    """208 and 320 block rows (a ragged 256-row tile) with the O and down projections on the
+    register-staged 256-row tiles with split K (128-, 192- and 256-column tiles; 1,024 columns
+    leave a ragged 192-column tile): their units store row-major partials and the fused
+    reduction writes the residual and the next RMSNorm, so the row-norm stage keeps only the
+    embedding, the first layer's attention norm and the final norm."""
+    sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
+                            n_layers=3, n_target_layers=2, vocab=2048, dtype="bf16")
+    wl = synth.Workload(name="fused-norm-w8r", shape=sh, batch=batch, block_len=16, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=60, ctx_hi=140, ctx_source="hidden",
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=8)
+    print(f"draft_block workload=fused-norm-w8r batch={batch} overrides="
+          f"{FUSED_NORM_OVERRIDES[ov]}", flush=True)
+    for st, (cfg, sp) in FUSED_NORM_OVERRIDES[ov].items():
+        dbd.gemm_override(st, cfg, sp)
+    try:
+        case = Case(wl, dev=DEV)
+        case.fill_cache()
+        drafts, logits, status = case.step()
+        torch.cuda.synchronize()
+        assert torch.all(status == 0)
+        _check_drafts_property(case, drafts, logits)
+        _compare(case, logits, range(wl.batch), [])
+        dbd.timing_reset()
+        dbd.timing_enable(True)
+        try:
+            _, logits2, _ = case.step()
+            torch.cuda.synchronize()
+            launches = dbd.timing_read()["rownorm"][1]
+        finally:
+            dbd.timing_enable(False)
+            dbd.timing_reset()
+        assert launches == 3, launches
+        assert torch.equal(logits, logits2)
+    finally:
+        for st in FUSED_NORM_OVERRIDES[ov]:
+            dbd.gemm_override(st, -1, 0)
+
+
 def test_long_context_single_sequence_many_splits():
     """One sequence over a 716-position cache: 12 key chunks per kv head, fewer chunks than
     attention workgroups, so every chunk is a piece of its own and the combine kernel merges
