@@ -43,9 +43,10 @@ __device__ __forceinline__ float group_max4(float x) {
 // Work is counted in chunks of KCH keys.  A segment is one (sequence n, kv head g, row block rb)
 // with ceil(L_n / KCH) chunks; the segments lie end to end in (n, g, rb) order and their T
 // chunks are cut into P equal ranges, one per workgroup, whatever the context lengths, so every
-// workgroup streams the same number of bytes.  A range may begin or end inside a segment: such a
-// piece publishes its unnormalised output and (max, sum) as a partial that
-// attn_stream_combine_kernel merges; a piece holding a whole segment writes the output itself.
+// workgroup streams the same number of bytes.  The part of a segment one range holds (a piece,
+// the whole segment or a part of it) is published as a partial, its unnormalised output rows
+// and (max, sum) per row, and attn_stream_combine_kernel merges the pieces of every segment and
+// writes the output.
 //
 // Each workgroup is four waves of 16 query rows (one row block).  Chunk x of the range is
 // staged global -> registers -> LDS slot x & 1; DEPTH chunks are loaded ahead (two register
