@@ -330,14 +330,18 @@ __device__ __forceinline__ void wait_stages(int n) {
 }
 
 // Work unit -> (m tile, n tile, split): units go to the 8 XCDs round robin; each XCD takes a
-// contiguous range, split fastest, then m, so the splits of a tile and the m tiles of a weight
-// column tile run on one XCD close in time.
+// contiguous range of the order (split slowest, then n, then m), so the m tiles of a weight
+// column tile run on one XCD close in time, and an XCD reads only its splits' part of the
+// activation rows (with split 4 on 512 x 4096 x 12288, one quarter of the 12.6 MB activation
+// per XCD instead of all of it: down 0.488 -> 0.482 ms per step, the SpecDiff-2 step 7.02 ->
+// 6.95 ms, measured against split fastest).
 __device__ __forceinline__ void unit_of(int bid, int total, int tiles_m, int split, int* tm,
                                         int* tn, int* sp) {
   const int q = total >> 3;
   const int t = bid < (q << 3) ? (bid & 7) * q + (bid >> 3) : bid;
-  *sp = t % split;
-  const int tile = t / split;
+  const int tiles = total / split;
+  *sp = t / tiles;
+  const int tile = t - *sp * tiles;
   *tm = tile % tiles_m;
   *tn = tile / tiles_m;
 }
