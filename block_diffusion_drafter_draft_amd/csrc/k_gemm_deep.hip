@@ -888,26 +888,31 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
   run_epilogue<bf16, TM, BN, KIND, R::NT>(e, Cs, m0 + r0, n0, tn, z, M, N);
 }
 
-// Split-K reduction of a skinny residual projection fused with the RMSNorm that follows it: one
-// workgroup per row (a skinny launch has at most 64) adds the row's S row-major partials in
-// split order, adds the sum to the residual as the residual epilogue does, writes the residual
-// and the normalised row T(x / sqrt(mean(x^2) + eps) * g), with the low part of the bf16 pair
-// when norm_out_lo is set.  The loads of RB splits are in flight together.
-template <typename T>
+// Split-K reduction of a residual projection fused with the RMSNorm that follows it (skinny
+// tiles, or the register-staged 256-row tiles without pair rows): one workgroup per row adds the
+// row's S row-major partials in split order, adds the sum to the residual as the residual
+// epilogue does, and writes the residual and the normalised bf16 row x / sqrt(mean(x^2) + eps) * g,
+// with the low part of the bf16 pair when norm_out_lo is set.  Every thread covers 4 columns per
+// 4096: the gain and the residual are loaded with the first RB splits' partials, and the
+// normalised columns go out as 8-byte stores.
 __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e) {
   constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread, RB = 8;
   static_assert(NT * MAXG * 4 == kResidNormMaxCols, "row coverage of resid_norm_fits");
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   __shared__ float red[NT / 64];
   const int row = blockIdx.x, tid = threadIdx.x, N = a.N, S = a.split;
   const float* part = reinterpret_cast<const float*>(a.part) + (int64_t)row * N;
   const int64_t ps = (int64_t)a.M * N;                  // one split's partials
   float* xr = reinterpret_cast<float*>(e.C) + (int64_t)row * N;
+  const bf16* g = reinterpret_cast<const bf16*>(e.norm_g);
   f32x4 acc[MAXG], xv[MAXG];
+  bf16x4 gv[MAXG];
 #pragma unroll
   for (int q = 0; q < MAXG; ++q) {
     const int i = (tid + q * NT) * 4;
     if (i < N) {
       xv[q] = *reinterpret_cast<const f32x4*>(xr + i);
+      gv[q] = *reinterpret_cast<const bf16x4*>(g + i);
       acc[q] = *reinterpret_cast<const f32x4*>(part + i);
     }
   }
@@ -944,20 +949,21 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e)
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) tot += red[w];
   const float inv = rsqrtf(tot / (float)N + e.norm_eps);
-  const T* g = reinterpret_cast<const T*>(e.norm_g);
-  T* o = reinterpret_cast<T*>(e.norm_out) + (int64_t)row * N;
-  T* ol = e.norm_out_lo ? reinterpret_cast<T*>(e.norm_out_lo) + (int64_t)row * N : nullptr;
+  bf16* o = reinterpret_cast<bf16*>(e.norm_out) + (int64_t)row * N;
+  bf16* ol = e.norm_out_lo ? reinterpret_cast<bf16*>(e.norm_out_lo) + (int64_t)row * N : nullptr;
 #pragma unroll
   for (int q = 0; q < MAXG; ++q) {
     const int i = (tid + q * NT) * 4;
     if (i >= N) continue;
+    bf16x4 hi, lo;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float y = xv[q][c] * inv * to_f(g[i + c]);
-      const T hi = from_f<T>(y);
-      o[i + c] = hi;
-      if (ol) ol[i + c] = from_f<T>(y - to_f(hi));
+      const float y = xv[q][c] * inv * (float)gv[q][c];
+      hi[c] = (bf16)y;
+      lo[c] = (bf16)(y - (float)hi[c]);
     }
+    *reinterpret_cast<bf16x4*>(o + i) = hi;
+    if (ol) *reinterpret_cast<bf16x4*>(ol + i) = lo;
   }
 }
 
@@ -976,7 +982,7 @@ static void launch_w8r(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   hipLaunchKernelGGL((gemm_w8r_kernel<BN, KIND, WGM, PR>), dim3(units, 1, batch), dim3(512),
                      0, s, a, e);
   if (S > 1 && KIND == EPI_RESID && !PR && e.norm_g)
-    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+    hipLaunchKernelGGL(resid_norm_kernel, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
   else if (S > 1)
     launch_reduce<256, BN, WGM, 8 / WGM, KIND, PR>(a, e, batch, s);
 }
@@ -989,7 +995,7 @@ static void launch_skinny(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, KIND, SPLITA>), dim3(units, 1, batch), dim3(256), 0,
                      s, a, e);
   if (S > 1 && KIND == EPI_RESID && e.norm_g)
-    hipLaunchKernelGGL(resid_norm_kernel<bf16>, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+    hipLaunchKernelGGL(resid_norm_kernel, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
   else if (S > 1)
     launch_reduce<MT, 128, 1, 4, KIND>(a, e, batch, s);
 }

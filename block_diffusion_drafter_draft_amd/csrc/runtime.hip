@@ -483,6 +483,12 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   if (!w->attn_norm_w || !w->wq || !w->wk_draft || !w->wv_draft || !w->wo || !w->mlp_norm_w ||
       !w->w_gate || !w->w_up || !w->w_down || !w->final_norm_w || !w->embed || !w->lm_head)
     return fail(DBD_ERR_ARG, "a required weight pointer is NULL");
+  // the kernels read weights with 8- and 16-byte vector loads
+  for (const void* p : {(const void*)w->mix_logits, w->mix_norm_w, w->wk_ctx, w->wv_ctx,
+                        w->attn_norm_w, w->wq, w->wk_draft, w->wv_draft, w->wo, w->mlp_norm_w,
+                        w->w_gate, w->w_up, w->w_down, w->final_norm_w, w->embed, w->lm_head,
+                        w->fc_w, w->fc_norm_w})
+    if (p && !aligned16(p)) return fail(DBD_ERR_SHAPE, "weight pointer %p is not 16-byte aligned", p);
   const int es = elem_size(d.dtype);
   const int vec = 16 / es;
   if (d.n_target_layers > 0) {

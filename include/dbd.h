@@ -97,8 +97,9 @@ typedef struct {
                                 wk_draft / wv_draft (no K/V split; wk_ctx / wv_ctx unused) */
 } dbd_model_desc;
 
-/* Drafter weights (device pointers, element type desc.dtype unless noted).  Per-layer tensors
- * are stacked over the L_d draft layers. */
+/* Drafter weights (device pointers, element type desc.dtype unless noted, each 16-byte aligned:
+ * draft_block returns DBD_ERR_SHAPE otherwise).  Per-layer tensors are stacked over the L_d
+ * draft layers. */
 typedef struct {
   const float* mix_logits;   /* [L_d, L_t] fp32 mixing logits (unused if L_t == 0) */
   const void* mix_norm_w;    /* [L_d, H] RMSNorm gain after mixing (unused if L_t == 0) */

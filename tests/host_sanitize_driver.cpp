@@ -72,6 +72,20 @@ int main() {
   EXPECT(draft_block(&d, &w, 4, 16, 1, (int32_t*)fake, fake, 9 * 4096, 4096, 8, (int32_t*)fake,
                      (int32_t*)fake, fake, fake, 3136, 1, 0.f, 0, (int32_t*)fake, nullptr,
                      nullptr, fake, 1 << 30, nullptr) == DBD_ERR_ARG);        // NULL weights
+  {
+    // every weight present, one of them 8 bytes off a 16-byte boundary
+    dbd_weights wa;
+    const void** slots = reinterpret_cast<const void**>(&wa);
+    for (size_t i = 0; i < sizeof wa / sizeof(void*); ++i) slots[i] = fake + 4096 * (i + 1);
+    for (size_t bad = 0; bad < sizeof wa / sizeof(void*); ++bad) {
+      slots[bad] = fake + 4096 * (bad + 1) + 8;
+      EXPECT(draft_block(&d, &wa, 4, 16, 1, (int32_t*)fake, fake, 9 * 4096, 4096, 8,
+                         (int32_t*)fake, (int32_t*)fake, fake, fake, 3136, 1, 0.f, 0,
+                         (int32_t*)fake, nullptr, nullptr, fake, 1 << 30, nullptr) ==
+             DBD_ERR_SHAPE);
+      slots[bad] = fake + 4096 * (bad + 1);
+    }
+  }
   EXPECT(draft_block(&d, nullptr, 4, 16, 1, nullptr, nullptr, 0, 0, 0, nullptr, nullptr, nullptr,
                      nullptr, 3136, 1, 0.f, 0, nullptr, nullptr, nullptr, nullptr, 0,
                      nullptr) == DBD_ERR_ARG);
