@@ -99,9 +99,14 @@ __device__ __forceinline__ void rope8(const float* row, int c, int hd, const flo
   }
 }
 
+// cs_pre / pos_pre (Q/K/V only, optional): this thread's rotation factors (CPT of them, for the
+// columns it rotates) and, for threads tid < TM, its row's position, loaded by the caller ahead
+// of time so that the epilogue does not wait on them.
 template <typename T, int TM, int BN, int KIND, int NT = 256>
 __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, int m0, int n0,
-                                             int tn, int z, int M, int N) {
+                                             int tn, int z, int M, int N,
+                                             const float2* cs_pre = nullptr,
+                                             const int* pos_pre = nullptr) {
   constexpr int CS_LD = BN + 4;                 // fp32 tile row stride in LDS
   constexpr int TPR = NT / TM;                  // threads per tile row
   static_assert(NT % TM == 0 && BN % TPR == 0, "epilogue thread layout");
@@ -200,7 +205,7 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
     if (tid < TM) {
       const int mm = m0 + tid;
       const bool ok = tid < rows;
-      s_pos[tid] = ok ? e.row_pos[mm] : -1;
+      s_pos[tid] = ok ? (pos_pre ? *pos_pre : e.row_pos[mm]) : -1;
       s_seq[tid] = ok ? (ctx ? e.row_seq[mm] : mm / e.block_len) : -1;
     }
     __syncthreads();
@@ -220,7 +225,7 @@ __device__ __forceinline__ void run_epilogue(const EpiArgs& e, const float* Cs, 
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             const int i = ((cb + c8 + q) % e.hd) % half;
-            cs[q] = e.rope[(int64_t)m * half + i];
+            cs[q] = cs_pre ? cs_pre[c8 + q] : e.rope[(int64_t)m * half + i];
           }
 #pragma unroll
           for (int h8 = 0; h8 < 16; h8 += 8) {

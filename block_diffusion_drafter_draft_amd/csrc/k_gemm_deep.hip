@@ -855,6 +855,19 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
   const int wm = r0 / WTM, i0 = (r0 % WTM) / 16;
   const int wl = (r0 + BM / 2) / WTM, il = ((r0 + BM / 2) % WTM) / 16;   // PR: low-part rows
   const f32x4* part = reinterpret_cast<const f32x4*>(a.part) + (int64_t)tile * S * NW * FR;
+  // Q/K/V: the epilogue's rotation factors and row positions are loaded now, with the
+  // partials, instead of after them
+  constexpr int ETPR = R::NT / TM, ECPT = BN / ETPR;     // run_epilogue's thread layout
+  float2 cs_pre[KIND == EPI_QKV ? ECPT : 1];
+  int pos_pre = -1;
+  if constexpr (KIND == EPI_QKV) {
+    const int em = m0 + r0 + tid / ETPR, ecb = (tid % ETPR) * ECPT, half = e.hd / 2;
+    if (n0 < e.qd + e.kd && em < M) {
+#pragma unroll
+      for (int q = 0; q < ECPT; ++q) cs_pre[q] = e.rope[(int64_t)em * half + ((ecb + q) % e.hd) % half];
+    }
+    if (tid < TM && m0 + r0 + tid < M) pos_pre = e.row_pos[m0 + r0 + tid];
+  }
   int off[UPT], offl[PR ? UPT : 1];
   f32x4 v[UPT];
 #pragma unroll
@@ -885,7 +898,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
     for (int r = 0; r < 4; ++r) Cs[(di * 16 + (lane >> 4) * 4 + r) * CS_LD + col] = v[q][r];
   }
   __syncthreads();
-  run_epilogue<bf16, TM, BN, KIND, R::NT>(e, Cs, m0 + r0, n0, tn, z, M, N);
+  if constexpr (KIND == EPI_QKV)
+    run_epilogue<bf16, TM, BN, KIND, R::NT>(e, Cs, m0 + r0, n0, tn, z, M, N, cs_pre, &pos_pre);
+  else
+    run_epilogue<bf16, TM, BN, KIND, R::NT>(e, Cs, m0 + r0, n0, tn, z, M, N);
 }
 
 // Split-K reduction of a residual projection fused with the RMSNorm that follows it (skinny
