@@ -98,9 +98,11 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ mix + RMSNorm
-// One workgroup per ingested token.  Each thread owns CPT chunks of VEC consecutive hidden
-// elements, reads the token's L_t target layers once (16-byte coalesced loads) and keeps the L_d
-// mixed values in registers; the L_d sums of squares are reduced together.
+// One workgroup of NT threads per ingested token.  Each thread owns CPT chunks of VEC consecutive
+// hidden elements, reads the token's L_t target layers once (16-byte coalesced loads) and keeps
+// the L_d mixed values in registers; the L_d sums of squares are reduced together.  With one
+// chunk per thread every target layer's chunk and the L_d gain chunks are loaded at once, before
+// the mixing weights are ready; with more, target layer i + 1 is loaded while layer i is mixed.
 constexpr int kMaxLd = 8;
 constexpr int kMaxLt = 16;
 
@@ -108,16 +110,30 @@ template <typename T> struct Vec16;
 template <> struct Vec16<bf16> { static constexpr int n = 8; };
 template <> struct Vec16<float> { static constexpr int n = 4; };
 
-template <typename T, int CPT>
-__global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
+template <typename T, int CPT, int NT>
+__global__ __launch_bounds__(NT) void mix_rmsnorm_kernel(
     const T* __restrict__ hid, int64_t ts, int64_t ls, int n_tok, int H, int Lt, int Ld,
     const float* __restrict__ mix_logits, int raw, const T* __restrict__ g, T* __restrict__ out,
     T* __restrict__ out_lo, float eps) {
-  constexpr int VEC = Vec16<T>::n;
+  constexpr int VEC = Vec16<T>::n, NW = NT / 64;
+  constexpr bool ALL = CPT == 1;                 // every layer's chunk in flight at once
   __shared__ float w[kMaxLd * kMaxLt];
-  __shared__ float red[kMaxLd][4];
+  __shared__ float red[kMaxLd][NW];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int nch = H / VEC;
+  const T* base = hid + (int64_t)t * ts;
+  u32x4 hv[ALL ? kMaxLt : 1], gv[ALL ? kMaxLd : 1];
+  if constexpr (ALL) {
+    if (tid < nch) {
+#pragma unroll
+      for (int i = 0; i < kMaxLt; ++i)
+        if (i < Lt) hv[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * ls + tid * VEC);
+#pragma unroll
+      for (int l = 0; l < kMaxLd; ++l)
+        if (l < Ld) gv[l] = *reinterpret_cast<const u32x4*>(g + (int64_t)l * H + tid * VEC);
+    }
+  }
   if (tid < Ld) {
     const float* lg = mix_logits + tid * Lt;
     float m = -INFINITY;
@@ -127,35 +143,21 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
     for (int i = 0; i < Lt; ++i) w[tid * Lt + i] = raw ? lg[i] : expf(lg[i] - m) / sum;
   }
   __syncthreads();
-  const int nch = H / VEC;
   float acc[kMaxLd][CPT * VEC];
 #pragma unroll
   for (int l = 0; l < kMaxLd; ++l)
 #pragma unroll
     for (int e = 0; e < CPT * VEC; ++e) acc[l][e] = 0.f;
-  const T* base = hid + (int64_t)t * ts;
-  // target layer i + 1 is loaded while layer i is mixed, so the L_t loads of a thread do not
-  // wait for each other
-  u32x4 cur[CPT], nxt[CPT];
-  auto load = [&](u32x4* r, int i) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 256;
-      if (ch < nch) r[c] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * ls + ch * VEC);
-    }
-  };
-  load(cur, 0);
-  for (int i = 0; i < Lt; ++i) {
-    if (i + 1 < Lt) load(nxt, i + 1);
+  auto mix = [&](const u32x4* r, int i) __attribute__((always_inline)) {
     float wl[kMaxLd];
 #pragma unroll
     for (int l = 0; l < kMaxLd; ++l) wl[l] = l < Ld ? w[l * Lt + i] : 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 256;
+      const int ch = tid + c * NT;
       if (ch < nch) {
         T v[VEC];
-        *reinterpret_cast<u32x4*>(v) = cur[c];
+        *reinterpret_cast<u32x4*>(v) = r[c];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           const float x = to_f(v[e]);
@@ -164,8 +166,29 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
         }
       }
     }
+  };
+  if constexpr (ALL) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) cur[c] = nxt[c];
+    for (int i = 0; i < kMaxLt; ++i)
+      if (i < Lt) mix(&hv[i], i);
+  } else {
+    // target layer i + 1 is loaded while layer i is mixed, so the L_t loads of a thread do not
+    // wait for each other
+    u32x4 cur[CPT], nxt[CPT];
+    auto load = [&](u32x4* r, int i) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int ch = tid + c * NT;
+        if (ch < nch) r[c] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * ls + ch * VEC);
+      }
+    };
+    load(cur, 0);
+    for (int i = 0; i < Lt; ++i) {
+      if (i + 1 < Lt) load(nxt, i + 1);
+      mix(cur, i);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) cur[c] = nxt[c];
+    }
   }
   float ss[kMaxLd];
 #pragma unroll
@@ -183,19 +206,22 @@ __global__ __launch_bounds__(256) void mix_rmsnorm_kernel(
 #pragma unroll
   for (int l = 0; l < kMaxLd; ++l) {
     if (l >= Ld) break;
-    const float ms = (red[l][0] + red[l][1] + red[l][2] + red[l][3]) / (float)H;
-    const float inv = rsqrtf(ms + eps);
+    float tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) tot += red[l][q];
+    const float inv = rsqrtf(tot / (float)H + eps);
     T* o = out + ((int64_t)l * n_tok + t) * H;
     const T* gl = g + (int64_t)l * H;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 256;
+      const int ch = tid + c * NT;
       if (ch < nch) {
-        T gv[VEC], ov[VEC], lv[VEC];
-        *reinterpret_cast<u32x4*>(gv) = *reinterpret_cast<const u32x4*>(gl + ch * VEC);
+        T gr[VEC], ov[VEC], lv[VEC];
+        if constexpr (ALL) *reinterpret_cast<u32x4*>(gr) = gv[l];
+        else *reinterpret_cast<u32x4*>(gr) = *reinterpret_cast<const u32x4*>(gl + ch * VEC);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float y = acc[l][c * VEC + e] * inv * to_f(gv[e]);
+          const float y = acc[l][c * VEC + e] * inv * to_f(gr[e]);
           ov[e] = from_f<T>(y);
           lv[e] = from_f<T>(y - to_f(ov[e]));     // low part of the bf16 pair
         }
@@ -213,20 +239,22 @@ static hipError_t mix_dispatch(const void* hid, int64_t ts, int64_t ls, int n_to
                                int Ld, const float* ml, int raw, const void* g, void* out,
                                void* out_lo, float eps, hipStream_t s) {
   constexpr int VEC = Vec16<T>::n;
-  const int cpt = ceil_div(H / VEC, 256);
+  const int nch = H / VEC;
   const T* h = (const T*)hid;
   if (n_tok == 0) return hipSuccess;
-  if (cpt <= 1)
-    hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 1>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps);
-  else if (cpt <= 2)
-    hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 2>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps);
-  else if (cpt <= 4)
-    hipLaunchKernelGGL((mix_rmsnorm_kernel<T, 4>), dim3(n_tok), dim3(256), 0, s, h, ts, ls, n_tok,
-                       H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps);
-  else
+#define DBD_MIX(CPT, NT)                                                                       \
+  hipLaunchKernelGGL((mix_rmsnorm_kernel<T, CPT, NT>), dim3(n_tok), dim3(NT), 0, s, h, ts, ls, \
+                     n_tok, H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps)
+  if (nch <= 256) DBD_MIX(1, 256);
+  else if (nch <= 512) DBD_MIX(1, 512);
+  else if (nch <= 1024) DBD_MIX(2, 512);
+  else if constexpr (VEC == 4) {                  // fp32 rows of up to 8192
+    if (nch <= 2048) DBD_MIX(4, 512);
+    else return hipErrorInvalidValue;
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef DBD_MIX
   return hipGetLastError();
 }
 
@@ -298,12 +326,17 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
   const float* xr = x + (int64_t)ri * H;
   float4 v[MAXG];
+  T gv[MAXG][4];                                  // the gain, loaded with the row
   float s = 0.f;
 #pragma unroll
   for (int q = 0; q < MAXG; ++q) {
     const int i = (threadIdx.x + q * 256) * 4;
     if (i < H) {
       v[q] = *reinterpret_cast<const float4*>(xr + i);
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint2*>(gv[q]) = *reinterpret_cast<const uint2*>(g + i);
+      else
+        *reinterpret_cast<float4*>(gv[q]) = *reinterpret_cast<const float4*>(g + i);
       s += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
     }
   }
@@ -317,11 +350,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int q = 0; q < MAXG; ++q) {
     const int i = (threadIdx.x + q * 256) * 4;
     if (i >= H) continue;
-    T gv[4], hi[4], lo[4];
-    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(gv) = *reinterpret_cast<const uint2*>(g + i);
-    else *reinterpret_cast<float4*>(gv) = *reinterpret_cast<const float4*>(g + i);
-    const float y[4] = {v[q].x * inv * to_f(gv[0]), v[q].y * inv * to_f(gv[1]),
-                        v[q].z * inv * to_f(gv[2]), v[q].w * inv * to_f(gv[3])};
+    T hi[4], lo[4];
+    const float y[4] = {v[q].x * inv * to_f(gv[q][0]), v[q].y * inv * to_f(gv[q][1]),
+                        v[q].z * inv * to_f(gv[q][2]), v[q].w * inv * to_f(gv[q][3])};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       hi[e] = from_f<T>(y[e]);
