@@ -171,7 +171,8 @@ hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls
                               const void* g, void* out, void* out_lo, float eps, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H,
-                        int V, float* x, hipStream_t s);
+                        int V, float* x, const void* g, void* out, void* out_lo, float eps,
+                        hipStream_t s, bool* normed);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, void* out, void* out_lo,
                           int rows, int H, float eps, int block_len, int n_anchor, hipStream_t s);
 // cfg: bf16 block-tile configuration index (see dbd_gemm_nt in dbd.h), -1 = pick for the shape

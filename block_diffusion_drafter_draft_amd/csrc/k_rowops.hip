@@ -271,36 +271,90 @@ hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
                                                     const T* __restrict__ E, int H, int V,
-                                                    float* __restrict__ x) {
-  const int r = blockIdx.x;
+                                                    float* __restrict__ x,
+                                                    const T* __restrict__ g,
+                                                    T* __restrict__ out, T* __restrict__ out_lo,
+                                                    float eps) {
+  constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte load
+  constexpr int MAXC = 8192 / (256 * VEC);              // chunks per thread at H = 8192
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
   int id = tok[r];
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);       // out-of-range ids are clamped
   const T* e = E + (int64_t)id * H;
   float* o = x + (int64_t)r * H;
-  constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte load
-  if (H % VEC == 0 && (((uintptr_t)e | (uintptr_t)o) & 15) == 0) {
-    // 16-byte loads, two in flight per thread for H = 4096 bf16
-    for (int i = threadIdx.x * VEC; i < H; i += 256 * VEC) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(e + i);
-      const T* v = reinterpret_cast<const T*>(&raw);
+  if (H % VEC != 0 || ((((uintptr_t)e | (uintptr_t)o) & 15) != 0)) {
+    for (int i = tid; i < H; i += 256) o[i] = to_f(e[i]);   // (never with a norm: see launch)
+    return;
+  }
+  // 16-byte loads, all of a thread's chunks (and the gain's) in flight at once
+  u32x4 raw[MAXC], gr[MAXC];
 #pragma unroll
-      for (int q = 0; q < VEC; q += 4)
-        *reinterpret_cast<f32x4*>(o + i + q) =
-            f32x4{to_f(v[q]), to_f(v[q + 1]), to_f(v[q + 2]), to_f(v[q + 3])};
+  for (int c = 0; c < MAXC; ++c) {
+    const int i = (tid + c * 256) * VEC;
+    if (i < H) {
+      raw[c] = *reinterpret_cast<const u32x4*>(e + i);
+      if (g) gr[c] = *reinterpret_cast<const u32x4*>(g + i);
     }
-  } else {
-    for (int i = threadIdx.x; i < H; i += 256) o[i] = to_f(e[i]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int i = (tid + c * 256) * VEC;
+    if (i >= H) continue;
+    const T* v = reinterpret_cast<const T*>(&raw[c]);
+#pragma unroll
+    for (int q = 0; q < VEC; q += 4) {
+      const f32x4 f = f32x4{to_f(v[q]), to_f(v[q + 1]), to_f(v[q + 2]), to_f(v[q + 3])};
+      *reinterpret_cast<f32x4*>(o + i + q) = f;
+      ss += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
+    }
+  }
+  if (!g) return;
+  // the first layer's attention RMSNorm of the row (as rmsnorm_kernel computes it)
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  T* no = out + (int64_t)r * H;
+  T* nl = out_lo ? out_lo + (int64_t)r * H : nullptr;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int i = (tid + c * 256) * VEC;
+    if (i >= H) continue;
+    const T* v = reinterpret_cast<const T*>(&raw[c]);
+    const T* gv = reinterpret_cast<const T*>(&gr[c]);
+    T hi[VEC], lo[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      const float y = to_f(v[q]) * inv * to_f(gv[q]);
+      hi[q] = from_f<T>(y);
+      lo[q] = from_f<T>(y - to_f(hi[q]));
+    }
+    *reinterpret_cast<u32x4*>(no + i) = *reinterpret_cast<const u32x4*>(hi);
+    if (nl) *reinterpret_cast<u32x4*>(nl + i) = *reinterpret_cast<const u32x4*>(lo);
   }
 }
 
+// With g set (and H a multiple of the 16-byte vector, 16-byte aligned rows) the kernel also
+// writes the row's RMSNorm with gain g to out (and its bf16 low part to out_lo) and *normed is
+// set; otherwise the caller runs the norm itself.
 hipError_t launch_embed(int dtype, const int32_t* tokens, const void* E, int rows, int H, int V,
-                        float* x, hipStream_t s) {
+                        float* x, const void* g, void* out, void* out_lo, float eps,
+                        hipStream_t s, bool* normed) {
+  const int es = dtype == 1 ? 2 : 4;
+  const bool fuse = g && H % (16 / es) == 0 && H <= 8192 && ((uintptr_t)E & 15) == 0 &&
+                    ((uintptr_t)x & 15) == 0 && ((uintptr_t)g & 15) == 0 &&
+                    ((uintptr_t)out & 15) == 0 && ((uintptr_t)out_lo & 15) == 0 &&
+                    (int64_t)H * es % 16 == 0;
+  if (!fuse) g = out = out_lo = nullptr;
   if (dtype == 1)
     hipLaunchKernelGGL(embed_kernel<bf16>, dim3(rows), dim3(256), 0, s, tokens, (const bf16*)E,
-                       H, V, x);
+                       H, V, x, (const bf16*)g, (bf16*)out, (bf16*)out_lo, eps);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, s, tokens,
-                       (const float*)E, H, V, x);
+                       (const float*)E, H, V, x, (const float*)g, (float*)out, nullptr, eps);
+  if (normed) *normed = fuse;
   return hipGetLastError();
 }
 

@@ -605,9 +605,12 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
   }
 
   // 2. block forward
-  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_embed(d.dtype, block_tokens, w->embed, M, H, V, b.x, st));
+  // the embedding gather also writes the first layer's attention norm when it can
+  bool normed = false;        // the previous kernel already wrote this layer's norm
+  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_embed(d.dtype, block_tokens, w->embed, M, H, V, b.x,
+                                                w->attn_norm_w, b.xn, b.xn_lo, d.rms_eps, st,
+                                                &normed));
   const char* cw = nullptr;
-  bool normed = false;        // the previous down projection already wrote this layer's norm
   for (int l = 0; l < d.n_layers; ++l) {
     auto lw = [&](const void* p, int64_t per_layer) {
       return (const void*)((const char*)p + (int64_t)l * per_layer * es);

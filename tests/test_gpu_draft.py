@@ -502,7 +502,8 @@ def test_small_block_fused_residual_norm_matches_oracle(pairs):
     assert torch.all(status == 0)
     _check_drafts_property(case, drafts, logits)
     _compare(case, logits, range(wl.batch), [])
-    # the row-norm stage keeps the embedding, the first layer's attention norm and the final norm
+    # the row-norm stage keeps the embedding (which writes the first layer's attention norm) and
+    # the final norm
     dbd.timing_reset()
     dbd.timing_enable(True)
     try:
@@ -512,7 +513,7 @@ def test_small_block_fused_residual_norm_matches_oracle(pairs):
     finally:
         dbd.timing_enable(False)
         dbd.timing_reset()
-    assert launches == 3, launches
+    assert launches == 2, launches
     assert torch.equal(logits, logits2)
 
 
@@ -529,7 +530,7 @@ def test_register_staged_fused_residual_norm_matches_oracle(batch, ov):
     register-staged 256-row tiles with split K (128-, 192- and 256-column tiles; 1,024 columns
     leave a ragged 192-column tile): their units store row-major partials and the fused
     reduction writes the residual and the next RMSNorm, so the row-norm stage keeps only the
-    embedding, the first layer's attention norm and the final norm."""
+    embedding (which writes the first layer's attention norm) and the final norm."""
     sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
                             n_layers=3, n_target_layers=2, vocab=2048, dtype="bf16")
     wl = synth.Workload(name="fused-norm-w8r", shape=sh, batch=batch, block_len=16, n_anchor=1,
@@ -556,7 +557,7 @@ def test_register_staged_fused_residual_norm_matches_oracle(batch, ov):
         finally:
             dbd.timing_enable(False)
             dbd.timing_reset()
-        assert launches == 3, launches
+        assert launches == 2, launches
         assert torch.equal(logits, logits2)
     finally:
         for st in FUSED_NORM_OVERRIDES[ov]:
