@@ -194,8 +194,9 @@ struct GemmPlan {
 GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch, int gateup,
                    int F, bool pair, bool split_ok, int split_req = 0, bool norm = false);
 // Whether a residual projection planned as p, with (pair) or without a bf16-pair A operand,
-// runs the following RMSNorm in its split-K reduction (resid_norm_kernel): the skinny tiles and
-// the register-staged 256-row tiles without pair rows, split, one batch entry.
+// runs the following RMSNorm in its split-K reduction (resid_norm_kernel): the skinny tiles, the
+// register-staged 256-row tiles without pair rows and the deep-ring four-wave tiles, split, one
+// batch entry.
 bool gemm_fuses_norm(const GemmPlan& p, bool pair, int batch);
 constexpr int kMaxGemmCfg = 18;
 constexpr int kMaxGemmSplit = 16;

@@ -403,7 +403,8 @@ static double model_us(int kind, int cfg, int M, int Nv, int K, int batch, int S
     t += 1.3e-6 * (double)M * Nv * batch;
   // a requested residual norm: inside the split reduction it adds the normalised rows' writes;
   // otherwise it is a launch of its own that reads the residual back
-  if (norm) t += cfg == 16 && S > 1 && !pair ? 0.5e-6 * M * Nv : 2.0 + 1.5e-6 * M * Nv;
+  const bool fuses = S > 1 && ((cfg == 16 && !pair) || (cfg >= 8 && cfg <= 10));
+  if (norm) t += fuses ? 0.5e-6 * M * Nv : 2.0 + 1.5e-6 * M * Nv;
   return t;
 }
 
@@ -488,7 +489,10 @@ GemmPlan plan_gemm(int dtype, int kind, int cfg, int M, int N, int K, int batch,
 
 bool gemm_fuses_norm(const GemmPlan& p, bool pair, int batch) {
   if (p.cfg < 0 || p.split <= 1 || batch != 1) return false;
-  return is_skinny(p.cfg) || (p.cfg >= 14 && p.cfg <= 16 && !pair);
+  // the skinny tiles, the register-staged 256-row tiles without pair rows, and the deep-ring
+  // four-wave tiles (a bf16 pair there is a second A part, summed in the accumulators)
+  return is_skinny(p.cfg) || (p.cfg >= 14 && p.cfg <= 16 && !pair) ||
+         (p.cfg >= 8 && p.cfg <= 10);
 }
 
 template <int KIND>

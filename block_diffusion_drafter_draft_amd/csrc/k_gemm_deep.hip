@@ -186,6 +186,25 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a, EpiArgs e) {
   // split-K: publish this unit's partial; gemm_reduce_kernel adds the partials and runs the
   // epilogue
   if (S > 1) {
+    if constexpr (KIND == EPI_RESID) {
+      if (e.norm_g) {
+        // row-major partials [S][M][N] for resid_norm_kernel, which reduces whole rows and
+        // writes the RMSNorm that follows the projection (a bf16-pair A is already summed)
+        float* pr = reinterpret_cast<float*>(a.part) + (int64_t)sp * M * N;
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j) {
+            const int col = n0 + wn * C::WTN + j * 16 + fr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = m0 + wm * C::WTM + i * 16 + fk * 4 + r;
+              if (row < M && col < N) pr[(int64_t)row * N + col] = acc[i][j][r];
+            }
+          }
+        return;
+      }
+    }
     const int tiles_n = (N + BN - 1) / BN;
     const int tile = (z * tiles_n + tn) * tiles_m + tm;
     constexpr int FR = C::MI * C::NI * 64;                      // f32x4 per wave
@@ -1033,7 +1052,10 @@ static void launch_deep(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) 
   const int units = ceil_div(a.M, BM) * ceil_div(a.N, BN) * S;
   hipLaunchKernelGGL((gemm_big_kernel<BM, BN, NS, KIND, SPLITA>), dim3(units, 1, batch),
                      dim3(256), 0, s, a, e);
-  if (S > 1) launch_reduce<BM, BN, 2, 2, KIND>(a, e, batch, s);
+  if (S > 1 && KIND == EPI_RESID && e.norm_g)
+    hipLaunchKernelGGL(resid_norm_kernel, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+  else if (S > 1)
+    launch_reduce<BM, BN, 2, 2, KIND>(a, e, batch, s);
 }
 
 // 8: 256 x 128 (3 stages), 9: 128 x 256 (3), 10: 128 x 128 (4): four waves, 32-wide k stages;

@@ -518,27 +518,33 @@ def test_small_block_fused_residual_norm_matches_oracle(pairs):
 
 
 FUSED_NORM_OVERRIDES = [
-    {"gemm_o": (16, 4), "gemm_down": (16, 3)},
-    {"gemm_o": (15, 2), "gemm_down": (14, 5)},
+    ({"gemm_o": (16, 4), "gemm_down": (16, 3)}, 0),
+    ({"gemm_o": (15, 2), "gemm_down": (14, 5)}, 0),
+    ({"gemm_o": (8, 2), "gemm_down": (9, 3)}, 0),
+    ({"gemm_o": (10, 2), "gemm_down": (10, 4)}, 1),
 ]
 
 
 @pytest.mark.parametrize("batch", [13, 20])
 @pytest.mark.parametrize("ov", range(len(FUSED_NORM_OVERRIDES)))
 def test_register_staged_fused_residual_norm_matches_oracle(batch, ov):
-    """208 and 320 block rows (a ragged 256-row tile) with the O and down projections on the
-    register-staged 256-row tiles with split K (128-, 192- and 256-column tiles; 1,024 columns
-    leave a ragged 192-column tile): their units store row-major partials and the fused
-    reduction writes the residual and the next RMSNorm, so the row-norm stage keeps only the
-    embedding (which writes the first layer's attention norm) and the final norm."""
+    """208 and 320 block rows (a ragged last row tile) with the O and down projections split
+    along K on the register-staged 256-row tiles (128-, 192- and 256-column tiles; 1,024 columns
+    leave a ragged 192-column tile) and on the four-wave deep-ring tiles (256 x 128, 128 x 256,
+    and 128 x 128 with the bf16 activation pair as a second A part): their units store row-major
+    partials and the fused reduction writes the residual and the next RMSNorm, so the row-norm
+    stage keeps only the embedding (which writes the first layer's attention norm) and the final
+    norm."""
+    ovs, pairs = FUSED_NORM_OVERRIDES[ov]
     sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
                             n_layers=3, n_target_layers=2, vocab=2048, dtype="bf16")
     wl = synth.Workload(name="fused-norm-w8r", shape=sh, batch=batch, block_len=16, n_anchor=1,
                         n_drafts=1, temperature=0.0, ctx_lo=60, ctx_hi=140, ctx_source="hidden",
-                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=8)
-    print(f"draft_block workload=fused-norm-w8r batch={batch} overrides="
-          f"{FUSED_NORM_OVERRIDES[ov]}", flush=True)
-    for st, (cfg, sp) in FUSED_NORM_OVERRIDES[ov].items():
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=8,
+                        act_pairs=pairs)
+    print(f"draft_block workload=fused-norm-w8r batch={batch} overrides={ovs} pairs={pairs}",
+          flush=True)
+    for st, (cfg, sp) in ovs.items():
         dbd.gemm_override(st, cfg, sp)
     try:
         case = Case(wl, dev=DEV)
@@ -560,7 +566,7 @@ def test_register_staged_fused_residual_norm_matches_oracle(batch, ov):
         assert launches == 2, launches
         assert torch.equal(logits, logits2)
     finally:
-        for st in FUSED_NORM_OVERRIDES[ov]:
+        for st in ovs:
             dbd.gemm_override(st, -1, 0)
 
 
