@@ -924,12 +924,12 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
 }
 
 // Split-K reduction of a residual projection fused with the RMSNorm that follows it (skinny
-// tiles, or the register-staged 256-row tiles without pair rows): one workgroup per row adds the
-// row's S row-major partials in split order, adds the sum to the residual as the residual
-// epilogue does, and writes the residual and the normalised bf16 row x / sqrt(mean(x^2) + eps) * g,
-// with the low part of the bf16 pair when norm_out_lo is set.  Every thread covers 4 columns per
-// 4096: the gain and the residual are loaded with the first RB splits' partials, and the
-// normalised columns go out as 8-byte stores.
+// tiles, register-staged 256-row tiles without pair rows, deep-ring four-wave tiles): one
+// workgroup per row adds the row's S row-major partials in split order, adds the sum to the
+// residual as the residual epilogue does, and writes the residual and the normalised bf16 row
+// x / sqrt(mean(x^2) + eps) * g, with the low part of the bf16 pair when norm_out_lo is set.
+// Thread t owns the groups of 4 columns t and t + 1024; the gain and the residual are loaded
+// with the first RB splits' partials, and the normalised columns go out as 8-byte stores.
 __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e) {
   constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread, RB = 8;
   static_assert(NT * MAXG * 4 == kResidNormMaxCols, "row coverage of resid_norm_fits");

@@ -247,13 +247,8 @@ static hipError_t mix_dispatch(const void* hid, int64_t ts, int64_t ls, int n_to
                      n_tok, H, Lt, Ld, ml, raw, (const T*)g, (T*)out, (T*)out_lo, eps)
   if (nch <= 256) DBD_MIX(1, 256);
   else if (nch <= 512) DBD_MIX(1, 512);
-  else if (nch <= 1024) DBD_MIX(2, 512);
-  else if constexpr (VEC == 4) {                  // fp32 rows of up to 8192
-    if (nch <= 2048) DBD_MIX(4, 512);
-    else return hipErrorInvalidValue;
-  } else {
-    return hipErrorInvalidValue;
-  }
+  else if (nch <= 1024) DBD_MIX(2, 512);         // bf16 rows up to 8192, fp32 up to 4096
+  else return hipErrorInvalidValue;
 #undef DBD_MIX
   return hipGetLastError();
 }

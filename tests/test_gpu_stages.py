@@ -120,6 +120,26 @@ def test_mix_rmsnorm_strided_layer_major_input():
     assert rel_l2(out[1].cpu().numpy(), ref) < 1e-5
 
 
+@pytest.mark.parametrize("dtype,hidden", [("bf16", 6144), ("bf16", 8192), ("f32", 4096)])
+def test_mix_rmsnorm_wide_rows(dtype, hidden):
+    """Rows past 512 sixteen-byte chunks (the widest rows each dtype allows): two chunks per
+    thread, the target layers loaded one ahead of the mixing instead of all at once."""
+    sh = synth.DrafterShape(hidden=hidden, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1024,
+                            n_layers=3, n_target_layers=5, vocab=512, dtype=dtype)
+    W = synth.make_weights(sh, 5, DEV)
+    T = 13
+    hid = synth.make_hidden(sh, T, 5, 0, DEV)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.empty((sh.n_layers, T, sh.hidden), dtype=dt, device=DEV)
+    dbd.mix_rmsnorm(dbd.model_desc(sh), W["mix_logits"], W["mix_norm_w"], hid, out)
+    torch.cuda.synchronize()
+    Wc = {k: W[k].cpu() for k in ("mix_logits", "mix_norm_w")}
+    tol = 5e-3 if dtype == "bf16" else 1e-5
+    for l in range(sh.n_layers):
+        ref = od.context_features(sh, Wc, l, hid.cpu())
+        assert rel_l2(out[l].float().cpu().numpy(), ref) < tol
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_mix_rmsnorm_sixteen_target_layers_eight_draft_layers(dtype):
     """The mixing kernel at its limits: 16 target layers mixed into 8 draft layers."""
