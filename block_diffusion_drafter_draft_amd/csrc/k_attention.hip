@@ -494,11 +494,12 @@ __global__ __launch_bounds__(128) void attn_stream_combine_kernel(AttnArgs a, in
   const int r = (seg % RB) * kAttnRows + rl;
   if (threadIdx.x >= 4 * dq || r >= R) return;
   const int64_t sidx = (int64_t)n * segs + seg;
-  // one pass over the pieces, eight loads in flight at a time, rescaling the running sums to
-  // each batch's maximum
+  // one pass over the pieces, four loads in flight at a time (a segment rarely has more
+  // pieces; the 52 VGPRs this leaves let every workgroup of the launch be resident at once),
+  // rescaling the running sums to each batch's maximum
   float m = -INFINITY, l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  constexpr int SU = 8;
+  constexpr int SU = 4;
   for (int64_t w = w0; w <= w1; w += SU) {
     float2 ml[SU];
     f32x4 po[SU];
