@@ -931,7 +931,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
 // Thread t owns the groups of 4 columns t and t + 1024; the gain and the residual are loaded
 // with the first RB splits' partials, and the normalised columns go out as 8-byte stores.
 __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e) {
-  constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread, RB = 8;
+  constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread, RB = 4;
   static_assert(NT * MAXG * 4 == kResidNormMaxCols, "row coverage of resid_norm_fits");
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   __shared__ float red[NT / 64];
