@@ -121,12 +121,16 @@ struct EpiArgs {
   int ntiles;
   float* logits;        // optional [M, N] fp32
   // EPI_RESID: the RMSNorm of the updated residual rows, norm_out = T(x / rms(x) * norm_g) (and
-  // the low part of the bf16 pair); done in the split-K reduction of the skinny tiles, else
-  // left to the caller (launch_gemm reports which).  norm_g null: no norm.
+  // the low part of the bf16 pair); done in the split-K reduction of the tiles that can
+  // (gemm_fuses_norm), else left to the caller (launch_gemm reports which).  norm_g null: no
+  // norm.  norm_n_anchor > 0: only the mask rows of each block of norm_block_len rows are
+  // normalised, written compactly (row n * B + b to n * (B - n_anchor) + b - n_anchor).
   const void* norm_g;
   void* norm_out;
   void* norm_out_lo;
   float norm_eps;
+  int norm_block_len;
+  int norm_n_anchor;
 };
 
 // Attention over the cache: every block row of sequence n, head h, attends to cache positions

@@ -977,6 +977,13 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e)
       ss += xv[q][0] * xv[q][0] + xv[q][1] * xv[q][1] + xv[q][2] * xv[q][2] + xv[q][3] * xv[q][3];
     }
   }
+  // the normalised row's place: all rows, or the mask rows of each block, compacted
+  int orow = row;
+  if (e.norm_n_anchor > 0) {
+    const int B = e.norm_block_len, b = row % B;
+    if (b < e.norm_n_anchor) return;              // an anchor row: residual only (uniform)
+    orow = (row / B) * (B - e.norm_n_anchor) + b - e.norm_n_anchor;
+  }
   ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
@@ -984,8 +991,8 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e)
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) tot += red[w];
   const float inv = rsqrtf(tot / (float)N + e.norm_eps);
-  bf16* o = reinterpret_cast<bf16*>(e.norm_out) + (int64_t)row * N;
-  bf16* ol = e.norm_out_lo ? reinterpret_cast<bf16*>(e.norm_out_lo) + (int64_t)row * N : nullptr;
+  bf16* o = reinterpret_cast<bf16*>(e.norm_out) + (int64_t)orow * N;
+  bf16* ol = e.norm_out_lo ? reinterpret_cast<bf16*>(e.norm_out_lo) + (int64_t)orow * N : nullptr;
 #pragma unroll
   for (int q = 0; q < MAXG; ++q) {
     const int i = (tid + q * NT) * 4;

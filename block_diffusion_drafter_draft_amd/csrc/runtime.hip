@@ -745,20 +745,26 @@ int draft_block(const dbd_model_desc* desc, const dbd_weights* w, int32_t batch,
       e.kind = EPI_RESID;
       e.C = b.x;
       e.ldc = H;
-      // the next layer's attention norm (the final norm after the last layer takes only the
-      // mask rows and stays separate)
-      if (l + 1 < d.n_layers)
+      // the next layer's attention norm, or after the last layer the final norm of the mask
+      // rows, written compactly for the LM head
+      if (l + 1 < d.n_layers) {
         set_norm(&e, (const char*)w->attn_norm_w + (int64_t)(l + 1) * H * es, b.xn, b.xn_lo,
                  d.rms_eps);
+      } else {
+        set_norm(&e, w->final_norm_w, b.xn, b.xn_lo, d.rms_eps);
+        e.norm_block_len = B;
+        e.norm_n_anchor = n_anchor;
+      }
       HIP_STAGE(DBD_STAGE_GEMM_DOWN, st, launch_gemm(d.dtype, g, e, 1, st, g_ov_cfg[DBD_STAGE_GEMM_DOWN],
                                                   g_ov_split[DBD_STAGE_GEMM_DOWN], &normed));
     }
   }
   (void)cw;
 
-  // 3. final norm on the mask rows, LM head
-  HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, w->final_norm_w, b.xn, b.xn_lo, Md, H,
-                                                   d.rms_eps, B, n_anchor, st));
+  // 3. final norm on the mask rows (unless the last down projection wrote it), LM head
+  if (!normed)
+    HIP_STAGE(DBD_STAGE_ROWNORM, st, launch_rmsnorm(d.dtype, b.x, w->final_norm_w, b.xn, b.xn_lo,
+                                                     Md, H, d.rms_eps, B, n_anchor, st));
   const bool sampling = temperature > 0.f;
   float* logits = logits_out ? logits_out : (sampling ? b.logits : nullptr);
   {
