@@ -342,9 +342,6 @@ int check_desc(const dbd_model_desc* d) {
     return fail(DBD_ERR_ARG, "ctx_fusion, mix_raw and ctx_shared_kv must be 0 or 1");
   if (d->ctx_fusion && d->mix_raw)
     return fail(DBD_ERR_ARG, "mix_raw applies to the mixing path only (ctx_fusion == 0)");
-  if (d->n_target_layers > 0 && !d->ctx_fusion && d->n_layers > 8)
-    return fail(DBD_ERR_UNSUPPORTED, "target mixing supports at most 8 draft layers (got %d)",
-                d->n_layers);
   if (d->act_pairs != 0 && d->act_pairs != 1)
     return fail(DBD_ERR_ARG, "act_pairs must be 0 or 1");
   if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.0))

@@ -140,11 +140,12 @@ def test_mix_rmsnorm_wide_rows(dtype, hidden):
         assert rel_l2(out[l].float().cpu().numpy(), ref) < tol
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_mix_rmsnorm_sixteen_target_layers_eight_draft_layers(dtype):
-    """The mixing kernel at its limits: 16 target layers mixed into 8 draft layers."""
+@pytest.mark.parametrize("dtype,n_layers", [("bf16", 8), ("f32", 8), ("bf16", 12)])
+def test_mix_rmsnorm_sixteen_target_layers(dtype, n_layers):
+    """The mixing kernel at its target-layer limit: 16 target layers mixed into 8 and 12 draft
+    layers (one workgroup per token and draft layer, so the draft layers are not bounded)."""
     sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
-                            n_layers=8, n_target_layers=16, vocab=512, dtype=dtype)
+                            n_layers=n_layers, n_target_layers=16, vocab=512, dtype=dtype)
     W = synth.make_weights(sh, 3, DEV)
     T = 37
     hid = synth.make_hidden(sh, T, 3, 0, DEV)
