@@ -75,11 +75,13 @@ def test_gemm_nt_requested_split(cfg, split, M, N, K):
     assert torch.equal(C1, C2)
 
 
+@pytest.mark.parametrize("T", [77, 215])
 @pytest.mark.parametrize("name", ["tiny-fp32", "qwen3-8b", "gpt-oss-20b"])
-def test_mix_rmsnorm(name):
+def test_mix_rmsnorm(name, T):
+    """77 tokens: one workgroup per token and draft layer; 215 (the Qwen3-8B step's ingest):
+    one workgroup per token for all its draft layers."""
     sh = synth.workload(name).shape
     W = synth.make_weights(sh, 0, DEV)
-    T = 77
     hid = synth.make_hidden(sh, T, 0, 0, DEV)
     out = torch.empty((sh.n_layers, T, sh.hidden), dtype=hid.dtype, device=DEV)
     dbd.mix_rmsnorm(dbd.model_desc(sh), W["mix_logits"], W["mix_norm_w"], hid, out)
@@ -143,11 +145,12 @@ def test_mix_rmsnorm_wide_rows(dtype, hidden):
 @pytest.mark.parametrize("dtype,n_layers", [("bf16", 8), ("f32", 8), ("bf16", 12)])
 def test_mix_rmsnorm_sixteen_target_layers(dtype, n_layers):
     """The mixing kernel at its target-layer limit: 16 target layers mixed into 8 and 12 draft
-    layers (one workgroup per token and draft layer, so the draft layers are not bounded)."""
+    layers.  37 tokens take one workgroup per token and draft layer; 150 tokens (the 12-layer
+    case) take one workgroup per token and group of eight draft layers, two groups (8 + 4)."""
     sh = synth.DrafterShape(hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=2048,
                             n_layers=n_layers, n_target_layers=16, vocab=512, dtype=dtype)
     W = synth.make_weights(sh, 3, DEV)
-    T = 37
+    T = 37 if n_layers == 8 else 150
     hid = synth.make_hidden(sh, T, 3, 0, DEV)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     out = torch.empty((sh.n_layers, T, sh.hidden), dtype=dt, device=DEV)
