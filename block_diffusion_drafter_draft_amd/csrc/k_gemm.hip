@@ -344,6 +344,10 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
   // (one round of 198 units at the SpecDiff-2 shape; 2.37 against 3.76 ms per call for the
   // 128 x 128 tile)
   if (pair && M <= 128 && gateup) return 15;
+  // the LM head with a pair on at most 128 rows: the register-staged 256 x 128 tile as pair rows
+  // (SpecDiff-2 shape, 128 rows, V = 152,064: 0.338 against 0.374 ms per step for the four-wave
+  // 128 x 128 pair tile)
+  if (pair && M <= 128 && (kind == EPI_ARGMAX || kind == EPI_STORE_F32) && N >= 65536) return 16;
   if (M >= 64 && (pair || kind == EPI_QKV || kind == EPI_CTXKV)) return 10;
   // at most 128 rows without a pair: 128-row tiles rather than half-empty 256-row ones
   // (GPT-OSS-20B shape, 128 and 112 rows: gate/up 0.418 -> 0.367 ms per step with the
