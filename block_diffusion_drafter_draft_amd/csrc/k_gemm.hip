@@ -382,19 +382,22 @@ static int choose_cfg(int kind, int M, int N, int K, int batch, int gateup, int 
 // residual epilogues; within about 10% of the measured time).  A unit (one workgroup) costs a
 // fixed start plus a time per k stage; the stage time is set by the bytes each CU pulls from L2
 // per stage, and units beyond one per CU share it: in whole rounds for the one-per-CU tiles (3,
-// 16), proportionally past 192 units for the 128 x 128 tile, two of which fit on a CU.  A split
-// adds the reduction kernel (its launch plus writing and reading the fp32 partials); without a
-// split the rotation and cache-scatter epilogues run inside the main kernel (about 4.2 us per
-// million outputs for Q/K/V, 1.3 for the context K/V).
+// 16), proportionally past 192 units for the 128 x 128 tile, two of which fit on a CU (with a
+// bf16 pair one, in whole rounds).  A split adds the reduction kernel (its launch plus writing
+// and reading the fp32 partials); without a split the rotation and cache-scatter epilogues run
+// inside the main kernel (about 4.2 us per million outputs for Q/K/V, 1.3 for the context K/V).
 //   3: pipelined 64 x 128, 64-wide stages: 6.7 + 0.455 per stage
-//   10: four-wave 128 x 128, 32-wide stages: 5.3 + 0.356 per stage (x 1.5 with a bf16 pair A)
+//   10: four-wave 128 x 128, 32-wide stages: 5.3 + 0.356 per stage (x 1.5 with a bf16 pair A,
+//       whose units then share no CU: whole rounds of 256)
 //   16: register-staged eight-wave 256 x 128, 64-wide stages: 10.4 + 0.88 per stage
 static double model_us(int kind, int cfg, int M, int Nv, int K, int batch, int S, bool pair,
                        bool norm) {
   const double units = (double)ceil_div(M, kCfgBM[cfg]) * ceil_div(Nv, kCfgBN[cfg]) * batch * S;
   double t;
   if (cfg == 10)
-    t = 5.3 + 0.356 * (pair ? 1.5 : 1.0) * (K / 32.0 / S) * std::max(1.0, units / 192.0);
+    // with a bf16 pair the tile's six-stage ring (144 KB of LDS) leaves one unit per CU
+    t = 5.3 + 0.356 * (pair ? 1.5 : 1.0) * (K / 32.0 / S) *
+              (pair ? std::ceil(units / 256.0) : std::max(1.0, units / 192.0));
   else if (cfg == 16)
     t = 10.4 + 0.88 * (K / 64.0 / S) * std::ceil(units / 256.0);
   else
