@@ -1157,7 +1157,8 @@ hipError_t launch_verify_sample(const float* tl, const float* dl, const int32_t*
 // correctly rounded, kept in LDS; then thread k scores draft k, S = sum_m prod_{j<=m} p_j in
 // fp64 in position order (the same operations in the same order as one thread per draft doing
 // everything, so the scores are unchanged).  K, G <= 64.
-constexpr int SF_THREADS = 256;
+constexpr int SF_THREADS = 1024;
+constexpr int SF_TPR = 4;                 // threads per (draft, row): the chunk sums split 4 ways
 __global__ __launch_bounds__(SF_THREADS) void select_finalize_kernel(
     const float* __restrict__ x, int V, int nch, const uint64_t* __restrict__ zpart,
     const float* __restrict__ row_max, const int32_t* __restrict__ row_arg,
@@ -1172,15 +1173,24 @@ __global__ __launch_bounds__(SF_THREADS) void select_finalize_kernel(
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  for (int r = tid; r < K * G; r += SF_THREADS) {
-    const int k = r / G, j = r % G;
+  // Z of each (draft k, row j): SF_TPR neighbouring lanes add every SF_TPR-th chunk, then
+  // combine (integer sums: the order does not change them)
+  for (int r0 = 0; r0 < K * G; r0 += SF_THREADS / SF_TPR) {
+    const int r = r0 + tid / SF_TPR, part = tid % SF_TPR;
+    const bool live = r < K * G;
+    const int k = live ? r / G : 0, j = live ? r % G : 0;
     const int64_t row = ((int64_t)n * K + k) * R + j;
+    uint64_t q = 0;
+    if (live && part == 0) {
+      const int tok = drafts[((int64_t)n * K + k) * G + j];
+      if (tok >= 0 && tok < V) q = weight_q(x[row * V + tok], row_max[row], 1.0f);
+    }
     uint64_t Z = 0;
-    for (int c = 0; c < nch; ++c) Z += zpart[row * nch + c];
-    const int tok = drafts[((int64_t)n * K + k) * G + j];
-    const uint64_t q = (tok >= 0 && tok < V) ? weight_q(x[row * V + tok], row_max[row], 1.0f)
-                                             : 0;
-    s_p[r] = __ddiv_rn((double)q, (double)Z);
+    if (live)
+      for (int c = part; c < nch; c += SF_TPR) Z += zpart[row * nch + c];
+#pragma unroll
+    for (int o = 1; o < SF_TPR; o <<= 1) Z += __shfl_xor(Z, o, 64);
+    if (live && part == 0) s_p[r] = __ddiv_rn((double)q, (double)Z);
   }
   // non-finite flags of every row of the sequence (K x R rows)
   int bad = 0;
