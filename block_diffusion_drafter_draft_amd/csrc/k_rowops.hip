@@ -273,6 +273,10 @@ hipError_t launch_mix_rmsnorm(int dtype, const void* hid, int64_t ts, int64_t ls
 }
 
 // ------------------------------------------------------------------ embedding gather
+// One workgroup per block row: the row's token embedding (ids clamped to the vocabulary) becomes
+// the fp32 residual row x.  With a gain g the kernel also writes the first layer's attention
+// RMSNorm of the row, which it holds in registers, as rmsnorm_kernel would (out, and the bf16
+// low part in out_lo).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
                                                     const T* __restrict__ E, int H, int V,
