@@ -900,12 +900,31 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
       v[q] += part[offl[q]];
     }
   }
-  for (int sp = 1; sp < S; ++sp) {
-    const f32x4* ps = part + (int64_t)sp * NW * FR;
+  // the later splits in batches of RB, every load of a batch issued before any is added (the
+  // additions keep split order); RB shrinks with the loads per split so the batch fits the
+  // registers
+  constexpr int LPS = UPT * (PR ? 2 : 1);                   // f32x4 loads per split
+  constexpr int RB = LPS <= 4 ? 4 : (LPS <= 8 ? 2 : 1);
+  for (int sp0 = 1; sp0 < S; sp0 += RB) {
+    f32x4 w[RB][UPT], wl[PR ? RB : 1][PR ? UPT : 1];
 #pragma unroll
-    for (int q = 0; q < UPT; ++q) {
-      v[q] += ps[off[q]];
-      if constexpr (PR) v[q] += ps[offl[q]];
+    for (int b = 0; b < RB; ++b) {
+      if (sp0 + b >= S) break;
+      const f32x4* ps = part + (int64_t)(sp0 + b) * NW * FR;
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        w[b][q] = ps[off[q]];
+        if constexpr (PR) wl[b][q] = ps[offl[q]];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if (sp0 + b >= S) break;
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        v[q] += w[b][q];
+        if constexpr (PR) v[q] += wl[b][q];
+      }
     }
   }
 #pragma unroll
