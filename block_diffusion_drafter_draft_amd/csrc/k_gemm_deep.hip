@@ -949,8 +949,12 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, EpiArgs e)
 // x / sqrt(mean(x^2) + eps) * g, with the low part of the bf16 pair when norm_out_lo is set.
 // Thread t owns the groups of 4 columns t and t + 1024; the gain and the residual are loaded
 // with the first RB splits' partials, and the normalised columns go out as 8-byte stores.
+// RB splits' loads are in flight together: 4 keeps the kernel at 63 VGPRs, so two rows share a
+// CU (512 rows in one round); 8 (95 VGPRs, one row per CU) halves the round trips when the rows
+// fit on the CUs anyway.
+template <int RB>
 __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e) {
-  constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread, RB = 4;
+  constexpr int NT = kResidNormThreads, MAXG = kResidNormVecsPerThread;
   static_assert(NT * MAXG * 4 == kResidNormMaxCols, "row coverage of resid_norm_fits");
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   __shared__ float red[NT / 64];
@@ -1028,6 +1032,13 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(GemmArgs a, EpiArgs e)
   }
 }
 
+static void launch_resid_norm(const GemmArgs& a, const EpiArgs& e, hipStream_t s) {
+  if (a.M <= 256)
+    hipLaunchKernelGGL(resid_norm_kernel<8>, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+  else
+    hipLaunchKernelGGL(resid_norm_kernel<4>, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+}
+
 template <int BM, int BN, int WGM, int WGN, int KIND, bool PR = false>
 static void launch_reduce(const GemmArgs& a, const EpiArgs& e, int batch, hipStream_t s) {
   const int grid = ceil_div(a.M, BM) * ceil_div(a.N, BN) * (BM / ReduceCfg<BN>::TM);
@@ -1043,7 +1054,7 @@ static void launch_w8r(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) {
   hipLaunchKernelGGL((gemm_w8r_kernel<BN, KIND, WGM, PR>), dim3(units, 1, batch), dim3(512),
                      0, s, a, e);
   if (S > 1 && KIND == EPI_RESID && !PR && e.norm_g)
-    hipLaunchKernelGGL(resid_norm_kernel, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+    launch_resid_norm(a, e, s);
   else if (S > 1)
     launch_reduce<256, BN, WGM, 8 / WGM, KIND, PR>(a, e, batch, s);
 }
@@ -1056,7 +1067,7 @@ static void launch_skinny(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, KIND, SPLITA>), dim3(units, 1, batch), dim3(256), 0,
                      s, a, e);
   if (S > 1 && KIND == EPI_RESID && e.norm_g)
-    hipLaunchKernelGGL(resid_norm_kernel, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+    launch_resid_norm(a, e, s);
   else if (S > 1)
     launch_reduce<MT, 128, 1, 4, KIND>(a, e, batch, s);
 }
@@ -1079,7 +1090,7 @@ static void launch_deep(GemmArgs a, const EpiArgs& e, int batch, hipStream_t s) 
   hipLaunchKernelGGL((gemm_big_kernel<BM, BN, NS, KIND, SPLITA>), dim3(units, 1, batch),
                      dim3(256), 0, s, a, e);
   if (S > 1 && KIND == EPI_RESID && e.norm_g)
-    hipLaunchKernelGGL(resid_norm_kernel, dim3(a.M), dim3(kResidNormThreads), 0, s, a, e);
+    launch_resid_norm(a, e, s);
   else if (S > 1)
     launch_reduce<BM, BN, 2, 2, KIND>(a, e, batch, s);
 }
