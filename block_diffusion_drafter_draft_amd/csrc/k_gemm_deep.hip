@@ -617,6 +617,77 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
       for (int j = 0; j < C::NI; ++j) mine[(i * C::NI + j) * 64] = acc[i][j];
     return;
   }
+  if constexpr (KIND == EPI_ARGMAX && !PR) {
+    if (!e.logits) {
+      // The argmax straight from the accumulators, without the tile's LDS round trip.  Lane
+      // (fk, fr) holds rows wm*WTM + 16i + 4fk + r (k = 4i + r) at columns wn*WTN + 16j + fr.
+      // Each lane first reduces its NI columns per row; then the 16 lanes of a row group
+      // reduce by halving: at the step with lane offset o, a lane keeps half of its remaining
+      // rows (the upper half if its bit o is set), sends the other half to lane ^ o and folds
+      // in what it receives, so after four steps it holds the wave's result for two rows.
+      // The WGN waves along N then meet in LDS.  Out-of-range columns never enter; the
+      // lowest-index rule of argmax_combine makes the result independent of the order.
+      constexpr int KR = C::MI * 4;                       // rows per lane
+      static_assert(KR % 16 == 0, "rows per lane");
+      float bv[KR];
+      int bi[KR];
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bv[4 * i + r] = -INFINITY;
+          bi[4 * i + r] = 0x7fffffff;
+        }
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j) {
+        const int col = n0 + wn * C::WTN + j * 16 + fr;
+        if (col < N) {
+#pragma unroll
+          for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) argmax_combine(bv[4 * i + r], bi[4 * i + r], acc[i][j][r], col);
+        }
+      }
+#pragma unroll
+      for (int o = 1, h = KR / 2; o < 16; o <<= 1, h >>= 1) {
+        const bool up = (fr & o) != 0;
+#pragma unroll
+        for (int k = 0; k < h; ++k) {
+          const float sv = up ? bv[k] : bv[k + h];
+          const int si = up ? bi[k] : bi[k + h];
+          const float ov = __shfl_xor(sv, o, 64);
+          const int oi = __shfl_xor(si, o, 64);
+          if (up) {
+            bv[k] = bv[k + h];
+            bi[k] = bi[k + h];
+          }
+          argmax_combine(bv[k], bi[k], ov, oi);
+        }
+      }
+      // lane fr now holds the KR / 16 rows from k = kb on: the step at offset 2^s kept the
+      // upper half (KR / 2^(s+1) rows further on) exactly when bit s of fr is set
+      const int kb = (KR / 2) * (fr & 1) + (KR / 4) * ((fr >> 1) & 1) +
+                     (KR / 8) * ((fr >> 2) & 1) + (KR / 16) * ((fr >> 3) & 1);
+      float* sv = (float*)smem;                           // [WGN][BM]
+      int* si = (int*)(smem + C::WGN * BM * 4);
+#pragma unroll
+      for (int q = 0; q < KR / 16; ++q) {
+        const int k = kb + q, row = wm * C::WTM + 16 * (k >> 2) + 4 * fk + (k & 3);
+        sv[wn * BM + row] = bv[q];
+        si[wn * BM + row] = bi[q];
+      }
+      __syncthreads();
+      if (tid < BM && m0 + tid < M) {
+        float v = sv[tid];
+        int ix = si[tid];
+#pragma unroll
+        for (int w = 1; w < C::WGN; ++w) argmax_combine(v, ix, sv[w * BM + tid], si[w * BM + tid]);
+        e.part_val[(int64_t)(m0 + tid) * e.ntiles + tn] = v;
+        e.part_idx[(int64_t)(m0 + tid) * e.ntiles + tn] = ix;
+      }
+      return;
+    }
+  }
   store_tile([&](int i, int j) { return acc[i][j]; });
 }
 
