@@ -439,6 +439,41 @@ def test_lm_head_argmax_without_logits_matches(batch, cfg):
             dbd.gemm_override("gemm_lmhead", -1, 0)
 
 
+@pytest.mark.parametrize("cfg", [14, 15, 16])
+def test_lm_head_argmax_ties_go_to_the_lowest_index(cfg):
+    """Every LM-head weight row repeats row v mod 37, so each logit row takes 37 distinct values
+    and its maximum sits at about 81 columns (in every lane group, wave and column tile of the
+    tile), all bit-identical.  The draft is the lowest of them, so it is below 37, with and
+    without logits (the register argmax then folds the ties in another order)."""
+    sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
+                            n_layers=2, n_target_layers=2, vocab=3000, dtype="bf16")
+    wl = synth.Workload(name="lm-head-ties", shape=sh, batch=20, block_len=16, n_anchor=1,
+                        n_drafts=1, temperature=0.0, ctx_lo=60, ctx_hi=140, ctx_source="hidden",
+                        verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=4)
+    print(f"draft_block workload=lm-head-ties lmhead_cfg={cfg}", flush=True)
+    dbd.gemm_override("gemm_lmhead", cfg, 1)
+    try:
+        case = Case(wl, dev=DEV)
+        lm = case.W["lm_head"]
+        lm.copy_(lm[torch.arange(sh.vocab, device=DEV) % 37].clone())
+        case.fill_cache()
+        drafts, logits, status = case.step()
+        torch.cuda.synchronize()
+        assert torch.all(status == 0)
+        _check_drafts_property(case, drafts, logits)
+        lg = logits.cpu().numpy()
+        assert np.array_equal(lg[..., :37], lg[..., 37:74])
+        drafts2, _, status2 = case.step(logits=False)
+        torch.cuda.synchronize()
+        assert torch.all(status2 == 0)
+        assert torch.equal(drafts, drafts2)
+        d = drafts2[:, 0].cpu().numpy()
+        d = d[d >= 0]                                   # -1 marks rows past a sequence's end
+        assert d.size > 0 and d.max() < 37, d.max()
+    finally:
+        dbd.gemm_override("gemm_lmhead", -1, 0)
+
+
 @pytest.mark.parametrize("name", ["qwen3-4b-tiny-batch", "specdiff-tiny-batch"])
 @pytest.mark.parametrize("workgroups", [1, 5])
 def test_sequence_placement_in_the_batch_is_invisible(name, workgroups):
