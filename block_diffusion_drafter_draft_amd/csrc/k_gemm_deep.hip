@@ -624,8 +624,8 @@ __global__ __launch_bounds__(512) void gemm_w8r_kernel(GemmArgs a, EpiArgs e) {
       // Each lane first reduces its NI columns per row; then the 16 lanes of a row group
       // reduce by halving: at the step with lane offset o, a lane keeps half of its remaining
       // rows (the upper half if its bit o is set), sends the other half to lane ^ o and folds
-      // in what it receives, so after four steps it holds the wave's result for two rows.
-      // The WGN waves along N then meet in LDS.  Out-of-range columns never enter; the
+      // in what it receives, so after four steps it holds the wave's result for KR / 16 rows
+      // (two on the 2 x 4 wave grid, one on 4 x 2).  The WGN waves along N then meet in LDS.  Out-of-range columns never enter; the
       // lowest-index rule of argmax_combine makes the result independent of the order.
       constexpr int KR = C::MI * 4;                       // rows per lane
       static_assert(KR % 16 == 0, "rows per lane");
