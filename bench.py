@@ -241,7 +241,7 @@ def measured_mfma_busy(stage):
 # Epilogue kind (a template argument of every GEMM kernel) of each timed GEMM stage whose
 # launches all use one epilogue, and the kernel name fragment of the other stages.
 STAGE_EPILOGUE = {"gemm_gateup": 4, "gemm_lmhead": 5, "gemm_qkv": 2, "gemm_ctxkv": 3}
-STAGE_KERNEL = {"attn": "attn_bf16_kernel", "mix": "mix_rmsnorm_kernel"}
+STAGE_KERNEL = {"attn": "attn_stream_kernel", "mix": "mix_rmsnorm_kernel"}
 # position of the epilogue kind in each GEMM kernel's template argument list
 KIND_ARG = {"gemm_bf16_kernel": 3, "gemm_big_kernel": 3, "gemm_w8_kernel": 3,
             "gemm_w8r_kernel": 1}
