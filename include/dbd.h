@@ -41,7 +41,7 @@ enum {
   DBD_ERR_SHAPE = -2,        /* dimensions inconsistent or not supported by the kernels */
   DBD_ERR_CAPACITY = -3,     /* KV-cache capacity too small for the requested work */
   DBD_ERR_WORKSPACE = -4,    /* workspace NULL, misaligned (256 B) or smaller than required */
-  DBD_ERR_UNSUPPORTED = -5,  /* valid request outside what this build implements */
+  DBD_ERR_UNSUPPORTED = -5,  /* valid request outside what the library implements */
   DBD_ERR_HIP = -6           /* a HIP runtime call failed (message has the HIP error) */
 };
 
