@@ -405,21 +405,24 @@ def test_pair_rows_tiles_match_oracle(batch, ov):
             dbd.gemm_override(st, -1, 0)
 
 
+@pytest.mark.parametrize("vocab", [3000, 200])
 @pytest.mark.parametrize("batch", [5, 20])
 @pytest.mark.parametrize("cfg", [None, 14, 15, 16])
-def test_lm_head_argmax_without_logits_matches(batch, cfg):
+def test_lm_head_argmax_without_logits_matches(batch, cfg, vocab):
     """Greedy drafting with no logits output: the register-staged LM-head tiles (256, 192 and
     128 columns, unsplit) then take each row's argmax straight from their accumulators instead
     of from the tile staged in LDS.  75 and 300 block rows (one and two row tiles, ragged) over
-    a 3,000-token vocabulary (a ragged last column tile for every width): the drafts equal those
-    of the same step with logits, which equal the argmax of those logits, which match the
-    oracle."""
+    a 3,000-token vocabulary (a ragged last column tile for every width) and a 200-token one
+    (a single column tile, in which the 256-column tile's last wave along N sees no column of
+    the vocabulary): the drafts equal those of the same step with logits, which equal the
+    argmax of those logits, which match the oracle."""
     sh = synth.DrafterShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1024,
-                            n_layers=2, n_target_layers=2, vocab=3000, dtype="bf16")
+                            n_layers=2, n_target_layers=2, vocab=vocab, dtype="bf16")
     wl = synth.Workload(name="lm-head-argmax", shape=sh, batch=batch, block_len=16, n_anchor=1,
                         n_drafts=1, temperature=0.0, ctx_lo=60, ctx_hi=140, ctx_source="hidden",
                         verify="greedy", verify_rows=16, planted_alpha=0.8, fixed_new=4)
-    print(f"draft_block workload=lm-head-argmax batch={batch} lmhead_cfg={cfg}", flush=True)
+    print(f"draft_block workload=lm-head-argmax batch={batch} lmhead_cfg={cfg} vocab={vocab}",
+          flush=True)
     if cfg is not None:
         dbd.gemm_override("gemm_lmhead", cfg, 1)
     try:
